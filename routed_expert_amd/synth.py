@@ -1,0 +1,168 @@
+"""Seeded synthetic inputs for the routed-expert MoE layer.
+
+This module only draws random numbers and stores them in the layer's interchange
+layout. It contains none of the layer's arithmetic (no routing, no dequantisation,
+no matrix products), so both the HIP path and the CPU oracle can be fed from it.
+
+Interchange layout of one layer (E routed experts, S in {0,1} shared experts stacked
+after them as expert index E, hidden H, expert intermediate I, group size 64):
+
+  router_w  float32 [E, H]              router_b  float32 [E] or None
+  int4 format (``fmt == "int4"``):
+    w13_q  uint8  [E+S, 2I, H/2]   codes; byte j holds element 2j in its low nibble
+                                   and element 2j+1 in its high nibble
+    w13_s  uint16 [E+S, 2I, H/64]  bf16 bit patterns of the per-group scale
+    w13_b  uint16 [E+S, 2I, H/64]  bf16 bit patterns of the per-group bias
+    w2_q   uint8  [E+S, H, I/2]    w2_s / w2_b uint16 [E+S, H, I/64]
+  fp32 format (``fmt == "f32"``):
+    w13    float32 [E+S, 2I, H]    w2 float32 [E+S, H, I]
+
+Rows 0..I-1 of w13 are the gate projection, rows I..2I-1 the up projection.
+Activations are returned as bf16 bit patterns (uint16) for the bf16 configurations and
+float32 for the fp32 configuration.
+
+Workload shapes follow the Qwen3.6-35B-A3B MoE layer described in "Optimizing
+On-Device Inference for Apple Silicon" (section "Qwen creates three distinct workload
+shapes": 256 routed experts, eight selected, one shared) with the int4 group-64 format
+of its section "Dequantize weights during matrix multiplication".
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+GROUP = 64
+# standard deviation of a uniform 4-bit code in 0..15: sqrt((16**2 - 1) / 12)
+NIBBLE_STD = math.sqrt(21.25)
+
+
+def f32_to_bf16_bits(a) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest, ties to even); return uint16 bits."""
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+    u = a.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float32."""
+    b = np.ascontiguousarray(np.asarray(b, dtype=np.uint16))
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclasses.dataclass
+class Layer:
+    """One MoE layer in interchange layout (host numpy arrays)."""
+
+    hidden: int
+    inter: int
+    n_experts: int
+    top_k: int
+    n_shared: int
+    fmt: str  # "int4" or "f32"
+    router_w: np.ndarray
+    router_b: np.ndarray | None = None
+    w13_q: np.ndarray | None = None
+    w13_s: np.ndarray | None = None
+    w13_b: np.ndarray | None = None
+    w2_q: np.ndarray | None = None
+    w2_s: np.ndarray | None = None
+    w2_b: np.ndarray | None = None
+    w13: np.ndarray | None = None
+    w2: np.ndarray | None = None
+
+    @property
+    def n_total(self) -> int:
+        return self.n_experts + self.n_shared
+
+    def expert_bytes(self) -> int:
+        """Stored bytes of one expert (codes + scales + biases, or fp32 values)."""
+        H, I = self.hidden, self.inter
+        if self.fmt == "f32":
+            return 3 * H * I * 4
+        codes = 2 * I * H // 2 + H * I // 2
+        groups = 2 * I * H // GROUP + H * I // GROUP
+        return codes + 2 * 2 * groups
+
+
+def _int4_block(rng, rows_shape, K, scale_mag):
+    codes = rng.integers(0, 256, size=(*rows_shape, K // 2), dtype=np.uint8)
+    s = (rng.uniform(0.5, 1.5, size=(*rows_shape, K // GROUP)) * scale_mag).astype(np.float32)
+    s_bits = f32_to_bf16_bits(s)
+    s_val = bf16_bits_to_f32(s_bits)
+    b = (-s_val * rng.uniform(6.5, 8.5, size=s_val.shape)).astype(np.float32)
+    return codes, s_bits, f32_to_bf16_bits(b)
+
+
+def make_int4_layer(seed: int, hidden=2048, inter=512, n_experts=256, top_k=8,
+                    n_shared=1, router_std=0.02, weight_std=0.02,
+                    router_bias: np.ndarray | None = None) -> Layer:
+    """Int4 group-64 layer. Draw order per seed: router, W13 codes/scales/biases,
+    W2 codes/scales/biases (expert index n_experts is the shared expert)."""
+    assert hidden % GROUP == 0 and inter % GROUP == 0
+    rng = np.random.default_rng(seed)
+    E, H, I, n = n_experts, hidden, inter, n_experts + n_shared
+    router_w = rng.normal(0.0, router_std, size=(E, H)).astype(np.float32)
+    mag = weight_std / NIBBLE_STD
+    w13_q, w13_s, w13_b = _int4_block(rng, (n, 2 * I), H, mag)
+    w2_q, w2_s, w2_b = _int4_block(rng, (n, H), I, mag)
+    rb = None if router_bias is None else np.ascontiguousarray(router_bias, dtype=np.float32)
+    return Layer(H, I, E, top_k, n_shared, "int4", router_w, rb,
+                 w13_q=w13_q, w13_s=w13_s, w13_b=w13_b, w2_q=w2_q, w2_s=w2_s, w2_b=w2_b)
+
+
+def make_f32_layer(seed: int, hidden=128, inter=64, n_experts=256, top_k=8, n_shared=1,
+                   std=0.05) -> tuple[Layer, np.random.Generator]:
+    """Unquantised fp32 layer; returns the generator so activations continue the stream."""
+    rng = np.random.default_rng(seed)
+    E, H, I, n = n_experts, hidden, inter, n_experts + n_shared
+    router_w = rng.normal(0.0, std, size=(E, H)).astype(np.float32)
+    w13 = rng.normal(0.0, std, size=(n, 2 * I, H)).astype(np.float32)
+    w2 = rng.normal(0.0, std, size=(n, H, I)).astype(np.float32)
+    return Layer(H, I, E, top_k, n_shared, "f32", router_w, None, w13=w13, w2=w2), rng
+
+
+def zipf_router_bias(n_experts=256, hidden=2048, router_std=0.02, gamma=0.7, s=1.1,
+                     seed=1) -> np.ndarray:
+    """Per-expert router bias whose induced popularity decays like rank**-s.
+
+    b_e = -gamma * sigma_z * s * ln(rank_e), sigma_z = router_std * sqrt(hidden), with
+    rank a seeded permutation of 1..n_experts."""
+    rank = np.random.default_rng(seed).permutation(n_experts) + 1
+    sigma_z = router_std * math.sqrt(hidden)
+    return (-gamma * sigma_z * s * np.log(rank)).astype(np.float32)
+
+
+def bf16_activations(seed: int, shape) -> np.ndarray:
+    """bf16 bit patterns of standard normal draws."""
+    return f32_to_bf16_bits(np.random.default_rng(seed).standard_normal(shape).astype(np.float32))
+
+
+# ---- named workloads -----------------------------------------------------------------
+
+def tiny_config(seed: int = 0):
+    """fp32 layer T=64, H=128, I=64, E=256, k=8, one shared expert; weights ~N(0,0.05),
+    x ~ N(0,1), all from one generator seeded with ``seed``."""
+    layer, rng = make_f32_layer(seed)
+    x = rng.standard_normal((64, layer.hidden)).astype(np.float32)
+    return layer, x
+
+
+def decode_layer(seed: int = 0) -> Layer:
+    """Decode-shaped layer: H=2048, I=512, E=256, k=8, S=1, int4 g64, router ~N(0,0.02)."""
+    return make_int4_layer(seed)
+
+
+def decode_token(t: int, hidden: int = 2048) -> np.ndarray:
+    """bf16 bits of decode token t (1 x H)."""
+    return bf16_activations(1_000_000 + t, (1, hidden))
+
+
+def prefill_x(T: int = 4096, hidden: int = 2048, seed: int = 2) -> np.ndarray:
+    return bf16_activations(seed, (T, hidden))
+
+
+def skewed_layer(seed: int = 0, gamma: float = 0.7) -> Layer:
+    return make_int4_layer(seed, router_bias=zipf_router_bias(gamma=gamma))
