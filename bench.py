@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert MoE layer on one MI355X.
+
+Headline workload: batch-1 decode of one MoE layer (T=1; hidden 2048, 256 routed
+experts top-8 plus one shared expert, SwiGLU intermediate 512, int4 group-64 weights
+with bf16 scale and bias; fp32 router). One step is one token through the whole layer
+(router GEMV + top-8 + 8+1 expert GEMVs + combine). Weights are cache-cold: 20 seeded
+copies of the layer (9.1 GB) rotate per token, so a copy is reused only after 19 other
+tokens have streamed 342 MB, more than the 256 MB Infinity Cache plus L2. Steps are
+replayed from a HIP graph (the host enqueues ahead and never synchronises in between).
+
+Also reported in the same line: prefill of T=4096 tokens with near-uniform routing and
+with Zipf(1.1)-skewed routing (tokens/s and fraction of the dense bf16 MFMA peak), the
+dominant kernel's roofline (durations from HIP events on its stream) and the CPU
+oracle's throughput on a bounded sample of the decode tokens.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-prefill]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+H, I, E, K_TOP, S = 2048, 512, 256, 8, 1
+N_COPIES = 20
+N_TOKENS = 1000
+
+
+def expert_bytes():
+    w13 = 2 * I * H // 2 + 2 * (2 * I * H // 64) * 2
+    w2 = H * I // 2 + 2 * (H * I // 64) * 2
+    return w13, w2
+
+
+def decode_bytes_per_token():
+    w13, w2 = expert_bytes()
+    return E * H * 4 + (K_TOP + S) * (w13 + w2) + H * 2 * 2
+
+
+def prefill_flops_per_token():
+    return (K_TOP + S) * 3 * 2 * H * I + 2 * H * E
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(kernel, src):
+    """HBM traffic per launch from a committed rocprofv3 --pmc summary, if the kernel
+    source has not changed since the counters were taken."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != source_hash(src):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def gpu_copies(moe, torch, synth, dev):
+    """Layer copy 0 from the seeded numpy generator; copies 1..19 drawn on the GPU with
+    the same distributions (seeded torch generators), used only for timing."""
+    layers = [moe.DeviceLayer.from_host(synth.decode_layer(0), dev)]
+    mag = 0.02 / synth.NIBBLE_STD
+    for c in range(1, N_COPIES):
+        g = torch.Generator(device=dev)
+        g.manual_seed(c)
+
+        def int4(rows, K):
+            q = torch.randint(0, 256, (E + S, rows, K // 2), dtype=torch.uint8, device=dev,
+                              generator=g)
+            s = (torch.rand((E + S, rows, K // 64), device=dev, generator=g) + 0.5) * mag
+            s = s.to(torch.bfloat16)
+            b = (-s.float() * (6.5 + 2.0 * torch.rand(s.shape, device=dev, generator=g)))
+            return q, s, b.to(torch.bfloat16)
+
+        rw = torch.randn((E, H), device=dev, generator=g) * 0.02
+        q13, s13, b13 = int4(2 * I, H)
+        q2, s2, b2 = int4(H, I)
+        layers.append(moe.DeviceLayer.from_tensors(H, I, E, K_TOP, S, "int4", router_w=rw,
+                                                   router_b=None, w13_q=q13, w13_s=s13,
+                                                   w13_b=b13, w2_q=q2, w2_s=s2, w2_b=b2))
+    return layers
+
+
+def bench_decode(moe, torch, synth, dev, steps, warmup):
+    import numpy as np
+    layers = gpu_copies(moe, torch, synth, dev)
+    xs = moe.bf16_from_bits(np.concatenate([synth.decode_token(t) for t in range(N_TOKENS)]),
+                            dev)
+    ws = moe.workspace(layers[0], 1, dev)
+    y = torch.empty((1, H), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        moe.moe_decode(layers[i % N_COPIES], xs[i % N_TOKENS:i % N_TOKENS + 1], y=y, ws=ws)
+
+    # one graph holds GRAPH_STEPS tokens; replays walk through all copies and tokens
+    graph_steps = 100
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(3):
+            step(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graphs = []
+    for gi in range(N_TOKENS // graph_steps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(gi * graph_steps, (gi + 1) * graph_steps):
+                step(i)
+        graphs.append(g)
+    n_rep = max(1, math.ceil(steps / graph_steps))
+    w_rep = max(1, math.ceil(warmup / graph_steps))
+    for r in range(w_rep):
+        graphs[r % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for r in range(n_rep):
+        graphs[r % len(graphs)].replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1)
+    timed_steps = n_rep * graph_steps
+
+    # eager (no graph) rate, for context
+    torch.cuda.synchronize()
+    e0 = time.perf_counter()
+    for i in range(timed_steps):
+        step(i)
+    torch.cuda.synchronize()
+    eager_s = time.perf_counter() - e0
+
+    # per-kernel durations from HIP events recorded by the library on its stream
+    moe.profile_reset()
+    moe.profile_enable(True)
+    for i in range(timed_steps):
+        step(i)
+    torch.cuda.synchronize()
+    moe.profile_enable(False)
+    kern = {}
+    for name in ("k_dec_router", "k_tok_gateup", "k_tok_down"):
+        tot, n = moe.profile_query(name)
+        kern[name] = {"avg_us": 1e3 * tot / max(n, 1), "launches": n}
+    moe.profile_reset()
+    return {"ms": ms, "steps": timed_steps, "eager_tok_s": timed_steps / eager_s,
+            "kernels": kern}
+
+
+def bench_prefill(moe, torch, synth, dev, layer_host, reps=20):
+    T = 4096
+    dl = moe.DeviceLayer.from_host(layer_host, dev)
+    x = moe.bf16_from_bits(synth.prefill_x(T, seed=2), dev)
+    ws = moe.workspace(dl, T, dev)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        moe.moe_prefill(dl, x, y=y, ws=ws)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        moe.moe_prefill(dl, x, y=y, ws=ws)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    moe.profile_reset()
+    moe.profile_enable(True)
+    for _ in range(reps):
+        moe.moe_prefill(dl, x, y=y, ws=ws)
+    torch.cuda.synchronize()
+    moe.profile_enable(False)
+    kern = {}
+    for name in ("k_router_logits", "k_topk_hist", "k_scan", "k_scatter", "k_grouped_gateup",
+                 "k_grouped_down", "k_combine"):
+        tot, n = moe.profile_query(name)
+        kern[name] = {"avg_us": 1e3 * tot / max(n, 1), "launches": n}
+    moe.profile_reset()
+    buf = moe.moe_route(dl, x, ws=ws)
+    rows = int(buf["counts"].sum().item()) + T * S
+    flops = prefill_flops_per_token() * T
+    tok_s = T / (ms * 1e-3)
+    gateup_flops = rows * 2 * H * 2 * I
+    gu_us = kern["k_grouped_gateup"]["avg_us"]
+    del dl, ws, x, y
+    torch.cuda.empty_cache()
+    return {"tokens_per_s": tok_s, "ms_per_call": ms,
+            "tflops": flops / (ms * 1e-3) / 1e12,
+            "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "max_group": int(buf["counts"].max().item()),
+            "gateup_tflops": gateup_flops / (gu_us * 1e-6) / 1e12 if gu_us > 0 else None,
+            "kernels": kern}
+
+
+def cpu_baseline(synth):
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    threads = len(os.sched_getaffinity(0))
+    layer = synth.decode_layer(0)
+    n = 256
+    xs = np.concatenate([synth.decode_token(t) for t in range(n)])
+    olayer = oracle.OracleLayer(layer)
+    t0 = time.perf_counter()
+    oracle.moe(olayer, xs, nthreads=threads)
+    dt = time.perf_counter() - t0
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} decode tokens (seeds 1000000..{1000000 + n - 1}) through layer "
+                      f"copy 0, full layer per token, fp64, {dt:.1f} s on {cpu}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from routed_expert_amd import moe, synth
+    dev = "cuda:0"
+    moe.lib()
+    dec = bench_decode(moe, torch, synth, dev, args.steps, args.warmup)
+    ms_step = dec["ms"] / dec["steps"]
+    tok_s = dec["steps"] / (dec["ms"] * 1e-3)
+    bpt = decode_bytes_per_token()
+
+    w13, _ = expert_bytes()
+    gu_bytes = (K_TOP + S) * w13 + H * 2
+    gu_us = dec["kernels"]["k_tok_gateup"]["avg_us"]
+    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
+    src = os.path.join(ROOT, "routed_expert_amd", "csrc", "gemv_tokens.hip")
+    roofline = {"bound": "hbm", "kernel": "k_tok_gateup", "achieved": achieved,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                "traffic": traffic_for("k_tok_gateup", src),
+                "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_us": gu_us}
+    out = {
+        "metric": "MoE-layer tokens/s: prefill T=4096 and decode T=1, % of MFMA/HBM roofline",
+        "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": dec["steps"],
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int4-weights/bf16-act/fp32-acc",
+        "data": "synthetic (seeded int4 g64 layer, 20 rotating cache-cold copies)",
+        "config": {"workload": "moe_decode_T1", "hidden": H, "inter": I, "experts": E,
+                   "top_k": K_TOP, "shared": S, "weights": "int4-g64", "copies": N_COPIES,
+                   "graph_steps": 100, "parallelism": "single-gpu"},
+        "roofline": roofline,
+        "layer_roofline": {"bound": "hbm", "bytes_per_token": bpt,
+                           "achieved": bpt / (ms_step * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": bpt / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "decode_eager_tokens_per_s": dec["eager_tok_s"],
+        "decode_kernels_us": {k: round(v["avg_us"], 3) for k, v in dec["kernels"].items()},
+    }
+    if not args.no_prefill:
+        out["prefill_uniform"] = bench_prefill(moe, torch, synth, dev, synth.decode_layer(0))
+        out["prefill_skewed"] = bench_prefill(moe, torch, synth, dev, synth.skewed_layer(0))
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(synth)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

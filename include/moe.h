@@ -1,0 +1,141 @@
+/* moe.h -- C ABI of the routed-expert MoE layer for MI355X (gfx950).
+ *
+ * The layer: a router scores E experts per token, the k best are kept with softmax
+ * weights renormalised over the selection, one shared expert is added for every
+ * token, and every expert is a SwiGLU MLP whose weights stay int4 (groups of 64, one
+ * bf16 scale and one bf16 bias per group) until they are dequantised on chip
+ * ("Optimizing On-Device Inference for Apple Silicon", sections "Qwen creates three
+ * distinct workload shapes" and "Dequantize weights during matrix multiplication").
+ *
+ * Conventions for every call below:
+ *   - Pointers named x, y, residual, router_*, w*_*, ws and the moe_route_out fields
+ *     are DEVICE pointers; moe_layer / moe_route_out structs and `bytes` are HOST.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Calls
+ *     only enqueue work on it: they never synchronise the host and never copy device
+ *     memory to the host, so a whole layer can be captured into a HIP graph.
+ *   - The caller owns all memory (inputs, outputs, weights, workspace). The library
+ *     never allocates or frees device memory.
+ *   - Errors are detected on the host before anything is enqueued (except MOE_E_HIP,
+ *     a launch failure). A failing call returns a negative moe_status, enqueues
+ *     nothing (or nothing further) and sets a thread-local message readable with
+ *     moe_last_error(). Nothing throws across the ABI.
+ *   - Calls that share one workspace must not overlap in time (same stream is fine).
+ */
+#ifndef ROUTED_EXPERT_MOE_H
+#define ROUTED_EXPERT_MOE_H
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_E_INVALID = -1,      /* null pointer, bad size, inconsistent descriptor */
+  MOE_E_UNSUPPORTED = -2,  /* valid but outside what the kernels implement */
+  MOE_E_WORKSPACE = -3,    /* workspace smaller than moe_workspace_bytes() */
+  MOE_E_HIP = -4           /* a HIP call or kernel launch failed (no device, ...) */
+} moe_status;
+
+typedef enum { MOE_W_F32 = 0, MOE_W_INT4_G64 = 1 } moe_w_format;
+typedef enum { MOE_ACT_F32 = 0, MOE_ACT_BF16 = 1 } moe_act_dtype;
+
+/* One layer. Experts 0..E-1 are routed; with n_shared == 1 the shared expert is
+ * stacked after them as expert index E.
+ *   router_w  float [E, H] row-major;  router_b  float [E] or NULL (added to logits)
+ *   MOE_W_INT4_G64 (requires act_dtype == MOE_ACT_BF16):
+ *     w13_q uint8 [E+S, 2I, H/2]: row r holds the gate projection for r < I and the up
+ *           projection for r >= I; byte j of a row holds element 2j in its low nibble
+ *           and element 2j+1 in its high nibble (unsigned codes 0..15)
+ *     w13_s, w13_b  bf16 bit patterns [E+S, 2I, H/64]: scale and bias of each group of
+ *           64 consecutive elements of a row; weight = scale * code + bias
+ *     w2_q uint8 [E+S, H, I/2], w2_s / w2_b bf16 [E+S, H, I/64]: output projection
+ *   MOE_W_F32 (requires act_dtype == MOE_ACT_F32):
+ *     w13_q float [E+S, 2I, H], w2_q float [E+S, H, I]; the *_s / *_b pointers unused
+ * Supported: 1 <= k <= 8, k <= E <= 256, S in {0,1}; H % 64 == 0, I % 64 == 0,
+ * and for int4 additionally H % 128 == 0. */
+typedef struct {
+  int32_t abi_version;  /* must be MOE_ABI_VERSION */
+  int32_t hidden, inter, n_experts, top_k, n_shared;
+  int32_t w_format, act_dtype;
+  const float *router_w;
+  const float *router_b;
+  const void *w13_q, *w13_s, *w13_b;
+  const void *w2_q, *w2_s, *w2_b;
+} moe_layer;
+
+/* Routing results, all caller-owned device buffers of int32 / float:
+ *   topk_ids  [T, k]  selected expert ids of each token in ascending id order
+ *   topk_w    [T, k]  matching weights (softmax of the selected logits, sum 1)
+ *   counts    [E]     assignments per routed expert
+ *   offsets   [E+1]   exclusive prefix sum of counts; offsets[E] = k*T
+ *   sorted_tok[k*T]   token of each slot; slots of expert e are
+ *                     offsets[e] .. offsets[e+1]-1, tokens ascending within an expert
+ *   slot_of   [T, k]  slot of assignment (t, j), i.e. sorted_tok[slot_of[t,j]] == t */
+typedef struct {
+  int32_t *topk_ids;
+  float *topk_w;
+  int32_t *counts;
+  int32_t *offsets;
+  int32_t *sorted_tok;
+  int32_t *slot_of;
+} moe_route_out;
+
+/* ABI version compiled into the library. */
+int32_t moe_abi_version(void);
+
+/* Message of the last failing call on this thread ("" if none). Host string owned by
+ * the library, valid until the next call on this thread. */
+const char *moe_last_error(void);
+
+/* Workspace size in bytes for calls with up to max_tokens tokens (host out param).
+ * The workspace must be ZERO-FILLED once when it is allocated (e.g. torch.zeros);
+ * every call leaves its internal counters at zero again. */
+moe_status moe_workspace_bytes(const moe_layer *layer, int64_t max_tokens, size_t *bytes);
+
+/* Router, top-k and grouping: logits z = x W_r^T (+ b), k experts by (z desc, id asc),
+ * weights = softmax restricted to the selection, then the per-expert histogram,
+ * exclusive prefix scan and stable scatter ("Keep expert routing on the GPU").
+ * x: [T, H] of act_dtype. All six moe_route_out buffers must be non-NULL. */
+moe_status moe_route(const moe_layer *layer, const void *x, int64_t T,
+                     const moe_route_out *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Whole layer for T >= 1 tokens (prefill path): routing as moe_route, then for int4
+ * a grouped gate/up GEMM with SwiGLU, a grouped down GEMM (int4 codes dequantised to
+ * bf16 in LDS, bf16 MFMA, fp32 accumulation, bf16 results) and a weighted combine
+ * back to token order. y[t] = shared(x_t) + sum_j w[t,j] expert_{ids[t,j]}(x_t)
+ * (+ residual[t]). x, y, residual: [T, H] of act_dtype; residual may be NULL and may
+ * alias y. route_out may be NULL; when given it receives the routing results.
+ * Results are deterministic: identical inputs give identical bytes. */
+moe_status moe_prefill(const moe_layer *layer, const void *x, int64_t T, void *y,
+                       const void *residual, const moe_route_out *route_out, void *ws,
+                       size_t ws_bytes, void *stream);
+
+/* One token (batch-1 decode path): router GEMV with top-k, then the 8+1 selected
+ * experts' packed weights streamed through wavefront-reduced GEMVs on the vector ALUs
+ * ("Optimize the one-row weight path", "Reduce intermediate and state traffic"):
+ * gate/up + SwiGLU fused, then down + routing weights + shared expert fused.
+ * x, y, residual: [1, H] of act_dtype; residual may be NULL and may alias y. */
+moe_status moe_decode(const moe_layer *layer, const void *x, void *y, const void *residual,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/* RMSNorm with unit gain for stacking layers: out[t] = h[t] / sqrt(mean(h[t]^2) + eps),
+ * fp32 arithmetic. h, out: [T, H] of act_dtype (may alias). */
+moe_status moe_rmsnorm(const void *h, int64_t T, int32_t hidden, float eps, int32_t act_dtype,
+                       void *out, void *stream);
+
+/* Kernel timing for measurement tools. When enabled, every kernel the library launches
+ * is bracketed by HIP events on its stream. moe_profile_query() waits for the recorded
+ * events, and returns the summed duration (ms) and launch count of every kernel whose
+ * name equals `kernel`; moe_profile_reset() drops all records. Disabled by default. */
+moe_status moe_profile_enable(int32_t on);
+moe_status moe_profile_query(const char *kernel, double *total_ms, int64_t *launches);
+moe_status moe_profile_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

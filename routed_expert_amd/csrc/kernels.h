@@ -1,0 +1,106 @@
+// kernels.h -- internal launch interface between the host library and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Kernel timing hooks (host side, implemented in moe_api.hip). When profiling is off
+// both are no-ops costing one branch.
+void *prof_begin(const char *name, hipStream_t s);
+void prof_end(void *rec, hipStream_t s);
+
+struct ProfScope {
+  void *rec;
+  hipStream_t s;
+  ProfScope(const char *name, hipStream_t st) : rec(prof_begin(name, st)), s(st) {}
+  ~ProfScope() { prof_end(rec, s); }
+};
+
+#define MOE_LAUNCH(name, kern, grid, block, shm, stream, ...)          \
+  do {                                                                 \
+    ::moe::ProfScope moe_ps_(name, stream);                            \
+    hipLaunchKernelGGL(kern, grid, block, shm, stream, __VA_ARGS__);   \
+    const hipError_t moe_err_ = hipGetLastError();                     \
+    if (moe_err_ != hipSuccess) return moe_err_;                       \
+  } while (0)
+
+struct RouteArgs {
+  bool bf16;
+  const void *x;
+  const float *router_w, *router_b;
+  int64_t T;
+  int H, E, k, S;
+  float *logits;          // [T, E] (decode: [E])
+  int32_t *ids;           // [T, k]
+  float *w;               // [T, k]
+  int32_t *blk;           // [NB, E] per-block counts, then per-block bases
+  int32_t *offsets;       // [E + 2]
+  int32_t *counts_user;   // [E] or null
+  int32_t *offsets_user;  // [E + 1] or null
+  int32_t *sorted_tok;    // [k T]
+  int32_t *slot_of;       // [T, k]
+  int2 *tiles;            // [max tiles]: (group, first row)
+  int32_t *n_tiles;       // [1]
+  uint32_t *counter;      // decode: last-workgroup counter, zero between calls
+};
+
+hipError_t launch_route_prefill(const RouteArgs &a, hipStream_t s);
+hipError_t launch_route_decode(const RouteArgs &a, hipStream_t s);
+
+struct ExpertWeights {
+  const uint8_t *w13_q, *w2_q;     // int4 codes
+  const uint16_t *w13_s, *w13_b;   // bf16 scale / bias
+  const uint16_t *w2_s, *w2_b;
+  const float *w13_f, *w2_f;       // fp32 weights (MOE_W_F32)
+};
+
+// Grouped int4 GEMMs of the prefill path.
+struct GroupedArgs {
+  const uint16_t *x;          // [T, H] bf16
+  const int32_t *sorted_tok;  // [k T]
+  const int32_t *offsets;     // [E + 2]
+  const int2 *tiles;
+  const int32_t *n_tiles;
+  int max_tiles;
+  int64_t T;
+  int H, I, E;
+  ExpertWeights wt;
+  uint16_t *h;    // [(k+S) T, I] bf16, slot order
+  uint16_t *out;  // [(k+S) T, H] bf16, slot order
+};
+hipError_t launch_grouped_gateup(const GroupedArgs &a, hipStream_t s);
+hipError_t launch_grouped_down(const GroupedArgs &a, hipStream_t s);
+
+// Weighted combine of the slot-ordered expert outputs back to token order.
+struct CombineArgs {
+  const uint16_t *out;       // [(k+S) T, H] bf16
+  const int32_t *slot_of;    // [T, k]
+  const float *w;            // [T, k]
+  const uint16_t *residual;  // [T, H] or null
+  uint16_t *y;               // [T, H]
+  int64_t T;
+  int H, k, S;
+};
+hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
+
+// Per-token GEMV path (batch-1 decode; also the fp32-weight layers).
+struct TokenArgs {
+  bool bf16;                 // activation dtype (int4 weights imply bf16)
+  bool int4;
+  const void *x;             // [T, H]
+  const int32_t *ids;        // [T, k]
+  const float *w;            // [T, k]
+  const void *residual;      // [T, H] or null
+  void *y;                   // [T, H]
+  float *h;                  // [T, k+S, I] fp32
+  int64_t T;
+  int H, I, E, k, S;
+  ExpertWeights wt;
+};
+hipError_t launch_token_experts(const TokenArgs &a, hipStream_t s);
+
+hipError_t launch_rmsnorm(const void *h, int64_t T, int H, float eps, bool bf16, void *out,
+                          hipStream_t s);
+
+}  // namespace moe

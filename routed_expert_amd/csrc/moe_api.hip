@@ -1,0 +1,437 @@
+// moe_api.hip -- host side of the C ABI declared in include/moe.h: descriptor and
+// size validation, the workspace plan, kernel dispatch and error reporting.
+// No call allocates device memory, synchronises the host or copies device data to it.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+moe_status hip_fail(hipError_t e, const char *where) {
+  return fail(MOE_E_HIP, "%s: %s (%s)", where, hipGetErrorName(e), hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxTokens = int64_t(1) << 24;
+
+moe_status check_layer(const moe_layer *L) {
+  if (!L) return fail(MOE_E_INVALID, "layer descriptor is NULL");
+  if (L->abi_version != MOE_ABI_VERSION)
+    return fail(MOE_E_INVALID, "abi_version %d, library is %d", L->abi_version,
+                MOE_ABI_VERSION);
+  if (L->hidden <= 0 || L->inter <= 0 || L->n_experts <= 0)
+    return fail(MOE_E_INVALID, "hidden, inter and n_experts must be positive");
+  if (L->top_k < 1 || L->top_k > L->n_experts)
+    return fail(MOE_E_INVALID, "top_k %d outside [1, n_experts]", L->top_k);
+  if (L->n_shared < 0 || L->n_shared > 1)
+    return fail(MOE_E_INVALID, "n_shared must be 0 or 1");
+  if (L->n_experts > moe::kMaxExperts)
+    return fail(MOE_E_UNSUPPORTED, "n_experts %d > %d", L->n_experts, moe::kMaxExperts);
+  if (L->top_k > moe::kMaxTopK)
+    return fail(MOE_E_UNSUPPORTED, "top_k %d > %d", L->top_k, moe::kMaxTopK);
+  if (L->hidden % 64 || L->inter % 64)
+    return fail(MOE_E_UNSUPPORTED, "hidden and inter must be multiples of 64");
+  if (!L->router_w || !L->w13_q || !L->w2_q)
+    return fail(MOE_E_INVALID, "router_w, w13_q and w2_q must be non-NULL");
+  if (L->w_format == MOE_W_INT4_G64) {
+    if (L->act_dtype != MOE_ACT_BF16)
+      return fail(MOE_E_UNSUPPORTED, "int4 weights need bf16 activations");
+    if (L->hidden % 128) return fail(MOE_E_UNSUPPORTED, "int4 layers need hidden %% 128 == 0");
+    if (!L->w13_s || !L->w13_b || !L->w2_s || !L->w2_b)
+      return fail(MOE_E_INVALID, "int4 scale/bias pointers must be non-NULL");
+    if (!aligned16(L->w13_q) || !aligned16(L->w2_q) || ((uintptr_t)L->w13_s & 1) ||
+        ((uintptr_t)L->w13_b & 1) || ((uintptr_t)L->w2_s & 1) || ((uintptr_t)L->w2_b & 1))
+      return fail(MOE_E_INVALID, "weight pointers misaligned (codes need 16 bytes)");
+  } else if (L->w_format == MOE_W_F32) {
+    if (L->act_dtype != MOE_ACT_F32)
+      return fail(MOE_E_UNSUPPORTED, "fp32 weights need fp32 activations");
+    if (!aligned16(L->w13_q) || !aligned16(L->w2_q))
+      return fail(MOE_E_INVALID, "fp32 weight pointers must be 16-byte aligned");
+  } else {
+    return fail(MOE_E_INVALID, "unknown w_format %d", L->w_format);
+  }
+  if (!aligned16(L->router_w)) return fail(MOE_E_INVALID, "router_w must be 16-byte aligned");
+  if ((uintptr_t)L->router_b & 3) return fail(MOE_E_INVALID, "router_b misaligned");
+  return MOE_OK;
+}
+
+
+// Workspace layout. The decode region comes first at fixed offsets so that prefill
+// calls (whose region grows with T) never overwrite the decode counter.
+struct Plan {
+  size_t dec_counter, dec_logits, dec_ids, dec_w, dec_h;
+  size_t logits, ids, w, blk, offsets, sorted, slot, tiles, ntiles, h, out;
+  size_t total;
+  int max_tiles;
+};
+
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+Plan make_plan(const moe_layer *L, int64_t T) {
+  Plan p{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const size_t E = L->n_experts, k = L->top_k, S = L->n_shared, H = L->hidden, I = L->inter;
+  const size_t Tn = (size_t)(T > 0 ? T : 1);
+  const size_t NB = (Tn + moe::kRouteBlock - 1) / moe::kRouteBlock;
+  p.dec_counter = take(sizeof(uint32_t));
+  p.dec_logits = take(E * 4);
+  p.dec_ids = take(k * 4);
+  p.dec_w = take(k * 4);
+  p.dec_h = take((k + S) * I * 4);
+  const size_t tiles = (k * Tn + moe::kTileM - 1) / moe::kTileM + E +
+                       (S ? (Tn + moe::kTileM - 1) / moe::kTileM : 0);
+  p.max_tiles = (int)tiles;
+  p.logits = take(Tn * E * 4);
+  p.ids = take(Tn * k * 4);
+  p.w = take(Tn * k * 4);
+  p.blk = take(NB * E * 4);
+  p.offsets = take((E + 2) * 4);
+  p.sorted = take(k * Tn * 4);
+  p.slot = take(k * Tn * 4);
+  p.tiles = take(tiles * 8);
+  p.ntiles = take(4);
+  if (L->w_format == MOE_W_INT4_G64) {
+    p.h = take((k + S) * Tn * I * 2);
+    p.out = take((k + S) * Tn * H * 2);
+  } else {
+    p.h = take((k + S) * Tn * I * 4);
+    p.out = off;
+  }
+  p.total = off;
+  return p;
+}
+
+template <typename Tp>
+Tp *at(void *ws, size_t off) {
+  return reinterpret_cast<Tp *>(static_cast<char *>(ws) + off);
+}
+
+moe::ExpertWeights weights_of(const moe_layer *L) {
+  moe::ExpertWeights w{};
+  if (L->w_format == MOE_W_INT4_G64) {
+    w.w13_q = static_cast<const uint8_t *>(L->w13_q);
+    w.w2_q = static_cast<const uint8_t *>(L->w2_q);
+    w.w13_s = static_cast<const uint16_t *>(L->w13_s);
+    w.w13_b = static_cast<const uint16_t *>(L->w13_b);
+    w.w2_s = static_cast<const uint16_t *>(L->w2_s);
+    w.w2_b = static_cast<const uint16_t *>(L->w2_b);
+  } else {
+    w.w13_f = static_cast<const float *>(L->w13_q);
+    w.w2_f = static_cast<const float *>(L->w2_q);
+  }
+  return w;
+}
+
+moe_status check_ws(const moe_layer *L, int64_t T, void *ws, size_t ws_bytes, Plan *p) {
+  *p = make_plan(L, T);
+  if (!ws) return fail(MOE_E_INVALID, "workspace is NULL");
+  if (!aligned16(ws)) return fail(MOE_E_INVALID, "workspace must be 16-byte aligned");
+  if (ws_bytes < p->total)
+    return fail(MOE_E_WORKSPACE, "workspace %zu bytes < %zu needed for T=%lld", ws_bytes,
+                p->total, (long long)T);
+  return MOE_OK;
+}
+
+moe::RouteArgs route_args(const moe_layer *L, const void *x, int64_t T) {
+  moe::RouteArgs a{};
+  a.bf16 = L->act_dtype == MOE_ACT_BF16;
+  a.x = x;
+  a.router_w = L->router_w;
+  a.router_b = L->router_b;
+  a.T = T;
+  a.H = L->hidden;
+  a.E = L->n_experts;
+  a.k = L->top_k;
+  a.S = L->n_shared;
+  return a;
+}
+
+// Routing results go to the caller's buffers when given, else to the workspace.
+void route_targets(moe::RouteArgs &a, const Plan &p, void *ws, const moe_route_out *ro) {
+  a.logits = at<float>(ws, p.logits);
+  a.blk = at<int32_t>(ws, p.blk);
+  a.offsets = at<int32_t>(ws, p.offsets);
+  a.tiles = at<int2>(ws, p.tiles);
+  a.n_tiles = at<int32_t>(ws, p.ntiles);
+  a.ids = ro ? ro->topk_ids : at<int32_t>(ws, p.ids);
+  a.w = ro ? ro->topk_w : at<float>(ws, p.w);
+  a.sorted_tok = ro ? ro->sorted_tok : at<int32_t>(ws, p.sorted);
+  a.slot_of = ro ? ro->slot_of : at<int32_t>(ws, p.slot);
+  a.counts_user = ro ? ro->counts : nullptr;
+  a.offsets_user = ro ? ro->offsets : nullptr;
+}
+
+moe_status check_route_out(const moe_route_out *ro) {
+  if (!ro->topk_ids || !ro->topk_w || !ro->counts || !ro->offsets || !ro->sorted_tok ||
+      !ro->slot_of)
+    return fail(MOE_E_INVALID, "every moe_route_out buffer must be non-NULL");
+  return MOE_OK;
+}
+
+// ---- kernel timing -----------------------------------------------------------------------
+struct ProfRec {
+  std::string name;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+std::vector<ProfRec> g_prof;
+std::atomic<bool> g_prof_on{false};
+
+}  // namespace
+
+namespace moe {
+
+void *prof_begin(const char *name, hipStream_t s) {
+  if (!g_prof_on.load(std::memory_order_relaxed)) return nullptr;
+  ProfRec *r = new ProfRec{name, nullptr, nullptr};
+  if (hipEventCreate(&r->a) != hipSuccess || hipEventCreate(&r->b) != hipSuccess ||
+      hipEventRecord(r->a, s) != hipSuccess) {
+    delete r;
+    return nullptr;
+  }
+  return r;
+}
+
+void prof_end(void *rec, hipStream_t s) {
+  if (!rec) return;
+  ProfRec *r = static_cast<ProfRec *>(rec);
+  (void)hipEventRecord(r->b, s);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof.push_back(*r);
+  delete r;
+}
+
+}  // namespace moe
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char *moe_last_error(void) { return g_err.c_str(); }
+
+moe_status moe_workspace_bytes(const moe_layer *layer, int64_t max_tokens, size_t *bytes) {
+  g_err.clear();
+  moe_status st = check_layer(layer);
+  if (st) return st;
+  if (!bytes) return fail(MOE_E_INVALID, "bytes is NULL");
+  if (max_tokens < 1 || max_tokens > kMaxTokens)
+    return fail(MOE_E_INVALID, "max_tokens %lld outside [1, %lld]", (long long)max_tokens,
+                (long long)kMaxTokens);
+  *bytes = make_plan(layer, max_tokens).total;
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_layer *layer, const void *x, int64_t T, const moe_route_out *out,
+                     void *ws, size_t ws_bytes, void *stream) {
+  g_err.clear();
+  moe_status st = check_layer(layer);
+  if (st) return st;
+  if (T < 0 || T > kMaxTokens) return fail(MOE_E_INVALID, "T %lld out of range", (long long)T);
+  if (!out) return fail(MOE_E_INVALID, "route output descriptor is NULL");
+  if ((st = check_route_out(out))) return st;
+  if (!x || !aligned16(x)) return fail(MOE_E_INVALID, "x must be non-NULL and 16-byte aligned");
+  Plan p;
+  if ((st = check_ws(layer, T, ws, ws_bytes, &p))) return st;
+  if (T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  moe::RouteArgs ra = route_args(layer, x, T);
+  route_targets(ra, p, ws, out);
+  hipError_t e = moe::launch_route_prefill(ra, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_route");
+  return MOE_OK;
+}
+
+moe_status moe_prefill(const moe_layer *layer, const void *x, int64_t T, void *y,
+                       const void *residual, const moe_route_out *route_out, void *ws,
+                       size_t ws_bytes, void *stream) {
+  g_err.clear();
+  moe_status st = check_layer(layer);
+  if (st) return st;
+  if (T < 0 || T > kMaxTokens) return fail(MOE_E_INVALID, "T %lld out of range", (long long)T);
+  if (!x || !y || !aligned16(x) || !aligned16(y))
+    return fail(MOE_E_INVALID, "x and y must be non-NULL and 16-byte aligned");
+  if (residual && !aligned16(residual)) return fail(MOE_E_INVALID, "residual misaligned");
+  if (route_out && (st = check_route_out(route_out))) return st;
+  Plan p;
+  if ((st = check_ws(layer, T, ws, ws_bytes, &p))) return st;
+  if (T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  moe::RouteArgs ra = route_args(layer, x, T);
+  route_targets(ra, p, ws, route_out);
+  hipError_t e = moe::launch_route_prefill(ra, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_prefill route");
+  const moe::ExpertWeights wt = weights_of(layer);
+  if (layer->w_format == MOE_W_INT4_G64) {
+    moe::GroupedArgs ga{};
+    ga.x = static_cast<const uint16_t *>(x);
+    ga.sorted_tok = ra.sorted_tok;
+    ga.offsets = ra.offsets;
+    ga.tiles = ra.tiles;
+    ga.n_tiles = ra.n_tiles;
+    ga.max_tiles = p.max_tiles;
+    ga.T = T;
+    ga.H = layer->hidden;
+    ga.I = layer->inter;
+    ga.E = layer->n_experts;
+    ga.wt = wt;
+    ga.h = at<uint16_t>(ws, p.h);
+    ga.out = at<uint16_t>(ws, p.out);
+    if ((e = moe::launch_grouped_gateup(ga, s)) != hipSuccess)
+      return hip_fail(e, "moe_prefill gate/up");
+    if ((e = moe::launch_grouped_down(ga, s)) != hipSuccess)
+      return hip_fail(e, "moe_prefill down");
+    moe::CombineArgs ca{};
+    ca.out = ga.out;
+    ca.slot_of = ra.slot_of;
+    ca.w = ra.w;
+    ca.residual = static_cast<const uint16_t *>(residual);
+    ca.y = static_cast<uint16_t *>(y);
+    ca.T = T;
+    ca.H = layer->hidden;
+    ca.k = layer->top_k;
+    ca.S = layer->n_shared;
+    if ((e = moe::launch_combine(ca, s)) != hipSuccess) return hip_fail(e, "moe_prefill combine");
+  } else {
+    moe::TokenArgs ta{};
+    ta.bf16 = false;
+    ta.int4 = false;
+    ta.x = x;
+    ta.ids = ra.ids;
+    ta.w = ra.w;
+    ta.residual = residual;
+    ta.y = y;
+    ta.h = at<float>(ws, p.h);
+    ta.T = T;
+    ta.H = layer->hidden;
+    ta.I = layer->inter;
+    ta.E = layer->n_experts;
+    ta.k = layer->top_k;
+    ta.S = layer->n_shared;
+    ta.wt = wt;
+    if ((e = moe::launch_token_experts(ta, s)) != hipSuccess)
+      return hip_fail(e, "moe_prefill experts");
+  }
+  return MOE_OK;
+}
+
+moe_status moe_decode(const moe_layer *layer, const void *x, void *y, const void *residual,
+                      void *ws, size_t ws_bytes, void *stream) {
+  g_err.clear();
+  moe_status st = check_layer(layer);
+  if (st) return st;
+  if (!x || !y || !aligned16(x) || !aligned16(y))
+    return fail(MOE_E_INVALID, "x and y must be non-NULL and 16-byte aligned");
+  if (residual && !aligned16(residual)) return fail(MOE_E_INVALID, "residual misaligned");
+  Plan p;
+  if ((st = check_ws(layer, 1, ws, ws_bytes, &p))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  moe::RouteArgs ra = route_args(layer, x, 1);
+  ra.logits = at<float>(ws, p.dec_logits);
+  ra.ids = at<int32_t>(ws, p.dec_ids);
+  ra.w = at<float>(ws, p.dec_w);
+  ra.counter = at<uint32_t>(ws, p.dec_counter);
+  hipError_t e = moe::launch_route_decode(ra, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_decode router");
+  moe::TokenArgs ta{};
+  ta.bf16 = layer->act_dtype == MOE_ACT_BF16;
+  ta.int4 = layer->w_format == MOE_W_INT4_G64;
+  ta.x = x;
+  ta.ids = ra.ids;
+  ta.w = ra.w;
+  ta.residual = residual;
+  ta.y = y;
+  ta.h = at<float>(ws, p.dec_h);
+  ta.T = 1;
+  ta.H = layer->hidden;
+  ta.I = layer->inter;
+  ta.E = layer->n_experts;
+  ta.k = layer->top_k;
+  ta.S = layer->n_shared;
+  ta.wt = weights_of(layer);
+  if ((e = moe::launch_token_experts(ta, s)) != hipSuccess)
+    return hip_fail(e, "moe_decode experts");
+  return MOE_OK;
+}
+
+moe_status moe_rmsnorm(const void *h, int64_t T, int32_t hidden, float eps, int32_t act_dtype,
+                       void *out, void *stream) {
+  g_err.clear();
+  if (!h || !out) return fail(MOE_E_INVALID, "h and out must be non-NULL");
+  if (T < 0 || T > kMaxTokens || hidden <= 0)
+    return fail(MOE_E_INVALID, "bad T or hidden");
+  if (!(eps >= 0.f)) return fail(MOE_E_INVALID, "eps must be >= 0");
+  if (act_dtype != MOE_ACT_BF16 && act_dtype != MOE_ACT_F32)
+    return fail(MOE_E_INVALID, "unknown act_dtype %d", act_dtype);
+  if (T == 0) return MOE_OK;
+  const hipError_t e = moe::launch_rmsnorm(h, T, hidden, eps, act_dtype == MOE_ACT_BF16, out,
+                                           static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "moe_rmsnorm");
+  return MOE_OK;
+}
+
+moe_status moe_profile_enable(int32_t on) {
+  g_err.clear();
+  g_prof_on.store(on != 0);
+  return MOE_OK;
+}
+
+moe_status moe_profile_query(const char *kernel, double *total_ms, int64_t *launches) {
+  g_err.clear();
+  if (!kernel || !total_ms || !launches) return fail(MOE_E_INVALID, "NULL argument");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  double sum = 0.0;
+  int64_t n = 0;
+  for (ProfRec &r : g_prof) {
+    if (r.name != kernel) continue;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e != hipSuccess) return hip_fail(e, "moe_profile_query");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) return hip_fail(e, "moe_profile_query");
+    sum += ms;
+    ++n;
+  }
+  *total_ms = sum;
+  *launches = n;
+  return MOE_OK;
+}
+
+moe_status moe_profile_reset(void) {
+  g_err.clear();
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (ProfRec &r : g_prof) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  g_prof.clear();
+  return MOE_OK;
+}
+
+}  // extern "C"

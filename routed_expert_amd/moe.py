@@ -1,0 +1,258 @@
+"""Python binding of the C-ABI MoE library (``libmoe.so``, declared in include/moe.h).
+
+Argument marshalling only: torch provides device memory and the current HIP stream,
+every step of the layer runs in the library's HIP kernels. There is no fallback: if
+the library is missing, or no GPU is present, the calls raise.
+
+torch is imported before the library is loaded so that the library binds to the HIP
+runtime torch already mapped (both carry the soname libamdhip64.so.7).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+ABI_VERSION = 1
+OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
+W_F32, W_INT4_G64 = 0, 1
+ACT_F32, ACT_BF16 = 0, 1
+
+EXPORTS = ("moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_route",
+           "moe_prefill", "moe_decode", "moe_rmsnorm", "moe_profile_enable",
+           "moe_profile_query", "moe_profile_reset")
+
+
+class MoeLayer(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("inter", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("n_shared", ctypes.c_int32),
+                ("w_format", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
+                ("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
+                ("w13_q", ctypes.c_void_p), ("w13_s", ctypes.c_void_p),
+                ("w13_b", ctypes.c_void_p), ("w2_q", ctypes.c_void_p),
+                ("w2_s", ctypes.c_void_p), ("w2_b", ctypes.c_void_p)]
+
+
+class MoeRouteOut(ctypes.Structure):
+    _fields_ = [("topk_ids", ctypes.c_void_p), ("topk_w", ctypes.c_void_p),
+                ("counts", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
+                ("sorted_tok", ctypes.c_void_p), ("slot_of", ctypes.c_void_p)]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, code, msg):
+        super().__init__(f"{fn} failed with status {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def hip_runtimes_mapped() -> list[str]:
+    """Distinct libamdhip64 files mapped into this process."""
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        pass
+    return sorted(paths)
+
+
+def lib():
+    """Load libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with routed_expert_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "moe_abi_version": ([], I32),
+        "moe_last_error": ([], ctypes.c_char_p),
+        "moe_workspace_bytes": ([P, I64, ctypes.POINTER(SZ)], ctypes.c_int),
+        "moe_route": ([P, P, I64, P, P, SZ, P], ctypes.c_int),
+        "moe_prefill": ([P, P, I64, P, P, P, P, SZ, P], ctypes.c_int),
+        "moe_decode": ([P, P, P, P, P, SZ, P], ctypes.c_int),
+        "moe_rmsnorm": ([P, I64, I32, ctypes.c_float, I32, P, P], ctypes.c_int),
+        "moe_profile_enable": ([I32], ctypes.c_int),
+        "moe_profile_query": ([ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                               ctypes.POINTER(I64)], ctypes.c_int),
+        "moe_profile_reset": ([], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes, fn.restype = args, res
+    if L.moe_abi_version() != ABI_VERSION:
+        raise RuntimeError("libmoe.so ABI version mismatch")
+    runtimes = hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise RuntimeError(f"two HIP runtimes mapped: {runtimes}")
+    _lib = L
+    return L
+
+
+def _check(fn, code):
+    if code != OK:
+        raise MoeError(fn, code, lib().moe_last_error().decode())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(a, device, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.to(device)
+
+
+class DeviceLayer:
+    """A layer's weights in device memory plus its C descriptor.
+
+    Built from a host layer in interchange layout (routed_expert_amd.synth.Layer) or
+    from device tensors already in that layout (``from_tensors``)."""
+
+    def __init__(self, hidden, inter, n_experts, top_k, n_shared, fmt, tensors):
+        self.hidden, self.inter = hidden, inter
+        self.n_experts, self.top_k, self.n_shared = n_experts, top_k, n_shared
+        self.fmt = fmt
+        self.t = tensors
+        g = tensors.get
+        self.desc = MoeLayer(ABI_VERSION, hidden, inter, n_experts, top_k, n_shared,
+                             W_INT4_G64 if fmt == "int4" else W_F32,
+                             ACT_BF16 if fmt == "int4" else ACT_F32,
+                             *[None if g(n) is None else g(n).data_ptr() for n in
+                               ("router_w", "router_b", "w13_q", "w13_s", "w13_b",
+                                "w2_q", "w2_s", "w2_b")])
+
+    @classmethod
+    def from_host(cls, layer, device="cuda"):
+        t = {"router_w": _dev(layer.router_w, device),
+             "router_b": None if layer.router_b is None else _dev(layer.router_b, device)}
+        if layer.fmt == "int4":
+            t.update(w13_q=_dev(layer.w13_q, device), w2_q=_dev(layer.w2_q, device),
+                     w13_s=_dev(layer.w13_s.view(np.int16), device, torch.bfloat16),
+                     w13_b=_dev(layer.w13_b.view(np.int16), device, torch.bfloat16),
+                     w2_s=_dev(layer.w2_s.view(np.int16), device, torch.bfloat16),
+                     w2_b=_dev(layer.w2_b.view(np.int16), device, torch.bfloat16))
+        else:
+            t.update(w13_q=_dev(layer.w13, device), w2_q=_dev(layer.w2, device))
+        return cls(layer.hidden, layer.inter, layer.n_experts, layer.top_k, layer.n_shared,
+                   layer.fmt, t)
+
+    @classmethod
+    def from_tensors(cls, hidden, inter, n_experts, top_k, n_shared, fmt, **tensors):
+        return cls(hidden, inter, n_experts, top_k, n_shared, fmt, tensors)
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.desc)
+
+    @property
+    def act_dtype(self):
+        return torch.bfloat16 if self.fmt == "int4" else torch.float32
+
+
+def moe_workspace_bytes(layer: DeviceLayer, max_tokens: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_workspace_bytes", lib().moe_workspace_bytes(layer.ref, int(max_tokens),
+                                                            ctypes.byref(n)))
+    return n.value
+
+
+def workspace(layer: DeviceLayer, max_tokens: int, device="cuda") -> torch.Tensor:
+    """Zero-filled workspace for calls with up to max_tokens tokens."""
+    return torch.zeros(moe_workspace_bytes(layer, max_tokens), dtype=torch.uint8, device=device)
+
+
+def route_buffers(layer: DeviceLayer, T: int, device="cuda") -> dict:
+    E, k = layer.n_experts, layer.top_k
+    i32 = dict(dtype=torch.int32, device=device)
+    return {"topk_ids": torch.empty((T, k), **i32),
+            "topk_w": torch.empty((T, k), dtype=torch.float32, device=device),
+            "counts": torch.empty(E, **i32), "offsets": torch.empty(E + 1, **i32),
+            "sorted_tok": torch.empty(T * k, **i32), "slot_of": torch.empty((T, k), **i32)}
+
+
+def _route_desc(b):
+    return MoeRouteOut(*[b[n].data_ptr() for n in ("topk_ids", "topk_w", "counts", "offsets",
+                                                    "sorted_tok", "slot_of")])
+
+
+def _ws(layer, ws, T, device):
+    return workspace(layer, max(T, 1), device) if ws is None else ws
+
+
+def moe_route(layer: DeviceLayer, x: torch.Tensor, ws=None, out=None, stream=None) -> dict:
+    T = x.shape[0]
+    ws = _ws(layer, ws, T, x.device)
+    out = route_buffers(layer, T, x.device) if out is None else out
+    desc = _route_desc(out)
+    _check("moe_route", lib().moe_route(layer.ref, _ptr(x), T, ctypes.byref(desc), _ptr(ws),
+                                        ws.numel(), _stream(stream)))
+    return out
+
+
+def moe_prefill(layer: DeviceLayer, x: torch.Tensor, y=None, residual=None, ws=None,
+                route_out=None, stream=None) -> torch.Tensor:
+    T = x.shape[0]
+    ws = _ws(layer, ws, T, x.device)
+    y = torch.empty_like(x) if y is None else y
+    rd = None if route_out is None else ctypes.byref(_route_desc(route_out))
+    _check("moe_prefill", lib().moe_prefill(layer.ref, _ptr(x), T, _ptr(y), _ptr(residual), rd,
+                                            _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+def moe_decode(layer: DeviceLayer, x: torch.Tensor, y=None, residual=None, ws=None,
+               stream=None) -> torch.Tensor:
+    ws = _ws(layer, ws, 1, x.device)
+    y = torch.empty_like(x) if y is None else y
+    _check("moe_decode", lib().moe_decode(layer.ref, _ptr(x), _ptr(y), _ptr(residual),
+                                          _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+def moe_rmsnorm(h: torch.Tensor, eps: float = 1e-6, out=None, stream=None) -> torch.Tensor:
+    out = torch.empty_like(h) if out is None else out
+    act = ACT_BF16 if h.dtype == torch.bfloat16 else ACT_F32
+    _check("moe_rmsnorm", lib().moe_rmsnorm(_ptr(h), h.shape[0], h.shape[1], float(eps), act,
+                                            _ptr(out), _stream(stream)))
+    return out
+
+
+def profile_enable(on: bool = True):
+    _check("moe_profile_enable", lib().moe_profile_enable(1 if on else 0))
+
+
+def profile_reset():
+    _check("moe_profile_reset", lib().moe_profile_reset())
+
+
+def profile_query(kernel: str) -> tuple[float, int]:
+    ms, n = ctypes.c_double(0), ctypes.c_int64(0)
+    _check("moe_profile_query", lib().moe_profile_query(kernel.encode(), ctypes.byref(ms),
+                                                        ctypes.byref(n)))
+    return ms.value, n.value
+
+
+def bf16_from_bits(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    """Device bf16 tensor holding the given bf16 bit patterns."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)

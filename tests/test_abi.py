@@ -1,0 +1,125 @@
+"""Host-side checks of the C-ABI library: it loads, exports every declared entry point,
+and rejects bad arguments on the host before touching the GPU (no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def M():
+    from routed_expert_amd import build, moe
+    if not os.path.exists(moe.LIB_PATH):
+        build.build()
+    moe.lib()
+    return moe
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("moe_route", "moe_prefill", "moe_decode", "moe_workspace_bytes",
+                     "moe_last_error"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(M):
+    lib = ctypes.CDLL(M.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(M.EXPORTS)
+
+
+def test_single_hip_runtime(M):
+    assert len(M.hip_runtimes_mapped()) <= 1
+
+
+def fake_layer(M, **kw):
+    """Descriptor with plausible aligned (never dereferenced) device addresses."""
+    p = dict(abi_version=M.ABI_VERSION, hidden=2048, inter=512, n_experts=256, top_k=8,
+             n_shared=1, w_format=M.W_INT4_G64, act_dtype=M.ACT_BF16, router_w=0x10000,
+             router_b=None, w13_q=0x20000, w13_s=0x30000, w13_b=0x40000, w2_q=0x50000,
+             w2_s=0x60000, w2_b=0x70000)
+    p.update(kw)
+    return M.MoeLayer(*[p[f] for f, _ in M.MoeLayer._fields_])
+
+
+def ws_bytes(M, layer, T):
+    n = ctypes.c_size_t(0)
+    st = M.lib().moe_workspace_bytes(ctypes.byref(layer), T, ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(abi_version=99), -1),
+    (dict(hidden=0), -1),
+    (dict(top_k=0), -1),
+    (dict(top_k=300, n_experts=256), -1),
+    (dict(n_shared=2), -1),
+    (dict(n_experts=512, top_k=8), -2),
+    (dict(top_k=9), -2),
+    (dict(hidden=2000), -2),
+    (dict(inter=500), -2),
+    (dict(hidden=192), -2),             # int4 needs hidden % 128 == 0
+    (dict(act_dtype=0), -2),            # int4 weights with fp32 activations
+    (dict(w_format=0), -2),             # fp32 weights with bf16 activations
+    (dict(w_format=7), -1),
+    (dict(router_w=None), -1),
+    (dict(w13_s=None), -1),
+    (dict(w13_q=0x20008), -1),          # codes must be 16-byte aligned
+    (dict(router_b=0x10002), -1),
+])
+def test_descriptor_validation(M, kw, code):
+    st, _ = ws_bytes(M, fake_layer(M, **kw), 16)
+    assert st == code
+    assert M.lib().moe_last_error().decode() != ""
+
+
+def test_workspace_size_grows_with_tokens(M):
+    layer = fake_layer(M)
+    sizes = [ws_bytes(M, layer, T) for T in (1, 64, 4096)]
+    assert all(st == 0 for st, _ in sizes)
+    assert sizes[0][1] < sizes[1][1] < sizes[2][1]
+    assert ws_bytes(M, layer, 0)[0] == -1
+
+
+def test_call_argument_errors_before_any_launch(M):
+    L = M.lib()
+    layer = fake_layer(M)
+    ref = ctypes.byref(layer)
+    _, need = ws_bytes(M, layer, 4096)
+    x, y, ws = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), ctypes.c_void_p(0x300000)
+    # workspace too small
+    assert L.moe_prefill(ref, x, 4096, y, None, None, ws, need - 1, None) == M.E_WORKSPACE
+    assert "workspace" in L.moe_last_error().decode()
+    # null / misaligned activations, bad T
+    assert L.moe_prefill(ref, None, 4, y, None, None, ws, need, None) == M.E_INVALID
+    assert L.moe_prefill(ref, ctypes.c_void_p(0x100002), 4, y, None, None, ws, need,
+                         None) == M.E_INVALID
+    assert L.moe_prefill(ref, x, -1, y, None, None, ws, need, None) == M.E_INVALID
+    assert L.moe_decode(ref, x, None, None, ws, need, None) == M.E_INVALID
+    assert L.moe_decode(ref, x, y, None, None, need, None) == M.E_INVALID
+    # route outputs must all be given
+    ro = M.MoeRouteOut(0x400000, 0x500000, 0x600000, 0x700000, None, 0x800000)
+    assert L.moe_route(ref, x, 4, ctypes.byref(ro), ws, need, None) == M.E_INVALID
+    assert L.moe_route(ref, x, 4, None, ws, need, None) == M.E_INVALID
+    # empty input is a valid no-op that enqueues nothing
+    assert L.moe_prefill(ref, x, 0, y, None, None, ws, need, None) == M.OK
+    assert L.moe_last_error().decode() == ""
+    assert L.moe_rmsnorm(x, 4, 2048, ctypes.c_float(-1.0), M.ACT_BF16, y, None) == M.E_INVALID
+    assert L.moe_rmsnorm(x, 4, 2048, ctypes.c_float(1e-6), 5, y, None) == M.E_INVALID
+
+
+def test_profile_controls_without_records(M):
+    M.profile_reset()
+    M.profile_enable(False)
+    assert M.profile_query("k_grouped_gateup") == (0.0, 0)

@@ -1,0 +1,265 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Workloads (seeded, synthetic; shapes of the Qwen3.6-35B-A3B MoE layer described in
+"Optimizing On-Device Inference for Apple Silicon", sections "Qwen creates three
+distinct workload shapes" and "Dequantize weights during matrix multiplication"):
+  - fp32 layer, T=64, H=128, I=64, E=256, k=8, one shared expert;
+  - int4 g64 layer, H=2048, I=512, E=256, k=8, one shared expert: batch-1 decode
+    tokens, ragged prefill sizes, T=4096 with near-uniform routing and with Zipf-skewed
+    routing;
+  - small int4 layers for edge cases (T=1, ragged tails, no shared expert).
+Bar: routing ids/weights exact off the tie window, grouping bit-exact, outputs within
+1e-4 (fp32) or 2e-2 (bf16) of the output RMS.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity_util import (BF16_TOL, F32_TOL, check_grouping, check_routing, delta_for,
+                         rel_err, to_np)
+from routed_expert_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def M():
+    from routed_expert_amd import moe
+    moe.lib()
+    return moe
+
+
+@pytest.fixture(scope="module")
+def tiny(M):
+    layer, x = synth.tiny_config(0)
+    return layer, x, M.DeviceLayer.from_host(layer, DEV)
+
+
+@pytest.fixture(scope="module")
+def big(M):
+    layer = synth.decode_layer(0)
+    return layer, M.DeviceLayer.from_host(layer, DEV)
+
+
+@pytest.fixture(scope="module")
+def skewed(M):
+    layer = synth.skewed_layer(0)
+    return layer, M.DeviceLayer.from_host(layer, DEV)
+
+
+def bf16_dev(M, bits):
+    return M.bf16_from_bits(bits, DEV)
+
+
+def y_np(y):
+    return y.float().cpu().numpy()
+
+
+def announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+# ---- fp32 tiny layer ------------------------------------------------------------------------
+
+def test_tiny_prefill_fp32(M, tiny):
+    layer, x, dl = tiny
+    announce("moe_prefill fp32 T=64 H=128 I=64 E=256 k=8 S=1 seed 0")
+    buf = M.route_buffers(dl, 64, DEV)
+    y = M.moe_prefill(dl, torch.from_numpy(x).to(DEV), route_out=buf)
+    torch.cuda.synchronize()
+    g = to_np(buf)
+    assert check_routing(layer, x, g["topk_ids"], g["topk_w"], delta_for(128)) == 0
+    check_grouping(layer, g)
+    assert rel_err(y.cpu().numpy(), oracle.moe(layer, x)) <= F32_TOL
+
+
+def test_tiny_decode_fp32(M, tiny):
+    layer, x, dl = tiny
+    announce("moe_decode fp32 tokens 0..15 of the T=64 fp32 layer")
+    ws = M.workspace(dl, 1)
+    ref = oracle.moe(layer, x[:16])
+    for t in range(16):
+        y = M.moe_decode(dl, torch.from_numpy(x[t:t + 1]).to(DEV), ws=ws)
+        assert rel_err(y.cpu().numpy()[0], ref[t]) <= F32_TOL, t
+
+
+def test_tiny_route_api(M, tiny):
+    layer, x, dl = tiny
+    announce("moe_route fp32 T=64")
+    g = to_np(M.moe_route(dl, torch.from_numpy(x).to(DEV)))
+    assert check_routing(layer, x, g["topk_ids"], g["topk_w"], delta_for(128)) == 0
+    check_grouping(layer, g)
+
+
+# ---- int4 decode ----------------------------------------------------------------------------
+
+def test_decode_int4_tokens(M, big):
+    layer, dl = big
+    n = 48
+    announce(f"moe_decode int4 H=2048 I=512 E=256 k=8 S=1 layer seed 0, tokens 0..{n - 1}")
+    xs = np.concatenate([synth.decode_token(t) for t in range(n)])
+    _, _, margin = oracle.route(layer, xs)
+    ref = oracle.moe(layer, xs)
+    ws = M.workspace(dl, 1)
+    errs = []
+    for t in range(n):
+        y = M.moe_decode(dl, bf16_dev(M, xs[t:t + 1]), ws=ws)
+        if margin[t] >= delta_for(2048):
+            errs.append(rel_err(y_np(y)[0], ref[t]))
+    assert len(errs) >= n - 2
+    assert max(errs) <= BF16_TOL, max(errs)
+
+
+def test_decode_residual_alias_and_determinism(M, big):
+    layer, dl = big
+    announce("moe_decode int4 residual (aliasing y) and repeat determinism, token 3")
+    xb = synth.decode_token(3)
+    x = bf16_dev(M, xb)
+    ws = M.workspace(dl, 1)
+    y1 = M.moe_decode(dl, x, ws=ws)
+    y2 = M.moe_decode(dl, x, ws=ws)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    r = bf16_dev(M, synth.bf16_activations(77, (1, 2048)))
+    yr = r.clone()
+    M.moe_decode(dl, x, y=yr, residual=yr, ws=ws)
+    ref = oracle.moe(layer, xb)[0] + synth.bf16_bits_to_f32(
+        synth.bf16_activations(77, (1, 2048)))[0]
+    assert rel_err(y_np(yr)[0], ref) <= BF16_TOL
+
+
+# ---- int4 prefill ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [1, 5, 300])
+def test_prefill_int4_full_compare(M, big, T):
+    layer, dl = big
+    announce(f"moe_prefill int4 full-shape layer T={T}")
+    xb = synth.prefill_x(T, seed=11)
+    buf = M.route_buffers(dl, T, DEV)
+    y = M.moe_prefill(dl, bf16_dev(M, xb), route_out=buf)
+    torch.cuda.synchronize()
+    g = to_np(buf)
+    unsure = check_routing(layer, xb, g["topk_ids"], g["topk_w"], delta_for(2048))
+    check_grouping(layer, g)
+    ref = oracle.moe(layer, xb)
+    _, _, margin = oracle.route(layer, xb)
+    sure = margin >= delta_for(2048)
+    assert unsure <= max(2, T // 100)
+    assert rel_err(y_np(y)[sure], ref[sure]) <= BF16_TOL
+
+
+def _prefill_4096(M, layer, dl, seed, n_sample=96):
+    T = 4096
+    xb = synth.prefill_x(T, seed=seed)
+    buf = M.route_buffers(dl, T, DEV)
+    y = M.moe_prefill(dl, bf16_dev(M, xb), route_out=buf)
+    torch.cuda.synchronize()
+    g = to_np(buf)
+    unsure = check_routing(layer, xb, g["topk_ids"], g["topk_w"], delta_for(2048))
+    check_grouping(layer, g)
+    _, _, margin = oracle.route(layer, xb)
+    rng = np.random.default_rng(seed + 1)
+    sample = np.unique(np.concatenate([[0, 1, 127, 128, T - 1],
+                                       rng.choice(T, n_sample, replace=False)]))
+    sample = sample[margin[sample] >= delta_for(2048)]
+    ref = oracle.moe(layer, xb[sample])
+    got = y_np(y)[sample]
+    return g, unsure, rel_err(got, ref), y
+
+
+def test_prefill_uniform_4096(M, big):
+    layer, dl = big
+    announce("moe_prefill int4 T=4096 near-uniform routing, x seed 2")
+    g, unsure, err, _ = _prefill_4096(M, layer, dl, 2)
+    c = g["counts"]
+    assert c.sum() == 8 * 4096 and c.min() > 0
+    assert unsure <= 20
+    assert err <= BF16_TOL, err
+
+
+def test_prefill_skewed_4096(M, skewed):
+    layer, dl = skewed
+    announce("moe_prefill int4 T=4096 Zipf(1.1)-skewed routing, x seed 2")
+    g, unsure, err, _ = _prefill_4096(M, layer, dl, 2)
+    c = g["counts"]
+    assert c.max() > 500 and (c <= 5).sum() >= 32   # very uneven groups, some empty-ish
+    assert unsure <= 20
+    assert err <= BF16_TOL, err
+
+
+def test_prefill_determinism_and_residual(M, big):
+    layer, dl = big
+    T = 700
+    announce(f"moe_prefill int4 T={T} repeat determinism and residual")
+    xb = synth.prefill_x(T, seed=21)
+    x = bf16_dev(M, xb)
+    ws = M.workspace(dl, T)
+    y1 = M.moe_prefill(dl, x, ws=ws)
+    y2 = M.moe_prefill(dl, x, ws=ws)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    rb = synth.bf16_activations(22, (T, 2048))
+    yr = bf16_dev(M, rb)
+    M.moe_prefill(dl, x, y=yr, residual=yr, ws=ws)
+    # y + r evaluated in fp32 then rounded once: compare with the unrounded sum
+    sample = np.arange(0, T, 37)
+    ref = oracle.moe(layer, xb[sample]) + synth.bf16_bits_to_f32(rb[sample])
+    assert rel_err(y_np(yr)[sample], ref) <= BF16_TOL
+
+
+def test_prefill_rows_match_decode(M, big):
+    layer, dl = big
+    announce("prefill rows vs per-token decode, T=16")
+    xb = synth.prefill_x(16, seed=31)
+    yp = y_np(M.moe_prefill(dl, bf16_dev(M, xb)))
+    ws = M.workspace(dl, 1)
+    _, _, margin = oracle.route(layer, xb)
+    for t in range(16):
+        if margin[t] < delta_for(2048):
+            continue
+        yd = y_np(M.moe_decode(dl, bf16_dev(M, xb[t:t + 1]), ws=ws))[0]
+        assert rel_err(yp[t], yd) <= BF16_TOL
+
+
+# ---- small int4 layers: edge cases ----------------------------------------------------------
+
+@pytest.mark.parametrize("T,E,k,S", [(1, 64, 4, 1), (63, 64, 4, 1), (65, 64, 4, 0),
+                                     (129, 32, 8, 1), (257, 16, 1, 1)])
+def test_small_int4_layers(M, T, E, k, S):
+    announce(f"moe_prefill/moe_decode small int4 H=256 I=128 E={E} k={k} S={S} T={T}")
+    layer = synth.make_int4_layer(100 + T, hidden=256, inter=128, n_experts=E, top_k=k,
+                                  n_shared=S, router_std=0.1)
+    dl = M.DeviceLayer.from_host(layer, DEV)
+    xb = synth.bf16_activations(200 + T, (T, 256))
+    buf = M.route_buffers(dl, T, DEV)
+    y = M.moe_prefill(dl, bf16_dev(M, xb), route_out=buf)
+    torch.cuda.synchronize()
+    g = to_np(buf)
+    check_routing(layer, xb, g["topk_ids"], g["topk_w"], delta_for(256))
+    check_grouping(layer, g)
+    ref = oracle.moe(layer, xb)
+    _, _, margin = oracle.route(layer, xb)
+    sure = margin >= delta_for(256)
+    assert rel_err(y_np(y)[sure], ref[sure]) <= BF16_TOL
+    t = int(np.argmax(margin))
+    yd = M.moe_decode(dl, bf16_dev(M, xb[t:t + 1]))
+    assert rel_err(y_np(yd)[0], ref[t]) <= BF16_TOL
+
+
+def test_empty_prefill_is_noop(M, big):
+    _, dl = big
+    announce("moe_prefill T=0")
+    x = torch.empty((0, 2048), dtype=torch.bfloat16, device=DEV)
+    y = M.moe_prefill(dl, x, ws=M.workspace(dl, 1))
+    assert y.shape == (0, 2048)
+
+
+def test_rmsnorm(M):
+    announce("moe_rmsnorm bf16 and fp32, T=33 H=2048")
+    hb = synth.bf16_activations(41, (33, 2048))
+    out = M.moe_rmsnorm(bf16_dev(M, hb), 1e-6)
+    ref = oracle.rmsnorm(hb, 1e-6)
+    assert rel_err(y_np(out), ref) <= 1e-2
+    hf = np.random.default_rng(42).standard_normal((33, 2048)).astype(np.float32)
+    outf = M.moe_rmsnorm(torch.from_numpy(hf).to(DEV), 1e-6)
+    assert rel_err(outf.cpu().numpy(), oracle.rmsnorm(hf, 1e-6)) <= 1e-5
