@@ -3,10 +3,11 @@
 //
 // "Optimizing On-Device Inference for Apple Silicon", section "Reduce intermediate
 // and state traffic": each expert's output projection is combined with its routing
-// score and with the shared-expert result. In the prefill path the expert outputs are
-// produced in slot order by the grouped GEMM; this kernel gathers a token's k + 1 rows
-// in a fixed order (shared first, then ascending expert id), so the sum is
-// deterministic.
+// score and with the shared-expert result. In the prefill path the down GEMM writes each
+// routed slot's output already scaled by its routing weight (fp16, slot order) and the
+// shared expert's output in fp32 (token order); this kernel gathers a token's rows in a
+// fixed order (shared first, then ascending expert id) and sums them in fp32, so the
+// result is deterministic.
 #include "common.h"
 #include "kernels.h"
 
@@ -15,21 +16,20 @@ namespace moe {
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   const int64_t t = blockIdx.x;
   const int k = a.k, H = a.H;
-  float wj[kMaxTopK];
   size_t row[kMaxTopK];
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) {
     if (j >= k) break;
-    wj[j] = a.w[t * k + j];
     row[j] = (size_t)a.slot_of[t * k + j] * H;
   }
-  const size_t shared_row = ((size_t)k * a.T + t) * H;
   for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+    const size_t o = (size_t)t * H + c;
     float acc[8];
-    if (a.S) {
-      const uint4 v = *reinterpret_cast<const uint4 *>(a.out + shared_row + c);
-      acc[0] = bf16lo(v.x); acc[1] = bf16hi(v.x); acc[2] = bf16lo(v.y); acc[3] = bf16hi(v.y);
-      acc[4] = bf16lo(v.z); acc[5] = bf16hi(v.z); acc[6] = bf16lo(v.w); acc[7] = bf16hi(v.w);
+    if (a.out_sh) {
+      const float4 *p = reinterpret_cast<const float4 *>(a.out_sh + o);
+      const float4 u = p[0], v = p[1];
+      acc[0] = u.x; acc[1] = u.y; acc[2] = u.z; acc[3] = u.w;
+      acc[4] = v.x; acc[5] = v.y; acc[6] = v.z; acc[7] = v.w;
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = 0.f;
@@ -38,12 +38,10 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
     for (int j = 0; j < kMaxTopK; ++j) {
       if (j >= k) break;
       const uint4 v = *reinterpret_cast<const uint4 *>(a.out + row[j] + c);
-      const float f[8] = {bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y),
-                          bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w)};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wj[j], f[i], acc[i]);
+      acc[0] += f16lo(v.x); acc[1] += f16hi(v.x); acc[2] += f16lo(v.y);
+      acc[3] += f16hi(v.y); acc[4] += f16lo(v.z); acc[5] += f16hi(v.z);
+      acc[6] += f16lo(v.w); acc[7] += f16hi(v.w);
     }
-    const size_t o = (size_t)t * H + c;
     if (a.residual) {
       const uint4 v = *reinterpret_cast<const uint4 *>(a.residual + o);
       acc[0] += bf16lo(v.x); acc[1] += bf16hi(v.x); acc[2] += bf16lo(v.y);

@@ -15,7 +15,8 @@ constexpr int kMaxExperts = 256;
 constexpr int kTileM = 128;       // rows of a grouped-GEMM tile
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 MOE_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
@@ -31,6 +32,22 @@ MOE_DEV uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Round to nearest even fp16 (v_cvt_pk_f16_f32). Values outside the fp16 range
+// become +-inf; callers keep operands inside it.
+MOE_DEV uint32_t pack_f16x2(float lo, float hi) {
+  f16x2_t v;
+  v[0] = (_Float16)lo;
+  v[1] = (_Float16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+MOE_DEV uint16_t f32_to_f16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+MOE_DEV float f16lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w)[0]; }
+MOE_DEV float f16hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w)[1]; }
+
+// Two bf16 values (one 32-bit word) to two fp16 values; exact inside the fp16 range.
+MOE_DEV uint32_t bf16x2_to_f16x2(uint32_t w) { return pack_f16x2(bf16lo(w), bf16hi(w)); }
+
 // The 8 codes held in one 32-bit word, element order: byte0.lo, byte0.hi, byte1.lo, ...
 // q[0..7] receive the codes as floats.
 MOE_DEV void unpack8(uint32_t w, float q[8]) {
@@ -45,16 +62,15 @@ MOE_DEV void unpack8(uint32_t w, float q[8]) {
   q[7] = (float)(hi >> 24);
 }
 
-// Dequantise 8 codes to 4 packed bf16 pairs: w = bf16_rne(fma(s, q, b)).
-// The fp32 fma is exact for a bf16 scale and bias and a 4-bit code.
-MOE_DEV uint4 dequant8_bf16(uint32_t w, float s, float b) {
+// Dequantise 8 codes to 4 packed fp16 pairs: w = fp16_rne(fma(s, q, b)).
+MOE_DEV uint4 dequant8_f16(uint32_t w, float s, float b) {
   float q[8];
   unpack8(w, q);
   uint4 r;
-  r.x = pack_bf16x2(__builtin_fmaf(s, q[0], b), __builtin_fmaf(s, q[1], b));
-  r.y = pack_bf16x2(__builtin_fmaf(s, q[2], b), __builtin_fmaf(s, q[3], b));
-  r.z = pack_bf16x2(__builtin_fmaf(s, q[4], b), __builtin_fmaf(s, q[5], b));
-  r.w = pack_bf16x2(__builtin_fmaf(s, q[6], b), __builtin_fmaf(s, q[7], b));
+  r.x = pack_f16x2(__builtin_fmaf(s, q[0], b), __builtin_fmaf(s, q[1], b));
+  r.y = pack_f16x2(__builtin_fmaf(s, q[2], b), __builtin_fmaf(s, q[3], b));
+  r.z = pack_f16x2(__builtin_fmaf(s, q[4], b), __builtin_fmaf(s, q[5], b));
+  r.w = pack_f16x2(__builtin_fmaf(s, q[6], b), __builtin_fmaf(s, q[7], b));
   return r;
 }
 

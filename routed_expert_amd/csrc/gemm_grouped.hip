@@ -1,18 +1,26 @@
 // gemm_grouped.hip -- grouped expert GEMMs of the prefill path on the MFMA units.
 //
 // "Optimizing On-Device Inference for Apple Silicon", section "Dequantize weights
-// during matrix multiplication": the int4 weights are reconstructed to bf16 one small
-// tile at a time in on-chip memory (LDS here), multiplied with the routed activation
-// rows with fp32 accumulation, and the result is written in bf16; the expanded weight
-// array never exists in device memory. Section "Match tile size to expert load": each
-// expert's output is split into fixed-size tiles listed by the routing block map.
+// during matrix multiplication": the int4 weights are reconstructed one small tile at a
+// time in on-chip memory (LDS here) and multiplied with the routed activation rows with
+// fp32 accumulation; the expanded weight array never exists in device memory. Section
+// "Match tile size to expert load": each expert's output is split into fixed-size tiles
+// listed by the routing block map.
+//
+// Operand precision differs from the page (which reconstructs bf16 for a bf16 matrix
+// unit): gfx950 runs fp16 MFMA at the bf16 rate, and fp16 keeps 3 more mantissa bits of
+// every reconstructed weight and of h. x (bf16) is exact in fp16. Operands must stay
+// inside the fp16 range (|value| < 65504).
 //
 // Tile: 128 slot rows x 128 weight rows, K in steps of 64 (one quantisation group).
-// 4 waves in a 2x2 layout, each computing 64x64 with v_mfma_f32_32x32x16_bf16.
+// 4 waves in a 2x2 layout, each computing 64x64 with v_mfma_f32_32x32x16_f16.
 //   gate/up: the 128 weight rows are 64 gate rows i0.. and the 64 matching up rows, so a
 //            wave holds gate and up accumulators of the same (row, i) and applies
-//            SwiGLU in registers; h is written in slot order [slots, I] bf16.
-//   down:    128 output columns of W2; out is written in slot order [slots, H] bf16.
+//            SwiGLU in registers; h is written in slot order [slots, I] fp16.
+//   down:    128 output columns of W2. A routed slot's row is scaled by its routing
+//            weight and written fp16 in slot order; the shared expert's rows are written
+//            fp32 in token order (section "Reduce intermediate and state traffic": the
+//            output projection is combined with the routing score).
 // Operand staging: LDS double buffer; global loads of step s+1 are issued before the
 // MFMAs of step s, dequantised and stored after them.
 #include "common.h"
@@ -22,7 +30,7 @@ namespace moe {
 
 namespace {
 constexpr int BM = kTileM, BN = 128, BK = 64;
-constexpr int LDP = BK + 8;  // LDS row pitch in bf16 elements (16-byte pad)
+constexpr int LDP = BK + 8;  // LDS row pitch in fp16 elements (16-byte pad)
 }  // namespace
 
 template <bool kGateUp>
@@ -54,9 +62,9 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
   const uint16_t *arow;
   if (kGateUp) {
     const int tok = (e == a.E) ? (row0 + rr) : a.sorted_tok[slot0 + rr];
-    arow = a.x + (size_t)tok * a.H;
+    arow = a.x16 + (size_t)tok * a.H;
   } else {
-    arow = a.h + (size_t)(slot0 + rr) * a.I;
+    arow = a.h16 + (size_t)(slot0 + rr) * a.I;
   }
   int wrow;
   if (kGateUp)
@@ -88,10 +96,10 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
     pa[3] = ra3;
     const float s = bf16_to_f32(rs), b = bf16_to_f32(rb);
     uint4 *pb = reinterpret_cast<uint4 *>(&Bs[buf][lr * LDP + lh * 32]);
-    pb[0] = dequant8_bf16(rq.x, s, b);
-    pb[1] = dequant8_bf16(rq.y, s, b);
-    pb[2] = dequant8_bf16(rq.z, s, b);
-    pb[3] = dequant8_bf16(rq.w, s, b);
+    pb[0] = dequant8_f16(rq.x, s, b);
+    pb[1] = dequant8_f16(rq.y, s, b);
+    pb[2] = dequant8_f16(rq.z, s, b);
+    pb[3] = dequant8_f16(rq.w, s, b);
   };
 
   // B sub-tile rows of this wave
@@ -112,15 +120,15 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       const int ko = kk * 16 + fk;
-      const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t *>(A_ + (wm * 64 + frow) * LDP + ko);
-      const bf16x8_t a1 =
-          *reinterpret_cast<const bf16x8_t *>(A_ + (wm * 64 + 32 + frow) * LDP + ko);
-      const bf16x8_t b0 = *reinterpret_cast<const bf16x8_t *>(B_ + (nb0 + frow) * LDP + ko);
-      const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t *>(B_ + (nb1 + frow) * LDP + ko);
-      acc00 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc00, 0, 0, 0);
-      acc01 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc01, 0, 0, 0);
-      acc10 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc10, 0, 0, 0);
-      acc11 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc11, 0, 0, 0);
+      const f16x8_t a0 = *reinterpret_cast<const f16x8_t *>(A_ + (wm * 64 + frow) * LDP + ko);
+      const f16x8_t a1 =
+          *reinterpret_cast<const f16x8_t *>(A_ + (wm * 64 + 32 + frow) * LDP + ko);
+      const f16x8_t b0 = *reinterpret_cast<const f16x8_t *>(B_ + (nb0 + frow) * LDP + ko);
+      const f16x8_t b1 = *reinterpret_cast<const f16x8_t *>(B_ + (nb1 + frow) * LDP + ko);
+      acc00 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, acc00, 0, 0, 0);
+      acc01 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b1, acc01, 0, 0, 0);
+      acc10 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b0, acc10, 0, 0, 0);
+      acc11 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, acc11, 0, 0, 0);
     }
     if (st + 1 < nsteps) lstore(cur ^ 1);
     __syncthreads();
@@ -140,11 +148,18 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
       const size_t slot = (size_t)(slot0 + m);
       if (kGateUp) {
         const int i = n_tile * 64 + wn * 32 + col;
-        a.h[slot * a.I + i] = f32_to_bf16(silu(c0[r]) * c1[r]);
+        a.h16[slot * a.I + i] = f32_to_f16(silu(c0[r]) * c1[r]);
       } else {
         const int n = n_tile * BN + wn * 64 + col;
-        a.out[slot * a.H + n] = f32_to_bf16(c0[r]);
-        a.out[slot * a.H + n + 32] = f32_to_bf16(c1[r]);
+        if (e < a.E) {
+          const float wv = a.slot_w[slot];
+          a.out[slot * a.H + n] = f32_to_f16(wv * c0[r]);
+          a.out[slot * a.H + n + 32] = f32_to_f16(wv * c1[r]);
+        } else {
+          const size_t t = (size_t)(row0 + m);
+          a.out_sh[t * a.H + n] = c0[r];
+          a.out_sh[t * a.H + n + 32] = c1[r];
+        }
       }
     }
   }

@@ -40,6 +40,8 @@ struct RouteArgs {
   int32_t *offsets_user;  // [E + 1] or null
   int32_t *sorted_tok;    // [k T]
   int32_t *slot_of;       // [T, k]
+  float *slot_w;          // [k T] routing weight of each slot (prefill only)
+  uint16_t *x16;          // [T, H] fp16 copy of x for the MFMA path (or null)
   int2 *tiles;            // [max tiles]: (group, first row)
   int32_t *n_tiles;       // [1]
   uint32_t *counter;      // decode: last-workgroup counter, zero between calls
@@ -55,28 +57,30 @@ struct ExpertWeights {
   const float *w13_f, *w2_f;       // fp32 weights (MOE_W_F32)
 };
 
-// Grouped int4 GEMMs of the prefill path.
+// Grouped int4 GEMMs of the prefill path (fp16 operands, fp32 accumulation).
 struct GroupedArgs {
-  const uint16_t *x;          // [T, H] bf16
+  const uint16_t *x16;        // [T, H] fp16
   const int32_t *sorted_tok;  // [k T]
+  const float *slot_w;        // [k T]
   const int32_t *offsets;     // [E + 2]
   const int2 *tiles;
   const int32_t *n_tiles;
   int max_tiles;
   int64_t T;
-  int H, I, E;
+  int H, I, E, k;
   ExpertWeights wt;
-  uint16_t *h;    // [(k+S) T, I] bf16, slot order
-  uint16_t *out;  // [(k+S) T, H] bf16, slot order
+  uint16_t *h16;   // [(k+S) T, I] fp16, slot order
+  uint16_t *out;   // [k T, H] fp16, routed slots, already scaled by the routing weight
+  float *out_sh;   // [T, H] fp32, shared expert output in token order
 };
 hipError_t launch_grouped_gateup(const GroupedArgs &a, hipStream_t s);
 hipError_t launch_grouped_down(const GroupedArgs &a, hipStream_t s);
 
 // Weighted combine of the slot-ordered expert outputs back to token order.
 struct CombineArgs {
-  const uint16_t *out;       // [(k+S) T, H] bf16
+  const uint16_t *out;       // [k T, H] fp16, weighted routed outputs
+  const float *out_sh;       // [T, H] fp32 shared-expert output (null if S == 0)
   const int32_t *slot_of;    // [T, k]
-  const float *w;            // [T, k]
   const uint16_t *residual;  // [T, H] or null
   uint16_t *y;               // [T, H]
   int64_t T;

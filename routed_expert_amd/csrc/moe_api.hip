@@ -82,7 +82,7 @@ moe_status check_layer(const moe_layer *L) {
 // calls (whose region grows with T) never overwrite the decode counter.
 struct Plan {
   size_t dec_counter, dec_logits, dec_ids, dec_w, dec_h;
-  size_t logits, ids, w, blk, offsets, sorted, slot, tiles, ntiles, h, out;
+  size_t logits, ids, w, blk, offsets, sorted, slot, slot_w, x16, tiles, ntiles, h, out, out_sh;
   size_t total;
   int max_tiles;
 };
@@ -118,11 +118,14 @@ Plan make_plan(const moe_layer *L, int64_t T) {
   p.tiles = take(tiles * 8);
   p.ntiles = take(4);
   if (L->w_format == MOE_W_INT4_G64) {
+    p.slot_w = take(k * Tn * 4);
+    p.x16 = take(Tn * H * 2);
     p.h = take((k + S) * Tn * I * 2);
-    p.out = take((k + S) * Tn * H * 2);
+    p.out = take(k * Tn * H * 2);
+    p.out_sh = take(S * Tn * H * 4);
   } else {
     p.h = take((k + S) * Tn * I * 4);
-    p.out = off;
+    p.slot_w = p.x16 = p.out = p.out_sh = off;
   }
   p.total = off;
   return p;
@@ -186,6 +189,8 @@ void route_targets(moe::RouteArgs &a, const Plan &p, void *ws, const moe_route_o
   a.slot_of = ro ? ro->slot_of : at<int32_t>(ws, p.slot);
   a.counts_user = ro ? ro->counts : nullptr;
   a.offsets_user = ro ? ro->offsets : nullptr;
+  a.slot_w = nullptr;
+  a.x16 = nullptr;
 }
 
 moe_status check_route_out(const moe_route_out *ro) {
@@ -275,6 +280,7 @@ moe_status moe_prefill(const moe_layer *layer, const void *x, int64_t T, void *y
   moe_status st = check_layer(layer);
   if (st) return st;
   if (T < 0 || T > kMaxTokens) return fail(MOE_E_INVALID, "T %lld out of range", (long long)T);
+  if (T == 0) return MOE_OK;  // empty input: nothing to read or write
   if (!x || !y || !aligned16(x) || !aligned16(y))
     return fail(MOE_E_INVALID, "x and y must be non-NULL and 16-byte aligned");
   if (residual && !aligned16(residual)) return fail(MOE_E_INVALID, "residual misaligned");
@@ -285,13 +291,19 @@ moe_status moe_prefill(const moe_layer *layer, const void *x, int64_t T, void *y
   hipStream_t s = static_cast<hipStream_t>(stream);
   moe::RouteArgs ra = route_args(layer, x, T);
   route_targets(ra, p, ws, route_out);
+  const bool int4 = layer->w_format == MOE_W_INT4_G64;
+  if (int4) {
+    ra.slot_w = at<float>(ws, p.slot_w);
+    ra.x16 = at<uint16_t>(ws, p.x16);
+  }
   hipError_t e = moe::launch_route_prefill(ra, s);
   if (e != hipSuccess) return hip_fail(e, "moe_prefill route");
   const moe::ExpertWeights wt = weights_of(layer);
-  if (layer->w_format == MOE_W_INT4_G64) {
+  if (int4) {
     moe::GroupedArgs ga{};
-    ga.x = static_cast<const uint16_t *>(x);
+    ga.x16 = ra.x16;
     ga.sorted_tok = ra.sorted_tok;
+    ga.slot_w = ra.slot_w;
     ga.offsets = ra.offsets;
     ga.tiles = ra.tiles;
     ga.n_tiles = ra.n_tiles;
@@ -300,17 +312,19 @@ moe_status moe_prefill(const moe_layer *layer, const void *x, int64_t T, void *y
     ga.H = layer->hidden;
     ga.I = layer->inter;
     ga.E = layer->n_experts;
+    ga.k = layer->top_k;
     ga.wt = wt;
-    ga.h = at<uint16_t>(ws, p.h);
+    ga.h16 = at<uint16_t>(ws, p.h);
     ga.out = at<uint16_t>(ws, p.out);
+    ga.out_sh = layer->n_shared ? at<float>(ws, p.out_sh) : nullptr;
     if ((e = moe::launch_grouped_gateup(ga, s)) != hipSuccess)
       return hip_fail(e, "moe_prefill gate/up");
     if ((e = moe::launch_grouped_down(ga, s)) != hipSuccess)
       return hip_fail(e, "moe_prefill down");
     moe::CombineArgs ca{};
     ca.out = ga.out;
+    ca.out_sh = ga.out_sh;
     ca.slot_of = ra.slot_of;
-    ca.w = ra.w;
     ca.residual = static_cast<const uint16_t *>(residual);
     ca.y = static_cast<uint16_t *>(y);
     ca.T = T;

@@ -22,7 +22,8 @@ template <bool kBf16>
 __global__ __launch_bounds__(256) void k_router_logits(const void *__restrict__ xv,
                                                        const float *__restrict__ W,
                                                        const float *__restrict__ bias,
-                                                       float *__restrict__ z, int T, int H,
+                                                       float *__restrict__ z,
+                                                       uint16_t *__restrict__ x16, int T, int H,
                                                        int E) {
   __shared__ float xs[32][68];
   __shared__ float wsm[32][68];
@@ -44,6 +45,15 @@ __global__ __launch_bounds__(256) void k_router_logits(const void *__restrict__ 
             static_cast<const uint16_t *>(xv) + (size_t)t * H + k0 + lk);
         xr[0] = bf16lo(u.x); xr[1] = bf16hi(u.x); xr[2] = bf16lo(u.y); xr[3] = bf16hi(u.y);
         xr[4] = bf16lo(u.z); xr[5] = bf16hi(u.z); xr[6] = bf16lo(u.w); xr[7] = bf16hi(u.w);
+        if (x16 && blockIdx.y == 0) {
+          // fp16 copy of x for the fp16 MFMA GEMMs (exact inside the fp16 range)
+          uint4 h;
+          h.x = bf16x2_to_f16x2(u.x);
+          h.y = bf16x2_to_f16x2(u.y);
+          h.z = bf16x2_to_f16x2(u.z);
+          h.w = bf16x2_to_f16x2(u.w);
+          *reinterpret_cast<uint4 *>(x16 + (size_t)t * H + k0 + lk) = h;
+        }
       } else {
         const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(xv) +
                                                            (size_t)t * H + k0 + lk);
@@ -266,8 +276,10 @@ __global__ __launch_bounds__(256) void k_scan(int32_t *__restrict__ blk_cnt, int
 __global__ __launch_bounds__(256) void k_scatter(const int32_t *__restrict__ ids, int T, int E,
                                                  int k, const int32_t *__restrict__ offsets,
                                                  const int32_t *__restrict__ blk_base,
+                                                 const float *__restrict__ w,
                                                  int32_t *__restrict__ sorted_tok,
-                                                 int32_t *__restrict__ slot_of) {
+                                                 int32_t *__restrict__ slot_of,
+                                                 float *__restrict__ slot_w) {
   __shared__ int sid[kRouteBlock * kMaxTopK];
   const int b = blockIdx.x, t0 = b * kRouteBlock;
   const int nt = min(kRouteBlock, T - t0);
@@ -280,6 +292,7 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t *__restrict__ ids
         if (sid[tt * k + j] == e) {
           sorted_tok[slot] = t0 + tt;
           slot_of[(size_t)(t0 + tt) * k + j] = slot;
+          if (slot_w) slot_w[slot] = w[(size_t)(t0 + tt) * k + j];
           ++slot;
         }
       }
@@ -365,16 +378,16 @@ hipError_t launch_route_prefill(const RouteArgs &a, hipStream_t s) {
   dim3 g1((unsigned)((a.T + 63) / 64), (unsigned)((a.E + 63) / 64));
   if (a.bf16)
     MOE_LAUNCH("k_router_logits", (k_router_logits<true>), g1, dim3(256), 0, s, a.x,
-               a.router_w, a.router_b, a.logits, (int)a.T, a.H, a.E);
+               a.router_w, a.router_b, a.logits, a.x16, (int)a.T, a.H, a.E);
   else
     MOE_LAUNCH("k_router_logits", (k_router_logits<false>), g1, dim3(256), 0, s, a.x,
-               a.router_w, a.router_b, a.logits, (int)a.T, a.H, a.E);
+               a.router_w, a.router_b, a.logits, nullptr, (int)a.T, a.H, a.E);
   MOE_LAUNCH("k_topk_hist", k_topk_hist, dim3(NB), dim3(256), 0, s, a.logits, (int)a.T, a.E,
              a.k, a.ids, a.w, a.blk);
   MOE_LAUNCH("k_scan", k_scan, dim3(1), dim3(256), 0, s, a.blk, NB, a.E, (int)a.T, a.k, a.S,
              a.offsets, a.counts_user, a.offsets_user, a.tiles, a.n_tiles);
   MOE_LAUNCH("k_scatter", k_scatter, dim3(NB), dim3(256), 0, s, a.ids, (int)a.T, a.E, a.k,
-             a.offsets, a.blk, a.sorted_tok, a.slot_of);
+             a.offsets, a.blk, a.w, a.sorted_tok, a.slot_of, a.slot_w);
   return hipSuccess;
 }
 

@@ -259,7 +259,8 @@ def test_rmsnorm(M):
     hb = synth.bf16_activations(41, (33, 2048))
     out = M.moe_rmsnorm(bf16_dev(M, hb), 1e-6)
     ref = oracle.rmsnorm(hb, 1e-6)
-    assert rel_err(y_np(out), ref) <= 1e-2
+    # bf16 output: round-to-nearest error is at most 2^-8 of the value (plus fp32 noise)
+    assert np.all(np.abs(y_np(out) - ref) <= 2.0 ** -8 * np.abs(ref) * 1.001 + 1e-6)
     hf = np.random.default_rng(42).standard_normal((33, 2048)).astype(np.float32)
     outf = M.moe_rmsnorm(torch.from_numpy(hf).to(DEV), 1e-6)
     assert rel_err(outf.cpu().numpy(), oracle.rmsnorm(hf, 1e-6)) <= 1e-5
