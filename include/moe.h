@@ -92,8 +92,7 @@ int32_t moe_abi_version(void);
 const char *moe_last_error(void);
 
 /* Workspace size in bytes for calls with up to max_tokens tokens (host out param).
- * The workspace must be ZERO-FILLED once when it is allocated (e.g. torch.zeros);
- * every call leaves its internal counters at zero again. */
+ * No call needs the workspace to hold any particular contents on entry. */
 moe_status moe_workspace_bytes(const moe_layer *layer, int64_t max_tokens, size_t *bytes);
 
 /* Router, top-k and grouping: logits z = x W_r^T (+ b), k experts by (z desc, id asc),
@@ -128,7 +127,8 @@ moe_status moe_rmsnorm(const void *h, int64_t T, int32_t hidden, float eps, int3
                        void *out, void *stream);
 
 /* Kernel timing for measurement tools. When enabled, every kernel the library launches
- * is bracketed by HIP events on its stream. moe_profile_query() waits for the recorded
+ * is dispatched with a start/stop HIP event pair bound to the dispatch itself
+ * (hipExtLaunchKernel), on the kernel's stream. moe_profile_query() waits for the recorded
  * events, and returns the summed duration (ms) and launch count of every kernel whose
  * name equals `kernel`; moe_profile_reset() drops all records. Disabled by default. */
 moe_status moe_profile_enable(int32_t on);

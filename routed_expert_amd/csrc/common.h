@@ -90,9 +90,138 @@ MOE_DEV float group_sum(float v) {
 
 MOE_DEV float silu(float v) { return v / (1.0f + expf(-v)); }
 
-// Coherent (L1-bypassing) load for data written by other workgroups of the same grid.
-MOE_DEV float load_coherent(const float *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// ---- wave-wide reductions on the DPP path (no LDS traffic) --------------------------------
+// Inclusive-scan pattern: row shifts by 1, 2, 4, 8 inside each row of 16 lanes, then row
+// broadcasts of lanes 15 and 31; lane 63 ends with the result, which is broadcast.
+template <typename Op>
+MOE_DEV uint32_t wave_reduce_u32(uint32_t v, uint32_t identity, Op op) {
+  const int id = (int)identity;
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x111, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x112, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x114, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x118, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x142, 0xa, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+MOE_DEV float wave_sum_dpp(float v) {
+  const uint32_t r = wave_reduce_u32(__float_as_uint(v), 0u, [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  });
+  return __uint_as_float(r);
+}
+
+MOE_DEV uint32_t wave_max_u32(uint32_t v) {
+  return wave_reduce_u32(v, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+
+MOE_DEV uint32_t wave_min_u32(uint32_t v) {
+  return wave_reduce_u32(v, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
+
+// Order-preserving map of a float to an unsigned key (larger float, larger key).
+MOE_DEV uint32_t float_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+MOE_DEV float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Order within a wave's LDS scratch: a release/acquire pair at wavefront scope keeps the
+// compiler from moving LDS accesses across it; LDS operations of one wave complete in
+// order.
+MOE_DEV void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+constexpr int kTopkScratch = 64 + 4 * kMaxTopK + kMaxTopK;  // uint64 entries per wave
+
+// Top-k of up to 256 logits in one wave: lane l holds experts l, l+64, l+128, l+192 (NaN
+// read as -inf, experts >= E excluded). The order is (logit desc, id asc), encoded in one
+// 64-bit key: float key in the high word, ~id in the low word. Each lane sorts its four
+// keys; the k best elements lie in the k lanes whose heads rank highest, so the wave
+// ranks the 64 heads, gathers those lanes' 4k keys and ranks them. Every lane receives
+// the k ids in ascending id order and their weights: softmax over the selected logits.
+// scratch: kTopkScratch uint64 entries of LDS private to the calling wave (16-B aligned).
+MOE_DEV void wave_topk(const float v[4], int E, int k, uint64_t *scratch, int ids[kMaxTopK],
+                       float w[kMaxTopK]) {
+  const int lane = threadIdx.x & 63;
+  uint64_t key[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int e = lane + 64 * c;
+    const float f = v[c] != v[c] ? -INFINITY : v[c];
+    // real experts have a nonzero high word (float key of -inf is > 0); 0 = absent
+    key[c] = e < E ? ((uint64_t)float_key(f) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e)
+                   : 0ull;
+  }
+#define MOE_CSWAP(a, b)                                          \
+  if (key[b] > key[a]) {                                         \
+    const uint64_t t_ = key[a];                                  \
+    key[a] = key[b];                                             \
+    key[b] = t_;                                                 \
+  }
+  MOE_CSWAP(0, 1) MOE_CSWAP(2, 3) MOE_CSWAP(0, 2) MOE_CSWAP(1, 3) MOE_CSWAP(1, 2)
+#undef MOE_CSWAP
+  uint64_t *heads = scratch, *cand = scratch + 64, *best = scratch + 64 + 4 * kMaxTopK;
+  heads[lane] = key[0];
+  wave_lds_sync();
+  int r = 0;
+#pragma unroll 8
+  for (int q = 0; q < 64; q += 2) {
+    const ulonglong2 h2 = *reinterpret_cast<const ulonglong2 *>(heads + q);
+    r += (h2.x > key[0]) + (h2.y > key[0]);
+  }
+  if (r < k) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) cand[4 * r + c] = key[c];
+  }
+  wave_lds_sync();
+  const int nc = 4 * k;
+  if (lane < nc) {
+    const uint64_t mine = cand[lane];
+    int r2 = 0;
+    for (int q = 0; q < nc; ++q) r2 += cand[q] > mine;
+    if (r2 < k) best[r2] = mine;
+  }
+  wave_lds_sync();
+  int sel[kMaxTopK];
+  float val[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j >= k) break;
+    const uint64_t b = best[j];
+    sel[j] = (int)(0xFFFFFFFFu - (uint32_t)b);
+    val[j] = key_float((uint32_t)(b >> 32));
+  }
+  wave_lds_sync();  // scratch may be reused by the caller's next token
+  float ex[kMaxTopK], denom = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j >= k) break;
+    ex[j] = val[0] == -INFINITY ? 1.0f : expf(val[j] - val[0]);
+    denom += ex[j];
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j >= k) break;
+    int rk = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxTopK; ++q) {
+      if (q >= k) break;
+      rk += sel[q] < sel[j] ? 1 : 0;
+    }
+#pragma unroll
+    for (int q = 0; q < kMaxTopK; ++q)
+      if (q == rk) {
+        ids[q] = sel[j];
+        w[q] = ex[j] / denom;
+      }
+  }
 }
 
 }  // namespace moe

@@ -1,28 +1,26 @@
 // kernels.h -- internal launch interface between the host library and the kernels.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace moe {
 
-// Kernel timing hooks (host side, implemented in moe_api.hip). When profiling is off
-// both are no-ops costing one branch.
-void *prof_begin(const char *name, hipStream_t s);
-void prof_end(void *rec, hipStream_t s);
+// Kernel timing hook (host side, implemented in moe_api.hip). When profiling is on it
+// hands out a start/stop event pair bound to the next dispatch (hipExtLaunchKernel
+// timestamps the kernel itself, not the queue around it); otherwise it returns false.
+bool prof_events(const char *name, hipEvent_t *start, hipEvent_t *stop);
 
-struct ProfScope {
-  void *rec;
-  hipStream_t s;
-  ProfScope(const char *name, hipStream_t st) : rec(prof_begin(name, st)), s(st) {}
-  ~ProfScope() { prof_end(rec, s); }
-};
-
-#define MOE_LAUNCH(name, kern, grid, block, shm, stream, ...)          \
-  do {                                                                 \
-    ::moe::ProfScope moe_ps_(name, stream);                            \
-    hipLaunchKernelGGL(kern, grid, block, shm, stream, __VA_ARGS__);   \
-    const hipError_t moe_err_ = hipGetLastError();                     \
-    if (moe_err_ != hipSuccess) return moe_err_;                       \
+#define MOE_LAUNCH(name, kern, grid, block, shm, stream, ...)                               \
+  do {                                                                                      \
+    hipEvent_t moe_ev_a_ = nullptr, moe_ev_b_ = nullptr;                                    \
+    if (::moe::prof_events(name, &moe_ev_a_, &moe_ev_b_))                                   \
+      hipExtLaunchKernelGGL(kern, grid, block, shm, stream, moe_ev_a_, moe_ev_b_, 0,         \
+                            __VA_ARGS__);                                                   \
+    else                                                                                    \
+      hipLaunchKernelGGL(kern, grid, block, shm, stream, __VA_ARGS__);                      \
+    const hipError_t moe_err_ = hipGetLastError();                                          \
+    if (moe_err_ != hipSuccess) return moe_err_;                                            \
   } while (0)
 
 struct RouteArgs {
@@ -44,11 +42,9 @@ struct RouteArgs {
   uint16_t *x16;          // [T, H] fp16 copy of x for the MFMA path (or null)
   int2 *tiles;            // [max tiles]: (group, first row)
   int32_t *n_tiles;       // [1]
-  uint32_t *counter;      // decode: last-workgroup counter, zero between calls
 };
 
 hipError_t launch_route_prefill(const RouteArgs &a, hipStream_t s);
-hipError_t launch_route_decode(const RouteArgs &a, hipStream_t s);
 
 struct ExpertWeights {
   const uint8_t *w13_q, *w2_q;     // int4 codes
@@ -103,6 +99,22 @@ struct TokenArgs {
   ExpertWeights wt;
 };
 hipError_t launch_token_experts(const TokenArgs &a, hipStream_t s);
+
+// Batch-1 layer in three kernels (hidden 2048, intermediate 512, int4).
+struct DecodeArgs {
+  const uint16_t *x;          // [H] bf16
+  const float *router_w, *router_b;
+  ExpertWeights wt;
+  const uint16_t *residual;   // [H] or null
+  uint16_t *y;                // [H]
+  float *z;                   // [E] logits
+  float *h;                   // [k+S, I] fp32
+  int32_t *ids_out;           // [k]
+  float *w_out;               // [k]
+  int H, I, E, k, S;
+};
+bool decode_gemv_supported(int H, int I, int E, int k, int S, bool int4);
+hipError_t launch_decode_gemv(const DecodeArgs &a, hipStream_t s);
 
 hipError_t launch_rmsnorm(const void *h, int64_t T, int H, float eps, bool bf16, void *out,
                           hipStream_t s);

@@ -78,10 +78,9 @@ moe_status check_layer(const moe_layer *L) {
 }
 
 
-// Workspace layout. The decode region comes first at fixed offsets so that prefill
-// calls (whose region grows with T) never overwrite the decode counter.
+// Workspace layout: the batch-1 decode buffers first, then the T-dependent region.
 struct Plan {
-  size_t dec_counter, dec_logits, dec_ids, dec_w, dec_h;
+  size_t dec_logits, dec_ids, dec_w, dec_h;
   size_t logits, ids, w, blk, offsets, sorted, slot, slot_w, x16, tiles, ntiles, h, out, out_sh;
   size_t total;
   int max_tiles;
@@ -100,7 +99,6 @@ Plan make_plan(const moe_layer *L, int64_t T) {
   const size_t E = L->n_experts, k = L->top_k, S = L->n_shared, H = L->hidden, I = L->inter;
   const size_t Tn = (size_t)(T > 0 ? T : 1);
   const size_t NB = (Tn + moe::kRouteBlock - 1) / moe::kRouteBlock;
-  p.dec_counter = take(sizeof(uint32_t));
   p.dec_logits = take(E * 4);
   p.dec_ids = take(k * 4);
   p.dec_w = take(k * 4);
@@ -213,24 +211,19 @@ std::atomic<bool> g_prof_on{false};
 
 namespace moe {
 
-void *prof_begin(const char *name, hipStream_t s) {
-  if (!g_prof_on.load(std::memory_order_relaxed)) return nullptr;
-  ProfRec *r = new ProfRec{name, nullptr, nullptr};
-  if (hipEventCreate(&r->a) != hipSuccess || hipEventCreate(&r->b) != hipSuccess ||
-      hipEventRecord(r->a, s) != hipSuccess) {
-    delete r;
-    return nullptr;
+bool prof_events(const char *name, hipEvent_t *start, hipEvent_t *stop) {
+  if (!g_prof_on.load(std::memory_order_relaxed)) return false;
+  ProfRec r{name, nullptr, nullptr};
+  if (hipEventCreate(&r.a) != hipSuccess) return false;
+  if (hipEventCreate(&r.b) != hipSuccess) {
+    (void)hipEventDestroy(r.a);
+    return false;
   }
-  return r;
-}
-
-void prof_end(void *rec, hipStream_t s) {
-  if (!rec) return;
-  ProfRec *r = static_cast<ProfRec *>(rec);
-  (void)hipEventRecord(r->b, s);
+  *start = r.a;
+  *stop = r.b;
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  g_prof.push_back(*r);
-  delete r;
+  g_prof.push_back(r);
+  return true;
 }
 
 }  // namespace moe
@@ -366,16 +359,36 @@ moe_status moe_decode(const moe_layer *layer, const void *x, void *y, const void
   Plan p;
   if ((st = check_ws(layer, 1, ws, ws_bytes, &p))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  const bool int4 = layer->w_format == MOE_W_INT4_G64;
+  if (moe::decode_gemv_supported(layer->hidden, layer->inter, layer->n_experts, layer->top_k,
+                                 layer->n_shared, int4)) {
+    moe::DecodeArgs da{};
+    da.x = static_cast<const uint16_t *>(x);
+    da.router_w = layer->router_w;
+    da.router_b = layer->router_b;
+    da.wt = weights_of(layer);
+    da.residual = static_cast<const uint16_t *>(residual);
+    da.y = static_cast<uint16_t *>(y);
+    da.z = at<float>(ws, p.dec_logits);
+    da.h = at<float>(ws, p.dec_h);
+    da.ids_out = at<int32_t>(ws, p.dec_ids);
+    da.w_out = at<float>(ws, p.dec_w);
+    da.H = layer->hidden;
+    da.I = layer->inter;
+    da.E = layer->n_experts;
+    da.k = layer->top_k;
+    da.S = layer->n_shared;
+    if ((e = moe::launch_decode_gemv(da, s)) != hipSuccess) return hip_fail(e, "moe_decode");
+    return MOE_OK;
+  }
+  // other shapes: the T = 1 case of the routing kernels, then the per-token GEMVs
   moe::RouteArgs ra = route_args(layer, x, 1);
-  ra.logits = at<float>(ws, p.dec_logits);
-  ra.ids = at<int32_t>(ws, p.dec_ids);
-  ra.w = at<float>(ws, p.dec_w);
-  ra.counter = at<uint32_t>(ws, p.dec_counter);
-  hipError_t e = moe::launch_route_decode(ra, s);
-  if (e != hipSuccess) return hip_fail(e, "moe_decode router");
+  route_targets(ra, p, ws, nullptr);
+  if ((e = moe::launch_route_prefill(ra, s)) != hipSuccess) return hip_fail(e, "moe_decode route");
   moe::TokenArgs ta{};
   ta.bf16 = layer->act_dtype == MOE_ACT_BF16;
-  ta.int4 = layer->w_format == MOE_W_INT4_G64;
+  ta.int4 = int4;
   ta.x = x;
   ta.ids = ra.ids;
   ta.w = ra.w;

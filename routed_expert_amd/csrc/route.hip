@@ -104,74 +104,6 @@ __global__ __launch_bounds__(256) void k_router_logits(const void *__restrict__ 
   }
 }
 
-// ---- top-k of one token's logits in one wavefront ---------------------------------------
-// Lane l holds the logits of experts l, l+64, l+128, l+192 (-inf past E, NaN read as
-// -inf). k rounds of a wave-wide argmax, ties to the lower id. Every lane ends with the
-// k selected (id, logit) pairs in selection order (largest first).
-MOE_DEV void wave_topk(const float v[4], int E, int k, int sel_id[kMaxTopK],
-                       float sel_val[kMaxTopK]) {
-  const int lane = threadIdx.x & (kWave - 1);
-  bool taken[4] = {false, false, false, false};
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    if (j >= k) break;
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int e = lane + kWave * c;
-      if (e < E && !taken[c] && (v[c] > bv || (v[c] == bv && e < be))) {
-        bv = v[c];
-        be = e;
-      }
-    }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float ov = __shfl_xor(bv, m, kWave);
-      const int oe = __shfl_xor(be, m, kWave);
-      if (ov > bv || (ov == bv && oe < be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (lane + kWave * c == be) taken[c] = true;
-    sel_id[j] = be;
-    sel_val[j] = bv;
-  }
-}
-
-// Softmax over the selected logits and the ascending-id order of the selection.
-// Lane j < k returns its slot (rank of its id) and its id and weight.
-MOE_DEV void topk_finish(const int sel_id[kMaxTopK], const float sel_val[kMaxTopK], int k,
-                         int *rank, int *id, float *weight) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const float m = sel_val[0];
-  float denom = 0.f, mine_v = 0.f;
-  int mine = 0;
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    if (j >= k) break;
-    denom += expf(sel_val[j] - m);
-    if (j == lane) {
-      mine = sel_id[j];
-      mine_v = sel_val[j];
-    }
-  }
-  int r = 0;
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    if (j >= k) break;
-    r += sel_id[j] < mine ? 1 : 0;
-  }
-  *rank = r;
-  *id = mine;
-  *weight = (m == -INFINITY) ? 1.0f / (float)k : expf(mine_v - m) / denom;
-}
-
-MOE_DEV float sanitize(float v) { return v != v ? -INFINITY : v; }
-
 // ---- top-k and per-block histogram for T tokens -----------------------------------------
 // One workgroup per routing block of 64 tokens; each wave handles 16 tokens in order.
 __global__ __launch_bounds__(256) void k_topk_hist(const float *__restrict__ z, int T, int E,
@@ -179,6 +111,7 @@ __global__ __launch_bounds__(256) void k_topk_hist(const float *__restrict__ z, 
                                                    float *__restrict__ w,
                                                    int32_t *__restrict__ blk_cnt) {
   __shared__ int hist[kMaxExperts];
+  __shared__ __attribute__((aligned(16))) uint64_t s_topk[4][kTopkScratch];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   hist[tid] = 0;
   __syncthreads();
@@ -190,17 +123,22 @@ __global__ __launch_bounds__(256) void k_topk_hist(const float *__restrict__ z, 
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int e = lane + kWave * c;
-      v[c] = e < E ? sanitize(z[(size_t)t * E + e]) : -INFINITY;
+      v[c] = e < E ? z[(size_t)t * E + e] : -INFINITY;
     }
-    int sel_id[kMaxTopK];
-    float sel_val[kMaxTopK];
-    wave_topk(v, E, k, sel_id, sel_val);
-    int rank, id;
-    float weight;
-    topk_finish(sel_id, sel_val, k, &rank, &id, &weight);
+    int sel[kMaxTopK];
+    float sw[kMaxTopK];
+    wave_topk(v, E, k, s_topk[wave], sel, sw);
+    int id = 0;
+    float weight = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (j == lane) {
+        id = sel[j];
+        weight = sw[j];
+      }
     if (lane < k) {
-      ids[(size_t)t * k + rank] = id;
-      w[(size_t)t * k + rank] = weight;
+      ids[(size_t)t * k + lane] = id;
+      w[(size_t)t * k + lane] = weight;
       atomicAdd(&hist[id], 1);
     }
   }
@@ -300,78 +238,6 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t *__restrict__ ids
   }
 }
 
-// ---- batch-1 router GEMV with fused top-k -------------------------------------------------
-// One workgroup per expert computes its logit; the last workgroup to finish (device-scope
-// counter) runs the top-k on all E logits and resets the counter for the next call.
-template <bool kBf16>
-__global__ __launch_bounds__(256) void k_dec_router(const void *__restrict__ xv,
-                                                    const float *__restrict__ W,
-                                                    const float *__restrict__ bias, int H,
-                                                    int E, int k, float *__restrict__ z,
-                                                    int32_t *__restrict__ ids,
-                                                    float *__restrict__ w,
-                                                    uint32_t *__restrict__ counter) {
-  __shared__ float part[4];
-  __shared__ int last;
-  const int tid = threadIdx.x, e = blockIdx.x;
-  float acc = 0.f;
-  for (int c = tid * 8; c < H; c += 256 * 8) {
-    const float4 *wp = reinterpret_cast<const float4 *>(W + (size_t)e * H + c);
-    const float4 a = wp[0], b = wp[1];
-    float xr[8];
-    if (kBf16) {
-      const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(xv) + c);
-      xr[0] = bf16lo(u.x); xr[1] = bf16hi(u.x); xr[2] = bf16lo(u.y); xr[3] = bf16hi(u.y);
-      xr[4] = bf16lo(u.z); xr[5] = bf16hi(u.z); xr[6] = bf16lo(u.w); xr[7] = bf16hi(u.w);
-    } else {
-      const float4 *xp = reinterpret_cast<const float4 *>(static_cast<const float *>(xv) + c);
-      const float4 p = xp[0], q = xp[1];
-      xr[0] = p.x; xr[1] = p.y; xr[2] = p.z; xr[3] = p.w;
-      xr[4] = q.x; xr[5] = q.y; xr[6] = q.z; xr[7] = q.w;
-    }
-    acc = __builtin_fmaf(a.x, xr[0], acc);
-    acc = __builtin_fmaf(a.y, xr[1], acc);
-    acc = __builtin_fmaf(a.z, xr[2], acc);
-    acc = __builtin_fmaf(a.w, xr[3], acc);
-    acc = __builtin_fmaf(b.x, xr[4], acc);
-    acc = __builtin_fmaf(b.y, xr[5], acc);
-    acc = __builtin_fmaf(b.z, xr[6], acc);
-    acc = __builtin_fmaf(b.w, xr[7], acc);
-  }
-  acc = wave_sum(acc);
-  if ((tid & 63) == 0) part[tid >> 6] = acc;
-  __syncthreads();
-  if (tid == 0) {
-    const float s = ((part[0] + part[1]) + (part[2] + part[3])) + (bias ? bias[e] : 0.f);
-    __hip_atomic_store(z + e, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __threadfence();
-    const uint32_t prev = atomicAdd(counter, 1u);
-    last = (prev == gridDim.x - 1) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  if (tid < kWave) {
-    float v[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int ee = tid + kWave * c;
-      v[c] = ee < E ? sanitize(load_coherent(z + ee)) : -INFINITY;
-    }
-    int sel_id[kMaxTopK];
-    float sel_val[kMaxTopK];
-    wave_topk(v, E, k, sel_id, sel_val);
-    int rank, id;
-    float weight;
-    topk_finish(sel_id, sel_val, k, &rank, &id, &weight);
-    if (tid < k) {
-      ids[rank] = id;
-      w[rank] = weight;
-    }
-    if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
 // ---- launchers ------------------------------------------------------------------------------
 hipError_t launch_route_prefill(const RouteArgs &a, hipStream_t s) {
   const int NB = (int)((a.T + kRouteBlock - 1) / kRouteBlock);
@@ -388,16 +254,6 @@ hipError_t launch_route_prefill(const RouteArgs &a, hipStream_t s) {
              a.offsets, a.counts_user, a.offsets_user, a.tiles, a.n_tiles);
   MOE_LAUNCH("k_scatter", k_scatter, dim3(NB), dim3(256), 0, s, a.ids, (int)a.T, a.E, a.k,
              a.offsets, a.blk, a.w, a.sorted_tok, a.slot_of, a.slot_w);
-  return hipSuccess;
-}
-
-hipError_t launch_route_decode(const RouteArgs &a, hipStream_t s) {
-  if (a.bf16)
-    MOE_LAUNCH("k_dec_router", (k_dec_router<true>), dim3(a.E), dim3(256), 0, s, a.x,
-               a.router_w, a.router_b, a.H, a.E, a.k, a.logits, a.ids, a.w, a.counter);
-  else
-    MOE_LAUNCH("k_dec_router", (k_dec_router<false>), dim3(a.E), dim3(256), 0, s, a.x,
-               a.router_w, a.router_b, a.H, a.E, a.k, a.logits, a.ids, a.w, a.counter);
   return hipSuccess;
 }
 
