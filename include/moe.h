@@ -56,7 +56,9 @@ typedef enum { MOE_ACT_F32 = 0, MOE_ACT_BF16 = 1 } moe_act_dtype;
  *   MOE_W_F32 (requires act_dtype == MOE_ACT_F32):
  *     w13_q float [E+S, 2I, H], w2_q float [E+S, H, I]; the *_s / *_b pointers unused
  * Supported: 1 <= k <= 8, k <= E <= 256, S in {0,1}; H % 64 == 0, I % 64 == 0,
- * and for int4 additionally H % 128 == 0. */
+ * and for int4 additionally H % 256 == 0 and I % 128 == 0. Pointers to codes, fp32
+ * weights, activations and the workspace must be 16-byte aligned; int4 scale and bias
+ * pointers 4-byte aligned. */
 typedef struct {
   int32_t abi_version;  /* must be MOE_ABI_VERSION */
   int32_t hidden, inter, n_experts, top_k, n_shared;
@@ -104,7 +106,7 @@ moe_status moe_route(const moe_layer *layer, const void *x, int64_t T,
 
 /* Whole layer for T >= 1 tokens (prefill path): routing as moe_route, then for int4
  * a grouped gate/up GEMM with SwiGLU, a grouped down GEMM (int4 codes dequantised to
- * bf16 in LDS, bf16 MFMA, fp32 accumulation, bf16 results) and a weighted combine
+ * fp16 in registers, fp16 MFMA, fp32 accumulation) and a weighted combine
  * back to token order. y[t] = shared(x_t) + sum_j w[t,j] expert_{ids[t,j]}(x_t)
  * (+ residual[t]). x, y, residual: [T, H] of act_dtype; residual may be NULL and may
  * alias y. route_out may be NULL; when given it receives the routing results.

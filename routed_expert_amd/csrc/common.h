@@ -15,6 +15,7 @@ constexpr int kMaxExperts = 256;
 constexpr int kTileM = 128;       // rows of a grouped-GEMM tile
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -72,6 +73,44 @@ MOE_DEV uint4 dequant8_f16(uint32_t w, float s, float b) {
   r.z = pack_f16x2(__builtin_fmaf(s, q[4], b), __builtin_fmaf(s, q[5], b));
   r.w = pack_f16x2(__builtin_fmaf(s, q[6], b), __builtin_fmaf(s, q[7], b));
   return r;
+}
+
+// K order inside every 8-element chunk of the fp16 operand rows of the grouped GEMMs
+// (the copy of x and h): position p holds element kChunkOrder[p] = 0,4,1,5,2,6,3,7. It
+// is the order in which dequant8_pk produces the eight weights of one 32-bit code word,
+// so A and B operands agree without shuffles. kChunkPos is the inverse map.
+__device__ constexpr int kChunkPos[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+
+// Eight codes of one 32-bit word to fp16 weights w = fp16_rne(s * q + b), packed math:
+// a nibble pair OR-ed into 0x6400 is the fp16 pair (1024 + q_lo, 1024 + q_hi); subtracting
+// 1024 is exact, and one fused multiply-add rounds s*q + b once. Output pairs are
+// (q0,q4), (q1,q5), (q2,q6), (q3,q7). s2 / b2 hold the scale / bias twice; both must be
+// representable in fp16 (true for bf16 values in [2^-14, 65504]).
+MOE_DEV uint4 dequant8_pk(uint32_t w, f16x2_t s2, f16x2_t b2) {
+  constexpr uint32_t kMask = 0x000F000Fu, kMagic = 0x64006400u;
+  const f16x2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+  const uint32_t t0 = (w & kMask) | kMagic, t1 = ((w >> 4) & kMask) | kMagic;
+  const uint32_t t2 = ((w >> 8) & kMask) | kMagic, t3 = ((w >> 12) & kMask) | kMagic;
+  uint4 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(
+                                         __builtin_bit_cast(f16x2_t, t0) - k1024, s2, b2));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(
+                                         __builtin_bit_cast(f16x2_t, t1) - k1024, s2, b2));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(
+                                         __builtin_bit_cast(f16x2_t, t2) - k1024, s2, b2));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(
+                                         __builtin_bit_cast(f16x2_t, t3) - k1024, s2, b2));
+  return r;
+}
+
+// Eight bf16 values (natural order) to eight fp16 values in kChunkOrder.
+MOE_DEV uint4 bf16x8_to_f16x8_chunk(uint4 u) {
+  uint4 h;
+  h.x = pack_f16x2(bf16lo(u.x), bf16lo(u.z));
+  h.y = pack_f16x2(bf16hi(u.x), bf16hi(u.z));
+  h.z = pack_f16x2(bf16lo(u.y), bf16lo(u.w));
+  h.w = pack_f16x2(bf16hi(u.y), bf16hi(u.w));
+  return h;
 }
 
 MOE_DEV float wave_sum(float v) {

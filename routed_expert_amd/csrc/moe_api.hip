@@ -10,7 +10,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -58,12 +58,14 @@ moe_status check_layer(const moe_layer *L) {
   if (L->w_format == MOE_W_INT4_G64) {
     if (L->act_dtype != MOE_ACT_BF16)
       return fail(MOE_E_UNSUPPORTED, "int4 weights need bf16 activations");
-    if (L->hidden % 128) return fail(MOE_E_UNSUPPORTED, "int4 layers need hidden %% 128 == 0");
+    if (L->hidden % 256 || L->inter % 128)
+      return fail(MOE_E_UNSUPPORTED, "int4 layers need hidden %% 256 == 0 and inter %% 128 == 0");
     if (!L->w13_s || !L->w13_b || !L->w2_s || !L->w2_b)
       return fail(MOE_E_INVALID, "int4 scale/bias pointers must be non-NULL");
-    if (!aligned16(L->w13_q) || !aligned16(L->w2_q) || ((uintptr_t)L->w13_s & 1) ||
-        ((uintptr_t)L->w13_b & 1) || ((uintptr_t)L->w2_s & 1) || ((uintptr_t)L->w2_b & 1))
-      return fail(MOE_E_INVALID, "weight pointers misaligned (codes need 16 bytes)");
+    if (!aligned16(L->w13_q) || !aligned16(L->w2_q) || ((uintptr_t)L->w13_s & 3) ||
+        ((uintptr_t)L->w13_b & 3) || ((uintptr_t)L->w2_s & 3) || ((uintptr_t)L->w2_b & 3))
+      return fail(MOE_E_INVALID,
+                  "weight pointers misaligned (codes need 16 bytes, scales and biases 4)");
   } else if (L->w_format == MOE_W_F32) {
     if (L->act_dtype != MOE_ACT_F32)
       return fail(MOE_E_UNSUPPORTED, "fp32 weights need fp32 activations");
@@ -81,7 +83,8 @@ moe_status check_layer(const moe_layer *L) {
 // Workspace layout: the batch-1 decode buffers first, then the T-dependent region.
 struct Plan {
   size_t dec_logits, dec_ids, dec_w, dec_h;
-  size_t logits, ids, w, blk, offsets, sorted, slot, slot_w, x16, tiles, ntiles, h, out, out_sh;
+  size_t logits, planes, ids, w, blk, offsets, sorted, slot, slot_w, x16, tiles, ntiles, h, out,
+      out_sh;
   size_t total;
   int max_tiles;
 };
@@ -107,6 +110,7 @@ Plan make_plan(const moe_layer *L, int64_t T) {
                        (S ? (Tn + moe::kTileM - 1) / moe::kTileM : 0);
   p.max_tiles = (int)tiles;
   p.logits = take(Tn * E * 4);
+  p.planes = take(L->act_dtype == MOE_ACT_BF16 ? 3 * E * H * 2 : 0);
   p.ids = take(Tn * k * 4);
   p.w = take(Tn * k * 4);
   p.blk = take(NB * E * 4);
@@ -177,6 +181,7 @@ moe::RouteArgs route_args(const moe_layer *L, const void *x, int64_t T) {
 // Routing results go to the caller's buffers when given, else to the workspace.
 void route_targets(moe::RouteArgs &a, const Plan &p, void *ws, const moe_route_out *ro) {
   a.logits = at<float>(ws, p.logits);
+  a.router_planes = at<uint16_t>(ws, p.planes);
   a.blk = at<int32_t>(ws, p.blk);
   a.offsets = at<int32_t>(ws, p.offsets);
   a.tiles = at<int2>(ws, p.tiles);

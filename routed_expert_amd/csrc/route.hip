@@ -10,57 +10,166 @@
 //
 // The scatter here is a stable counting sort (tokens ascending within an expert), so
 // the grouping is a pure function of the routing: no atomics decide any position.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-// ---- router logits for many tokens: z[T,E] = x[T,H] W[E,H]^T + b ------------------------
-// 64 tokens x 64 experts per workgroup, fp32 FMA on the vector ALUs, K staged in LDS
-// in chunks of 32. Each thread owns a 4x4 block of outputs.
-template <bool kBf16>
-__global__ __launch_bounds__(256) void k_router_logits(const void *__restrict__ xv,
-                                                       const float *__restrict__ W,
-                                                       const float *__restrict__ bias,
-                                                       float *__restrict__ z,
-                                                       uint16_t *__restrict__ x16, int T, int H,
-                                                       int E) {
+// ---- router logits for many tokens: z[T,E] = x[T,H] W[E,H]^T + b --------------------------
+// bf16 activations: MFMA with the fp32 router weights split into three bf16 planes
+// (w = hi + mid + lo to ~24 mantissa bits); x is exact in bf16, every product is exact in
+// fp32 and the MFMA accumulates in fp32, so the logits carry fp32-class error.
+// Tile: 64 tokens x 64 experts per workgroup, K in steps of 64; 4 waves in 2x2, each one
+// 32x32 accumulator. Side jobs: the fp16 copy of x for the expert GEMMs (expert tile 0,
+// chunks in kChunkOrder) and zeroing this token block's histogram row (the top-k kernel
+// adds into it).
+namespace {
+constexpr int RP = 64 + 8;  // LDS row pitch (elements)
+}
+
+MOE_DEV void split3(float w, uint16_t &hi, uint16_t &mid, uint16_t &lo) {
+  const __bf16 h = (__bf16)w;
+  const float r1 = w - (float)h;
+  const __bf16 m = (__bf16)r1;
+  const float r2 = r1 - (float)m;
+  hi = __builtin_bit_cast(uint16_t, h);
+  mid = __builtin_bit_cast(uint16_t, m);
+  lo = __builtin_bit_cast(uint16_t, (__bf16)r2);
+}
+
+// Router weights split once per call into three bf16 planes [3][E][H] (workspace).
+__global__ __launch_bounds__(256) void k_router_split(const float *__restrict__ W, size_t n,
+                                                      uint16_t *__restrict__ planes) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n / 4;
+       i += (size_t)gridDim.x * 256) {
+    const float4 f = reinterpret_cast<const float4 *>(W)[i];
+    const float v[4] = {f.x, f.y, f.z, f.w};
+    uint16_t h[4], m[4], l[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) split3(v[q], h[q], m[q], l[q]);
+    reinterpret_cast<uint2 *>(planes)[i] =
+        make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+    reinterpret_cast<uint2 *>(planes + n)[i] =
+        make_uint2(m[0] | ((uint32_t)m[1] << 16), m[2] | ((uint32_t)m[3] << 16));
+    reinterpret_cast<uint2 *>(planes + 2 * n)[i] =
+        make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
+  }
+}
+
+__global__ __launch_bounds__(256) void k_router_mfma(const uint16_t *__restrict__ x,
+                                                     const uint16_t *__restrict__ planes,
+                                                     const float *__restrict__ bias,
+                                                     float *__restrict__ z,
+                                                     uint16_t *__restrict__ x16,
+                                                     int32_t *__restrict__ blk_cnt, int T,
+                                                     int H, int E) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][64 * RP];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][3][64 * RP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  if (tid < 64 && e0 + tid < E) blk_cnt[(size_t)blockIdx.x * E + e0 + tid] = 0;
+  // loader: row lr (token / expert), 16 elements at column lc
+  const int lr = tid >> 2, lc = (tid & 3) * 16;
+  const int t = t0 + lr, e = e0 + lr;
+  const int frow = lane & 31, fk = (lane >> 5) * 8;
+  const size_t plane = (size_t)E * H;
+  uint4 ra[2], rb[3][2];
+  auto gload = [&](int k0) {
+    ra[0] = ra[1] = make_uint4(0, 0, 0, 0);
+    if (t < T) {
+      const uint4 *p = reinterpret_cast<const uint4 *>(x + (size_t)t * H + k0 + lc);
+      ra[0] = p[0];
+      ra[1] = p[1];
+    }
+#pragma unroll
+    for (int pl = 0; pl < 3; ++pl) {
+      rb[pl][0] = rb[pl][1] = make_uint4(0, 0, 0, 0);
+      if (e < E) {
+        const uint4 *p =
+            reinterpret_cast<const uint4 *>(planes + pl * plane + (size_t)e * H + k0 + lc);
+        rb[pl][0] = p[0];
+        rb[pl][1] = p[1];
+      }
+    }
+  };
+  auto lstore = [&](int buf, int k0) {
+    uint4 *pa = reinterpret_cast<uint4 *>(&As[buf][lr * RP + lc]);
+    pa[0] = ra[0];
+    pa[1] = ra[1];
+#pragma unroll
+    for (int pl = 0; pl < 3; ++pl) {
+      uint4 *pb = reinterpret_cast<uint4 *>(&Bs[buf][pl][lr * RP + lc]);
+      pb[0] = rb[pl][0];
+      pb[1] = rb[pl][1];
+    }
+    if (x16 && blockIdx.y == 0 && t < T) {
+      // fp16 copy of x for the expert GEMMs, each 8-element chunk in kChunkOrder
+      uint4 *q = reinterpret_cast<uint4 *>(x16 + (size_t)t * H + k0 + lc);
+      q[0] = bf16x8_to_f16x8_chunk(ra[0]);
+      q[1] = bf16x8_to_f16x8_chunk(ra[1]);
+    }
+  };
+  f32x16_t acc = {};
+  gload(0);
+  lstore(0, 0);
+  __syncthreads();
+  const int nsteps = H / 64;
+  for (int st = 0; st < nsteps; ++st) {
+    const int cur = st & 1;
+    if (st + 1 < nsteps) gload((st + 1) * 64);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int ko = kk * 16 + fk;
+      const bf16x8_t av =
+          *reinterpret_cast<const bf16x8_t *>(&As[cur][(wm * 32 + frow) * RP + ko]);
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl) {
+        const bf16x8_t bv =
+            *reinterpret_cast<const bf16x8_t *>(&Bs[cur][pl][(wn * 32 + frow) * RP + ko]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+      }
+    }
+    if (st + 1 < nsteps) lstore(cur ^ 1, (st + 1) * 64);
+    __syncthreads();
+  }
+  const int col = lane & 31, rq4 = (lane >> 5) * 4;
+  const int ee = e0 + wn * 32 + col;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int tt = t0 + wm * 32 + (r >> 2) * 8 + rq4 + (r & 3);
+    if (tt < T && ee < E) z[(size_t)tt * E + ee] = acc[r] + (bias ? bias[ee] : 0.f);
+  }
+}
+
+// fp32 activations (fp32-weight layers): plain fp32 FMA on the vector ALUs.
+__global__ __launch_bounds__(256) void k_router_f32(const float *__restrict__ x,
+                                                    const float *__restrict__ W,
+                                                    const float *__restrict__ bias,
+                                                    float *__restrict__ z,
+                                                    int32_t *__restrict__ blk_cnt, int T, int H,
+                                                    int E) {
   __shared__ float xs[32][68];
   __shared__ float wsm[32][68];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  if (tid < 64 && e0 + tid < E) blk_cnt[(size_t)blockIdx.x * E + e0 + tid] = 0;
   const int lr = tid >> 2, lk = (tid & 3) * 8;
   float acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-
   for (int k0 = 0; k0 < H; k0 += 32) {
     float xr[8], wr[8];
     const int t = t0 + lr, e = e0 + lr;
     if (t < T) {
-      if (kBf16) {
-        const uint4 u = *reinterpret_cast<const uint4 *>(
-            static_cast<const uint16_t *>(xv) + (size_t)t * H + k0 + lk);
-        xr[0] = bf16lo(u.x); xr[1] = bf16hi(u.x); xr[2] = bf16lo(u.y); xr[3] = bf16hi(u.y);
-        xr[4] = bf16lo(u.z); xr[5] = bf16hi(u.z); xr[6] = bf16lo(u.w); xr[7] = bf16hi(u.w);
-        if (x16 && blockIdx.y == 0) {
-          // fp16 copy of x for the fp16 MFMA GEMMs (exact inside the fp16 range)
-          uint4 h;
-          h.x = bf16x2_to_f16x2(u.x);
-          h.y = bf16x2_to_f16x2(u.y);
-          h.z = bf16x2_to_f16x2(u.z);
-          h.w = bf16x2_to_f16x2(u.w);
-          *reinterpret_cast<uint4 *>(x16 + (size_t)t * H + k0 + lk) = h;
-        }
-      } else {
-        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(xv) +
-                                                           (size_t)t * H + k0 + lk);
-        const float4 a = p[0], b = p[1];
-        xr[0] = a.x; xr[1] = a.y; xr[2] = a.z; xr[3] = a.w;
-        xr[4] = b.x; xr[5] = b.y; xr[6] = b.z; xr[7] = b.w;
-      }
+      const float4 *p = reinterpret_cast<const float4 *>(x + (size_t)t * H + k0 + lk);
+      const float4 a = p[0], b = p[1];
+      xr[0] = a.x; xr[1] = a.y; xr[2] = a.z; xr[3] = a.w;
+      xr[4] = b.x; xr[5] = b.y; xr[6] = b.z; xr[7] = b.w;
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) xr[i] = 0.f;
@@ -104,46 +213,38 @@ __global__ __launch_bounds__(256) void k_router_logits(const void *__restrict__ 
   }
 }
 
-// ---- top-k and per-block histogram for T tokens -----------------------------------------
-// One workgroup per routing block of 64 tokens; each wave handles 16 tokens in order.
-__global__ __launch_bounds__(256) void k_topk_hist(const float *__restrict__ z, int T, int E,
-                                                   int k, int32_t *__restrict__ ids,
-                                                   float *__restrict__ w,
-                                                   int32_t *__restrict__ blk_cnt) {
-  __shared__ int hist[kMaxExperts];
+// ---- top-k, one wave per token; per-block histogram by device atomics -----------------
+// Workgroup = 4 waves = 4 tokens. blk_cnt[t / 64][e] was zeroed by the router kernel.
+__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ z, int T, int E, int k,
+                                              int32_t *__restrict__ ids,
+                                              float *__restrict__ w,
+                                              int32_t *__restrict__ blk_cnt) {
   __shared__ __attribute__((aligned(16))) uint64_t s_topk[4][kTopkScratch];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  hist[tid] = 0;
-  __syncthreads();
-  const int tbase = blockIdx.x * kRouteBlock + wave * 16;
-  for (int tt = 0; tt < 16; ++tt) {
-    const int t = tbase + tt;
-    if (t >= T) break;
-    float v[4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  float v[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int e = lane + kWave * c;
-      v[c] = e < E ? z[(size_t)t * E + e] : -INFINITY;
-    }
-    int sel[kMaxTopK];
-    float sw[kMaxTopK];
-    wave_topk(v, E, k, s_topk[wave], sel, sw);
-    int id = 0;
-    float weight = 0.f;
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j)
-      if (j == lane) {
-        id = sel[j];
-        weight = sw[j];
-      }
-    if (lane < k) {
-      ids[(size_t)t * k + lane] = id;
-      w[(size_t)t * k + lane] = weight;
-      atomicAdd(&hist[id], 1);
-    }
+  for (int c = 0; c < 4; ++c) {
+    const int e = lane + kWave * c;
+    v[c] = e < E ? z[(size_t)t * E + e] : -INFINITY;
   }
-  __syncthreads();
-  if (tid < E) blk_cnt[(size_t)blockIdx.x * E + tid] = hist[tid];
+  int sel[kMaxTopK];
+  float sw[kMaxTopK];
+  wave_topk(v, E, k, s_topk[wave], sel, sw);
+  int id = 0;
+  float weight = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j)
+    if (j == lane) {
+      id = sel[j];
+      weight = sw[j];
+    }
+  if (lane < k) {
+    ids[(size_t)t * k + lane] = id;
+    w[(size_t)t * k + lane] = weight;
+    atomicAdd(&blk_cnt[(size_t)(t / kRouteBlock) * E + id], 1);
+  }
 }
 
 // Inclusive block-wide scan over 256 threads (LDS, Hillis-Steele).
@@ -176,10 +277,16 @@ __global__ __launch_bounds__(256) void k_scan(int32_t *__restrict__ blk_cnt, int
   const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
-    for (int b = 0; b < NB; ++b) {
-      const int c = blk_cnt[(size_t)b * E + e];
-      blk_cnt[(size_t)b * E + e] = run;
-      run += c;
+    // 16 block counts per round: the loads of a round are issued together
+    for (int b0 = 0; b0 < NB; b0 += 16) {
+      int c[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c[i] = b0 + i < NB ? blk_cnt[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (b0 + i < NB) blk_cnt[(size_t)(b0 + i) * E + e] = run;
+        run += c[i];
+      }
     }
   }
   const int incl = block_scan_incl(run, sc);
@@ -210,7 +317,10 @@ __global__ __launch_bounds__(256) void k_scan(int32_t *__restrict__ blk_cnt, int
   }
 }
 
-// ---- stable scatter: slot of every assignment --------------------------------------------
+// ---- stable scatter: slot of every assignment ---------------------------------------
+// One workgroup per routing block of 64 tokens. mask[e] has bit tt set when token t0+tt
+// chose expert e, so the rank of (t, j) inside its expert's run of this block is the
+// number of earlier tokens in the mask: slot = offsets[e] + base[b][e] + rank.
 __global__ __launch_bounds__(256) void k_scatter(const int32_t *__restrict__ ids, int T, int E,
                                                  int k, const int32_t *__restrict__ offsets,
                                                  const int32_t *__restrict__ blk_base,
@@ -218,38 +328,45 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t *__restrict__ ids
                                                  int32_t *__restrict__ sorted_tok,
                                                  int32_t *__restrict__ slot_of,
                                                  float *__restrict__ slot_w) {
-  __shared__ int sid[kRouteBlock * kMaxTopK];
-  const int b = blockIdx.x, t0 = b * kRouteBlock;
-  const int nt = min(kRouteBlock, T - t0);
-  for (int i = threadIdx.x; i < nt * k; i += 256) sid[i] = ids[(size_t)t0 * k + i];
+  __shared__ unsigned long long mask[kMaxExperts];
+  const int b = blockIdx.x, t0 = b * kRouteBlock, tid = threadIdx.x;
+  const int nt = min(kRouteBlock, T - t0), na = nt * k;
+  mask[tid] = 0ull;
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) {
-    int slot = offsets[e] + blk_base[(size_t)b * E + e];
-    for (int tt = 0; tt < nt; ++tt) {
-      for (int j = 0; j < k; ++j) {
-        if (sid[tt * k + j] == e) {
-          sorted_tok[slot] = t0 + tt;
-          slot_of[(size_t)(t0 + tt) * k + j] = slot;
-          if (slot_w) slot_w[slot] = w[(size_t)(t0 + tt) * k + j];
-          ++slot;
-        }
-      }
-    }
+  for (int i = tid; i < na; i += 256) {
+    const int e = ids[(size_t)t0 * k + i];
+    atomicOr(&mask[e], 1ull << (i / k));
+  }
+  __syncthreads();
+  for (int i = tid; i < na; i += 256) {
+    const int tt = i / k, e = ids[(size_t)t0 * k + i];
+    const unsigned long long before = tt ? (mask[e] & (~0ull >> (64 - tt))) : 0ull;
+    const int slot = offsets[e] + blk_base[(size_t)b * E + e] + __popcll(before);
+    sorted_tok[slot] = t0 + tt;
+    slot_of[(size_t)t0 * k + i] = slot;
+    if (slot_w) slot_w[slot] = w[(size_t)t0 * k + i];
   }
 }
 
 // ---- launchers ------------------------------------------------------------------------------
 hipError_t launch_route_prefill(const RouteArgs &a, hipStream_t s) {
   const int NB = (int)((a.T + kRouteBlock - 1) / kRouteBlock);
-  dim3 g1((unsigned)((a.T + 63) / 64), (unsigned)((a.E + 63) / 64));
-  if (a.bf16)
-    MOE_LAUNCH("k_router_logits", (k_router_logits<true>), g1, dim3(256), 0, s, a.x,
-               a.router_w, a.router_b, a.logits, a.x16, (int)a.T, a.H, a.E);
+  const dim3 g1((unsigned)NB, (unsigned)((a.E + 63) / 64));
+  if (a.bf16) {
+    const size_t n = (size_t)a.E * a.H;
+    MOE_LAUNCH("k_router_split", k_router_split,
+               dim3((unsigned)std::min<size_t>((n / 4 + 255) / 256, 2048)), dim3(256), 0, s,
+               a.router_w, n, a.router_planes);
+    MOE_LAUNCH("k_router_mfma", k_router_mfma, g1, dim3(256), 0, s,
+               static_cast<const uint16_t *>(a.x), a.router_planes, a.router_b, a.logits,
+               a.x16, a.blk, (int)a.T, a.H, a.E);
+  }
   else
-    MOE_LAUNCH("k_router_logits", (k_router_logits<false>), g1, dim3(256), 0, s, a.x,
-               a.router_w, a.router_b, a.logits, nullptr, (int)a.T, a.H, a.E);
-  MOE_LAUNCH("k_topk_hist", k_topk_hist, dim3(NB), dim3(256), 0, s, a.logits, (int)a.T, a.E,
-             a.k, a.ids, a.w, a.blk);
+    MOE_LAUNCH("k_router_f32", k_router_f32, g1, dim3(256), 0, s,
+               static_cast<const float *>(a.x), a.router_w, a.router_b, a.logits, a.blk,
+               (int)a.T, a.H, a.E);
+  MOE_LAUNCH("k_topk", k_topk, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, s, a.logits,
+             (int)a.T, a.E, a.k, a.ids, a.w, a.blk);
   MOE_LAUNCH("k_scan", k_scan, dim3(1), dim3(256), 0, s, a.blk, NB, a.E, (int)a.T, a.k, a.S,
              a.offsets, a.counts_user, a.offsets_user, a.tiles, a.n_tiles);
   MOE_LAUNCH("k_scatter", k_scatter, dim3(NB), dim3(256), 0, s, a.ids, (int)a.T, a.E, a.k,

@@ -69,7 +69,8 @@ def ws_bytes(M, layer, T):
     (dict(top_k=9), -2),
     (dict(hidden=2000), -2),
     (dict(inter=500), -2),
-    (dict(hidden=192), -2),             # int4 needs hidden % 128 == 0
+    (dict(hidden=384), -2),             # int4 needs hidden % 256 == 0
+    (dict(inter=192), -2),              # int4 needs inter % 128 == 0
     (dict(act_dtype=0), -2),            # int4 weights with fp32 activations
     (dict(w_format=0), -2),             # fp32 weights with bf16 activations
     (dict(w_format=7), -1),
@@ -77,6 +78,7 @@ def ws_bytes(M, layer, T):
     (dict(w13_s=None), -1),
     (dict(w13_q=0x20008), -1),          # codes must be 16-byte aligned
     (dict(router_b=0x10002), -1),
+    (dict(w2_b=0x70002), -1),           # scales and biases are read as dwords
 ])
 def test_descriptor_validation(M, kw, code):
     st, _ = ws_bytes(M, fake_layer(M, **kw), 16)
