@@ -30,7 +30,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -46,19 +46,21 @@ typedef enum { MOE_ACT_F32 = 0, MOE_ACT_BF16 = 1 } moe_act_dtype;
 /* One layer. Experts 0..E-1 are routed; with n_shared == 1 the shared expert is
  * stacked after them as expert index E.
  *   router_w  float [E, H] row-major;  router_b  float [E] or NULL (added to logits)
- *   MOE_W_INT4_G64 (requires act_dtype == MOE_ACT_BF16):
+ *   MOE_W_INT4_G64 (requires act_dtype == MOE_ACT_BF16), interchange layout:
  *     w13_q uint8 [E+S, 2I, H/2]: row r holds the gate projection for r < I and the up
  *           projection for r >= I; byte j of a row holds element 2j in its low nibble
  *           and element 2j+1 in its high nibble (unsigned codes 0..15)
  *     w13_s, w13_b  bf16 bit patterns [E+S, 2I, H/64]: scale and bias of each group of
  *           64 consecutive elements of a row; weight = scale * code + bias
  *     w2_q uint8 [E+S, H, I/2], w2_s / w2_b bf16 [E+S, H, I/64]: output projection
+ *     w13_t, w13_tsb, w2_t, w2_tsb: the same weights in the tiled layout written by
+ *           moe_pack_weights (NULL until packed); moe_prefill needs them
  *   MOE_W_F32 (requires act_dtype == MOE_ACT_F32):
- *     w13_q float [E+S, 2I, H], w2_q float [E+S, H, I]; the *_s / *_b pointers unused
+ *     w13_q float [E+S, 2I, H], w2_q float [E+S, H, I]; the other weight pointers unused
  * Supported: 1 <= k <= 8, k <= E <= 256, S in {0,1}; H % 64 == 0, I % 64 == 0,
- * and for int4 additionally H % 256 == 0 and I % 128 == 0. Pointers to codes, fp32
- * weights, activations and the workspace must be 16-byte aligned; int4 scale and bias
- * pointers 4-byte aligned. */
+ * and for int4 additionally H % 256 == 0 and I % 128 == 0. Pointers to codes, tiled
+ * arrays, fp32 weights, activations and the workspace must be 16-byte aligned; int4
+ * scale and bias pointers 4-byte aligned. */
 typedef struct {
   int32_t abi_version;  /* must be MOE_ABI_VERSION */
   int32_t hidden, inter, n_experts, top_k, n_shared;
@@ -67,6 +69,7 @@ typedef struct {
   const float *router_b;
   const void *w13_q, *w13_s, *w13_b;
   const void *w2_q, *w2_s, *w2_b;
+  const void *w13_t, *w13_tsb, *w2_t, *w2_tsb;
 } moe_layer;
 
 /* Routing results, all caller-owned device buffers of int32 / float:
@@ -96,6 +99,23 @@ const char *moe_last_error(void);
 /* Workspace size in bytes for calls with up to max_tokens tokens (host out param).
  * No call needs the workspace to hold any particular contents on entry. */
 moe_status moe_workspace_bytes(const moe_layer *layer, int64_t max_tokens, size_t *bytes);
+
+/* Bytes of device memory moe_pack_weights needs for an int4 layer (host out param). */
+moe_status moe_pack_bytes(const moe_layer *layer, size_t *bytes);
+
+/* One-time repack of an int4 layer's expert weights into the tiled layout read by the
+ * grouped GEMMs of moe_prefill ("Dequantize weights during matrix multiplication": the
+ * weights stay int4; only their order changes). Writes into caller memory `dst` (device,
+ * 256-byte aligned, at least moe_pack_bytes) and sets *packed (host) to a copy of *layer
+ * whose w13_t, w13_tsb, w2_t, w2_tsb point into dst. The interchange arrays are only
+ * read. Layout, for a matrix with R rows (2I for W13, H for W2) and reduction length K,
+ * per expert, in blocks of 64 rows (W13 block j: gate rows 32j..32j+31, then up rows
+ * 32j..32j+31; W2 block j: rows 64j..64j+63) and steps of 64 along K:
+ *   *_t    uint8 [E+S][R/64][K/64][64 rows][32 bytes]  (the row's 32 code bytes of the step)
+ *   *_tsb  bf16  [E+S][R/64][ceil(K/256)][64 rows][4 groups][scale, bias]  (zero padded)
+ * Stream-ordered like every call; dst must not overlap the source arrays. */
+moe_status moe_pack_weights(const moe_layer *layer, void *dst, size_t dst_bytes,
+                            moe_layer *packed, void *stream);
 
 /* Router, top-k and grouping: logits z = x W_r^T (+ b), k experts by (z desc, id asc),
  * weights = softmax restricted to the selection, then the per-expert histogram,

@@ -86,11 +86,18 @@ __device__ constexpr int kChunkPos[8] = {0, 2, 4, 6, 1, 3, 5, 7};
 // 1024 is exact, and one fused multiply-add rounds s*q + b once. Output pairs are
 // (q0,q4), (q1,q5), (q2,q6), (q3,q7). s2 / b2 hold the scale / bias twice; both must be
 // representable in fp16 (true for bf16 values in [2^-14, 65504]).
+MOE_DEV uint32_t and_or(uint32_t v, uint32_t mask, uint32_t bits) {
+  // (v & mask) | bits in one v_and_or_b32 (the compiler emits two instructions here)
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "s"(mask), "v"(bits));
+  return r;
+}
+
 MOE_DEV uint4 dequant8_pk(uint32_t w, f16x2_t s2, f16x2_t b2) {
   constexpr uint32_t kMask = 0x000F000Fu, kMagic = 0x64006400u;
   const f16x2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
-  const uint32_t t0 = (w & kMask) | kMagic, t1 = ((w >> 4) & kMask) | kMagic;
-  const uint32_t t2 = ((w >> 8) & kMask) | kMagic, t3 = ((w >> 12) & kMask) | kMagic;
+  const uint32_t t0 = and_or(w, kMask, kMagic), t1 = and_or(w >> 4, kMask, kMagic);
+  const uint32_t t2 = and_or(w >> 8, kMask, kMagic), t3 = and_or(w >> 12, kMask, kMagic);
   uint4 r;
   r.x = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(
                                          __builtin_bit_cast(f16x2_t, t0) - k1024, s2, b2));

@@ -16,9 +16,9 @@
 //     per lane per K step). Only the gathered activation rows (shared by the four waves)
 //     and the raw codes are staged in LDS.
 //
-// Tile: 128 slot rows x 256 weight rows, K in steps of 64 (one quantisation group).
-// Wave w computes all 128 rows x weight rows {w's 64}: 4 x 2 tiles of
-// v_mfma_f32_32x32x16_f16 (128 fp32 accumulators).
+// Tile: up to 128 slot rows x 256 weight rows, K in steps of 64 (one quantisation group).
+// Wave w computes all rows x weight rows {w's 64}: MB x 2 tiles of v_mfma_f32_32x32x16_f16
+// (up to 128 fp32 accumulators), MB = the tile's 32-row blocks that hold valid rows.
 //   gate/up: weight rows = gate rows i0 + 32w .. +32 and the matching up rows, so the gate
 //            and up accumulators of a (row, i) sit in the same lane and SwiGLU is applied
 //            in registers; h is written in slot order [slots, I] fp16.
@@ -46,10 +46,9 @@ constexpr int kStages = 3;                         // LDS ring depth (loads run 
 constexpr int kABytes = BM * BK * 2;               // activation rows of one step: 16 KB
 constexpr int kBBytes = 4 * 2 * 1024;              // codes: 4 waves x 2 columns x 64 lanes x 16 B
 constexpr int kStageBytes = kABytes + kBBytes;
-// Scales and biases travel as dwords: the dword at an even group index g holds groups g and
-// g+1, i.e. K steps g and g+1, so they are loaded every other step into a 2-slot ring
-// (4 arrays x 64 lanes x 4 B per wave and slot).
-constexpr int kSSlot = 4 * 4 * 256;
+// Scales and biases arrive four K steps at a time (one tiled 1 KB block per wave: 64 rows x
+// 4 groups x {scale, bias}) into a 2-slot ring.
+constexpr int kSSlot = 4 * 1024;
 constexpr int kSmemBytes = kStages * kStageBytes + 2 * kSSlot;  // 80 KB: two workgroups per CU
 }  // namespace
 
@@ -58,35 +57,32 @@ MOE_DEV f16x2_t f16_pair_from_bf16(uint16_t v) {
   return f16x2_t{h, h};
 }
 
-template <bool kGateUp>
-__global__ __launch_bounds__(256, 2) void k_grouped(GroupedArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+template <int N>
+MOE_DEV void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
-  // XCD-aware tile order: workgroup ids are dealt round-robin over the 8 XCDs; this map
-  // gives each XCD all N tiles of one M tile back to back, so the activation rows of a
-  // tile are fetched into that XCD's L2 once.
-  const int nN = kGateUp ? a.I / (BNW / 2) : a.H / BNW;
-  const int id = blockIdx.x, xcd = id & 7, j = id >> 3;
-  const int n_tile = j % nN, m_tile = (j / nN) * 8 + xcd;
-  if (m_tile >= *a.n_tiles) return;
-  const int2 tile = a.tiles[m_tile];
-  const int e = tile.x, row0 = tile.y;
+// One tile: rows [row0, row0 + nvalid) of group e, weight rows of N tile n_tile. MB is the
+// number of 32-row blocks holding valid rows (1..4); blocks past them are neither loaded nor
+// multiplied, so a group's last, partial tile costs MFMA work in proportion to its rows.
+template <bool kGateUp, int MB>
+MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, int nvalid,
+                          int n_tile) {
   const int gbase = a.offsets[e];
-  const int nvalid = min(BM, a.offsets[e + 1] - gbase - row0);
   const int slot0 = gbase + row0;
   const int K = kGateUp ? a.H : a.I;
   const int Nw = kGateUp ? 2 * a.I : a.H;
-
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   // Activation rows of one step land in LDS swizzled: 16-byte chunk c of row r sits at
   // chunk c ^ ((r >> 1) & 7) of the row, which keeps the MFMA operand reads (16 rows, one
-  // chunk) free of bank conflicts. Each wave loads rows 32*wave .. +32 with 4 direct
-  // loads of 8 rows; lane l fills physical chunk l % 8 of row l / 8 of such a group.
-  const uint16_t *asrc[4];
+  // chunk) free of bank conflicts. The 4*MB groups of 8 rows are spread over the waves:
+  // direct load j of wave w fills row group w + 4j; lane l fills physical chunk l % 8 of
+  // row l / 8 of its group.
+  const uint16_t *asrc[MB];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = 32 * wave + 8 * q + (lane >> 3);
+  for (int j = 0; j < MB; ++j) {
+    const int r = 8 * (wave + 4 * j) + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     const int rr = min(r, nvalid - 1);
     const uint16_t *row;
@@ -96,35 +92,29 @@ __global__ __launch_bounds__(256, 2) void k_grouped(GroupedArgs a) {
     } else {
       row = a.h16 + (size_t)(slot0 + rr) * a.I;
     }
-    asrc[q] = row + 8 * c;
+    asrc[j] = row + 8 * c;
   }
 
-  // this lane's two B columns (weight rows) and K half
-  const int bn = lane & 31, bh = lane >> 5;
-  int wrow0, wrow1;
-  if (kGateUp) {
-    wrow0 = n_tile * (BNW / 2) + 32 * wave + bn;
-    wrow1 = a.I + wrow0;
-  } else {
-    wrow0 = n_tile * BNW + 64 * wave + bn;
-    wrow1 = wrow0 + 32;
-  }
-  const uint8_t *q_base = kGateUp ? a.wt.w13_q : a.wt.w2_q;
-  const uint16_t *s_base = kGateUp ? a.wt.w13_s : a.wt.w2_s;
-  const uint16_t *b_base = kGateUp ? a.wt.w13_b : a.wt.w2_b;
-  const size_t r0 = (size_t)e * Nw + wrow0, r1 = (size_t)e * Nw + wrow1;
-  const uint8_t *bq0 = q_base + r0 * (size_t)(K / 2) + 16 * bh;
-  const uint8_t *bq1 = q_base + r1 * (size_t)(K / 2) + 16 * bh;
-  const uint16_t *bs0 = s_base + r0 * (size_t)(K / kGroup), *bb0 = b_base + r0 * (size_t)(K / kGroup);
-  const uint16_t *bs1 = s_base + r1 * (size_t)(K / kGroup), *bb1 = b_base + r1 * (size_t)(K / kGroup);
+  // This wave's weight rows are one 64-row block of the tiled layout: gate rows 32w..+32
+  // of the N tile and the matching up rows (gate/up), or output rows 64w..+64 (down). Per
+  // K step the block's codes are 2 KB contiguous (column block c = rows 32c..32c+31 at
+  // c * 1 KB); its scales and biases come as 1 KB per four steps.
+  const int nb = kGateUp ? 2 * a.I / 64 : a.H / 64;
+  const int blk = n_tile * 4 + wave;
+  const int ns = K / BK, ns4 = (ns + 3) / 4;
+  const uint8_t *tq = (kGateUp ? a.wt.w13_t : a.wt.w2_t) +
+                      ((size_t)e * nb + blk) * ns * 2048 + 16 * lane;
+  const uint16_t *tsb = (kGateUp ? a.wt.w13_tsb : a.wt.w2_tsb) +
+                        ((size_t)e * nb + blk) * ns4 * 512 + 8 * lane;
 
   // The direct-to-LDS loads and the step barrier are issued as inline assembly: the
   // compiler cannot tell the ring stages apart and would wait for every load in flight
   // (vmcnt(0)) before each LDS read and at each barrier, which serialises the pipeline.
-  // Completion is tracked explicitly instead: before reading stage `st`, each wave waits
-  // until only the loads of step st+1 are outstanding (6, plus 4 scale/bias dwords when
-  // st+1 is even), then all waves meet at s_barrier. Compiler-generated vmcnt waits stay
-  // correct (outstanding loads only add).
+  // Completion is tracked explicitly instead: during step st each wave waits until only
+  // the loads of step st+2 are outstanding (MB + 2, plus the scale/bias block when st+2 is
+  // a multiple of 4), so its own loads of step st+1 have landed; the barrier at the top of
+  // step st+1 then covers every wave's. Compiler-generated vmcnt waits stay correct (outstanding
+  // loads only add).
   // M0 holds the wave-uniform LDS byte address; lane l's data lands at M0 + l * size.
   // The s_nop covers the wait states a load that reads M0 needs after M0 is written.
   const uint32_t smem_lds = (uint32_t)(uintptr_t)smem;
@@ -132,96 +122,135 @@ __global__ __launch_bounds__(256, 2) void k_grouped(GroupedArgs a) {
 #define MOE_DMA16(gptr, lds)                                                            \
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %0, off"         \
                :: "v"(gptr), "s"(lds) : "memory", "m0")
-#define MOE_DMA4(gptr, lds)                                                             \
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 1\n\tglobal_load_lds_dword %0, off"           \
-               :: "v"(gptr), "s"(lds) : "memory", "m0")
-  // issue the direct-to-LDS loads of K step `step` (6 memory instructions per wave, 10 on
-  // even steps, which also fetch the scales and biases of this step and the next)
+  // issue the direct-to-LDS loads of K step `step` (MB + 2 memory instructions per wave,
+  // one more on every fourth step, which fetches the scales and biases of four steps)
 #define MOE_ISSUE(step)                                                                 \
   do {                                                                                  \
     const uint32_t base_ = smem_lds + ((step) % kStages) * kStageBytes;                 \
     const int k0_ = (step) * BK;                                                        \
-    _Pragma("unroll") for (int q = 0; q < 4; ++q)                                       \
-      MOE_DMA16(asrc[q] + k0_, base_ + (32 * wave_u + 8 * q) * 128);                    \
+    _Pragma("unroll") for (int j = 0; j < MB; ++j)                                      \
+      MOE_DMA16(asrc[j] + k0_, base_ + (wave_u + 4 * j) * 1024);                        \
     const uint32_t bb_ = base_ + kABytes + wave_u * 2048;                               \
-    MOE_DMA16(bq0 + k0_ / 2, bb_);                                                      \
-    MOE_DMA16(bq1 + k0_ / 2, bb_ + 1024);                                               \
-    if (((step) & 1) == 0) {                                                            \
+    MOE_DMA16(tq + (size_t)(step) * 2048, bb_);                                         \
+    MOE_DMA16(tq + (size_t)(step) * 2048 + 1024, bb_ + 1024);                           \
+    if (((step) & 3) == 0) {                                                            \
       const uint32_t sb_ =                                                              \
-          smem_lds + kStages * kStageBytes + (((step) >> 1) & 1) * kSSlot + wave_u * 1024; \
-      MOE_DMA4(bs0 + (step), sb_);                                                      \
-      MOE_DMA4(bb0 + (step), sb_ + 256);                                                \
-      MOE_DMA4(bs1 + (step), sb_ + 512);                                                \
-      MOE_DMA4(bb1 + (step), sb_ + 768);                                                \
+          smem_lds + kStages * kStageBytes + (((step) >> 2) & 1) * kSSlot + wave_u * 1024; \
+      MOE_DMA16(tsb + (size_t)((step) >> 2) * 512, sb_);                                \
     }                                                                                   \
   } while (0)
 
-  f32x16_t acc[4][2];
+  f32x16_t acc[MB][2];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) acc[m][0] = acc[m][1] = f32x16_t{};
+  for (int m = 0; m < MB; ++m) acc[m][0] = acc[m][1] = f32x16_t{};
 
   const int nsteps = K / BK;
-  const int arow_l = lane & 31, ahalf = lane >> 5;
+  // A operand of lane l: row 32m + l % 32, logical chunk 4*(l / 32) + kk of the step
+  const int arow_l = lane & 31, ahalf = lane >> 5, asw = (arow_l >> 1) & 7;
+
+  // This wave's codes, scales and biases of a step come from its own direct loads, so
+  // they are read into registers as soon as this wave's loads of that step have landed,
+  // half a step early and without a barrier; only the activation rows, which all four
+  // waves load together, wait for the step barrier.
+  uint32_t w0[4], w1[4];
+  f16x2_t s0, b0, s1, b1;
+  const int bn = lane & 31, bh = lane >> 5;
+#define MOE_READ_B(step)                                                                \
+  do {                                                                                  \
+    const uint8_t *bsrc_ = smem + ((step) % kStages) * kStageBytes + kABytes + wave * 2048 + \
+                           32 * bn + 16 * bh;                                           \
+    const uint4 q0_ = *reinterpret_cast<const uint4 *>(bsrc_);                          \
+    const uint4 q1_ = *reinterpret_cast<const uint4 *>(bsrc_ + 1024);                   \
+    const uint32_t *sv_ = reinterpret_cast<const uint32_t *>(                           \
+        smem + kStages * kStageBytes + (((step) >> 2) & 1) * kSSlot + wave * 1024 + 16 * bn + \
+        4 * ((step) & 3));                                                              \
+    const uint32_t sb0_ = sv_[0], sb1_ = sv_[128];                                      \
+    s0 = f16_pair_from_bf16((uint16_t)sb0_);                                            \
+    b0 = f16_pair_from_bf16((uint16_t)(sb0_ >> 16));                                    \
+    s1 = f16_pair_from_bf16((uint16_t)sb1_);                                            \
+    b1 = f16_pair_from_bf16((uint16_t)(sb1_ >> 16));                                    \
+    w0[0] = q0_.x; w0[1] = q0_.y; w0[2] = q0_.z; w0[3] = q0_.w;                         \
+    w1[0] = q1_.x; w1[1] = q1_.y; w1[2] = q1_.z; w1[3] = q1_.w;                         \
+  } while (0)
+
   // every lane's source pointers are computed (their loads done) before the first DMA
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   MOE_ISSUE(0);
   if (nsteps > 1) MOE_ISSUE(1);
+  // step 0's own loads: everything after them is step 1's (MB + 2 loads, step 1 is odd)
+  if (nsteps > 1)
+    wait_vmcnt<MB + 2>();
+  else
+    wait_vmcnt<0>();
+  MOE_READ_B(0);
+  f16x8_t bc0 = __builtin_bit_cast(f16x8_t, dequant8_pk(w0[0], s0, b0));
+  f16x8_t bc1 = __builtin_bit_cast(f16x8_t, dequant8_pk(w1[0], s1, b1));
   for (int st = 0; st < nsteps; ++st) {
-    // this wave's loads of step st have landed (step st+1's may still be in flight),
-    // then everyone's have, and everyone is done with the stage step st+2 will reuse
-    if (st + 1 < nsteps) {
-      if (st & 1)
-        asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    } else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // every wave's loads of step st have landed (each wave waited for its own before its
+    // mid-step read of step st's codes), and every wave is done with the stage step st+2
+    // will reuse
     asm volatile("s_barrier" ::: "memory");
-    if (st + 2 < nsteps) MOE_ISSUE(st + 2);
-    const uint8_t *base = smem + (st % kStages) * kStageBytes;
-    const uint8_t *bsrc = base + kABytes + wave * 2048;
-    const uint32_t *sv = reinterpret_cast<const uint32_t *>(
-        smem + kStages * kStageBytes + ((st >> 1) & 1) * kSSlot + wave * 1024);
-    const uint4 q0 = *reinterpret_cast<const uint4 *>(bsrc + 16 * lane);
-    const uint4 q1 = *reinterpret_cast<const uint4 *>(bsrc + 1024 + 16 * lane);
-    const int sh = 16 * (st & 1);
-    const f16x2_t s0 = f16_pair_from_bf16((uint16_t)(sv[lane] >> sh));
-    const f16x2_t b0 = f16_pair_from_bf16((uint16_t)(sv[64 + lane] >> sh));
-    const f16x2_t s1 = f16_pair_from_bf16((uint16_t)(sv[128 + lane] >> sh));
-    const f16x2_t b1 = f16_pair_from_bf16((uint16_t)(sv[192 + lane] >> sh));
-    const uint32_t w0[4] = {q0.x, q0.y, q0.z, q0.w}, w1[4] = {q1.x, q1.y, q1.z, q1.w};
-    f16x8_t bc0 = __builtin_bit_cast(f16x8_t, dequant8_pk(w0[0], s0, b0));
-    f16x8_t bc1 = __builtin_bit_cast(f16x8_t, dequant8_pk(w1[0], s1, b1));
+    const uint8_t *arow = smem + (st % kStages) * kStageBytes + arow_l * 128;
+    // A fragments are double-buffered: substep kk+1's are read while kk's MFMAs run
+    f16x8_t av[2][MB];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+      av[0][m] = *reinterpret_cast<const f16x8_t *>(arow + m * 4096 + ((4 * ahalf) ^ asw) * 16);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      f16x8_t av[4];
+      if (kk < 3) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int r = 32 * m + arow_l;
-        const int pc = (4 * ahalf + kk) ^ ((r >> 1) & 7);
-        av[m] = *reinterpret_cast<const f16x8_t *>(base + r * 128 + pc * 16);
+        for (int m = 0; m < MB; ++m)
+          av[(kk + 1) & 1][m] = *reinterpret_cast<const f16x8_t *>(
+              arow + m * 4096 + ((4 * ahalf + kk + 1) ^ asw) * 16);
       }
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[m], bc0, acc[m][0], 0, 0, 0);
-        acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[m], bc1, acc[m][1], 0, 0, 0);
+      for (int m = 0; m < MB; ++m) {
+        acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[kk & 1][m], bc0, acc[m][0], 0, 0, 0);
+        acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[kk & 1][m], bc1, acc[m][1], 0, 0, 0);
+      }
+      if (kk == 0 && st + 2 < nsteps) MOE_ISSUE(st + 2);
+      if (kk == 2 && st + 1 < nsteps) {
+        // this wave's loads of step st+1 have landed once only step st+2's are younger
+        if (st + 2 < nsteps) {
+          if (((st + 2) & 3) == 0)
+            wait_vmcnt<MB + 3>();
+          else
+            wait_vmcnt<MB + 2>();
+        } else {
+          wait_vmcnt<0>();
+        }
       }
       if (kk < 3) {
         // next substep's weights while the MFMAs above run
         bc0 = __builtin_bit_cast(f16x8_t, dequant8_pk(w0[kk + 1], s0, b0));
         bc1 = __builtin_bit_cast(f16x8_t, dequant8_pk(w1[kk + 1], s1, b1));
+        // A wave issues in order: interleave the dequantisation (and the next fragments'
+        // LDS reads) between the MFMAs so the vector ALU works in the matrix unit's shadow
+        // instead of after the last MFMA of the substep.
+#pragma unroll
+        for (int i = 0; i < 2 * MB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // 1 MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, (40 + 2 * MB - 1) / (2 * MB), 0);  // VALU
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                   // 1 LDS read
+        }
+      } else if (st + 1 < nsteps) {
+        // the next step's codes and its first substep's weights, before its barrier
+        MOE_READ_B(st + 1);
+        bc0 = __builtin_bit_cast(f16x8_t, dequant8_pk(w0[0], s0, b0));
+        bc1 = __builtin_bit_cast(f16x8_t, dequant8_pk(w1[0], s1, b1));
       }
     }
   }
+#undef MOE_READ_B
 #undef MOE_ISSUE
 #undef MOE_DMA16
-#undef MOE_DMA4
 
   // 32x32 accumulator layout: lane l holds column l%32, register r holds row
   // 8*(r/4) + 4*(l/32) + r%4.
   const int col = lane & 31, rq4 = (lane >> 5) * 4;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < MB; ++m) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = 32 * m + (r >> 2) * 8 + rq4 + (r & 3);
@@ -245,6 +274,28 @@ __global__ __launch_bounds__(256, 2) void k_grouped(GroupedArgs a) {
         }
       }
     }
+  }
+}
+
+template <bool kGateUp>
+__global__ __launch_bounds__(256, 2) void k_grouped(GroupedArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+
+  // XCD-aware tile order: workgroup ids are dealt round-robin over the 8 XCDs; this map
+  // gives each XCD all N tiles of one M tile back to back, so the activation rows of a
+  // tile are fetched into that XCD's L2 once.
+  const int nN = kGateUp ? a.I / (BNW / 2) : a.H / BNW;
+  const int id = blockIdx.x, xcd = id & 7, j = id >> 3;
+  const int n_tile = j % nN, m_tile = (j / nN) * 8 + xcd;
+  if (m_tile >= *a.n_tiles) return;
+  const int2 tile = a.tiles[m_tile];
+  const int e = tile.x, row0 = tile.y;
+  const int nvalid = min(BM, a.offsets[e + 1] - a.offsets[e] - row0);
+  switch ((nvalid + 31) >> 5) {
+    case 1: grouped_tile<kGateUp, 1>(a, smem, e, row0, nvalid, n_tile); break;
+    case 2: grouped_tile<kGateUp, 2>(a, smem, e, row0, nvalid, n_tile); break;
+    case 3: grouped_tile<kGateUp, 3>(a, smem, e, row0, nvalid, n_tile); break;
+    default: grouped_tile<kGateUp, 4>(a, smem, e, row0, nvalid, n_tile); break;
   }
 }
 

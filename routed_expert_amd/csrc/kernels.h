@@ -48,11 +48,26 @@ struct RouteArgs {
 hipError_t launch_route_prefill(const RouteArgs &a, hipStream_t s);
 
 struct ExpertWeights {
-  const uint8_t *w13_q, *w2_q;     // int4 codes
+  const uint8_t *w13_q, *w2_q;     // int4 codes, interchange layout
   const uint16_t *w13_s, *w13_b;   // bf16 scale / bias
   const uint16_t *w2_s, *w2_b;
+  const uint8_t *w13_t, *w2_t;     // int4 codes, tiled layout (moe_pack_weights)
+  const uint16_t *w13_tsb, *w2_tsb;  // tiled {scale, bias} pairs
   const float *w13_f, *w2_f;       // fp32 weights (MOE_W_F32)
 };
+
+// Repack of one stacked int4 matrix (n_mat experts of rows x K) into the tiled layout.
+struct PackArgs {
+  const uint8_t *q;
+  const uint16_t *sc, *bi;
+  int rows, K, n_mat, inter;
+  bool gate_up;
+  uint8_t *t;
+  uint16_t *tsb;
+};
+size_t tiled_code_bytes(int n_mat, int rows, int K);
+size_t tiled_sb_bytes(int n_mat, int rows, int K);
+hipError_t launch_pack(const PackArgs &a, hipStream_t s);
 
 // Grouped int4 GEMMs of the prefill path (fp16 operands, fp32 accumulation).
 struct GroupedArgs {

@@ -147,11 +147,45 @@ moe::ExpertWeights weights_of(const moe_layer *L) {
     w.w13_b = static_cast<const uint16_t *>(L->w13_b);
     w.w2_s = static_cast<const uint16_t *>(L->w2_s);
     w.w2_b = static_cast<const uint16_t *>(L->w2_b);
+    w.w13_t = static_cast<const uint8_t *>(L->w13_t);
+    w.w2_t = static_cast<const uint8_t *>(L->w2_t);
+    w.w13_tsb = static_cast<const uint16_t *>(L->w13_tsb);
+    w.w2_tsb = static_cast<const uint16_t *>(L->w2_tsb);
   } else {
     w.w13_f = static_cast<const float *>(L->w13_q);
     w.w2_f = static_cast<const float *>(L->w2_q);
   }
   return w;
+}
+
+// The grouped GEMMs read the tiled copy written by moe_pack_weights.
+moe_status check_tiled(const moe_layer *L) {
+  if (!L->w13_t || !L->w13_tsb || !L->w2_t || !L->w2_tsb)
+    return fail(MOE_E_INVALID, "int4 prefill needs the tiled weights (call moe_pack_weights)");
+  if (!aligned16(L->w13_t) || !aligned16(L->w13_tsb) || !aligned16(L->w2_t) ||
+      !aligned16(L->w2_tsb))
+    return fail(MOE_E_INVALID, "tiled weight pointers must be 16-byte aligned");
+  return MOE_OK;
+}
+
+struct PackPlan {
+  size_t w13_t, w13_tsb, w2_t, w2_tsb, total;
+};
+
+PackPlan pack_plan(const moe_layer *L) {
+  const int n = L->n_experts + L->n_shared, H = L->hidden, I = L->inter;
+  PackPlan p{};
+  size_t off = 0;
+  p.w13_t = off;
+  off += align256(moe::tiled_code_bytes(n, 2 * I, H));
+  p.w13_tsb = off;
+  off += align256(moe::tiled_sb_bytes(n, 2 * I, H));
+  p.w2_t = off;
+  off += align256(moe::tiled_code_bytes(n, H, I));
+  p.w2_tsb = off;
+  off += align256(moe::tiled_sb_bytes(n, H, I));
+  p.total = off;
+  return p;
 }
 
 moe_status check_ws(const moe_layer *L, int64_t T, void *ws, size_t ws_bytes, Plan *p) {
@@ -251,6 +285,62 @@ moe_status moe_workspace_bytes(const moe_layer *layer, int64_t max_tokens, size_
   return MOE_OK;
 }
 
+moe_status moe_pack_bytes(const moe_layer *layer, size_t *bytes) {
+  g_err.clear();
+  moe_status st = check_layer(layer);
+  if (st) return st;
+  if (!bytes) return fail(MOE_E_INVALID, "bytes is NULL");
+  if (layer->w_format != MOE_W_INT4_G64)
+    return fail(MOE_E_UNSUPPORTED, "only int4 layers are packed");
+  *bytes = pack_plan(layer).total;
+  return MOE_OK;
+}
+
+moe_status moe_pack_weights(const moe_layer *layer, void *dst, size_t dst_bytes,
+                            moe_layer *packed, void *stream) {
+  g_err.clear();
+  moe_status st = check_layer(layer);
+  if (st) return st;
+  if (layer->w_format != MOE_W_INT4_G64)
+    return fail(MOE_E_UNSUPPORTED, "only int4 layers are packed");
+  if (!packed) return fail(MOE_E_INVALID, "packed is NULL");
+  if (!dst || (reinterpret_cast<uintptr_t>(dst) & 255u))
+    return fail(MOE_E_INVALID, "dst must be non-NULL and 256-byte aligned");
+  const PackPlan pp = pack_plan(layer);
+  if (dst_bytes < pp.total)
+    return fail(MOE_E_WORKSPACE, "dst holds %zu bytes, packing needs %zu", dst_bytes, pp.total);
+  const int n = layer->n_experts + layer->n_shared;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  moe::PackArgs a{};
+  a.n_mat = n;
+  a.inter = layer->inter;
+  a.gate_up = true;
+  a.rows = 2 * layer->inter;
+  a.K = layer->hidden;
+  a.q = static_cast<const uint8_t *>(layer->w13_q);
+  a.sc = static_cast<const uint16_t *>(layer->w13_s);
+  a.bi = static_cast<const uint16_t *>(layer->w13_b);
+  a.t = at<uint8_t>(dst, pp.w13_t);
+  a.tsb = at<uint16_t>(dst, pp.w13_tsb);
+  hipError_t e = moe::launch_pack(a, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_pack_weights gate/up");
+  a.gate_up = false;
+  a.rows = layer->hidden;
+  a.K = layer->inter;
+  a.q = static_cast<const uint8_t *>(layer->w2_q);
+  a.sc = static_cast<const uint16_t *>(layer->w2_s);
+  a.bi = static_cast<const uint16_t *>(layer->w2_b);
+  a.t = at<uint8_t>(dst, pp.w2_t);
+  a.tsb = at<uint16_t>(dst, pp.w2_tsb);
+  if ((e = moe::launch_pack(a, s)) != hipSuccess) return hip_fail(e, "moe_pack_weights down");
+  *packed = *layer;
+  packed->w13_t = at<uint8_t>(dst, pp.w13_t);
+  packed->w13_tsb = at<uint16_t>(dst, pp.w13_tsb);
+  packed->w2_t = at<uint8_t>(dst, pp.w2_t);
+  packed->w2_tsb = at<uint16_t>(dst, pp.w2_tsb);
+  return MOE_OK;
+}
+
 moe_status moe_route(const moe_layer *layer, const void *x, int64_t T, const moe_route_out *out,
                      void *ws, size_t ws_bytes, void *stream) {
   g_err.clear();
@@ -283,9 +373,9 @@ moe_status moe_prefill(const moe_layer *layer, const void *x, int64_t T, void *y
     return fail(MOE_E_INVALID, "x and y must be non-NULL and 16-byte aligned");
   if (residual && !aligned16(residual)) return fail(MOE_E_INVALID, "residual misaligned");
   if (route_out && (st = check_route_out(route_out))) return st;
+  if (layer->w_format == MOE_W_INT4_G64 && (st = check_tiled(layer))) return st;
   Plan p;
   if ((st = check_ws(layer, T, ws, ws_bytes, &p))) return st;
-  if (T == 0) return MOE_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   moe::RouteArgs ra = route_args(layer, x, T);
   route_targets(ra, p, ws, route_out);

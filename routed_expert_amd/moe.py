@@ -18,14 +18,14 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
 W_F32, W_INT4_G64 = 0, 1
 ACT_F32, ACT_BF16 = 0, 1
 
-EXPORTS = ("moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_route",
-           "moe_prefill", "moe_decode", "moe_rmsnorm", "moe_profile_enable",
-           "moe_profile_query", "moe_profile_reset")
+EXPORTS = ("moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_pack_bytes",
+           "moe_pack_weights", "moe_route", "moe_prefill", "moe_decode", "moe_rmsnorm",
+           "moe_profile_enable", "moe_profile_query", "moe_profile_reset")
 
 
 class MoeLayer(ctypes.Structure):
@@ -36,7 +36,9 @@ class MoeLayer(ctypes.Structure):
                 ("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
                 ("w13_q", ctypes.c_void_p), ("w13_s", ctypes.c_void_p),
                 ("w13_b", ctypes.c_void_p), ("w2_q", ctypes.c_void_p),
-                ("w2_s", ctypes.c_void_p), ("w2_b", ctypes.c_void_p)]
+                ("w2_s", ctypes.c_void_p), ("w2_b", ctypes.c_void_p),
+                ("w13_t", ctypes.c_void_p), ("w13_tsb", ctypes.c_void_p),
+                ("w2_t", ctypes.c_void_p), ("w2_tsb", ctypes.c_void_p)]
 
 
 class MoeRouteOut(ctypes.Structure):
@@ -80,6 +82,8 @@ def lib():
         "moe_abi_version": ([], I32),
         "moe_last_error": ([], ctypes.c_char_p),
         "moe_workspace_bytes": ([P, I64, ctypes.POINTER(SZ)], ctypes.c_int),
+        "moe_pack_bytes": ([P, ctypes.POINTER(SZ)], ctypes.c_int),
+        "moe_pack_weights": ([P, P, SZ, P, P], ctypes.c_int),
         "moe_route": ([P, P, I64, P, P, SZ, P], ctypes.c_int),
         "moe_prefill": ([P, P, I64, P, P, P, P, SZ, P], ctypes.c_int),
         "moe_decode": ([P, P, P, P, P, SZ, P], ctypes.c_int),
@@ -141,6 +145,13 @@ class DeviceLayer:
                              *[None if g(n) is None else g(n).data_ptr() for n in
                                ("router_w", "router_b", "w13_q", "w13_s", "w13_b",
                                 "w2_q", "w2_s", "w2_b")])
+        if fmt == "int4":
+            self.desc = moe_pack_weights(self)
+
+    def packed_bytes(self) -> int:
+        n = ctypes.c_size_t(0)
+        _check("moe_pack_bytes", lib().moe_pack_bytes(self.ref, ctypes.byref(n)))
+        return n.value
 
     @classmethod
     def from_host(cls, layer, device="cuda"):
@@ -168,6 +179,20 @@ class DeviceLayer:
     @property
     def act_dtype(self):
         return torch.bfloat16 if self.fmt == "int4" else torch.float32
+
+
+def moe_pack_weights(layer: DeviceLayer, stream=None) -> MoeLayer:
+    """Tiled copy of an int4 layer's expert weights (kept alive in layer.t["tiled"]);
+    returns the descriptor that points at both layouts."""
+    device = layer.t["w13_q"].device
+    dst = torch.empty(layer.packed_bytes(), dtype=torch.uint8, device=device)
+    if dst.data_ptr() % 256:
+        raise RuntimeError("tiled weight buffer is not 256-byte aligned")
+    packed = MoeLayer()
+    _check("moe_pack_weights", lib().moe_pack_weights(layer.ref, _ptr(dst), dst.numel(),
+                                                      ctypes.byref(packed), _stream(stream)))
+    layer.t["tiled"] = dst
+    return packed
 
 
 def moe_workspace_bytes(layer: DeviceLayer, max_tokens: int) -> int:

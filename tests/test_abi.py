@@ -28,7 +28,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("moe_route", "moe_prefill", "moe_decode", "moe_workspace_bytes",
-                     "moe_last_error"):
+                     "moe_last_error", "moe_pack_weights", "moe_pack_bytes"):
         assert required in names
 
 
@@ -48,7 +48,8 @@ def fake_layer(M, **kw):
     p = dict(abi_version=M.ABI_VERSION, hidden=2048, inter=512, n_experts=256, top_k=8,
              n_shared=1, w_format=M.W_INT4_G64, act_dtype=M.ACT_BF16, router_w=0x10000,
              router_b=None, w13_q=0x20000, w13_s=0x30000, w13_b=0x40000, w2_q=0x50000,
-             w2_s=0x60000, w2_b=0x70000)
+             w2_s=0x60000, w2_b=0x70000, w13_t=0x80000, w13_tsb=0x90000, w2_t=0xa0000,
+             w2_tsb=0xb0000)
     p.update(kw)
     return M.MoeLayer(*[p[f] for f, _ in M.MoeLayer._fields_])
 
@@ -118,7 +119,34 @@ def test_call_argument_errors_before_any_launch(M):
     assert L.moe_prefill(ref, x, 0, y, None, None, ws, need, None) == M.OK
     assert L.moe_last_error().decode() == ""
     assert L.moe_rmsnorm(x, 4, 2048, ctypes.c_float(-1.0), M.ACT_BF16, y, None) == M.E_INVALID
+    # int4 prefill needs the tiled weights
+    bare = fake_layer(M, w13_t=None)
+    assert L.moe_prefill(ctypes.byref(bare), x, 4, y, None, None, ws, need, None) == M.E_INVALID
+    assert "moe_pack_weights" in L.moe_last_error().decode()
+    assert L.moe_prefill(ctypes.byref(fake_layer(M, w2_tsb=0xb0008)), x, 4, y, None, None, ws,
+                         need, None) == M.E_INVALID
     assert L.moe_rmsnorm(x, 4, 2048, ctypes.c_float(1e-6), 5, y, None) == M.E_INVALID
+
+
+def test_pack_size_and_argument_errors(M):
+    L = M.lib()
+    layer = fake_layer(M)
+    n = ctypes.c_size_t(0)
+    assert L.moe_pack_bytes(ctypes.byref(layer), ctypes.byref(n)) == M.OK
+    # codes keep their size; {scale, bias} pairs of 4 groups per row and block
+    E1, H, I = 257, 2048, 512
+    codes = E1 * 2 * I * H // 2 + E1 * H * I // 2
+    sb = E1 * (2 * I // 64) * (H // 256) * 64 * 16 + E1 * (H // 64) * (I // 256) * 64 * 16
+    assert n.value == codes + sb
+    out = M.MoeLayer()
+    dst = ctypes.c_void_p(0x1000000)
+    assert L.moe_pack_weights(ctypes.byref(layer), dst, n.value - 1, ctypes.byref(out),
+                              None) == M.E_WORKSPACE
+    assert L.moe_pack_weights(ctypes.byref(layer), ctypes.c_void_p(0x1000010), n.value,
+                              ctypes.byref(out), None) == M.E_INVALID
+    assert L.moe_pack_weights(ctypes.byref(layer), dst, n.value, None, None) == M.E_INVALID
+    f32 = fake_layer(M, w_format=M.W_F32, act_dtype=M.ACT_F32)
+    assert L.moe_pack_bytes(ctypes.byref(f32), ctypes.byref(n)) == M.E_UNSUPPORTED
 
 
 def test_profile_controls_without_records(M):

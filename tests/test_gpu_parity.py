@@ -246,6 +246,57 @@ def test_small_int4_layers(M, T, E, k, S):
     assert rel_err(y_np(yd)[0], ref[t]) <= BF16_TOL
 
 
+def _tile_reference(q, sc, bi, rows, K, inter, gate_up):
+    """Tiled layout of moe_pack_weights written out with numpy reshapes (layout only)."""
+    n = q.shape[0]
+    order = np.arange(rows)
+    if gate_up:  # block j: gate rows 32j..32j+31, then up rows 32j..32j+31
+        order = np.stack([order[:inter].reshape(-1, 32), order[inter:].reshape(-1, 32)],
+                         1).reshape(-1)
+    qb = q[:, order].reshape(n, rows // 64, 64, K // 64, 32).transpose(0, 1, 3, 2, 4)
+    ng = K // 64
+    ng4 = (ng + 3) // 4 * 4
+    pairs = np.zeros((n, rows, ng4, 2), np.uint16)
+    pairs[:, :, :ng, 0], pairs[:, :, :ng, 1] = sc, bi
+    sb = pairs[:, order].reshape(n, rows // 64, 64, ng4 // 4, 4, 2).transpose(0, 1, 3, 2, 4, 5)
+    return np.ascontiguousarray(qb).reshape(-1), np.ascontiguousarray(sb).reshape(-1)
+
+
+@pytest.mark.parametrize("H,I", [(256, 128), (512, 384)])
+def test_pack_weights_layout(M, H, I):
+    announce(f"moe_pack_weights H={H} I={I} E=4 S=1")
+    layer = synth.make_int4_layer(7, hidden=H, inter=I, n_experts=4, top_k=2, n_shared=1)
+    dl = M.DeviceLayer.from_host(layer, DEV)
+    torch.cuda.synchronize()
+    buf = dl.t["tiled"].cpu().numpy()
+    base = dl.t["tiled"].data_ptr()
+    d = dl.desc
+    for qa, sa, ba, rows, K, gu, tp, sp in (
+            (layer.w13_q, layer.w13_s, layer.w13_b, 2 * I, H, True, d.w13_t, d.w13_tsb),
+            (layer.w2_q, layer.w2_s, layer.w2_b, H, I, False, d.w2_t, d.w2_tsb)):
+        want_q, want_sb = _tile_reference(qa, sa, ba, rows, K, I, gu)
+        got_q = buf[tp - base: tp - base + want_q.size]
+        got_sb = buf[sp - base: sp - base + 2 * want_sb.size].view(np.uint16)
+        assert np.array_equal(got_q, want_q)
+        assert np.array_equal(got_sb, want_sb)
+
+
+def test_prefill_small_layer_padded_scale_blocks(M):
+    # I = 384: the down GEMM has 6 K steps, so its last scale block is half padding
+    announce("moe_prefill int4 H=512 I=384 E=16 k=4 S=1 T=77")
+    layer = synth.make_int4_layer(55, hidden=512, inter=384, n_experts=16, top_k=4,
+                                  n_shared=1, router_std=0.1)
+    dl = M.DeviceLayer.from_host(layer, DEV)
+    xb = synth.bf16_activations(56, (77, 512))
+    y = M.moe_prefill(dl, bf16_dev(M, xb))
+    torch.cuda.synchronize()
+    ref = oracle.moe(layer, xb)
+    _, _, margin = oracle.route(layer, xb)
+    sure = margin >= delta_for(512)
+    assert sure.sum() >= 70
+    assert rel_err(y_np(y)[sure], ref[sure]) <= BF16_TOL
+
+
 def test_empty_prefill_is_noop(M, big):
     _, dl = big
     announce("moe_prefill T=0")
