@@ -14,7 +14,11 @@ with Zipf(1.1)-skewed routing (tokens/s and fraction of the dense bf16 MFMA peak
 dominant kernel's roofline (durations from HIP events on its stream) and the CPU
 oracle's throughput on a bounded sample of the decode tokens.
 
+Also: a stack of 40 such layers (pre-norm residual blocks) with batch-1 decode of 256
+tokens and a 32,768-token prompt in chunks of 4096 tokens.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-prefill]
+                       [--no-stack]
 """
 import argparse
 import hashlib
@@ -82,29 +86,35 @@ def traffic_for(kernel, src):
     return rec.get("bytes_per_launch")
 
 
+def gpu_layer(moe, torch, synth, dev, seed):
+    """A layer of the decode shape drawn on the GPU (seeded torch generator) with the
+    distributions of synth.make_int4_layer; used only for timing."""
+    mag = 0.02 / synth.NIBBLE_STD
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+
+    def int4(rows, K):
+        q = torch.randint(0, 256, (E + S, rows, K // 2), dtype=torch.uint8, device=dev,
+                          generator=g)
+        s = (torch.rand((E + S, rows, K // 64), device=dev, generator=g) + 0.5) * mag
+        s = s.to(torch.bfloat16)
+        b = (-s.float() * (6.5 + 2.0 * torch.rand(s.shape, device=dev, generator=g)))
+        return q, s, b.to(torch.bfloat16)
+
+    rw = torch.randn((E, H), device=dev, generator=g) * 0.02
+    q13, s13, b13 = int4(2 * I, H)
+    q2, s2, b2 = int4(H, I)
+    return moe.DeviceLayer.from_tensors(H, I, E, K_TOP, S, "int4", router_w=rw, router_b=None,
+                                        w13_q=q13, w13_s=s13, w13_b=b13, w2_q=q2, w2_s=s2,
+                                        w2_b=b2)
+
+
 def gpu_copies(moe, torch, synth, dev):
     """Layer copy 0 from the seeded numpy generator; copies 1..19 drawn on the GPU with
-    the same distributions (seeded torch generators), used only for timing."""
+    the same distributions, used only for timing."""
     layers = [moe.DeviceLayer.from_host(synth.decode_layer(0), dev)]
-    mag = 0.02 / synth.NIBBLE_STD
     for c in range(1, N_COPIES):
-        g = torch.Generator(device=dev)
-        g.manual_seed(c)
-
-        def int4(rows, K):
-            q = torch.randint(0, 256, (E + S, rows, K // 2), dtype=torch.uint8, device=dev,
-                              generator=g)
-            s = (torch.rand((E + S, rows, K // 64), device=dev, generator=g) + 0.5) * mag
-            s = s.to(torch.bfloat16)
-            b = (-s.float() * (6.5 + 2.0 * torch.rand(s.shape, device=dev, generator=g)))
-            return q, s, b.to(torch.bfloat16)
-
-        rw = torch.randn((E, H), device=dev, generator=g) * 0.02
-        q13, s13, b13 = int4(2 * I, H)
-        q2, s2, b2 = int4(H, I)
-        layers.append(moe.DeviceLayer.from_tensors(H, I, E, K_TOP, S, "int4", router_w=rw,
-                                                   router_b=None, w13_q=q13, w13_s=s13,
-                                                   w13_b=b13, w2_q=q2, w2_s=s2, w2_b=b2))
+        layers.append(gpu_layer(moe, torch, synth, dev, c))
     return layers
 
 
@@ -220,6 +230,70 @@ def bench_prefill(moe, torch, synth, dev, layer_host, reps=20):
             "kernels": kern}
 
 
+STACK_LAYERS, STACK_DECODE_TOKENS, STACK_PROMPT, STACK_CHUNK = 40, 256, 32768, 4096
+
+
+def bench_stack(moe, torch, synth, dev, eps=1e-6):
+    """40 layers of the decode shape (18.3 GB of int4 weights, plus their tiled copies)
+    resident in HBM, as pre-norm residual blocks: batch-1 decode of 256 tokens, and a
+    32,768-token prompt in chunks of 4096 tokens reusing one workspace."""
+    layers = [gpu_layer(moe, torch, synth, dev, 1000 + l) for l in range(STACK_LAYERS)]
+    # decode: each token's output is the next token's input; 8 tokens per graph
+    ws1 = moe.stack_workspace(layers, 1, dev)
+    h = moe.bf16_from_bits(synth.decode_token(0), dev)
+    per_graph = 8
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            moe.moe_stack_forward(layers, h, chunk_tokens=1, eps=eps, ws=ws1)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            moe.moe_stack_forward(layers, h, chunk_tokens=1, eps=eps, ws=ws1)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(STACK_DECODE_TOKENS // per_graph):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    dec_ms = t0.elapsed_time(t1)
+    del g, ws1
+    # prefill: the same prompt each time, restored outside the timed region
+    wsp = moe.stack_workspace(layers, STACK_CHUNK, dev)
+    x0 = moe.bf16_from_bits(synth.bf16_activations(3, (STACK_PROMPT, H)), dev)
+    hp = x0.clone()
+    moe.moe_stack_forward(layers, hp, chunk_tokens=STACK_CHUNK, eps=eps, ws=wsp)
+    times = []
+    for _ in range(3):
+        hp.copy_(x0)
+        torch.cuda.synchronize()
+        t0.record()
+        moe.moe_stack_forward(layers, hp, chunk_tokens=STACK_CHUNK, eps=eps, ws=wsp)
+        t1.record()
+        torch.cuda.synchronize()
+        times.append(t0.elapsed_time(t1))
+    pre_ms = min(times)
+    bpt = STACK_LAYERS * decode_bytes_per_token()
+    us_tok = 1e3 * dec_ms / STACK_DECODE_TOKENS
+    flops = STACK_LAYERS * prefill_flops_per_token() * STACK_PROMPT
+    del layers, wsp, x0, hp
+    torch.cuda.empty_cache()
+    return {"layers": STACK_LAYERS, "decode_tokens": STACK_DECODE_TOKENS,
+            "decode_tokens_per_s": 1e6 / us_tok, "decode_us_per_token": us_tok,
+            "decode_hbm_frac": bpt / (us_tok * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "prefill_prompt_tokens": STACK_PROMPT, "prefill_chunk": STACK_CHUNK,
+            "prefill_ms_per_prompt": pre_ms,
+            "prefill_tokens_per_s": STACK_PROMPT / (pre_ms * 1e-3),
+            "prefill_mfma_frac": flops / (pre_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "weights": "seeded GPU draws of the decode-layer distributions, layer l seed 1000+l"}
+
+
 def cpu_baseline(synth):
     import numpy as np
     import oracle
@@ -253,6 +327,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-stack", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -299,6 +374,8 @@ def main():
     if not args.no_prefill:
         out["prefill_uniform"] = bench_prefill(moe, torch, synth, dev, synth.decode_layer(0))
         out["prefill_skewed"] = bench_prefill(moe, torch, synth, dev, synth.skewed_layer(0))
+    if not args.no_stack:
+        out["stack_40"] = bench_stack(moe, torch, synth, dev)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(synth)
     print(json.dumps(out), flush=True)

@@ -125,8 +125,9 @@ moe_status moe_route(const moe_layer *layer, const void *x, int64_t T,
                      const moe_route_out *out, void *ws, size_t ws_bytes, void *stream);
 
 /* Whole layer for T >= 1 tokens (prefill path): routing as moe_route, then for int4
- * a grouped gate/up GEMM with SwiGLU, a grouped down GEMM (int4 codes dequantised to
- * fp16 in registers, fp16 MFMA, fp32 accumulation) and a weighted combine
+ * (tiled weights required, see moe_pack_weights) a grouped gate/up GEMM with SwiGLU, a
+ * grouped down GEMM (int4 codes dequantised to fp16 in registers, fp16 MFMA, fp32
+ * accumulation) and a weighted combine
  * back to token order. y[t] = shared(x_t) + sum_j w[t,j] expert_{ids[t,j]}(x_t)
  * (+ residual[t]). x, y, residual: [T, H] of act_dtype; residual may be NULL and may
  * alias y. route_out may be NULL; when given it receives the routing results.
@@ -142,6 +143,24 @@ moe_status moe_prefill(const moe_layer *layer, const void *x, int64_t T, void *y
  * x, y, residual: [1, H] of act_dtype; residual may be NULL and may alias y. */
 moe_status moe_decode(const moe_layer *layer, const void *x, void *y, const void *residual,
                       void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes for moe_stack_forward with chunks of up to chunk_tokens rows. */
+moe_status moe_stack_workspace_bytes(const moe_layer *layers, int32_t n_layers,
+                                     int64_t chunk_tokens, size_t *bytes);
+
+/* A stack of n_layers MoE layers (host array of descriptors) as pre-norm residual
+ * blocks, applied in place to h [T, H]:
+ *     for l = 0 .. n_layers-1:   h <- h + MoE_l(RMSNorm(h))
+ * with RMSNorm of unit gain in fp32 arithmetic (eps as given; the normalised rows are
+ * rounded to the activation dtype before the layer reads them). Rows are processed in
+ * chunks of at most chunk_tokens, each chunk through every layer, all reusing one
+ * workspace of moe_stack_workspace_bytes ("Bound temporary memory with prompt chunking");
+ * every layer is independent per token, so the chunk size does not change the result.
+ * T == 1 runs the decode path of each layer, T > 1 the prefill path (int4 layers must be
+ * packed). All layers need the same hidden size and activation dtype. */
+moe_status moe_stack_forward(const moe_layer *layers, int32_t n_layers, void *h, int64_t T,
+                             int64_t chunk_tokens, float eps, void *ws, size_t ws_bytes,
+                             void *stream);
 
 /* RMSNorm with unit gain for stacking layers: out[t] = h[t] / sqrt(mean(h[t]^2) + eps),
  * fp32 arithmetic. h, out: [T, H] of act_dtype (may alias). */

@@ -3,6 +3,7 @@
 // No call allocates device memory, synchronises the host or copies device data to it.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -188,6 +189,30 @@ PackPlan pack_plan(const moe_layer *L) {
   return p;
 }
 
+struct StackPlan {
+  size_t norm, layer_ws, total;
+};
+
+// Workspace of a stack: the normalised rows of one chunk, then one layer workspace (sized
+// for the largest layer) that every layer and chunk reuses.
+moe_status stack_plan(const moe_layer *layers, int32_t n_layers, int64_t chunk, StackPlan *sp) {
+  if (!layers || n_layers < 1) return fail(MOE_E_INVALID, "need at least one layer");
+  if (chunk < 1 || chunk > kMaxTokens) return fail(MOE_E_INVALID, "bad chunk_tokens");
+  size_t lws = 0;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const moe_status st = check_layer(&layers[l]);
+    if (st) return st;
+    if (layers[l].hidden != layers[0].hidden || layers[l].act_dtype != layers[0].act_dtype)
+      return fail(MOE_E_INVALID, "layer %d: hidden size or activation dtype differs", l);
+    lws = std::max(lws, make_plan(&layers[l], chunk).total);
+  }
+  const size_t elt = layers[0].act_dtype == MOE_ACT_BF16 ? 2 : 4;
+  sp->norm = 0;
+  sp->layer_ws = align256((size_t)chunk * layers[0].hidden * elt);
+  sp->total = sp->layer_ws + lws;
+  return MOE_OK;
+}
+
 moe_status check_ws(const moe_layer *L, int64_t T, void *ws, size_t ws_bytes, Plan *p) {
   *p = make_plan(L, T);
   if (!ws) return fail(MOE_E_INVALID, "workspace is NULL");
@@ -361,22 +386,10 @@ moe_status moe_route(const moe_layer *layer, const void *x, int64_t T, const moe
   return MOE_OK;
 }
 
-moe_status moe_prefill(const moe_layer *layer, const void *x, int64_t T, void *y,
-                       const void *residual, const moe_route_out *route_out, void *ws,
-                       size_t ws_bytes, void *stream) {
-  g_err.clear();
-  moe_status st = check_layer(layer);
-  if (st) return st;
-  if (T < 0 || T > kMaxTokens) return fail(MOE_E_INVALID, "T %lld out of range", (long long)T);
-  if (T == 0) return MOE_OK;  // empty input: nothing to read or write
-  if (!x || !y || !aligned16(x) || !aligned16(y))
-    return fail(MOE_E_INVALID, "x and y must be non-NULL and 16-byte aligned");
-  if (residual && !aligned16(residual)) return fail(MOE_E_INVALID, "residual misaligned");
-  if (route_out && (st = check_route_out(route_out))) return st;
-  if (layer->w_format == MOE_W_INT4_G64 && (st = check_tiled(layer))) return st;
-  Plan p;
-  if ((st = check_ws(layer, T, ws, ws_bytes, &p))) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+// The layer for T >= 1 tokens after validation; p is the workspace plan for T tokens.
+static moe_status prefill_impl(const moe_layer *layer, const void *x, int64_t T, void *y,
+                               const void *residual, const moe_route_out *route_out, void *ws,
+                               const Plan &p, hipStream_t s) {
   moe::RouteArgs ra = route_args(layer, x, T);
   route_targets(ra, p, ws, route_out);
   const bool int4 = layer->w_format == MOE_W_INT4_G64;
@@ -443,17 +456,27 @@ moe_status moe_prefill(const moe_layer *layer, const void *x, int64_t T, void *y
   return MOE_OK;
 }
 
-moe_status moe_decode(const moe_layer *layer, const void *x, void *y, const void *residual,
-                      void *ws, size_t ws_bytes, void *stream) {
+moe_status moe_prefill(const moe_layer *layer, const void *x, int64_t T, void *y,
+                       const void *residual, const moe_route_out *route_out, void *ws,
+                       size_t ws_bytes, void *stream) {
   g_err.clear();
   moe_status st = check_layer(layer);
   if (st) return st;
+  if (T < 0 || T > kMaxTokens) return fail(MOE_E_INVALID, "T %lld out of range", (long long)T);
+  if (T == 0) return MOE_OK;  // empty input: nothing to read or write
   if (!x || !y || !aligned16(x) || !aligned16(y))
     return fail(MOE_E_INVALID, "x and y must be non-NULL and 16-byte aligned");
   if (residual && !aligned16(residual)) return fail(MOE_E_INVALID, "residual misaligned");
+  if (route_out && (st = check_route_out(route_out))) return st;
+  if (layer->w_format == MOE_W_INT4_G64 && (st = check_tiled(layer))) return st;
   Plan p;
-  if ((st = check_ws(layer, 1, ws, ws_bytes, &p))) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = check_ws(layer, T, ws, ws_bytes, &p))) return st;
+  return prefill_impl(layer, x, T, y, residual, route_out, ws, p, static_cast<hipStream_t>(stream));
+}
+
+// One token after validation; p is a workspace plan for at least one token.
+static moe_status decode_impl(const moe_layer *layer, const void *x, void *y,
+                              const void *residual, void *ws, const Plan &p, hipStream_t s) {
   hipError_t e;
   const bool int4 = layer->w_format == MOE_W_INT4_G64;
   if (moe::decode_gemv_supported(layer->hidden, layer->inter, layer->n_experts, layer->top_k,
@@ -499,6 +522,70 @@ moe_status moe_decode(const moe_layer *layer, const void *x, void *y, const void
   ta.wt = weights_of(layer);
   if ((e = moe::launch_token_experts(ta, s)) != hipSuccess)
     return hip_fail(e, "moe_decode experts");
+  return MOE_OK;
+}
+
+moe_status moe_decode(const moe_layer *layer, const void *x, void *y, const void *residual,
+                      void *ws, size_t ws_bytes, void *stream) {
+  g_err.clear();
+  moe_status st = check_layer(layer);
+  if (st) return st;
+  if (!x || !y || !aligned16(x) || !aligned16(y))
+    return fail(MOE_E_INVALID, "x and y must be non-NULL and 16-byte aligned");
+  if (residual && !aligned16(residual)) return fail(MOE_E_INVALID, "residual misaligned");
+  Plan p;
+  if ((st = check_ws(layer, 1, ws, ws_bytes, &p))) return st;
+  return decode_impl(layer, x, y, residual, ws, p, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_stack_workspace_bytes(const moe_layer *layers, int32_t n_layers,
+                                     int64_t chunk_tokens, size_t *bytes) {
+  g_err.clear();
+  if (!bytes) return fail(MOE_E_INVALID, "bytes is NULL");
+  StackPlan sp;
+  const moe_status st = stack_plan(layers, n_layers, chunk_tokens, &sp);
+  if (st) return st;
+  *bytes = sp.total;
+  return MOE_OK;
+}
+
+moe_status moe_stack_forward(const moe_layer *layers, int32_t n_layers, void *h, int64_t T,
+                             int64_t chunk_tokens, float eps, void *ws, size_t ws_bytes,
+                             void *stream) {
+  g_err.clear();
+  StackPlan sp;
+  moe_status st = stack_plan(layers, n_layers, chunk_tokens, &sp);
+  if (st) return st;
+  if (T < 0 || T > kMaxTokens) return fail(MOE_E_INVALID, "T %lld out of range", (long long)T);
+  if (!(eps >= 0.f)) return fail(MOE_E_INVALID, "eps must be >= 0");
+  if (T == 0) return MOE_OK;
+  if (!h || !aligned16(h)) return fail(MOE_E_INVALID, "h must be non-NULL and 16-byte aligned");
+  if (!ws || !aligned16(ws)) return fail(MOE_E_INVALID, "workspace must be 16-byte aligned");
+  if (ws_bytes < sp.total)
+    return fail(MOE_E_WORKSPACE, "workspace holds %zu bytes, the stack needs %zu", ws_bytes,
+                sp.total);
+  for (int32_t l = 0; l < n_layers; ++l)
+    if (layers[l].w_format == MOE_W_INT4_G64 && T > 1 && (st = check_tiled(&layers[l])))
+      return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int H = layers[0].hidden;
+  const bool bf16 = layers[0].act_dtype == MOE_ACT_BF16;
+  const size_t row_bytes = (size_t)H * (bf16 ? 2 : 4);
+  void *norm = at<void>(ws, sp.norm);
+  void *lws = at<void>(ws, sp.layer_ws);
+  // each chunk of rows goes through every layer before the next chunk starts
+  for (int64_t r0 = 0; r0 < T; r0 += chunk_tokens) {
+    const int64_t n = std::min<int64_t>(chunk_tokens, T - r0);
+    void *hc = static_cast<char *>(h) + (size_t)r0 * row_bytes;
+    for (int32_t l = 0; l < n_layers; ++l) {
+      hipError_t e = moe::launch_rmsnorm(hc, n, H, eps, bf16, norm, s);
+      if (e != hipSuccess) return hip_fail(e, "moe_stack_forward rmsnorm");
+      const Plan p = make_plan(&layers[l], n);
+      st = (T == 1) ? decode_impl(&layers[l], norm, hc, hc, lws, p, s)
+                    : prefill_impl(&layers[l], norm, n, hc, hc, nullptr, lws, p, s);
+      if (st) return st;
+    }
+  }
   return MOE_OK;
 }
 

@@ -24,7 +24,8 @@ W_F32, W_INT4_G64 = 0, 1
 ACT_F32, ACT_BF16 = 0, 1
 
 EXPORTS = ("moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_pack_bytes",
-           "moe_pack_weights", "moe_route", "moe_prefill", "moe_decode", "moe_rmsnorm",
+           "moe_pack_weights", "moe_route", "moe_prefill", "moe_decode",
+           "moe_stack_workspace_bytes", "moe_stack_forward", "moe_rmsnorm",
            "moe_profile_enable", "moe_profile_query", "moe_profile_reset")
 
 
@@ -87,6 +88,8 @@ def lib():
         "moe_route": ([P, P, I64, P, P, SZ, P], ctypes.c_int),
         "moe_prefill": ([P, P, I64, P, P, P, P, SZ, P], ctypes.c_int),
         "moe_decode": ([P, P, P, P, P, SZ, P], ctypes.c_int),
+        "moe_stack_workspace_bytes": ([P, I32, I64, ctypes.POINTER(SZ)], ctypes.c_int),
+        "moe_stack_forward": ([P, I32, P, I64, I64, ctypes.c_float, P, SZ, P], ctypes.c_int),
         "moe_rmsnorm": ([P, I64, I32, ctypes.c_float, I32, P, P], ctypes.c_int),
         "moe_profile_enable": ([I32], ctypes.c_int),
         "moe_profile_query": ([ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
@@ -281,3 +284,30 @@ def profile_query(kernel: str) -> tuple[float, int]:
 def bf16_from_bits(bits: np.ndarray, device="cuda") -> torch.Tensor:
     """Device bf16 tensor holding the given bf16 bit patterns."""
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def _layer_array(layers):
+    arr = (MoeLayer * len(layers))(*[l.desc for l in layers])
+    return arr
+
+
+def stack_workspace(layers, chunk_tokens: int, device="cuda") -> torch.Tensor:
+    n = ctypes.c_size_t(0)
+    _check("moe_stack_workspace_bytes",
+           lib().moe_stack_workspace_bytes(_layer_array(layers), len(layers), int(chunk_tokens),
+                                           ctypes.byref(n)))
+    return torch.zeros(n.value, dtype=torch.uint8, device=device)
+
+
+def moe_stack_forward(layers, h: torch.Tensor, chunk_tokens: int = 4096, eps: float = 1e-6,
+                      ws: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """h <- h + MoE_l(RMSNorm(h)) for every layer in order, in place on h [T, H]."""
+    if not h.is_contiguous():
+        raise ValueError("h must be contiguous")
+    if ws is None:
+        ws = stack_workspace(layers, chunk_tokens, h.device)
+    arr = _layer_array(layers)
+    _check("moe_stack_forward",
+           lib().moe_stack_forward(arr, len(layers), _ptr(h), h.shape[0], int(chunk_tokens),
+                                   ctypes.c_float(eps), _ptr(ws), ws.numel(), _stream(stream)))
+    return h

@@ -149,6 +149,31 @@ def test_pack_size_and_argument_errors(M):
     assert L.moe_pack_bytes(ctypes.byref(f32), ctypes.byref(n)) == M.E_UNSUPPORTED
 
 
+def test_stack_argument_errors(M):
+    L = M.lib()
+    layers = (M.MoeLayer * 3)(fake_layer(M), fake_layer(M), fake_layer(M))
+    n = ctypes.c_size_t(0)
+    assert L.moe_stack_workspace_bytes(layers, 3, 4096, ctypes.byref(n)) == M.OK
+    one = ctypes.c_size_t(0)
+    assert L.moe_workspace_bytes(ctypes.byref(layers[0]), 4096, ctypes.byref(one)) == M.OK
+    assert n.value == one.value + 4096 * 2048 * 2   # one layer workspace + normalised rows
+    assert L.moe_stack_workspace_bytes(layers, 0, 4096, ctypes.byref(n)) == M.E_INVALID
+    assert L.moe_stack_workspace_bytes(layers, 3, 0, ctypes.byref(n)) == M.E_INVALID
+    odd = (M.MoeLayer * 2)(fake_layer(M), fake_layer(M, hidden=1024))
+    assert L.moe_stack_workspace_bytes(odd, 2, 64, ctypes.byref(n)) == M.E_INVALID
+    assert "hidden" in L.moe_last_error().decode()
+    h, ws = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x300000)
+    assert L.moe_stack_workspace_bytes(layers, 3, 64, ctypes.byref(n)) == M.OK
+    f = ctypes.c_float(1e-6)
+    assert L.moe_stack_forward(layers, 3, h, 64, 64, f, ws, n.value - 1, None) == M.E_WORKSPACE
+    assert L.moe_stack_forward(layers, 3, h, 64, 64, ctypes.c_float(-1.0), ws, n.value,
+                               None) == M.E_INVALID
+    assert L.moe_stack_forward(layers, 3, None, 64, 64, f, ws, n.value, None) == M.E_INVALID
+    assert L.moe_stack_forward(layers, 3, h, 0, 64, f, ws, n.value, None) == M.OK
+    unpacked = (M.MoeLayer * 1)(fake_layer(M, w2_t=None))
+    assert L.moe_stack_forward(unpacked, 1, h, 64, 64, f, ws, n.value, None) == M.E_INVALID
+
+
 def test_profile_controls_without_records(M):
     M.profile_reset()
     M.profile_enable(False)

@@ -1,0 +1,105 @@
+"""GPU parity of the layer stack (pre-norm residual blocks h <- h + MoE_l(RMSNorm(h))) and of
+its chunk loop, through the C ABI (moe_stack_forward).
+
+The stack is checked teacher-forced, layer by layer: the oracle takes the GPU's bf16 input of
+layer l, applies its own fp64 RMSNorm and MoE, adds the residual, and the GPU's output of
+layer l must agree within the bf16 rounding of the residual stream plus 2e-2 of the RMS of
+the layer's MoE output. Prompt chunking ("Optimizing On-Device Inference for Apple Silicon",
+section "Bound temporary memory with prompt chunking") must not change any output bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity_util import BF16_TOL
+from routed_expert_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+EPS = 1e-6
+
+
+@pytest.fixture(scope="module")
+def M():
+    from routed_expert_amd import moe
+    moe.lib()
+    return moe
+
+
+def announce(msg):
+    print(f"\n[stack] {msg}", flush=True)
+
+
+def small_stack(M, n_layers, H=256, I=128, E=16, k=4, S=1):
+    layers = [synth.make_int4_layer(300 + l, hidden=H, inter=I, n_experts=E, top_k=k,
+                                    n_shared=S, router_std=0.1) for l in range(n_layers)]
+    return layers, [M.DeviceLayer.from_host(L, DEV) for L in layers]
+
+
+def bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def check_layer_step(layer, h_in_bits, h_out_bits, rows=None):
+    """GPU output of one stack layer against the oracle fed with the GPU's input."""
+    if rows is not None:
+        h_in_bits, h_out_bits = h_in_bits[rows], h_out_bits[rows]
+    h_in = oracle.to_f64(h_in_bits)
+    y_ref = oracle.moe(layer, oracle.rmsnorm(h_in, EPS))
+    ref = h_in + y_ref
+    got = oracle.to_f64(h_out_bits)
+    y_rms = np.sqrt(np.mean(y_ref ** 2))
+    bound = 2.0 ** -8 * np.abs(ref) + BF16_TOL * y_rms
+    assert np.all(np.abs(got - ref) <= bound), float(np.max(np.abs(got - ref) - bound))
+    assert np.max(np.abs(got - ref)) / np.sqrt(np.mean(ref ** 2)) <= BF16_TOL
+
+
+@pytest.mark.parametrize("T,chunk", [(37, 16), (1, 16)])
+def test_stack_teacher_forced_small(M, T, chunk):
+    announce(f"moe_stack_forward 4 small int4 layers T={T} chunk={chunk}")
+    layers, dls = small_stack(M, 4)
+    h0 = M.bf16_from_bits(synth.bf16_activations(400 + T, (T, 256)), DEV)
+    hs = [h0.clone()]
+    for dl in dls:                              # one layer per call
+        h = hs[-1].clone()
+        M.moe_stack_forward([dl], h, chunk_tokens=chunk, eps=EPS)
+        hs.append(h)
+    whole = h0.clone()                           # all layers in one call
+    M.moe_stack_forward(dls, whole, chunk_tokens=chunk, eps=EPS)
+    torch.cuda.synchronize()
+    assert torch.equal(whole, hs[-1])
+    for l, layer in enumerate(layers):
+        check_layer_step(layer, bits(hs[l]), bits(hs[l + 1]))
+
+
+def test_stack_chunked_equals_unchunked(M):
+    announce("moe_stack_forward 3 small int4 layers T=300, chunks of 64 vs one chunk")
+    _, dls = small_stack(M, 3)
+    h0 = M.bf16_from_bits(synth.bf16_activations(401, (300, 256)), DEV)
+    a, b = h0.clone(), h0.clone()
+    M.moe_stack_forward(dls, a, chunk_tokens=64, eps=EPS)
+    M.moe_stack_forward(dls, b, chunk_tokens=300, eps=EPS)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert not torch.equal(a, h0)
+
+
+def test_stack_full_shape_layers(M):
+    # two layers of the model's shape (H=2048, I=512, E=256, k=8, one shared expert)
+    announce("moe_stack_forward 2 int4 layers H=2048 T=96 chunk=40, decode T=1")
+    layers = [synth.decode_layer(l) for l in range(2)]
+    dls = [M.DeviceLayer.from_host(L, DEV) for L in layers]
+    h0 = M.bf16_from_bits(synth.bf16_activations(402, (96, 2048)), DEV)
+    h1 = h0.clone()
+    M.moe_stack_forward(dls[:1], h1, chunk_tokens=40, eps=EPS)
+    h2 = h1.clone()
+    M.moe_stack_forward(dls[1:], h2, chunk_tokens=40, eps=EPS)
+    d = h0[:1].clone()                           # the decode path of the same stack
+    M.moe_stack_forward(dls[:1], d, chunk_tokens=40, eps=EPS)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(5).choice(96, 24, replace=False)
+    rows[0] = 39                                 # the last row of the first chunk
+    check_layer_step(layers[0], bits(h0), bits(h1), rows)
+    check_layer_step(layers[1], bits(h1), bits(h2), rows)
+    check_layer_step(layers[0], bits(h0[:1]), bits(d))
