@@ -1,11 +1,12 @@
 // decode_gemv.hip -- batch-1 MoE layer (hidden 2048, intermediate 512, int4 g64) in three
-// lean kernels on the vector ALUs.
+// lean kernels on the vector ALUs, reading the tiled weight layout of moe_pack_weights.
 //
 // "Optimizing On-Device Inference for Apple Silicon":
 //   section "Decode: minimize the bytes moved per token" -- only the router, the k
 //   selected experts and the shared expert are read, each byte once;
-//   section "Optimize the one-row weight path" -- row-parallel GEMVs: a wavefront
-//   cooperates on one output row while its lanes read adjacent 16-byte pieces of it;
+//   section "Optimize the one-row weight path" -- row-parallel GEMVs whose lanes read
+//   adjacent 16-byte pieces: in the tiled layout one load instruction of a wave is one
+//   contiguous 1 KB block (32 rows x 32 code bytes of one K step);
 //   section "Overlap independent GPU work" -- the shared expert does not depend on the
 //   routing, so its gate/up projection runs next to the router;
 //   section "Reduce intermediate and state traffic" -- gate/up are fused with SwiGLU and
@@ -13,16 +14,22 @@
 //
 // The kernel boundaries are the two device-wide exchanges the layer needs (all router
 // logits before the top-k, all of h before the output projection). Inside a HIP graph a
-// boundary costs about 1.8 us on MI355X, measured below a grid barrier built on
-// device-scope atomics across 256 workgroups (2.4-3.7 us), so no kernel spins.
+// boundary costs about 1.4 us on MI355X, less than a grid barrier built on device-scope
+// atomics across 256 workgroups (2.4-3.7 us), so no kernel spins.
 //
-//   A  256 workgroups x 512 threads: workgroup w computes router logit z[w]; waves 0-1
-//      compute shared-expert gate/up pairs i = wave*256 + w and store h_shared[i].
-//   B  every workgroup runs the top-k on z (same data, same code, same answer) and
-//      computes routed gate/up tasks (j, i) = slot and slot + 2048, slot = wave*256 + w.
-//      Workgroup 0 stores the ids and weights for C.
-//   C  wave computes output row c = wave*256 + w of the down projection over all k+1
-//      experts (h staged in LDS), adds the residual and stores y[c].
+//   A  256 workgroups: workgroup w computes router logit z[w]; 32 more workgroups compute
+//      the shared expert's gate/up, 16 gate + 16 up rows each (as in B).
+//   B  every workgroup runs the top-k on z (same data, same code, same answer), then
+//      computes 16 gate + 16 up rows of one selected expert: workgroup (slot j, block b,
+//      half f) -> rows 32b + 16f .. +16. Workgroup 0 stores the ids and weights for C.
+//   C  256 workgroups of 8 output rows each: all k+1 experts' W2 rows times h (staged
+//      in LDS), scaled by the routing weights, plus the residual.
+//
+// Dot products: a nibble pair OR-ed into 0x6400 is the fp16 pair (1024 + q_lo, 1024 + q_hi)
+// of elements (8m + p, 8m + p + 4) of a 32-bit code word m; the activations sit in LDS as
+// fp16 pairs in the same order, so v_dot2_f32_f16 multiplies exactly and accumulates in
+// fp32, and per quantisation group sum (s q + b) x = s * dot + (b - 1024 s) * sum(x), all
+// in fp32. Activations must lie inside the fp16 range.
 #include "common.h"
 #include "kernels.h"
 
@@ -31,68 +38,83 @@ namespace moe {
 namespace {
 constexpr int DH = 2048, DI = 512, DWG = 256, DT = 512;
 constexpr int kSlots = kMaxTopK + 1;
+constexpr int kNB13 = 2 * DI / 64;  // 64-row blocks of W13 (32 gate + 32 up rows)
+constexpr int kNS13 = DH / 64;      // K steps of W13
+constexpr int kNB2 = DH / 64;       // 64-row blocks of W2
+constexpr int kNS2 = DI / 64;       // K steps of W2
+constexpr int kSharedWG = 2 * kNB13; // extra workgroups of A: shared-expert half blocks
+constexpr int kDownWG = kNB2 * 8;   // C: 8 output rows per workgroup
 }  // namespace
 
-// Lane's 32 activations [32*lane, 32*lane+32) of the 2048-element bf16 row.
-MOE_DEV void load_x32(const uint16_t *x, int lane, float xv[32]) {
-  const uint4 *xp = reinterpret_cast<const uint4 *>(x + lane * 32);
+// n fp32 / bf16 activations -> fp16 pairs (v[8c + p], v[8c + p + 4]) for chunk c, p < 4, in
+// LDS, and the sum of each 32-element segment (of the fp16 values) in seg[n / 32]. Called
+// by all DT threads (n a multiple of 32).
+template <bool kBf16In>
+MOE_DEV void stage_f16_pairs(const void *src, int n, f16x2_t *pairs, float *seg) {
+  const int nchunks = n / 8;
+  for (int base = 0; base < nchunks; base += DT) {
+    const int ch = base + threadIdx.x;  // 8 elements
+    const bool live = ch < nchunks;
+    float v[8] = {};
+    if (live) {
+      if (kBf16In) {
+        const uint4 u = reinterpret_cast<const uint4 *>(src)[ch];
+        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4 u = xp[i];
-    const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = bf16lo(wd[i]);
+          v[2 * i + 1] = bf16hi(wd[i]);
+        }
+      } else {
+        const float4 a = reinterpret_cast<const float4 *>(src)[2 * ch];
+        const float4 b = reinterpret_cast<const float4 *>(src)[2 * ch + 1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+      }
+    }
+    float sum = 0.f;
+    f16x2_t pr[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      xv[8 * i + 2 * p] = bf16lo(wd[p]);
-      xv[8 * i + 2 * p + 1] = bf16hi(wd[p]);
+      pr[p] = f16x2_t{(_Float16)v[p], (_Float16)v[p + 4]};
+      sum += (float)pr[p][0] + (float)pr[p][1];
     }
+    if (live) *reinterpret_cast<uint4 *>(pairs + 4 * ch) = __builtin_bit_cast(uint4, pr);
+    // 4 chunks per segment: lanes 4s .. 4s+3 (DT is a multiple of 4)
+    sum += __shfl_xor(sum, 1, 64);
+    sum += __shfl_xor(sum, 2, 64);
+    if ((ch & 3) == 0 && live) seg[ch >> 2] = sum;
   }
 }
 
-// Sum over the lane's 32 codes (16 bytes) times its 32 activations.
-MOE_DEV float dot32(const uint4 c, const float x[32]) {
+// Raw dot of one lane's 16 code bytes (32 elements = chunks c0 .. c0+3) with the staged
+// fp16 pairs: sum over the elements of (1024 + q) * x.
+MOE_DEV float dot_codes(const uint4 c, const f16x2_t *pairs, int c0) {
+  constexpr uint32_t kMask = 0x000F000Fu, kMagic = 0x64006400u;
   const uint32_t wd[4] = {c.x, c.y, c.z, c.w};
   float acc = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float q[8];
-    unpack8(wd[i], q);
+  for (int m = 0; m < 4; ++m) {
+    const uint4 xp = *reinterpret_cast<const uint4 *>(pairs + 4 * (c0 + m));
+    const uint32_t xs[4] = {xp.x, xp.y, xp.z, xp.w};
 #pragma unroll
-    for (int p = 0; p < 8; ++p) acc = __builtin_fmaf(q[p], x[8 * i + p], acc);
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t t = and_or(wd[m] >> (4 * p), kMask, kMagic);
+      acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, t),
+                                   __builtin_bit_cast(f16x2_t, xs[p]), acc, false);
+    }
   }
   return acc;
 }
 
-// One gate/up row pair (rows r and r + I of expert e's W13) against the lane's x.
-struct RowPair {
-  uint4 cg, cu;
-  uint16_t sg, bg, su, bu;
-};
-
-MOE_DEV RowPair load_pair(const ExpertWeights &wt, int e, int i, int lane) {
-  const size_t rg = (size_t)e * 2 * DI + i, ru = rg + DI;
-  const int grp = lane >> 1;
-  RowPair p;
-  p.cg = reinterpret_cast<const uint4 *>(wt.w13_q + rg * (DH / 2))[lane];
-  p.cu = reinterpret_cast<const uint4 *>(wt.w13_q + ru * (DH / 2))[lane];
-  p.sg = wt.w13_s[rg * (DH / kGroup) + grp];
-  p.bg = wt.w13_b[rg * (DH / kGroup) + grp];
-  p.su = wt.w13_s[ru * (DH / kGroup) + grp];
-  p.bu = wt.w13_b[ru * (DH / kGroup) + grp];
-  return p;
+// (s q + b) . x of one group-step segment from the raw dot, scale/bias as bf16 bits
+MOE_DEV float group_dot(float raw, uint32_t sb, float xsum) {
+  const float sc = bf16lo(sb), bi = bf16hi(sb);
+  return __builtin_fmaf(sc, raw, (bi - 1024.0f * sc) * xsum);
 }
 
-// silu(gate . x) * (up . x); sum over a group of (s q + b) x = s (q . x) + b (sum x)
-MOE_DEV float pair_h(const RowPair &p, const float xv[32], float sx) {
-  const float g = wave_sum_dpp(bf16_to_f32(p.sg) * dot32(p.cg, xv) + bf16_to_f32(p.bg) * sx);
-  const float u = wave_sum_dpp(bf16_to_f32(p.su) * dot32(p.cu, xv) + bf16_to_f32(p.bu) * sx);
-  return silu(g) * u;
-}
-
-MOE_DEV float lane_xsum(const float xv[32]) {
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) s += xv[i];
-  return s;
+MOE_DEV uint32_t word_of(const uint4 v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
 // Top-k of the E <= 256 router logits using all 8 waves of the workgroup (latency: the
@@ -166,13 +188,52 @@ MOE_DEV void block_topk(const float *z, int E, int k, uint64_t *K, uint64_t *can
   __syncthreads();
 }
 
+// 16 gate + 16 up rows (rows 32b + 16f .. +16 of expert e's tiled block b) against the
+// staged x: wave v takes K steps 4v .. 4v+3, one 1 KB load per step (lanes 0..31 the gate
+// rows, 32..63 the up rows; lane: row (l % 32) / 2, K half l % 2). Writes silu(g) * u of
+// the 16 rows to hout[0..15]. Called by all DT threads.
+MOE_DEV void gateup_half_block(const DecodeArgs &a, int e, int b, int f, const f16x2_t *xs,
+                               const float *xseg, float *red, float *hout) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const bool up = lane >= 32;
+  const int r16 = (lane & 31) >> 1, hh = lane & 1;
+  const size_t blk = (size_t)e * kNB13 + b;
+  const uint8_t *tq = a.wt.w13_t + (blk * kNS13 + 4 * wave) * 2048 + (up ? 1024 : 0) +
+                      512 * f + 16 * (lane & 31);
+  uint4 c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = *reinterpret_cast<const uint4 *>(tq + i * 2048);
+  const uint4 sb = *reinterpret_cast<const uint4 *>(
+      a.wt.w13_tsb + (blk * (kNS13 / 4) + wave) * 512 + 8 * ((up ? 32 : 0) + 16 * f + r16));
+  __syncthreads();  // x staged by the caller
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int st = 4 * wave + i;
+    acc += group_dot(dot_codes(c[i], xs, 8 * st + 4 * hh), word_of(sb, i), xseg[2 * st + hh]);
+  }
+  acc += __shfl_xor(acc, 1, 64);
+  if (hh == 0) red[wave * 32 + (up ? 16 : 0) + r16] = acc;
+  __syncthreads();
+  if (tid < 16) {
+    float gs = 0.f, us = 0.f;
+#pragma unroll
+    for (int v = 0; v < DT / 64; ++v) {
+      gs += red[v * 32 + tid];
+      us += red[v * 32 + 16 + tid];
+    }
+    hout[tid] = silu(gs) * us;
+  }
+}
+
 __global__ __launch_bounds__(DT) void k_dec_a(DecodeArgs a) {
-  __shared__ float red[DT / 64];
+  __shared__ float red[DT / 64 * 32];
+  __shared__ __attribute__((aligned(16))) f16x2_t xs[DH / 2];
+  __shared__ float xseg[DH / 32];
   const int w = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  RowPair sp;
-  const bool do_shared = a.S && wave < 2;
-  if (do_shared) sp = load_pair(a.wt, a.E, wave * DWG + w, lane);
-  if (w < a.E) {
+  if (w < DWG) {
+    // router logit w: 512 threads x 4 fp32 weights
+    if (w >= a.E) return;
     const float4 wr = reinterpret_cast<const float4 *>(a.router_w + (size_t)w * DH)[tid];
     const uint2 xb = reinterpret_cast<const uint2 *>(a.x)[tid];
     float d = wr.x * bf16lo(xb.x);
@@ -181,20 +242,19 @@ __global__ __launch_bounds__(DT) void k_dec_a(DecodeArgs a) {
     d = __builtin_fmaf(wr.w, bf16hi(xb.y), d);
     d = wave_sum_dpp(d);
     if (lane == 0) red[wave] = d;
-  }
-  if (do_shared) {
-    float xv[32];
-    load_x32(a.x, lane, xv);
-    const float hv = pair_h(sp, xv, lane_xsum(xv));
-    if (lane == 0) a.h[(size_t)a.k * DI + wave * DWG + w] = hv;
-  }
-  __syncthreads();
-  if (tid == 0 && w < a.E) {
-    float s = 0.f;
+    __syncthreads();
+    if (tid == 0) {
+      float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < DT / 64; ++i) s += red[i];
-    a.z[w] = s + (a.router_b ? a.router_b[w] : 0.f);
+      for (int i = 0; i < DT / 64; ++i) s += red[i];
+      a.z[w] = s + (a.router_b ? a.router_b[w] : 0.f);
+    }
+    return;
   }
+  // shared expert: half block (b, f) of workgroup DWG + 2b + f
+  const int b = (w - DWG) >> 1, f = (w - DWG) & 1;
+  stage_f16_pairs<true>(a.x, DH, xs, xseg);
+  gateup_half_block(a, a.E, b, f, xs, xseg, red, a.h + (size_t)a.k * DI + 32 * b + 16 * f);
 }
 
 __global__ __launch_bounds__(DT) void k_dec_b(DecodeArgs a) {
@@ -202,93 +262,77 @@ __global__ __launch_bounds__(DT) void k_dec_b(DecodeArgs a) {
   __shared__ float s_w[kMaxTopK];
   __shared__ __attribute__((aligned(16))) uint64_t s_key[256];
   __shared__ __attribute__((aligned(16))) uint64_t s_cand[64];
-  const int w = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  float xv[32];
-  load_x32(a.x, lane, xv);
+  __shared__ __attribute__((aligned(16))) f16x2_t xs[DH / 2];
+  __shared__ float xseg[DH / 32];
+  __shared__ float red[DT / 64 * 32];
+  const int w = blockIdx.x, tid = threadIdx.x;
+  stage_f16_pairs<true>(a.x, DH, xs, xseg);
   block_topk(a.z, a.E, a.k, s_key, s_cand, s_ids, s_w);
   if (w == 0 && tid < a.k) {
     a.ids_out[tid] = s_ids[tid];
     a.w_out[tid] = s_w[tid];
   }
-  const float sx = lane_xsum(xv);
-  const int slot = wave * DWG + w;
-  const int j0 = slot / DI, j1 = (slot + DWG * DT / 64) / DI;
-  const bool t0 = j0 < a.k, t1 = j1 < a.k;
-  RowPair p0, p1;
-  if (t0) p0 = load_pair(a.wt, s_ids[j0], slot % DI, lane);
-  if (t1) p1 = load_pair(a.wt, s_ids[j1], (slot + DWG * DT / 64) % DI, lane);
-  if (t0) {
-    const float hv = pair_h(p0, xv, sx);
-    if (lane == 0) a.h[(size_t)j0 * DI + slot % DI] = hv;
-  }
-  if (t1) {
-    const float hv = pair_h(p1, xv, sx);
-    if (lane == 0) a.h[(size_t)j1 * DI + (slot + DWG * DT / 64) % DI] = hv;
-  }
+  const int j = w >> 5, b = (w >> 1) & 15, f = w & 1;
+  if (j >= a.k) return;
+  gateup_half_block(a, s_ids[j], b, f, xs, xseg, red, a.h + (size_t)j * DI + 32 * b + 16 * f);
 }
 
 __global__ __launch_bounds__(DT) void k_dec_c(DecodeArgs a) {
-  __shared__ float hs[kSlots * DI];
-  __shared__ int s_ids[kMaxTopK];
-  __shared__ float s_w[kMaxTopK];
+  __shared__ __attribute__((aligned(16))) f16x2_t hs[kSlots * DI / 2];
+  __shared__ float hseg[kSlots * DI / 32];
+  __shared__ int s_ids[kSlots];
+  __shared__ float s_w[kSlots];
+  __shared__ float red[DT / 64 * 8];
   const int w = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int k = a.k, nslot = a.k + a.S;
-  // h of all k+1 experts into LDS (independent of the routing ids)
-  float hr[kSlots];
-#pragma unroll
-  for (int q = 0; q < kSlots; ++q) {
-    const int i = tid + q * DT;
-    hr[q] = i < nslot * DI ? a.h[i] : 0.f;
-  }
-  if (tid < k) {
-    s_ids[tid] = min(max(a.ids_out[tid], 0), a.E - 1);
-    s_w[tid] = a.w_out[tid];
-  }
-#pragma unroll
-  for (int q = 0; q < kSlots; ++q) {
-    const int i = tid + q * DT;
-    if (i < nslot * DI) hs[i] = hr[q];
+  if (tid < kSlots) {
+    s_ids[tid] = tid < k ? min(max(a.ids_out[tid], 0), a.E - 1) : a.E;
+    s_w[tid] = tid < k ? a.w_out[tid] : 1.0f;
   }
   __syncthreads();
-  // lane slots s = lane + 64 m: expert slot j = s / 32, 16-element chunk ch = s % 32
-  const int c_row = wave * DWG + w;
-  uint2 cw[5];
-  uint16_t sc[5], bc[5];
+  // output rows 64b + 8t .. +8; units (slot j, K step s) of 8 rows x 32 code bytes, four
+  // per load instruction: lane group l / 16 takes unit 4p + l / 16; lane: row (l % 16) / 2,
+  // K half l % 2
+  const int b = w >> 3, t = w & 7;
+  const int r8 = (lane & 15) >> 1, hh = lane & 1, ug = lane >> 4;
+  constexpr int kMaxQuads = (kSlots * kNS2 / 4 + DT / 64 - 1) / (DT / 64);
+  uint4 c[kMaxQuads], sb[kMaxQuads];
 #pragma unroll
-  for (int m = 0; m < 5; ++m) {
-    const int s = lane + 64 * m, j = s >> 5, ch = s & 31;
-    if (j < nslot) {
-      const int e = j < k ? s_ids[j] : a.E;
-      const size_t r = (size_t)e * DH + c_row;
-      cw[m] = reinterpret_cast<const uint2 *>(a.wt.w2_q + r * (DI / 2))[ch];
-      sc[m] = a.wt.w2_s[r * (DI / kGroup) + (ch >> 2)];
-      bc[m] = a.wt.w2_b[r * (DI / kGroup) + (ch >> 2)];
+  for (int i = 0; i < kMaxQuads; ++i) {
+    const int p = wave + (DT / 64) * i, u = 4 * p + ug, jj = u >> 3, st = u & 7;
+    if (jj < nslot) {
+      const size_t blk = (size_t)s_ids[jj] * kNB2 + b;
+      c[i] = *reinterpret_cast<const uint4 *>(a.wt.w2_t + (blk * kNS2 + st) * 2048 +
+                                              32 * (8 * t + r8) + 16 * hh);
+      sb[i] = *reinterpret_cast<const uint4 *>(a.wt.w2_tsb + (blk * (kNS2 / 4) + (st >> 2)) * 512 +
+                                               8 * (8 * t + r8));
     }
   }
+  // h of all k+1 experts into LDS as fp16 pairs (these loads overlap the weight loads)
+  stage_f16_pairs<false>(a.h, nslot * DI, hs, hseg);
+  __syncthreads();
   float acc = 0.f;
 #pragma unroll
-  for (int m = 0; m < 5; ++m) {
-    const int s = lane + 64 * m, j = s >> 5, ch = s & 31;
-    if (j < nslot) {
-      const float *hp = hs + j * DI + ch * 16;
-      float q0[8], q1[8];
-      unpack8(cw[m].x, q0);
-      unpack8(cw[m].y, q1);
-      float qh = 0.f, sh = 0.f;
-#pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        qh = __builtin_fmaf(q0[p], hp[p], qh);
-        qh = __builtin_fmaf(q1[p], hp[8 + p], qh);
-        sh += hp[p] + hp[8 + p];
-      }
-      const float wj = j < k ? s_w[j] : 1.0f;
-      acc = __builtin_fmaf(wj, bf16_to_f32(sc[m]) * qh + bf16_to_f32(bc[m]) * sh, acc);
+  for (int i = 0; i < kMaxQuads; ++i) {
+    const int p = wave + (DT / 64) * i, u = 4 * p + ug, jj = u >> 3, st = u & 7;
+    if (jj < nslot) {
+      const float raw = dot_codes(c[i], hs + jj * (DI / 2), 8 * st + 4 * hh);
+      acc = __builtin_fmaf(s_w[jj], group_dot(raw, word_of(sb[i], st & 3),
+                                               hseg[jj * (DI / 32) + 2 * st + hh]), acc);
     }
   }
-  acc = wave_sum_dpp(acc);
-  if (lane == 0) {
-    if (a.residual) acc += bf16_to_f32(a.residual[c_row]);
-    a.y[c_row] = f32_to_bf16(acc);
+  acc += __shfl_xor(acc, 1, 64);
+  acc += __shfl_xor(acc, 16, 64);
+  acc += __shfl_xor(acc, 32, 64);
+  if (lane < 16 && hh == 0) red[wave * 8 + r8] = acc;
+  __syncthreads();
+  if (tid < 8) {
+    float y = 0.f;
+#pragma unroll
+    for (int v = 0; v < DT / 64; ++v) y += red[v * 8 + tid];
+    const int row = 64 * b + 8 * t + tid;
+    if (a.residual) y += bf16_to_f32(a.residual[row]);
+    a.y[row] = f32_to_bf16(y);
   }
 }
 
@@ -297,9 +341,9 @@ bool decode_gemv_supported(int H, int I, int E, int k, int S, bool int4) {
 }
 
 hipError_t launch_decode_gemv(const DecodeArgs &a, hipStream_t s) {
-  MOE_LAUNCH("k_dec_a", k_dec_a, dim3(DWG), dim3(DT), 0, s, a);
+  MOE_LAUNCH("k_dec_a", k_dec_a, dim3(DWG + (a.S ? kSharedWG : 0)), dim3(DT), 0, s, a);
   MOE_LAUNCH("k_dec_b", k_dec_b, dim3(DWG), dim3(DT), 0, s, a);
-  MOE_LAUNCH("k_dec_c", k_dec_c, dim3(DWG), dim3(DT), 0, s, a);
+  MOE_LAUNCH("k_dec_c", k_dec_c, dim3(kDownWG), dim3(DT), 0, s, a);
   return hipSuccess;
 }
 

@@ -479,8 +479,10 @@ static moe_status decode_impl(const moe_layer *layer, const void *x, void *y,
                               const void *residual, void *ws, const Plan &p, hipStream_t s) {
   hipError_t e;
   const bool int4 = layer->w_format == MOE_W_INT4_G64;
+  // the three-kernel path reads the tiled weights; unpacked layers take the generic path
   if (moe::decode_gemv_supported(layer->hidden, layer->inter, layer->n_experts, layer->top_k,
-                                 layer->n_shared, int4)) {
+                                 layer->n_shared, int4) &&
+      layer->w13_t && layer->w13_tsb && layer->w2_t && layer->w2_tsb) {
     moe::DecodeArgs da{};
     da.x = static_cast<const uint16_t *>(x);
     da.router_w = layer->router_w;
