@@ -52,10 +52,10 @@ def decode_bytes_per_token():
 def _decode_kernel_bytes():
     w13, w2 = expert_bytes()
     return {
-        # router fp32 rows + shared expert gate/up + x
-        "k_dec_a": E * H * 4 + S * w13 + H * 2,
-        # routed experts' gate/up + logits + x
-        "k_dec_b": K_TOP * w13 + E * 4 + H * 2,
+        # router fp32 rows + x
+        "k_dec_a": E * H * 4 + H * 2,
+        # routed and shared experts' gate/up + logits + x
+        "k_dec_b": (K_TOP + S) * w13 + E * 4 + H * 2,
         # all k+1 experts' down projection + h (fp32) + routing + y
         "k_dec_c": (K_TOP + S) * w2 + (K_TOP + S) * I * 4 + K_TOP * 8 + H * 2,
     }

@@ -8,7 +8,7 @@
 //   adjacent 16-byte pieces: in the tiled layout one load instruction of a wave is one
 //   contiguous 1 KB block (32 rows x 32 code bytes of one K step);
 //   section "Overlap independent GPU work" -- the shared expert does not depend on the
-//   routing, so its gate/up projection runs next to the router;
+//   routing, so its gate/up projection runs next to the top-k;
 //   section "Reduce intermediate and state traffic" -- gate/up are fused with SwiGLU and
 //   the output projection with the routing weights and the shared-expert result.
 //
@@ -17,11 +17,12 @@
 // boundary costs about 1.4 us on MI355X, less than a grid barrier built on device-scope
 // atomics across 256 workgroups (2.4-3.7 us), so no kernel spins.
 //
-//   A  256 workgroups: workgroup w computes router logit z[w]; 32 more workgroups compute
-//      the shared expert's gate/up, 16 gate + 16 up rows each (as in B).
-//   B  every workgroup runs the top-k on z (same data, same code, same answer), then
-//      computes 16 gate + 16 up rows of one selected expert: workgroup (slot j, block b,
+//   A  256 workgroups: workgroup w computes router logit z[w].
+//   B  256 workgroups run the top-k on z (same data, same code, same answer), then
+//      compute 16 gate + 16 up rows of one selected expert: workgroup (slot j, block b,
 //      half f) -> rows 32b + 16f .. +16. Workgroup 0 stores the ids and weights for C.
+//      32 more workgroups compute the shared expert's gate/up the same way; they need no
+//      routing, so they skip the top-k and overlap it.
 //   C  256 workgroups of 8 output rows each: all k+1 experts' W2 rows times h (staged
 //      in LDS), scaled by the routing weights, plus the residual.
 //
@@ -42,7 +43,7 @@ constexpr int kNB13 = 2 * DI / 64;  // 64-row blocks of W13 (32 gate + 32 up row
 constexpr int kNS13 = DH / 64;      // K steps of W13
 constexpr int kNB2 = DH / 64;       // 64-row blocks of W2
 constexpr int kNS2 = DI / 64;       // K steps of W2
-constexpr int kSharedWG = 2 * kNB13; // extra workgroups of A: shared-expert half blocks
+constexpr int kSharedWG = 2 * kNB13; // extra workgroups of B: shared-expert half blocks
 constexpr int kDownWG = kNB2 * 8;   // C: 8 output rows per workgroup
 }  // namespace
 
@@ -227,34 +228,25 @@ MOE_DEV void gateup_half_block(const DecodeArgs &a, int e, int b, int f, const f
 }
 
 __global__ __launch_bounds__(DT) void k_dec_a(DecodeArgs a) {
-  __shared__ float red[DT / 64 * 32];
-  __shared__ __attribute__((aligned(16))) f16x2_t xs[DH / 2];
-  __shared__ float xseg[DH / 32];
+  __shared__ float red[DT / 64];
   const int w = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  if (w < DWG) {
-    // router logit w: 512 threads x 4 fp32 weights
-    if (w >= a.E) return;
-    const float4 wr = reinterpret_cast<const float4 *>(a.router_w + (size_t)w * DH)[tid];
-    const uint2 xb = reinterpret_cast<const uint2 *>(a.x)[tid];
-    float d = wr.x * bf16lo(xb.x);
-    d = __builtin_fmaf(wr.y, bf16hi(xb.x), d);
-    d = __builtin_fmaf(wr.z, bf16lo(xb.y), d);
-    d = __builtin_fmaf(wr.w, bf16hi(xb.y), d);
-    d = wave_sum_dpp(d);
-    if (lane == 0) red[wave] = d;
-    __syncthreads();
-    if (tid == 0) {
-      float s = 0.f;
+  // router logit w: 512 threads x 4 fp32 weights
+  if (w >= a.E) return;
+  const float4 wr = reinterpret_cast<const float4 *>(a.router_w + (size_t)w * DH)[tid];
+  const uint2 xb = reinterpret_cast<const uint2 *>(a.x)[tid];
+  float d = wr.x * bf16lo(xb.x);
+  d = __builtin_fmaf(wr.y, bf16hi(xb.x), d);
+  d = __builtin_fmaf(wr.z, bf16lo(xb.y), d);
+  d = __builtin_fmaf(wr.w, bf16hi(xb.y), d);
+  d = wave_sum_dpp(d);
+  if (lane == 0) red[wave] = d;
+  __syncthreads();
+  if (tid == 0) {
+    float s = 0.f;
 #pragma unroll
-      for (int i = 0; i < DT / 64; ++i) s += red[i];
-      a.z[w] = s + (a.router_b ? a.router_b[w] : 0.f);
-    }
-    return;
+    for (int i = 0; i < DT / 64; ++i) s += red[i];
+    a.z[w] = s + (a.router_b ? a.router_b[w] : 0.f);
   }
-  // shared expert: half block (b, f) of workgroup DWG + 2b + f
-  const int b = (w - DWG) >> 1, f = (w - DWG) & 1;
-  stage_f16_pairs<true>(a.x, DH, xs, xseg);
-  gateup_half_block(a, a.E, b, f, xs, xseg, red, a.h + (size_t)a.k * DI + 32 * b + 16 * f);
 }
 
 __global__ __launch_bounds__(DT) void k_dec_b(DecodeArgs a) {
@@ -267,6 +259,12 @@ __global__ __launch_bounds__(DT) void k_dec_b(DecodeArgs a) {
   __shared__ float red[DT / 64 * 32];
   const int w = blockIdx.x, tid = threadIdx.x;
   stage_f16_pairs<true>(a.x, DH, xs, xseg);
+  if (w >= DWG) {
+    // the shared expert needs no routing: half block (b, f) of workgroup DWG + 2b + f
+    const int b = (w - DWG) >> 1, f = (w - DWG) & 1;
+    gateup_half_block(a, a.E, b, f, xs, xseg, red, a.h + (size_t)a.k * DI + 32 * b + 16 * f);
+    return;
+  }
   block_topk(a.z, a.E, a.k, s_key, s_cand, s_ids, s_w);
   if (w == 0 && tid < a.k) {
     a.ids_out[tid] = s_ids[tid];
@@ -341,8 +339,8 @@ bool decode_gemv_supported(int H, int I, int E, int k, int S, bool int4) {
 }
 
 hipError_t launch_decode_gemv(const DecodeArgs &a, hipStream_t s) {
-  MOE_LAUNCH("k_dec_a", k_dec_a, dim3(DWG + (a.S ? kSharedWG : 0)), dim3(DT), 0, s, a);
-  MOE_LAUNCH("k_dec_b", k_dec_b, dim3(DWG), dim3(DT), 0, s, a);
+  MOE_LAUNCH("k_dec_a", k_dec_a, dim3(DWG), dim3(DT), 0, s, a);
+  MOE_LAUNCH("k_dec_b", k_dec_b, dim3(DWG + (a.S ? kSharedWG : 0)), dim3(DT), 0, s, a);
   MOE_LAUNCH("k_dec_c", k_dec_c, dim3(kDownWG), dim3(DT), 0, s, a);
   return hipSuccess;
 }
