@@ -263,6 +263,21 @@ MOE_DEV int block_scan_incl(int v, int *sc) {
   return r;
 }
 
+MOE_DEV uint64_t block_scan_incl64(uint64_t v, uint64_t *sc) {
+  const int tid = threadIdx.x;
+  sc[tid] = v;
+  __syncthreads();
+  for (int d = 1; d < 256; d <<= 1) {
+    const uint64_t o = tid >= d ? sc[tid - d] : 0;
+    __syncthreads();
+    sc[tid] += o;
+    __syncthreads();
+  }
+  const uint64_t r = sc[tid];
+  __syncthreads();
+  return r;
+}
+
 // ---- counts, offsets, per-block bases and the tile map (one workgroup) -------------------
 // blk_cnt[b][e] becomes the number of assignments to e in blocks before b. offsets has
 // E+2 entries: routed experts, then the shared expert's slots [kT, kT+T).
@@ -291,29 +306,50 @@ __global__ __launch_bounds__(256) void k_scan(int32_t *__restrict__ blk_cnt, int
   }
   const int incl = block_scan_incl(run, sc);
   const int off = incl - run;
-  const int ntile = (run + kTileM - 1) / kTileM;
-  const int tincl = block_scan_incl(ntile, sc);
-  const int tstart = tincl - ntile;
-  __shared__ int totals[2];
+  // Tile map in descending order of work (the GEMM workgroups start in index order, so the
+  // long tiles go first and the short ones fill the end): every full 128-row tile (routed
+  // experts in order, then the shared expert), then the partial tiles by their number of
+  // 32-row blocks, 4 down to 1. One 64-bit scan places them all: bits [0, 21) count full
+  // tiles, 9-bit fields at 21 + 9q count partial tiles of 4 - q blocks.
+  const int nfull = run >> 7, mb = ((run & 127) + 31) >> 5;
+  const uint64_t packed = (uint64_t)nfull | (mb ? (1ull << (21 + 9 * (4 - mb))) : 0ull);
+  __shared__ uint64_t sc64[256];
+  const uint64_t pincl = block_scan_incl64(packed, sc64);
+  const uint64_t pexcl = pincl - packed;
+  __shared__ int totals[1];
+  __shared__ uint64_t ptot[1];
   if (e == 255) {
     totals[0] = incl;
-    totals[1] = tincl;
+    ptot[0] = pincl;
   }
   __syncthreads();
-  const int nassign = totals[0], nt_routed = totals[1];
+  const int nassign = totals[0];
+  const uint64_t tot = ptot[0];
+  const int nfull_tot = (int)(tot & 0x1FFFFF);
+  const int sh_full = S ? T >> 7 : 0, sh_rem = S ? (T & 127) : 0;
+  int bstart[4];
+  bstart[0] = nfull_tot + sh_full;
+#pragma unroll
+  for (int q = 1; q < 4; ++q) bstart[q] = bstart[q - 1] + (int)((tot >> (21 + 9 * (q - 1))) & 0x1FF);
+  const int npart = bstart[3] + (int)((tot >> (21 + 27)) & 0x1FF);
   if (e < E) {
     offsets[e] = off;
     if (counts_user) counts_user[e] = run;
     if (offsets_user) offsets_user[e] = off;
-    for (int i = 0; i < ntile; ++i) tiles[tstart + i] = make_int2(e, i * kTileM);
+    const int f0 = (int)(pexcl & 0x1FFFFF);
+    for (int i = 0; i < nfull; ++i) tiles[f0 + i] = make_int2(e, i * kTileM);
+    if (mb) {
+      const int q = 4 - mb;
+      tiles[bstart[q] + (int)((pexcl >> (21 + 9 * q)) & 0x1FF)] = make_int2(e, nfull * kTileM);
+    }
   }
-  const int nt_shared = S ? (T + kTileM - 1) / kTileM : 0;
-  for (int i = e; i < nt_shared; i += 256) tiles[nt_routed + i] = make_int2(E, i * kTileM);
+  for (int i = e; i < sh_full; i += 256) tiles[nfull_tot + i] = make_int2(E, i * kTileM);
   if (e == 0) {
+    if (sh_rem) tiles[npart] = make_int2(E, sh_full * kTileM);
     offsets[E] = nassign;
     offsets[E + 1] = nassign + (S ? T : 0);
     if (offsets_user) offsets_user[E] = nassign;
-    *n_tiles = nt_routed + nt_shared;
+    *n_tiles = npart + (sh_rem ? 1 : 0);
   }
 }
 
