@@ -247,33 +247,67 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
 #undef MOE_DMA16
 
   // 32x32 accumulator layout: lane l holds column l%32, register r holds row
-  // 8*(r/4) + 4*(l/32) + r%4.
+  // 8*(r/4) + 4*(l/32) + r%4. The tile leaves through LDS (the stages are free now): each
+  // wave writes its fp16 results into a row-major tile, then every thread copies 16-byte
+  // pieces of whole rows to global memory, instead of 2-byte stores scattered by the
+  // accumulator layout. Rows are padded by 16 bytes, so the two rows an instruction
+  // writes (l < 32 and l >= 32) fall into different bank halves.
   const int col = lane & 31, rq4 = (lane >> 5) * 4;
+  __syncthreads();  // every wave is done reading the stages
+  if (kGateUp) {
+    // h: rows x 128 columns, stored in the chunk order of the fp16 operand rows (h is the
+    // down GEMM's A operand)
+    constexpr int HP = 128 + 8;
+    _Float16 *ht = reinterpret_cast<_Float16 *>(smem);
+    const int il = 32 * wave + col;
+    const int pos = (il & ~7) + kChunkPos[il & 7];
 #pragma unroll
-  for (int m = 0; m < MB; ++m) {
+    for (int m = 0; m < MB; ++m)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = 32 * m + (r >> 2) * 8 + rq4 + (r & 3);
-      if (row >= nvalid) continue;
-      const size_t slot = (size_t)(slot0 + row);
-      if (kGateUp) {
-        // h keeps the chunk order of the fp16 operand rows (it is the down GEMM's A)
-        const int i = n_tile * (BNW / 2) + 32 * wave + col;
-        a.h16[slot * a.I + (i & ~7) + kChunkPos[i & 7]] =
-            f32_to_f16(silu(acc[m][0][r]) * acc[m][1][r]);
-      } else {
-        const int n = n_tile * BNW + 64 * wave + col;
-        if (e < a.E) {
-          const float wv = a.slot_w[slot];
-          a.out[slot * a.H + n] = f32_to_f16(wv * acc[m][0][r]);
-          a.out[slot * a.H + n + 32] = f32_to_f16(wv * acc[m][1][r]);
-        } else {
-          const size_t t = (size_t)(row0 + row);
-          a.out_sh[t * a.H + n] = acc[m][0][r];
-          a.out_sh[t * a.H + n + 32] = acc[m][1][r];
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * m + (r >> 2) * 8 + rq4 + (r & 3);
+        ht[row * HP + pos] = (_Float16)(silu(acc[m][0][r]) * acc[m][1][r]);
       }
-    }
+    __syncthreads();
+    for (int rr = tid >> 4; rr < nvalid; rr += 16)
+      *reinterpret_cast<uint4 *>(a.h16 + (size_t)(slot0 + rr) * a.I + n_tile * (BNW / 2) +
+                                 8 * (tid & 15)) =
+          *reinterpret_cast<const uint4 *>(ht + rr * HP + 8 * (tid & 15));
+  } else if (e < a.E) {
+    // routed rows, pre-weighted by their routing weight: rows x 256 columns fp16
+    constexpr int OP = BNW + 8;
+    _Float16 *ot = reinterpret_cast<_Float16 *>(smem);
+    float *sw = reinterpret_cast<float *>(smem + BM * OP * 2);
+    if (tid < BM) sw[tid] = tid < nvalid ? a.slot_w[slot0 + tid] : 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * m + (r >> 2) * 8 + rq4 + (r & 3);
+        const float wv = sw[row];
+        ot[row * OP + 64 * wave + col] = (_Float16)(wv * acc[m][0][r]);
+        ot[row * OP + 64 * wave + 32 + col] = (_Float16)(wv * acc[m][1][r]);
+      }
+    __syncthreads();
+    for (int rr = tid >> 5; rr < nvalid; rr += 8)
+      *reinterpret_cast<uint4 *>(a.out + (size_t)(slot0 + rr) * a.H + n_tile * BNW +
+                                 8 * (tid & 31)) =
+          *reinterpret_cast<const uint4 *>(ot + rr * OP + 8 * (tid & 31));
+  } else {
+    // shared expert: fp32 in token order; each store instruction writes 128 contiguous
+    // bytes of a row already
+    const int n = n_tile * BNW + 64 * wave + col;
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * m + (r >> 2) * 8 + rq4 + (r & 3);
+        if (row >= nvalid) continue;
+        const size_t t = (size_t)(row0 + row);
+        a.out_sh[t * a.H + n] = acc[m][0][r];
+        a.out_sh[t * a.H + n + 32] = acc[m][1][r];
+      }
   }
 }
 
