@@ -135,6 +135,11 @@ MOE_DEV float group_sum(float v) {
 }
 
 MOE_DEV float silu(float v) { return v / (1.0f + expf(-v)); }
+// silu from the hardware exp2 and reciprocal (about 1 ulp each), for results that are
+// rounded to fp16 anyway: v / (1 + 2^(-v log2 e)).
+MOE_DEV float silu_fast(float v) {
+  return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v * 1.4426950408889634f));
+}
 
 // ---- wave-wide reductions on the DPP path (no LDS traffic) --------------------------------
 // Inclusive-scan pattern: row shifts by 1, 2, 4, 8 inside each row of 16 lanes, then row

@@ -266,7 +266,7 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = 32 * m + (r >> 2) * 8 + rq4 + (r & 3);
-        ht[row * HP + pos] = (_Float16)(silu(acc[m][0][r]) * acc[m][1][r]);
+        ht[row * HP + pos] = (_Float16)(silu_fast(acc[m][0][r]) * acc[m][1][r]);
       }
     __syncthreads();
     for (int rr = tid >> 4; rr < nvalid; rr += 16)
