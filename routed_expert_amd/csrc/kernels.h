@@ -30,6 +30,7 @@ struct RouteArgs {
   int64_t T;
   int H, E, k, S;
   float *logits;          // [T, E] (decode: [E])
+  float *logits2;         // [T, E] second half of the reduction (bf16 path)
   uint16_t *router_planes;  // [3, E, H] bf16 split of the router weights (bf16 path)
   int32_t *ids;           // [T, k]
   float *w;               // [T, k]

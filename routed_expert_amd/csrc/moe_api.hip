@@ -84,7 +84,8 @@ moe_status check_layer(const moe_layer *L) {
 // Workspace layout: the batch-1 decode buffers first, then the T-dependent region.
 struct Plan {
   size_t dec_logits, dec_ids, dec_w, dec_h;
-  size_t logits, planes, ids, w, blk, offsets, sorted, slot, slot_w, x16, tiles, ntiles, h, out,
+  size_t logits, logits2, planes, ids, w, blk, offsets, sorted, slot, slot_w, x16, tiles, ntiles,
+      h, out,
       out_sh;
   size_t total;
   int max_tiles;
@@ -111,6 +112,7 @@ Plan make_plan(const moe_layer *L, int64_t T) {
                        (S ? (Tn + moe::kTileM - 1) / moe::kTileM : 0);
   p.max_tiles = (int)tiles;
   p.logits = take(Tn * E * 4);
+  p.logits2 = take(L->act_dtype == MOE_ACT_BF16 ? Tn * E * 4 : 0);
   p.planes = take(L->act_dtype == MOE_ACT_BF16 ? 3 * E * H * 2 : 0);
   p.ids = take(Tn * k * 4);
   p.w = take(Tn * k * 4);
@@ -240,6 +242,7 @@ moe::RouteArgs route_args(const moe_layer *L, const void *x, int64_t T) {
 // Routing results go to the caller's buffers when given, else to the workspace.
 void route_targets(moe::RouteArgs &a, const Plan &p, void *ws, const moe_route_out *ro) {
   a.logits = at<float>(ws, p.logits);
+  a.logits2 = at<float>(ws, p.logits2);
   a.router_planes = at<uint16_t>(ws, p.planes);
   a.blk = at<int32_t>(ws, p.blk);
   a.offsets = at<int32_t>(ws, p.offsets);

@@ -62,6 +62,7 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t *__restrict_
                                                      const uint16_t *__restrict__ planes,
                                                      const float *__restrict__ bias,
                                                      float *__restrict__ z,
+                                                     float *__restrict__ z2,
                                                      uint16_t *__restrict__ x16,
                                                      int32_t *__restrict__ blk_cnt, int T,
                                                      int H, int E) {
@@ -70,7 +71,10 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t *__restrict_
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-  if (tid < 64 && e0 + tid < E) blk_cnt[(size_t)blockIdx.x * E + e0 + tid] = 0;
+  // blockIdx.z takes one half of the reduction axis; the halves land in z and z2 and the
+  // top-k adds them (z + z2, bias in z), so the sum is the same whatever runs first
+  const int kbase = blockIdx.z * (H / 2);
+  if (tid < 64 && e0 + tid < E && blockIdx.z == 0) blk_cnt[(size_t)blockIdx.x * E + e0 + tid] = 0;
   // loader: row lr (token / expert), 16 elements at column lc
   const int lr = tid >> 2, lc = (tid & 3) * 16;
   const int t = t0 + lr, e = e0 + lr;
@@ -113,13 +117,13 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t *__restrict_
     }
   };
   f32x16_t acc = {};
-  gload(0);
-  lstore(0, 0);
+  gload(kbase);
+  lstore(0, kbase);
   __syncthreads();
-  const int nsteps = H / 64;
+  const int nsteps = H / 2 / 64;
   for (int st = 0; st < nsteps; ++st) {
     const int cur = st & 1;
-    if (st + 1 < nsteps) gload((st + 1) * 64);
+    if (st + 1 < nsteps) gload(kbase + (st + 1) * 64);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int ko = kk * 16 + fk;
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t *__restrict_
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
       }
     }
-    if (st + 1 < nsteps) lstore(cur ^ 1, (st + 1) * 64);
+    if (st + 1 < nsteps) lstore(cur ^ 1, kbase + (st + 1) * 64);
     __syncthreads();
   }
   const int col = lane & 31, rq4 = (lane >> 5) * 4;
@@ -140,7 +144,12 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t *__restrict_
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int tt = t0 + wm * 32 + (r >> 2) * 8 + rq4 + (r & 3);
-    if (tt < T && ee < E) z[(size_t)tt * E + ee] = acc[r] + (bias ? bias[ee] : 0.f);
+    if (tt < T && ee < E) {
+      if (blockIdx.z == 0)
+        z[(size_t)tt * E + ee] = acc[r] + (bias ? bias[ee] : 0.f);
+      else
+        z2[(size_t)tt * E + ee] = acc[r];
+    }
   }
 }
 
@@ -155,7 +164,10 @@ __global__ __launch_bounds__(256) void k_router_f32(const float *__restrict__ x,
   __shared__ float wsm[32][68];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-  if (tid < 64 && e0 + tid < E) blk_cnt[(size_t)blockIdx.x * E + e0 + tid] = 0;
+  // blockIdx.z takes one half of the reduction axis; the halves land in z and z2 and the
+  // top-k adds them (z + z2, bias in z), so the sum is the same whatever runs first
+  const int kbase = blockIdx.z * (H / 2);
+  if (tid < 64 && e0 + tid < E && blockIdx.z == 0) blk_cnt[(size_t)blockIdx.x * E + e0 + tid] = 0;
   const int lr = tid >> 2, lk = (tid & 3) * 8;
   float acc[4][4];
 #pragma unroll
@@ -215,7 +227,8 @@ __global__ __launch_bounds__(256) void k_router_f32(const float *__restrict__ x,
 
 // ---- top-k, one wave per token; per-block histogram by device atomics -----------------
 // Workgroup = 4 waves = 4 tokens. blk_cnt[t / 64][e] was zeroed by the router kernel.
-__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ z, int T, int E, int k,
+__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ z,
+                                              const float *__restrict__ z2, int T, int E, int k,
                                               int32_t *__restrict__ ids,
                                               float *__restrict__ w,
                                               int32_t *__restrict__ blk_cnt) {
@@ -227,7 +240,8 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ z, int T
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int e = lane + kWave * c;
-    v[c] = e < E ? z[(size_t)t * E + e] : -INFINITY;
+    v[c] = e < E ? (z2 ? z[(size_t)t * E + e] + z2[(size_t)t * E + e] : z[(size_t)t * E + e])
+                 : -INFINITY;
   }
   int sel[kMaxTopK];
   float sw[kMaxTopK];
@@ -393,16 +407,16 @@ hipError_t launch_route_prefill(const RouteArgs &a, hipStream_t s) {
     MOE_LAUNCH("k_router_split", k_router_split,
                dim3((unsigned)std::min<size_t>((n / 4 + 255) / 256, 2048)), dim3(256), 0, s,
                a.router_w, n, a.router_planes);
-    MOE_LAUNCH("k_router_mfma", k_router_mfma, g1, dim3(256), 0, s,
+    MOE_LAUNCH("k_router_mfma", k_router_mfma, dim3(g1.x, g1.y, 2), dim3(256), 0, s,
                static_cast<const uint16_t *>(a.x), a.router_planes, a.router_b, a.logits,
-               a.x16, a.blk, (int)a.T, a.H, a.E);
+               a.logits2, a.x16, a.blk, (int)a.T, a.H, a.E);
   }
   else
     MOE_LAUNCH("k_router_f32", k_router_f32, g1, dim3(256), 0, s,
                static_cast<const float *>(a.x), a.router_w, a.router_b, a.logits, a.blk,
                (int)a.T, a.H, a.E);
   MOE_LAUNCH("k_topk", k_topk, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, s, a.logits,
-             (int)a.T, a.E, a.k, a.ids, a.w, a.blk);
+             a.bf16 ? a.logits2 : nullptr, (int)a.T, a.E, a.k, a.ids, a.w, a.blk);
   MOE_LAUNCH("k_scan", k_scan, dim3(1), dim3(256), 0, s, a.blk, NB, a.E, (int)a.T, a.k, a.S,
              a.offsets, a.counts_user, a.offsets_user, a.tiles, a.n_tiles);
   MOE_LAUNCH("k_scatter", k_scatter, dim3(NB), dim3(256), 0, s, a.ids, (int)a.T, a.E, a.k,
