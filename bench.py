@@ -320,6 +320,40 @@ def cpu_baseline(synth):
                       f"copy 0, full layer per token, fp64, {dt:.1f} s on {cpu}"}
 
 
+COPY_BYTES = 256 << 20
+
+
+def profile_run(moe, torch, synth, dev, what):
+    """Fixed work for rocprofv3 (kernel trace or counters): a plain device copy of
+    COPY_BYTES (the calibration for FETCH_SIZE / WRITE_SIZE), then a few calls of the
+    named path. Prints nothing but a done line."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    if what == "decode":
+        layers = [moe.DeviceLayer.from_host(synth.decode_layer(0), dev)] + \
+                 [gpu_layer(moe, torch, synth, dev, c) for c in range(1, N_COPIES)]
+        import numpy as np
+        xs = moe.bf16_from_bits(np.concatenate([synth.decode_token(t) for t in range(64)]), dev)
+        ws = moe.workspace(layers[0], 1, dev)
+        y = torch.empty((1, H), dtype=torch.bfloat16, device=dev)
+        for i in range(200):
+            moe.moe_decode(layers[i % N_COPIES], xs[i % 64:i % 64 + 1], y=y, ws=ws)
+    else:
+        layer = synth.skewed_layer(0) if what == "prefill_skewed" else synth.decode_layer(0)
+        dl = moe.DeviceLayer.from_host(layer, dev)
+        x = moe.bf16_from_bits(synth.prefill_x(4096, seed=2), dev)
+        ws = moe.workspace(dl, 4096, dev)
+        y = torch.empty_like(x)
+        for _ in range(10):
+            moe.moe_prefill(dl, x, y=y, ws=ws)
+    torch.cuda.synchronize()
+    print(f"profile run done: {what}", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -328,6 +362,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--profile", choices=["decode", "prefill_uniform", "prefill_skewed"],
+                    help="fixed work for rocprofv3 instead of the benchmark")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -338,6 +374,9 @@ def main():
     from routed_expert_amd import moe, synth
     dev = "cuda:0"
     moe.lib()
+    if args.profile:
+        profile_run(moe, torch, synth, dev, args.profile)
+        return
     dec = bench_decode(moe, torch, synth, dev, args.steps, args.warmup)
     ms_step = dec["ms"] / dec["steps"]
     tok_s = dec["steps"] / (dec["ms"] * 1e-3)
