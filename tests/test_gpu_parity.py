@@ -297,6 +297,30 @@ def test_prefill_small_layer_padded_scale_blocks(M):
     assert rel_err(y_np(y)[sure], ref[sure]) <= BF16_TOL
 
 
+@pytest.mark.parametrize("E,k,S", [(64, 4, 0), (32, 1, 1), (128, 8, 0)])
+def test_model_width_layers_other_routing(M, E, k, S):
+    # hidden 2048 / intermediate 512 takes the three-kernel decode path for any E <= 256,
+    # k + S <= 9: idle top-k slots, no shared expert, fewer router workgroups
+    announce(f"moe_decode/moe_prefill int4 H=2048 I=512 E={E} k={k} S={S}")
+    layer = synth.make_int4_layer(500 + E + k, n_experts=E, top_k=k, n_shared=S)
+    dl = M.DeviceLayer.from_host(layer, DEV)
+    xb = synth.bf16_activations(600 + E, (70, 2048))
+    ref = oracle.moe(layer, xb)
+    _, _, margin = oracle.route(layer, xb)
+    sure = margin >= delta_for(2048)
+    for t in np.flatnonzero(sure)[:6]:
+        yd = M.moe_decode(dl, bf16_dev(M, xb[t:t + 1]))
+        torch.cuda.synchronize()
+        assert rel_err(y_np(yd)[0], ref[t]) <= BF16_TOL, t
+    buf = M.route_buffers(dl, 70, DEV)
+    y = M.moe_prefill(dl, bf16_dev(M, xb), route_out=buf)
+    torch.cuda.synchronize()
+    g = to_np(buf)
+    check_routing(layer, xb, g["topk_ids"], g["topk_w"], delta_for(2048))
+    check_grouping(layer, g)
+    assert rel_err(y_np(y)[sure], ref[sure]) <= BF16_TOL
+
+
 def test_empty_prefill_is_noop(M, big):
     _, dl = big
     announce("moe_prefill T=0")
