@@ -283,9 +283,29 @@ __global__ __launch_bounds__(DT) void k_dec_c(DecodeArgs a) {
   __shared__ float red[DT / 64 * 8];
   const int w = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int k = a.k, nslot = a.k + a.S;
+  // three independent loads leave together: the routing (ids, weights), h of all k+1
+  // experts (two 8-element chunks per thread), then -- once the ids are known -- the W2
+  // rows; h is converted into LDS while the W2 rows are in flight
+  int my_id = 0;
+  float my_w = 1.0f;
+  if (tid < k) {
+    my_id = a.ids_out[tid];
+    my_w = a.w_out[tid];
+  }
+  const int nch = nslot * DI / 8;
+  static_assert(kSlots * DI / 8 <= 2 * DT, "h of all slots must fit two chunks per thread");
+  float4 hv[2][2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int ch = tid + q * DT;
+    if (ch < nch) {
+      hv[q][0] = reinterpret_cast<const float4 *>(a.h)[2 * ch];
+      hv[q][1] = reinterpret_cast<const float4 *>(a.h)[2 * ch + 1];
+    }
+  }
   if (tid < kSlots) {
-    s_ids[tid] = tid < k ? min(max(a.ids_out[tid], 0), a.E - 1) : a.E;
-    s_w[tid] = tid < k ? a.w_out[tid] : 1.0f;
+    s_ids[tid] = tid < k ? min(max(my_id, 0), a.E - 1) : a.E;
+    s_w[tid] = tid < k ? my_w : 1.0f;
   }
   __syncthreads();
   // output rows 64b + 8t .. +8; units (slot j, K step s) of 8 rows x 32 code bytes, four
@@ -306,8 +326,25 @@ __global__ __launch_bounds__(DT) void k_dec_c(DecodeArgs a) {
                                                8 * (8 * t + r8));
     }
   }
-  // h of all k+1 experts into LDS as fp16 pairs (these loads overlap the weight loads)
-  stage_f16_pairs<false>(a.h, nslot * DI, hs, hseg);
+  // h -> fp16 pairs (v[8c + p], v[8c + p + 4]) per chunk c, and the 32-element segment sums
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int ch = tid + q * DT;
+    const bool live = ch < nch;
+    const float v[8] = {hv[q][0].x, hv[q][0].y, hv[q][0].z, hv[q][0].w,
+                        hv[q][1].x, hv[q][1].y, hv[q][1].z, hv[q][1].w};
+    float sum = 0.f;
+    f16x2_t pr[4];
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      pr[pp] = live ? f16x2_t{(_Float16)v[pp], (_Float16)v[pp + 4]} : f16x2_t{};
+      sum += (float)pr[pp][0] + (float)pr[pp][1];
+    }
+    if (live) *reinterpret_cast<uint4 *>(hs + 4 * ch) = __builtin_bit_cast(uint4, pr);
+    sum += __shfl_xor(sum, 1, 64);
+    sum += __shfl_xor(sum, 2, 64);
+    if ((ch & 3) == 0 && live) hseg[ch >> 2] = sum;
+  }
   __syncthreads();
   float acc = 0.f;
 #pragma unroll
