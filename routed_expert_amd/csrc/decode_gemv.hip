@@ -127,12 +127,13 @@ MOE_DEV uint32_t word_of(const uint4 v, int i) {
 //      comparands 8(l/8) .. 8(l/8)+7, partial ranks summed over the 8 lane groups).
 //   3. lanes 0..k-1 of wave 0 turn the k winners into ids in ascending order and softmax
 //      weights.
-// Must be called by all DT threads; results land in s_ids / s_w.
-MOE_DEV void block_topk(const float *z, int E, int k, uint64_t *K, uint64_t *cand,
+// Must be called by all DT threads, thread t < E passing logit t (loaded by the caller, so
+// that the load can leave early); results land in s_ids / s_w.
+MOE_DEV void block_topk(float zv, int E, int k, uint64_t *K, uint64_t *cand,
                         int *s_ids, float *s_w) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   if (tid < 256) {
-    const float f = tid < E ? z[tid] : -INFINITY;
+    const float f = tid < E ? zv : -INFINITY;
     const float g = f != f ? -INFINITY : f;
     K[tid] = tid < E ? ((uint64_t)float_key(g) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)tid)
                      : 0ull;
@@ -258,6 +259,8 @@ __global__ __launch_bounds__(DT) void k_dec_b(DecodeArgs a) {
   __shared__ float xseg[DH / 32];
   __shared__ float red[DT / 64 * 32];
   const int w = blockIdx.x, tid = threadIdx.x;
+  // the logit this thread ranks and its chunk of x leave together
+  const float zv = (w < DWG && tid < a.E) ? a.z[tid] : 0.f;
   stage_f16_pairs<true>(a.x, DH, xs, xseg);
   if (w >= DWG) {
     // the shared expert needs no routing: half block (b, f) of workgroup DWG + 2b + f
@@ -265,7 +268,7 @@ __global__ __launch_bounds__(DT) void k_dec_b(DecodeArgs a) {
     gateup_half_block(a, a.E, b, f, xs, xseg, red, a.h + (size_t)a.k * DI + 32 * b + 16 * f);
     return;
   }
-  block_topk(a.z, a.E, a.k, s_key, s_cand, s_ids, s_w);
+  block_topk(zv, a.E, a.k, s_key, s_cand, s_ids, s_w);
   if (w == 0 && tid < a.k) {
     a.ids_out[tid] = s_ids[tid];
     a.w_out[tid] = s_w[tid];
