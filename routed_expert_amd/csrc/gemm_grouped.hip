@@ -210,17 +210,6 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
         acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[kk & 1][m], bc1, acc[m][1], 0, 0, 0);
       }
       if (kk == 0 && st + 2 < nsteps) MOE_ISSUE(st + 2);
-      if (kk == 2 && st + 1 < nsteps) {
-        // this wave's loads of step st+1 have landed once only step st+2's are younger
-        if (st + 2 < nsteps) {
-          if (((st + 2) & 3) == 0)
-            wait_vmcnt<MB + 3>();
-          else
-            wait_vmcnt<MB + 2>();
-        } else {
-          wait_vmcnt<0>();
-        }
-      }
       if (kk < 3) {
         // next substep's weights while the MFMAs above run
         bc0 = __builtin_bit_cast(f16x8_t, dequant8_pk(w0[kk + 1], s0, b0));
@@ -235,7 +224,16 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                   // 1 LDS read
         }
       } else if (st + 1 < nsteps) {
-        // the next step's codes and its first substep's weights, before its barrier
+        // the next step's codes and its first substep's weights, before its barrier, once
+        // this wave's loads of step st+1 have landed (only step st+2's are younger)
+        if (st + 2 < nsteps) {
+          if (((st + 2) & 3) == 0)
+            wait_vmcnt<MB + 3>();
+          else
+            wait_vmcnt<MB + 2>();
+        } else {
+          wait_vmcnt<0>();
+        }
         MOE_READ_B(st + 1);
         bc0 = __builtin_bit_cast(f16x8_t, dequant8_pk(w0[0], s0, b0));
         bc1 = __builtin_bit_cast(f16x8_t, dequant8_pk(w1[0], s1, b1));
