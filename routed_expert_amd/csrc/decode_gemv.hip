@@ -88,6 +88,54 @@ MOE_DEV void stage_f16_pairs(const void *src, int n, f16x2_t *pairs, float *seg)
   }
 }
 
+// 1 / sqrt(mean(x^2) + eps) of the row, from each thread's partial sum of squares (all DT
+// threads call it; red8 holds DT / 64 floats of LDS).
+MOE_DEV float block_inv_rms(float ss, float eps, float *red8) {
+  ss = wave_sum_dpp(ss);
+  if ((threadIdx.x & 63) == 0) red8[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float total = 0.f;
+#pragma unroll
+  for (int v = 0; v < DT / 64; ++v) total += red8[v];
+  return 1.0f / sqrtf(total / (float)DH + eps);
+}
+
+// The bf16 row x (normalised first when a.norm) as fp16 pairs in LDS plus its 32-element
+// segment sums (of the fp16 values): thread t < DH / 8 takes chunk t.
+MOE_DEV void stage_x(const DecodeArgs &a, f16x2_t *pairs, float *seg, float *red8) {
+  const int tid = threadIdx.x;
+  const bool live = tid < DH / 8;
+  float v[8] = {};
+  if (live) {
+    const uint4 u = reinterpret_cast<const uint4 *>(a.x)[tid];
+    const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16lo(wd[i]);
+      v[2 * i + 1] = bf16hi(wd[i]);
+    }
+  }
+  if (a.norm) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
+    const float inv = block_inv_rms(ss, a.eps, red8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = bf16_to_f32(f32_to_bf16(v[i] * inv));
+  }
+  float sum = 0.f;
+  f16x2_t pr[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    pr[p] = f16x2_t{(_Float16)v[p], (_Float16)v[p + 4]};
+    sum += (float)pr[p][0] + (float)pr[p][1];
+  }
+  if (live) *reinterpret_cast<uint4 *>(pairs + 4 * tid) = __builtin_bit_cast(uint4, pr);
+  sum += __shfl_xor(sum, 1, 64);
+  sum += __shfl_xor(sum, 2, 64);
+  if ((tid & 3) == 0 && live) seg[tid >> 2] = sum;
+}
+
 // Raw dot of one lane's 16 code bytes (32 elements = chunks c0 .. c0+3) with the staged
 // fp16 pairs: sum over the elements of (1024 + q) * x.
 MOE_DEV float dot_codes(const uint4 c, const f16x2_t *pairs, int c0) {
@@ -235,10 +283,18 @@ __global__ __launch_bounds__(DT) void k_dec_a(DecodeArgs a) {
   if (w >= a.E) return;
   const float4 wr = reinterpret_cast<const float4 *>(a.router_w + (size_t)w * DH)[tid];
   const uint2 xb = reinterpret_cast<const uint2 *>(a.x)[tid];
-  float d = wr.x * bf16lo(xb.x);
-  d = __builtin_fmaf(wr.y, bf16hi(xb.x), d);
-  d = __builtin_fmaf(wr.z, bf16lo(xb.y), d);
-  d = __builtin_fmaf(wr.w, bf16hi(xb.y), d);
+  float xv[4] = {bf16lo(xb.x), bf16hi(xb.x), bf16lo(xb.y), bf16hi(xb.y)};
+  if (a.norm) {
+    __shared__ float red8[DT / 64];
+    const float inv = block_inv_rms(xv[0] * xv[0] + xv[1] * xv[1] + xv[2] * xv[2] + xv[3] * xv[3],
+                                    a.eps, red8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xv[i] = bf16_to_f32(f32_to_bf16(xv[i] * inv));
+  }
+  float d = wr.x * xv[0];
+  d = __builtin_fmaf(wr.y, xv[1], d);
+  d = __builtin_fmaf(wr.z, xv[2], d);
+  d = __builtin_fmaf(wr.w, xv[3], d);
   d = wave_sum_dpp(d);
   if (lane == 0) red[wave] = d;
   __syncthreads();
@@ -261,7 +317,8 @@ __global__ __launch_bounds__(DT) void k_dec_b(DecodeArgs a) {
   const int w = blockIdx.x, tid = threadIdx.x;
   // the logit this thread ranks and its chunk of x leave together
   const float zv = (w < DWG && tid < a.E) ? a.z[tid] : 0.f;
-  stage_f16_pairs<true>(a.x, DH, xs, xseg);
+  __shared__ float red8[DT / 64];
+  stage_x(a, xs, xseg, red8);
   if (w >= DWG) {
     // the shared expert needs no routing: half block (b, f) of workgroup DWG + 2b + f
     const int b = (w - DWG) >> 1, f = (w - DWG) & 1;

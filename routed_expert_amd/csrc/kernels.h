@@ -129,6 +129,10 @@ struct DecodeArgs {
   int32_t *ids_out;           // [k]
   float *w_out;               // [k]
   int H, I, E, k, S;
+  // when set, the layer reads RMSNorm(x) (unit gain, rounded to bf16) instead of x; the
+  // residual is still the caller's (un-normalised) pointer
+  int norm;
+  float eps;
 };
 bool decode_gemv_supported(int H, int I, int E, int k, int S, bool int4);
 hipError_t launch_decode_gemv(const DecodeArgs &a, hipStream_t s);

@@ -478,14 +478,22 @@ moe_status moe_prefill(const moe_layer *layer, const void *x, int64_t T, void *y
 }
 
 // One token after validation; p is a workspace plan for at least one token.
+static bool decode_fast(const moe_layer *layer) {
+  return moe::decode_gemv_supported(layer->hidden, layer->inter, layer->n_experts,
+                                    layer->top_k, layer->n_shared,
+                                    layer->w_format == MOE_W_INT4_G64) &&
+         layer->w13_t && layer->w13_tsb && layer->w2_t && layer->w2_tsb;
+}
+
+// One token after validation; p is a workspace plan for at least one token. norm_eps >= 0
+// (three-kernel path only) makes the layer read RMSNorm(x) instead of x.
 static moe_status decode_impl(const moe_layer *layer, const void *x, void *y,
-                              const void *residual, void *ws, const Plan &p, hipStream_t s) {
+                              const void *residual, void *ws, const Plan &p, hipStream_t s,
+                              float norm_eps = -1.0f) {
   hipError_t e;
   const bool int4 = layer->w_format == MOE_W_INT4_G64;
   // the three-kernel path reads the tiled weights; unpacked layers take the generic path
-  if (moe::decode_gemv_supported(layer->hidden, layer->inter, layer->n_experts, layer->top_k,
-                                 layer->n_shared, int4) &&
-      layer->w13_t && layer->w13_tsb && layer->w2_t && layer->w2_tsb) {
+  if (decode_fast(layer)) {
     moe::DecodeArgs da{};
     da.x = static_cast<const uint16_t *>(x);
     da.router_w = layer->router_w;
@@ -502,6 +510,8 @@ static moe_status decode_impl(const moe_layer *layer, const void *x, void *y,
     da.E = layer->n_experts;
     da.k = layer->top_k;
     da.S = layer->n_shared;
+    da.norm = norm_eps >= 0.f;
+    da.eps = norm_eps;
     if ((e = moe::launch_decode_gemv(da, s)) != hipSuccess) return hip_fail(e, "moe_decode");
     return MOE_OK;
   }
@@ -583,9 +593,14 @@ moe_status moe_stack_forward(const moe_layer *layers, int32_t n_layers, void *h,
     const int64_t n = std::min<int64_t>(chunk_tokens, T - r0);
     void *hc = static_cast<char *>(h) + (size_t)r0 * row_bytes;
     for (int32_t l = 0; l < n_layers; ++l) {
+      const Plan p = make_plan(&layers[l], n);
+      if (T == 1 && decode_fast(&layers[l])) {
+        // the three decode kernels normalise x themselves: no separate RMSNorm launch
+        if ((st = decode_impl(&layers[l], hc, hc, hc, lws, p, s, eps))) return st;
+        continue;
+      }
       hipError_t e = moe::launch_rmsnorm(hc, n, H, eps, bf16, norm, s);
       if (e != hipSuccess) return hip_fail(e, "moe_stack_forward rmsnorm");
-      const Plan p = make_plan(&layers[l], n);
       st = (T == 1) ? decode_impl(&layers[l], norm, hc, hc, lws, p, s)
                     : prefill_impl(&layers[l], norm, n, hc, hc, nullptr, lws, p, s);
       if (st) return st;
