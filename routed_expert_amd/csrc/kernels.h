@@ -32,6 +32,7 @@ struct RouteArgs {
   float *logits;          // [T, E] (decode: [E])
   float *logits2;         // [T, E] second half of the reduction (bf16 path)
   uint16_t *router_planes;  // [3, E, H] bf16 split of the router weights (bf16 path)
+  bool planes_ready;        // router_planes already hold the split (packed layer)
   int32_t *ids;           // [T, k]
   float *w;               // [T, k]
   int32_t *blk;           // [NB, E] per-block counts, then per-block bases
@@ -69,6 +70,7 @@ struct PackArgs {
 size_t tiled_code_bytes(int n_mat, int rows, int K);
 size_t tiled_sb_bytes(int n_mat, int rows, int K);
 hipError_t launch_pack(const PackArgs &a, hipStream_t s);
+hipError_t launch_router_split(const float *W, size_t n, uint16_t *planes, hipStream_t s);
 
 // Grouped int4 GEMMs of the prefill path (fp16 operands, fp32 accumulation).
 struct GroupedArgs {

@@ -76,6 +76,7 @@ moe_status check_layer(const moe_layer *L) {
     return fail(MOE_E_INVALID, "unknown w_format %d", L->w_format);
   }
   if (!aligned16(L->router_w)) return fail(MOE_E_INVALID, "router_w must be 16-byte aligned");
+  if (!aligned16(L->router_planes)) return fail(MOE_E_INVALID, "router_planes misaligned");
   if ((uintptr_t)L->router_b & 3) return fail(MOE_E_INVALID, "router_b misaligned");
   return MOE_OK;
 }
@@ -172,7 +173,7 @@ moe_status check_tiled(const moe_layer *L) {
 }
 
 struct PackPlan {
-  size_t w13_t, w13_tsb, w2_t, w2_tsb, total;
+  size_t w13_t, w13_tsb, w2_t, w2_tsb, planes, total;
 };
 
 PackPlan pack_plan(const moe_layer *L) {
@@ -187,6 +188,8 @@ PackPlan pack_plan(const moe_layer *L) {
   off += align256(moe::tiled_code_bytes(n, H, I));
   p.w2_tsb = off;
   off += align256(moe::tiled_sb_bytes(n, H, I));
+  p.planes = off;
+  off += align256((size_t)3 * L->n_experts * H * 2);
   p.total = off;
   return p;
 }
@@ -236,6 +239,10 @@ moe::RouteArgs route_args(const moe_layer *L, const void *x, int64_t T) {
   a.E = L->n_experts;
   a.k = L->top_k;
   a.S = L->n_shared;
+  if (a.bf16 && L->router_planes) {
+    a.router_planes = const_cast<uint16_t *>(static_cast<const uint16_t *>(L->router_planes));
+    a.planes_ready = true;
+  }
   return a;
 }
 
@@ -243,7 +250,7 @@ moe::RouteArgs route_args(const moe_layer *L, const void *x, int64_t T) {
 void route_targets(moe::RouteArgs &a, const Plan &p, void *ws, const moe_route_out *ro) {
   a.logits = at<float>(ws, p.logits);
   a.logits2 = at<float>(ws, p.logits2);
-  a.router_planes = at<uint16_t>(ws, p.planes);
+  if (!a.planes_ready) a.router_planes = at<uint16_t>(ws, p.planes);
   a.blk = at<int32_t>(ws, p.blk);
   a.offsets = at<int32_t>(ws, p.offsets);
   a.tiles = at<int2>(ws, p.tiles);
@@ -361,11 +368,15 @@ moe_status moe_pack_weights(const moe_layer *layer, void *dst, size_t dst_bytes,
   a.t = at<uint8_t>(dst, pp.w2_t);
   a.tsb = at<uint16_t>(dst, pp.w2_tsb);
   if ((e = moe::launch_pack(a, s)) != hipSuccess) return hip_fail(e, "moe_pack_weights down");
+  if ((e = moe::launch_router_split(layer->router_w, (size_t)layer->n_experts * layer->hidden,
+                                    at<uint16_t>(dst, pp.planes), s)) != hipSuccess)
+    return hip_fail(e, "moe_pack_weights router");
   *packed = *layer;
   packed->w13_t = at<uint8_t>(dst, pp.w13_t);
   packed->w13_tsb = at<uint16_t>(dst, pp.w13_tsb);
   packed->w2_t = at<uint8_t>(dst, pp.w2_t);
   packed->w2_tsb = at<uint16_t>(dst, pp.w2_tsb);
+  packed->router_planes = at<uint16_t>(dst, pp.planes);
   return MOE_OK;
 }
 

@@ -262,34 +262,22 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ z,
 }
 
 // Inclusive block-wide scan over 256 threads (LDS, Hillis-Steele).
-MOE_DEV int block_scan_incl(int v, int *sc) {
-  const int tid = threadIdx.x;
-  sc[tid] = v;
-  __syncthreads();
-  for (int d = 1; d < 256; d <<= 1) {
-    const int o = tid >= d ? sc[tid - d] : 0;
-    __syncthreads();
-    sc[tid] += o;
-    __syncthreads();
+// Inclusive scan over the 256 threads of the workgroup: shuffle scan inside each wave,
+// then the totals of the waves before it (one LDS exchange, two barriers).
+template <typename V>
+MOE_DEV V block_scan_incl(V v, V *wtot) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const V o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
   }
-  const int r = sc[tid];
+  if (lane == 63) wtot[wave] = v;
   __syncthreads();
-  return r;
-}
-
-MOE_DEV uint64_t block_scan_incl64(uint64_t v, uint64_t *sc) {
-  const int tid = threadIdx.x;
-  sc[tid] = v;
-  __syncthreads();
-  for (int d = 1; d < 256; d <<= 1) {
-    const uint64_t o = tid >= d ? sc[tid - d] : 0;
-    __syncthreads();
-    sc[tid] += o;
-    __syncthreads();
-  }
-  const uint64_t r = sc[tid];
-  __syncthreads();
-  return r;
+  V before = 0;
+  for (int w = 0; w < wave; ++w) before += wtot[w];
+  __syncthreads();  // wtot may be reused by the next scan
+  return v + before;
 }
 
 // ---- counts, offsets, per-block bases and the tile map (one workgroup) -------------------
@@ -302,17 +290,17 @@ __global__ __launch_bounds__(256) void k_scan(int32_t *__restrict__ blk_cnt, int
                                               int32_t *__restrict__ offsets_user,
                                               int2 *__restrict__ tiles,
                                               int32_t *__restrict__ n_tiles) {
-  __shared__ int sc[256];
+  __shared__ int sc[4];
   const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
-    // 16 block counts per round: the loads of a round are issued together
-    for (int b0 = 0; b0 < NB; b0 += 16) {
-      int c[16];
+    // 32 block counts per round: the loads of a round are issued together
+    for (int b0 = 0; b0 < NB; b0 += 32) {
+      int c[32];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) c[i] = b0 + i < NB ? blk_cnt[(size_t)(b0 + i) * E + e] : 0;
+      for (int i = 0; i < 32; ++i) c[i] = b0 + i < NB ? blk_cnt[(size_t)(b0 + i) * E + e] : 0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < 32; ++i) {
         if (b0 + i < NB) blk_cnt[(size_t)(b0 + i) * E + e] = run;
         run += c[i];
       }
@@ -327,8 +315,8 @@ __global__ __launch_bounds__(256) void k_scan(int32_t *__restrict__ blk_cnt, int
   // tiles, 9-bit fields at 21 + 9q count partial tiles of 4 - q blocks.
   const int nfull = run >> 7, mb = ((run & 127) + 31) >> 5;
   const uint64_t packed = (uint64_t)nfull | (mb ? (1ull << (21 + 9 * (4 - mb))) : 0ull);
-  __shared__ uint64_t sc64[256];
-  const uint64_t pincl = block_scan_incl64(packed, sc64);
+  __shared__ uint64_t sc64[4];
+  const uint64_t pincl = block_scan_incl(packed, sc64);
   const uint64_t pexcl = pincl - packed;
   __shared__ int totals[1];
   __shared__ uint64_t ptot[1];
@@ -399,14 +387,21 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t *__restrict__ ids
 }
 
 // ---- launchers ------------------------------------------------------------------------------
+hipError_t launch_router_split(const float *W, size_t n, uint16_t *planes, hipStream_t s) {
+  MOE_LAUNCH("k_router_split", k_router_split,
+             dim3((unsigned)std::min<size_t>((n / 4 + 255) / 256, 2048)), dim3(256), 0, s, W, n,
+             planes);
+  return hipSuccess;
+}
+
 hipError_t launch_route_prefill(const RouteArgs &a, hipStream_t s) {
   const int NB = (int)((a.T + kRouteBlock - 1) / kRouteBlock);
   const dim3 g1((unsigned)NB, (unsigned)((a.E + 63) / 64));
   if (a.bf16) {
-    const size_t n = (size_t)a.E * a.H;
-    MOE_LAUNCH("k_router_split", k_router_split,
-               dim3((unsigned)std::min<size_t>((n / 4 + 255) / 256, 2048)), dim3(256), 0, s,
-               a.router_w, n, a.router_planes);
+    if (!a.planes_ready) {
+      const hipError_t e = launch_router_split(a.router_w, (size_t)a.E * a.H, a.router_planes, s);
+      if (e != hipSuccess) return e;
+    }
     MOE_LAUNCH("k_router_mfma", k_router_mfma, dim3(g1.x, g1.y, 2), dim3(256), 0, s,
                static_cast<const uint16_t *>(a.x), a.router_planes, a.router_b, a.logits,
                a.logits2, a.x16, a.blk, (int)a.T, a.H, a.E);

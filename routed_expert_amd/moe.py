@@ -18,7 +18,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
 W_F32, W_INT4_G64 = 0, 1
 ACT_F32, ACT_BF16 = 0, 1
@@ -39,7 +39,8 @@ class MoeLayer(ctypes.Structure):
                 ("w13_b", ctypes.c_void_p), ("w2_q", ctypes.c_void_p),
                 ("w2_s", ctypes.c_void_p), ("w2_b", ctypes.c_void_p),
                 ("w13_t", ctypes.c_void_p), ("w13_tsb", ctypes.c_void_p),
-                ("w2_t", ctypes.c_void_p), ("w2_tsb", ctypes.c_void_p)]
+                ("w2_t", ctypes.c_void_p), ("w2_tsb", ctypes.c_void_p),
+                ("router_planes", ctypes.c_void_p)]
 
 
 class MoeRouteOut(ctypes.Structure):

@@ -49,7 +49,7 @@ def fake_layer(M, **kw):
              n_shared=1, w_format=M.W_INT4_G64, act_dtype=M.ACT_BF16, router_w=0x10000,
              router_b=None, w13_q=0x20000, w13_s=0x30000, w13_b=0x40000, w2_q=0x50000,
              w2_s=0x60000, w2_b=0x70000, w13_t=0x80000, w13_tsb=0x90000, w2_t=0xa0000,
-             w2_tsb=0xb0000)
+             w2_tsb=0xb0000, router_planes=None)
     p.update(kw)
     return M.MoeLayer(*[p[f] for f, _ in M.MoeLayer._fields_])
 
@@ -79,6 +79,7 @@ def ws_bytes(M, layer, T):
     (dict(w13_s=None), -1),
     (dict(w13_q=0x20008), -1),          # codes must be 16-byte aligned
     (dict(router_b=0x10002), -1),
+    (dict(router_planes=0x10008), -1),
     (dict(w2_b=0x70002), -1),           # scales and biases are read as dwords
 ])
 def test_descriptor_validation(M, kw, code):
@@ -137,7 +138,8 @@ def test_pack_size_and_argument_errors(M):
     E1, H, I = 257, 2048, 512
     codes = E1 * 2 * I * H // 2 + E1 * H * I // 2
     sb = E1 * (2 * I // 64) * (H // 256) * 64 * 16 + E1 * (H // 64) * (I // 256) * 64 * 16
-    assert n.value == codes + sb
+    planes = 3 * (E1 - 1) * H * 2   # the router split into three bf16 planes
+    assert n.value == codes + sb + planes
     out = M.MoeLayer()
     dst = ctypes.c_void_p(0x1000000)
     assert L.moe_pack_weights(ctypes.byref(layer), dst, n.value - 1, ctypes.byref(out),

@@ -279,6 +279,11 @@ def test_pack_weights_layout(M, H, I):
         got_sb = buf[sp - base: sp - base + 2 * want_sb.size].view(np.uint16)
         assert np.array_equal(got_q, want_q)
         assert np.array_equal(got_sb, want_sb)
+    # router planes: hi + mid + lo == the fp32 weight exactly, each plane a bf16 value
+    E = layer.n_experts
+    planes = buf[d.router_planes - base: d.router_planes - base + 3 * E * H * 2].view(np.uint16)
+    pf = synth.bf16_bits_to_f32(planes).astype(np.float64).reshape(3, E, H)
+    assert np.array_equal(pf.sum(0), layer.router_w.astype(np.float64))
 
 
 def test_prefill_small_layer_padded_scale_blocks(M):
