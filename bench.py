@@ -202,6 +202,25 @@ def bench_prefill(moe, torch, synth, dev, layer_host, reps=20):
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / reps
+    # the same calls replayed from a HIP graph (no host work between kernels)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        moe.moe_prefill(dl, x, y=y, ws=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.moe_prefill(dl, x, y=y, ws=ws)
+    g.replay()
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(reps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_graph = t0.elapsed_time(t1) / reps
+    del g
     moe.profile_reset()
     moe.profile_enable(True)
     for _ in range(reps):
@@ -209,7 +228,7 @@ def bench_prefill(moe, torch, synth, dev, layer_host, reps=20):
     torch.cuda.synchronize()
     moe.profile_enable(False)
     kern = {}
-    for name in ("k_router_split", "k_router_mfma", "k_topk", "k_scan", "k_scatter", "k_grouped_gateup",
+    for name in ("k_router_mfma", "k_topk", "k_scan", "k_scatter", "k_grouped_gateup",
                  "k_grouped_down", "k_combine"):
         tot, n = moe.profile_query(name)
         kern[name] = {"avg_us": 1e3 * tot / max(n, 1), "launches": n}
@@ -222,7 +241,8 @@ def bench_prefill(moe, torch, synth, dev, layer_host, reps=20):
     gu_us = kern["k_grouped_gateup"]["avg_us"]
     del dl, ws, x, y
     torch.cuda.empty_cache()
-    return {"tokens_per_s": tok_s, "ms_per_call": ms,
+    return {"tokens_per_s": tok_s, "ms_per_call": ms, "ms_per_call_graph": ms_graph,
+            "tokens_per_s_graph": T / (ms_graph * 1e-3),
             "tflops": flops / (ms * 1e-3) / 1e12,
             "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
             "max_group": int(buf["counts"].max().item()),
