@@ -23,7 +23,7 @@
 //      half f) -> rows 32b + 16f .. +16. Workgroup 0 stores the ids and weights for C.
 //      32 more workgroups compute the shared expert's gate/up the same way; they need no
 //      routing, so they skip the top-k and overlap it.
-//   C  256 workgroups of 8 output rows each: all k+1 experts' W2 rows times h (staged
+//   C  512 workgroups of 4 output rows each: all k+1 experts' W2 rows times h (staged
 //      in LDS), scaled by the routing weights, plus the residual.
 //
 // Dot products: a nibble pair OR-ed into 0x6400 is the fp16 pair (1024 + q_lo, 1024 + q_hi)
@@ -44,7 +44,7 @@ constexpr int kNS13 = DH / 64;      // K steps of W13
 constexpr int kNB2 = DH / 64;       // 64-row blocks of W2
 constexpr int kNS2 = DI / 64;       // K steps of W2
 constexpr int kSharedWG = 2 * kNB13; // extra workgroups of B: shared-expert half blocks
-constexpr int kDownWG = kNB2 * 8;   // C: 8 output rows per workgroup
+constexpr int kDownWG = kNB2 * 16;  // C: 4 output rows per workgroup
 }  // namespace
 
 // n fp32 / bf16 activations -> fp16 pairs (v[8c + p], v[8c + p + 4]) for chunk c, p < 4, in
@@ -218,22 +218,38 @@ MOE_DEV void block_topk(float zv, int E, int k, uint64_t *K, uint64_t *cand,
     if (seg == 0 && mine != 0ull && r < k) K[r] = mine;  // K reused for the winners
   }
   __syncthreads();
-  if (tid < 64) {
-    const uint64_t b = tid < k ? K[tid] : 0ull;
-    const int id = (int)(0xFFFFFFFFu - (uint32_t)b);
-    const float v = key_float((uint32_t)(b >> 32));
-    const float top = key_float((uint32_t)(K[0] >> 32));
-    const float ex = tid < k ? (top == -INFINITY ? 1.0f : expf(v - top)) : 0.f;
-    float den = ex;
-    den += __shfl_xor(den, 1, 64);
-    den += __shfl_xor(den, 2, 64);
-    den += __shfl_xor(den, 4, 64);
-    int rk = 0;
-    for (int q = 0; q < k; ++q) rk += __shfl(id, q, 64) < id ? 1 : 0;
-    if (tid < k) {
-      s_ids[rk] = id;
-      s_w[rk] = ex / den;
+  if (tid < k) {
+    // the winners K[0..k-1] (K[0] the largest): every lane reads all of them, ranks its id
+    // among theirs and sums the softmax denominator in the same order (no shuffles)
+    uint64_t win[kMaxTopK];
+#pragma unroll
+    for (int q = 0; q < kMaxTopK; q += 2) {
+      const ulonglong2 p = *reinterpret_cast<const ulonglong2 *>(K + q);
+      win[q] = p.x;
+      win[q + 1] = p.y;
     }
+    const float top = key_float((uint32_t)(win[0] >> 32));
+    uint64_t mw = win[0];
+#pragma unroll
+    for (int q = 1; q < kMaxTopK; ++q)
+      if (q == tid) mw = win[q];
+    const int id = (int)(0xFFFFFFFFu - (uint32_t)mw);
+    float den = 0.f, mine = 0.f;
+    int rk = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxTopK; ++q) {
+      if (q < k) {
+        const float vq = key_float((uint32_t)(win[q] >> 32));
+        // exp(v - top) from the hardware exp2; top == -inf only when every logit is -inf
+        const float ex = top == -INFINITY ? 1.0f
+                                          : __builtin_amdgcn_exp2f((vq - top) * 1.4426950408889634f);
+        den += ex;
+        if (q == tid) mine = ex;
+        rk += (int)(0xFFFFFFFFu - (uint32_t)win[q]) < id ? 1 : 0;
+      }
+    }
+    s_ids[rk] = id;
+    s_w[rk] = mine / den;
   }
   __syncthreads();
 }
@@ -340,7 +356,7 @@ __global__ __launch_bounds__(DT) void k_dec_c(DecodeArgs a) {
   __shared__ float hseg[kSlots * DI / 32];
   __shared__ int s_ids[kSlots];
   __shared__ float s_w[kSlots];
-  __shared__ float red[DT / 64 * 8];
+  __shared__ float red[DT / 64 * 4];
   const int w = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int k = a.k, nslot = a.k + a.S;
   // three independent loads leave together: the routing (ids, weights), h of all k+1
@@ -368,22 +384,22 @@ __global__ __launch_bounds__(DT) void k_dec_c(DecodeArgs a) {
     s_w[tid] = tid < k ? my_w : 1.0f;
   }
   __syncthreads();
-  // output rows 64b + 8t .. +8; units (slot j, K step s) of 8 rows x 32 code bytes, four
-  // per load instruction: lane group l / 16 takes unit 4p + l / 16; lane: row (l % 16) / 2,
+  // output rows 64b + 4t .. +4; units (slot j, K step s) of 4 rows x 32 code bytes, eight
+  // per load instruction: lane group l / 8 takes unit 8p + l / 8; lane: row (l % 8) / 2,
   // K half l % 2
-  const int b = w >> 3, t = w & 7;
-  const int r8 = (lane & 15) >> 1, hh = lane & 1, ug = lane >> 4;
-  constexpr int kMaxQuads = (kSlots * kNS2 / 4 + DT / 64 - 1) / (DT / 64);
-  uint4 c[kMaxQuads], sb[kMaxQuads];
+  const int b = w >> 4, t = w & 15;
+  const int r4 = (lane & 7) >> 1, hh = lane & 1, ug = lane >> 3;
+  constexpr int kMaxOcts = (kSlots * kNS2 / 8 + DT / 64 - 1) / (DT / 64);
+  uint4 c[kMaxOcts], sb[kMaxOcts];
 #pragma unroll
-  for (int i = 0; i < kMaxQuads; ++i) {
-    const int p = wave + (DT / 64) * i, u = 4 * p + ug, jj = u >> 3, st = u & 7;
+  for (int i = 0; i < kMaxOcts; ++i) {
+    const int p = wave + (DT / 64) * i, u = 8 * p + ug, jj = u >> 3, st = u & 7;
     if (jj < nslot) {
       const size_t blk = (size_t)s_ids[jj] * kNB2 + b;
       c[i] = *reinterpret_cast<const uint4 *>(a.wt.w2_t + (blk * kNS2 + st) * 2048 +
-                                              32 * (8 * t + r8) + 16 * hh);
+                                              32 * (4 * t + r4) + 16 * hh);
       sb[i] = *reinterpret_cast<const uint4 *>(a.wt.w2_tsb + (blk * (kNS2 / 4) + (st >> 2)) * 512 +
-                                               8 * (8 * t + r8));
+                                               8 * (4 * t + r4));
     }
   }
   // h -> fp16 pairs (v[8c + p], v[8c + p + 4]) per chunk c, and the 32-element segment sums
@@ -408,24 +424,26 @@ __global__ __launch_bounds__(DT) void k_dec_c(DecodeArgs a) {
   __syncthreads();
   float acc = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxQuads; ++i) {
-    const int p = wave + (DT / 64) * i, u = 4 * p + ug, jj = u >> 3, st = u & 7;
+  for (int i = 0; i < kMaxOcts; ++i) {
+    const int p = wave + (DT / 64) * i, u = 8 * p + ug, jj = u >> 3, st = u & 7;
     if (jj < nslot) {
       const float raw = dot_codes(c[i], hs + jj * (DI / 2), 8 * st + 4 * hh);
       acc = __builtin_fmaf(s_w[jj], group_dot(raw, word_of(sb[i], st & 3),
                                                hseg[jj * (DI / 32) + 2 * st + hh]), acc);
     }
   }
+  // lanes of one row: both K halves (xor 1) and the eight unit groups (xor 8, 16, 32)
   acc += __shfl_xor(acc, 1, 64);
+  acc += __shfl_xor(acc, 8, 64);
   acc += __shfl_xor(acc, 16, 64);
   acc += __shfl_xor(acc, 32, 64);
-  if (lane < 16 && hh == 0) red[wave * 8 + r8] = acc;
+  if (lane < 8 && hh == 0) red[wave * 4 + r4] = acc;
   __syncthreads();
-  if (tid < 8) {
+  if (tid < 4) {
     float y = 0.f;
 #pragma unroll
-    for (int v = 0; v < DT / 64; ++v) y += red[v * 8 + tid];
-    const int row = 64 * b + 8 * t + tid;
+    for (int v = 0; v < DT / 64; ++v) y += red[v * 4 + tid];
+    const int row = 64 * b + 4 * t + tid;
     if (a.residual) y += bf16_to_f32(a.residual[row]);
     a.y[row] = f32_to_bf16(y);
   }
