@@ -320,7 +320,7 @@ def cpu_baseline(synth):
     oracle.build(force=False)
     threads = len(os.sched_getaffinity(0))
     layer = synth.decode_layer(0)
-    n = 256
+    n = 4096  # about 10 s of CPU work on 16 cores
     xs = np.concatenate([synth.decode_token(t) for t in range(n)])
     olayer = oracle.OracleLayer(layer)
     t0 = time.perf_counter()
