@@ -39,7 +39,8 @@ MOE_DEV void split3(float w, uint16_t &hi, uint16_t &mid, uint16_t &lo) {
   lo = __builtin_bit_cast(uint16_t, (__bf16)r2);
 }
 
-// Router weights split once per call into three bf16 planes [3][E][H] (workspace).
+// Router weights split into three bf16 planes [3][E][H]: once by moe_pack_weights for a
+// packed layer, else on every call into the workspace.
 __global__ __launch_bounds__(256) void k_router_split(const float *__restrict__ W, size_t n,
                                                       uint16_t *__restrict__ planes) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n / 4;

@@ -149,8 +149,7 @@ def test_prefill_int4_full_compare(M, big, T):
     assert rel_err(y_np(y)[sure], ref[sure]) <= BF16_TOL
 
 
-def _prefill_4096(M, layer, dl, seed, n_sample=96):
-    T = 4096
+def _prefill_big(M, layer, dl, seed, T=4096, n_sample=96):
     xb = synth.prefill_x(T, seed=seed)
     buf = M.route_buffers(dl, T, DEV)
     y = M.moe_prefill(dl, bf16_dev(M, xb), route_out=buf)
@@ -160,7 +159,7 @@ def _prefill_4096(M, layer, dl, seed, n_sample=96):
     check_grouping(layer, g)
     _, _, margin = oracle.route(layer, xb)
     rng = np.random.default_rng(seed + 1)
-    sample = np.unique(np.concatenate([[0, 1, 127, 128, T - 1],
+    sample = np.unique(np.concatenate([[0, 1, 127, 128, T - 33, T - 1],
                                        rng.choice(T, n_sample, replace=False)]))
     sample = sample[margin[sample] >= delta_for(2048)]
     ref = oracle.moe(layer, xb[sample])
@@ -171,7 +170,7 @@ def _prefill_4096(M, layer, dl, seed, n_sample=96):
 def test_prefill_uniform_4096(M, big):
     layer, dl = big
     announce("moe_prefill int4 T=4096 near-uniform routing, x seed 2")
-    g, unsure, err, _ = _prefill_4096(M, layer, dl, 2)
+    g, unsure, err, _ = _prefill_big(M, layer, dl, 2)
     c = g["counts"]
     assert c.sum() == 8 * 4096 and c.min() > 0
     assert unsure <= 20
@@ -181,10 +180,23 @@ def test_prefill_uniform_4096(M, big):
 def test_prefill_skewed_4096(M, skewed):
     layer, dl = skewed
     announce("moe_prefill int4 T=4096 Zipf(1.1)-skewed routing, x seed 2")
-    g, unsure, err, _ = _prefill_4096(M, layer, dl, 2)
+    g, unsure, err, _ = _prefill_big(M, layer, dl, 2)
     c = g["counts"]
     assert c.max() > 500 and (c <= 5).sum() >= 32   # very uneven groups, some empty-ish
     assert unsure <= 20
+    assert err <= BF16_TOL, err
+
+
+def test_prefill_ragged_12000(M, big):
+    # one call well past the benchmark size whose token count is not a multiple of 64:
+    # 188 count blocks, the last one half full, and a tile map of about 860 tiles
+    layer, dl = big
+    T = 12000
+    announce(f"moe_prefill int4 T={T} near-uniform routing, x seed 3")
+    g, unsure, err, _ = _prefill_big(M, layer, dl, 3, T=T, n_sample=128)
+    c = g["counts"]
+    assert c.sum() == 8 * T and c.min() > 0
+    assert unsure <= 60
     assert err <= BF16_TOL, err
 
 

@@ -97,7 +97,11 @@ def test_stack_full_shape_layers(M):
     M.moe_stack_forward(dls[1:], h2, chunk_tokens=40, eps=EPS)
     d = h0[:1].clone()                           # the decode path of the same stack
     M.moe_stack_forward(dls[:1], d, chunk_tokens=40, eps=EPS)
+    # the stack's T=1 step normalises inside the decode kernels; the separate RMSNorm
+    # kernel followed by moe_decode must give the same bits
+    sep = M.moe_decode(dls[0], M.moe_rmsnorm(h0[:1], EPS), residual=h0[:1])
     torch.cuda.synchronize()
+    assert torch.equal(sep, d)
     rows = np.random.default_rng(5).choice(96, 24, replace=False)
     rows[0] = 39                                 # the last row of the first chunk
     check_layer_step(layers[0], bits(h0), bits(h1), rows)
