@@ -120,10 +120,46 @@ MOE_DEV uint4 bf16x8_to_f16x8_chunk(uint4 u) {
   return h;
 }
 
+// v(l) + v(l ^ M) on every lane l, without the LDS crossbar (__shfl_xor is a ds_bpermute):
+//   M = 1, 2: DPP quad permutations (1,0,3,2) and (2,3,0,1);
+//   M = 4: DPP rotation by 4 inside each row of 16 lanes; it stands for lane l ^ 4 only
+//          when v is already equal on lanes l and l ^ 8, i.e. right after an xor-8 step;
+//   M = 8: DPP rotation by 8 inside each row of 16 lanes (lane l reads lane l ^ 8);
+//   M = 16, 32: v_permlane16_swap / v_permlane32_swap with v in both operands return the
+//          even and the odd rows (the low and the high 32 lanes), each replicated over the
+//          pair, so their sum is v(l) + v(l ^ M).
+// Addition is commutative, so every lane gets the same bits as v(l) + v(l ^ M).
+template <int M>
+MOE_DEV uint32_t xor_peer_dpp(uint32_t v) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8, "DPP exchange distance");
+  constexpr int ctl = M == 1 ? 0xB1 : M == 2 ? 0x4E : M == 4 ? 0x124 : 0x128;
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ctl, 0xF, 0xF, false);
+}
+
+template <int M, typename T>
+MOE_DEV T xor_sum(T v) {
+  static_assert(sizeof(T) == 4, "32-bit values");
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  if constexpr (M == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __builtin_bit_cast(T, (uint32_t)p[0]) + __builtin_bit_cast(T, (uint32_t)p[1]);
+  } else if constexpr (M == 32) {
+    const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(T, (uint32_t)p[0]) + __builtin_bit_cast(T, (uint32_t)p[1]);
+  } else {
+    return v + __builtin_bit_cast(T, xor_peer_dpp<M>(u));
+  }
+}
+
+// Sum over the wave, reduction order 32, 16, 8, 4, 2, 1 (xor 4 as a rotation is exact here:
+// after the xor-8 step v is equal on lanes l and l ^ 8).
 MOE_DEV float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
+  v = xor_sum<32>(v);
+  v = xor_sum<16>(v);
+  v = xor_sum<8>(v);
+  v = xor_sum<4>(v);
+  v = xor_sum<2>(v);
+  return xor_sum<1>(v);
 }
 
 // Sum over aligned groups of `width` lanes (width a power of two <= 64).

@@ -20,11 +20,13 @@
 //   A  256 workgroups: workgroup w computes router logit z[w].
 //   B  256 workgroups run the top-k on z (same data, same code, same answer), then
 //      compute 16 gate + 16 up rows of one selected expert: workgroup (slot j, block b,
-//      half f) -> rows 32b + 16f .. +16. Workgroup 0 stores the ids and weights for C.
-//      32 more workgroups compute the shared expert's gate/up the same way; they need no
-//      routing, so they skip the top-k and overlap it.
+//      half f) -> rows 32b + 16f .. +16, slot j being the j-th largest logit. Workgroup 0
+//      stores the selected ids and logits for C. 32 more workgroups compute the shared
+//      expert's gate/up the same way; they need no routing, so they skip the top-k and
+//      overlap it.
 //   C  512 workgroups of 4 output rows each: all k+1 experts' W2 rows times h (staged
-//      in LDS), scaled by the routing weights, plus the residual.
+//      in LDS), scaled by the routing weights (the softmax over the selected logits, formed
+//      while the W2 rows are in flight), plus the residual.
 //
 // Dot products: a nibble pair OR-ed into 0x6400 is the fp16 pair (1024 + q_lo, 1024 + q_hi)
 // of elements (8m + p, 8m + p + 4) of a 32-bit code word m; the activations sit in LDS as
@@ -82,8 +84,8 @@ MOE_DEV void stage_f16_pairs(const void *src, int n, f16x2_t *pairs, float *seg)
     }
     if (live) *reinterpret_cast<uint4 *>(pairs + 4 * ch) = __builtin_bit_cast(uint4, pr);
     // 4 chunks per segment: lanes 4s .. 4s+3 (DT is a multiple of 4)
-    sum += __shfl_xor(sum, 1, 64);
-    sum += __shfl_xor(sum, 2, 64);
+    sum = xor_sum<1>(sum);
+    sum = xor_sum<2>(sum);
     if ((ch & 3) == 0 && live) seg[ch >> 2] = sum;
   }
 }
@@ -131,8 +133,8 @@ MOE_DEV void stage_x(const DecodeArgs &a, f16x2_t *pairs, float *seg, float *red
     sum += (float)pr[p][0] + (float)pr[p][1];
   }
   if (live) *reinterpret_cast<uint4 *>(pairs + 4 * tid) = __builtin_bit_cast(uint4, pr);
-  sum += __shfl_xor(sum, 1, 64);
-  sum += __shfl_xor(sum, 2, 64);
+  sum = xor_sum<1>(sum);
+  sum = xor_sum<2>(sum);
   if ((tid & 3) == 0 && live) seg[tid >> 2] = sum;
 }
 
@@ -170,27 +172,23 @@ MOE_DEV uint32_t word_of(const uint4 v, int i) {
 // chain of dependent instructions is what costs time for a single wave). Keys are 64-bit:
 // float key high, ~id low, so one unsigned compare orders by (logit desc, id asc).
 //   1. wave v ranks elements [32v, 32v+32) among themselves (two lanes per element, 16
-//      comparisons each); its k best go to cand[8v ..].
-//   2. the 64 candidates are ranked among each other (lane: candidate 8v + l%8 against
-//      comparands 8(l/8) .. 8(l/8)+7, partial ranks summed over the 8 lane groups).
-//   3. lanes 0..k-1 of wave 0 turn the k winners into ids in ascending order and softmax
-//      weights.
-// Must be called by all DT threads, thread t < E passing logit t (loaded by the caller, so
-// that the load can leave early); results land in s_ids / s_w.
-MOE_DEV void block_topk(float zv, int E, int k, uint64_t *K, uint64_t *cand,
-                        int *s_ids, float *s_w) {
+//      comparisons each); its k best go to cand[8v ..]. The wave loaded these logits
+//      itself, so it needs no workgroup barrier, only the in-order LDS of one wave.
+//   2. after one barrier the 64 candidates are ranked among each other (lane: candidate
+//      8v + l%8 against comparands 8(l/8) .. 8(l/8)+7, partial ranks summed over the 8
+//      lane groups); the winners land in K[0 .. k-1] in rank order, K[0] the largest.
+// Must be called by all DT threads; thread t passes the logit of element 32 (t / 64) +
+// t % 32 (loaded by the caller, so that the load can leave early). Needs E >= k.
+MOE_DEV void block_topk(float zv, int E, int k, uint64_t *K, uint64_t *cand) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  if (tid < 256) {
-    const float f = tid < E ? zv : -INFINITY;
-    const float g = f != f ? -INFINITY : f;
-    K[tid] = tid < E ? ((uint64_t)float_key(g) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)tid)
-                     : 0ull;
-  }
-  if (tid < 64) cand[tid] = 0ull;
-  __syncthreads();
+  const int e = 32 * wave + (lane & 31), half = lane >> 5;
   {
-    const int e = 32 * wave + (lane & 31), half = lane >> 5;
-    const uint64_t mine = K[e];
+    const float g = (e >= E || zv != zv) ? -INFINITY : zv;
+    const uint64_t mine =
+        e < E ? ((uint64_t)float_key(g) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e) : 0ull;
+    if (half == 0) K[e] = mine;
+    if (lane < 8) cand[8 * wave + lane] = 0ull;
+    wave_lds_sync();
     const uint64_t *base = K + 32 * wave + 16 * half;
     int r = 0;
 #pragma unroll
@@ -198,7 +196,7 @@ MOE_DEV void block_topk(float zv, int E, int k, uint64_t *K, uint64_t *cand,
       const ulonglong2 p = *reinterpret_cast<const ulonglong2 *>(base + q);
       r += (p.x > mine) + (p.y > mine);
     }
-    r += __shfl_xor(r, 32, 64);
+    r = xor_sum<32>(r);
     if (half == 0 && r < k) cand[8 * wave + r] = mine;
   }
   __syncthreads();
@@ -212,47 +210,16 @@ MOE_DEV void block_topk(float zv, int E, int k, uint64_t *K, uint64_t *cand,
       const ulonglong2 p = *reinterpret_cast<const ulonglong2 *>(base + q);
       r += (p.x > mine) + (p.y > mine);
     }
-    r += __shfl_xor(r, 8, 64);
-    r += __shfl_xor(r, 16, 64);
-    r += __shfl_xor(r, 32, 64);
+    r = xor_sum<8>(r);
+    r = xor_sum<16>(r);
+    r = xor_sum<32>(r);
     if (seg == 0 && mine != 0ull && r < k) K[r] = mine;  // K reused for the winners
   }
   __syncthreads();
-  if (tid < k) {
-    // the winners K[0..k-1] (K[0] the largest): every lane reads all of them, ranks its id
-    // among theirs and sums the softmax denominator in the same order (no shuffles)
-    uint64_t win[kMaxTopK];
-#pragma unroll
-    for (int q = 0; q < kMaxTopK; q += 2) {
-      const ulonglong2 p = *reinterpret_cast<const ulonglong2 *>(K + q);
-      win[q] = p.x;
-      win[q + 1] = p.y;
-    }
-    const float top = key_float((uint32_t)(win[0] >> 32));
-    uint64_t mw = win[0];
-#pragma unroll
-    for (int q = 1; q < kMaxTopK; ++q)
-      if (q == tid) mw = win[q];
-    const int id = (int)(0xFFFFFFFFu - (uint32_t)mw);
-    float den = 0.f, mine = 0.f;
-    int rk = 0;
-#pragma unroll
-    for (int q = 0; q < kMaxTopK; ++q) {
-      if (q < k) {
-        const float vq = key_float((uint32_t)(win[q] >> 32));
-        // exp(v - top) from the hardware exp2; top == -inf only when every logit is -inf
-        const float ex = top == -INFINITY ? 1.0f
-                                          : __builtin_amdgcn_exp2f((vq - top) * 1.4426950408889634f);
-        den += ex;
-        if (q == tid) mine = ex;
-        rk += (int)(0xFFFFFFFFu - (uint32_t)win[q]) < id ? 1 : 0;
-      }
-    }
-    s_ids[rk] = id;
-    s_w[rk] = mine / den;
-  }
-  __syncthreads();
 }
+
+// Expert id of a top-k key.
+MOE_DEV int key_id(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
 
 // 16 gate + 16 up rows (rows 32b + 16f .. +16 of expert e's tiled block b) against the
 // staged x: wave v takes K steps 4v .. 4v+3, one 1 KB load per step (lanes 0..31 the gate
@@ -278,7 +245,7 @@ MOE_DEV void gateup_half_block(const DecodeArgs &a, int e, int b, int f, const f
     const int st = 4 * wave + i;
     acc += group_dot(dot_codes(c[i], xs, 8 * st + 4 * hh), word_of(sb, i), xseg[2 * st + hh]);
   }
-  acc += __shfl_xor(acc, 1, 64);
+  acc = xor_sum<1>(acc);
   if (hh == 0) red[wave * 32 + (up ? 16 : 0) + r16] = acc;
   __syncthreads();
   if (tid < 16) {
@@ -298,6 +265,10 @@ __global__ __launch_bounds__(DT) void k_dec_a(DecodeArgs a) {
   // router logit w: 512 threads x 4 fp32 weights
   if (w >= a.E) return;
   const float4 wr = reinterpret_cast<const float4 *>(a.router_w + (size_t)w * DH)[tid];
+  // the bias leaves with the first loads (a load in a branch here would be waited for
+  // only at the end, one more memory latency); without a bias the router row is read and
+  // ignored
+  const float braw = (a.router_b ? a.router_b : a.router_w)[w];
   const uint2 xb = reinterpret_cast<const uint2 *>(a.x)[tid];
   float xv[4] = {bf16lo(xb.x), bf16hi(xb.x), bf16lo(xb.y), bf16hi(xb.y)};
   if (a.norm) {
@@ -318,13 +289,11 @@ __global__ __launch_bounds__(DT) void k_dec_a(DecodeArgs a) {
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < DT / 64; ++i) s += red[i];
-    a.z[w] = s + (a.router_b ? a.router_b[w] : 0.f);
+    a.z[w] = s + (a.router_b ? braw : 0.f);
   }
 }
 
 __global__ __launch_bounds__(DT) void k_dec_b(DecodeArgs a) {
-  __shared__ int s_ids[kMaxTopK];
-  __shared__ float s_w[kMaxTopK];
   __shared__ __attribute__((aligned(16))) uint64_t s_key[256];
   __shared__ __attribute__((aligned(16))) uint64_t s_cand[64];
   __shared__ __attribute__((aligned(16))) f16x2_t xs[DH / 2];
@@ -332,7 +301,8 @@ __global__ __launch_bounds__(DT) void k_dec_b(DecodeArgs a) {
   __shared__ float red[DT / 64 * 32];
   const int w = blockIdx.x, tid = threadIdx.x;
   // the logit this thread ranks and its chunk of x leave together
-  const float zv = (w < DWG && tid < a.E) ? a.z[tid] : 0.f;
+  const int ze = 32 * (tid >> 6) + (tid & 31);
+  const float zv = (w < DWG && ze < a.E) ? a.z[ze] : 0.f;
   __shared__ float red8[DT / 64];
   stage_x(a, xs, xseg, red8);
   if (w >= DWG) {
@@ -341,66 +311,95 @@ __global__ __launch_bounds__(DT) void k_dec_b(DecodeArgs a) {
     gateup_half_block(a, a.E, b, f, xs, xseg, red, a.h + (size_t)a.k * DI + 32 * b + 16 * f);
     return;
   }
-  block_topk(zv, a.E, a.k, s_key, s_cand, s_ids, s_w);
+  block_topk(zv, a.E, a.k, s_key, s_cand);
   if (w == 0 && tid < a.k) {
-    a.ids_out[tid] = s_ids[tid];
-    a.w_out[tid] = s_w[tid];
+    // for C: the winners in rank order, as ids and logits (C forms the softmax weights)
+    const uint64_t kw = s_key[tid];
+    a.sel_ids[tid] = key_id(kw);
+    a.sel_z[tid] = key_float((uint32_t)(kw >> 32));
   }
   const int j = w >> 5, b = (w >> 1) & 15, f = w & 1;
   if (j >= a.k) return;
-  gateup_half_block(a, s_ids[j], b, f, xs, xseg, red, a.h + (size_t)j * DI + 32 * b + 16 * f);
+  gateup_half_block(a, key_id(s_key[j]), b, f, xs, xseg, red,
+                    a.h + (size_t)j * DI + 32 * b + 16 * f);
 }
 
 __global__ __launch_bounds__(DT) void k_dec_c(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) f16x2_t hs[kSlots * DI / 2];
   __shared__ float hseg[kSlots * DI / 32];
   __shared__ int s_ids[kSlots];
-  __shared__ float s_w[kSlots];
+  __shared__ float s_z[kSlots], s_w[kSlots];
   __shared__ float red[DT / 64 * 4];
   const int w = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int k = a.k, nslot = a.k + a.S;
-  // three independent loads leave together: the routing (ids, weights), h of all k+1
-  // experts (two 8-element chunks per thread), then -- once the ids are known -- the W2
-  // rows; h is converted into LDS while the W2 rows are in flight
-  int my_id = 0;
-  float my_w = 1.0f;
-  if (tid < k) {
-    my_id = a.ids_out[tid];
-    my_w = a.w_out[tid];
-  }
+  // three independent loads leave together: the routing (ids and logits of the winners),
+  // h of all k+1 experts (two 8-element chunks per thread), then -- once the ids are known
+  // -- the W2 rows; the routing weights are formed and h is converted into LDS while the W2
+  // rows are in flight
+  // (the loads are unconditional, with indices clamped into range, so that no branch makes
+  // the compiler wait for one before issuing the next)
+  const int tq = tid < k ? tid : 0;
+  const int my_id = a.sel_ids[tq];
+  const float my_z = a.sel_z[tq];
+  // output rows 64b + 4t .. +4; the residual of row 64b + 4t + tid % 4 (used by threads
+  // 0..3; y stands in when there is no residual, read before it is written)
+  const int b = w >> 4, t = w & 15;
+  const int orow = 64 * b + 4 * t + (tid & 3);
+  const uint16_t resid = (a.residual ? a.residual : a.y)[orow];
   const int nch = nslot * DI / 8;
   static_assert(kSlots * DI / 8 <= 2 * DT, "h of all slots must fit two chunks per thread");
   float4 hv[2][2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    const int ch = tid + q * DT;
-    if (ch < nch) {
-      hv[q][0] = reinterpret_cast<const float4 *>(a.h)[2 * ch];
-      hv[q][1] = reinterpret_cast<const float4 *>(a.h)[2 * ch + 1];
-    }
+    const int ch = min(tid + q * DT, nch - 1);
+    hv[q][0] = reinterpret_cast<const float4 *>(a.h)[2 * ch];
+    hv[q][1] = reinterpret_cast<const float4 *>(a.h)[2 * ch + 1];
   }
   if (tid < kSlots) {
     s_ids[tid] = tid < k ? min(max(my_id, 0), a.E - 1) : a.E;
-    s_w[tid] = tid < k ? my_w : 1.0f;
+    s_z[tid] = my_z;
   }
   __syncthreads();
   // output rows 64b + 4t .. +4; units (slot j, K step s) of 4 rows x 32 code bytes, eight
   // per load instruction: lane group l / 8 takes unit 8p + l / 8; lane: row (l % 8) / 2,
   // K half l % 2
-  const int b = w >> 4, t = w & 15;
   const int r4 = (lane & 7) >> 1, hh = lane & 1, ug = lane >> 3;
   constexpr int kMaxOcts = (kSlots * kNS2 / 8 + DT / 64 - 1) / (DT / 64);
   uint4 c[kMaxOcts], sb[kMaxOcts];
 #pragma unroll
   for (int i = 0; i < kMaxOcts; ++i) {
-    const int p = wave + (DT / 64) * i, u = 8 * p + ug, jj = u >> 3, st = u & 7;
-    if (jj < nslot) {
-      const size_t blk = (size_t)s_ids[jj] * kNB2 + b;
-      c[i] = *reinterpret_cast<const uint4 *>(a.wt.w2_t + (blk * kNS2 + st) * 2048 +
-                                              32 * (4 * t + r4) + 16 * hh);
-      sb[i] = *reinterpret_cast<const uint4 *>(a.wt.w2_tsb + (blk * (kNS2 / 4) + (st >> 2)) * 512 +
-                                               8 * (4 * t + r4));
+    // units past the last slot re-read the last slot's rows and go unused: with no branch
+    // around the loads, the compiler's wait counts for the later h loads stay exact and
+    // these loads stay in flight across the next barrier
+    const int p = wave + (DT / 64) * i, u = 8 * p + ug, jj = min(u >> 3, nslot - 1),
+              st = u & 7;
+    const size_t blk = (size_t)s_ids[jj] * kNB2 + b;
+    c[i] = *reinterpret_cast<const uint4 *>(a.wt.w2_t + (blk * kNS2 + st) * 2048 +
+                                            32 * (4 * t + r4) + 16 * hh);
+    sb[i] = *reinterpret_cast<const uint4 *>(a.wt.w2_tsb + (blk * (kNS2 / 4) + (st >> 2)) * 512 +
+                                             8 * (4 * t + r4));
+  }
+  // routing weights: softmax over the selected logits, s_z[0] the largest; the shared
+  // expert (slot k) has weight 1
+  if (tid < kSlots) {
+    float wj = 1.0f;
+    if (tid < k) {
+      const float top = s_z[0];
+      float den = 0.f, mine = 0.f;
+#pragma unroll
+      for (int q = 0; q < kMaxTopK; ++q) {
+        if (q < k) {
+          // exp(z - top) from the hardware exp2; top == -inf only when every logit is -inf
+          const float ex = top == -INFINITY
+                               ? 1.0f
+                               : __builtin_amdgcn_exp2f((s_z[q] - top) * 1.4426950408889634f);
+          den += ex;
+          if (q == tid) mine = ex;
+        }
+      }
+      wj = mine / den;
     }
+    s_w[tid] = wj;
   }
   // h -> fp16 pairs (v[8c + p], v[8c + p + 4]) per chunk c, and the 32-element segment sums
 #pragma unroll
@@ -417,8 +416,8 @@ __global__ __launch_bounds__(DT) void k_dec_c(DecodeArgs a) {
       sum += (float)pr[pp][0] + (float)pr[pp][1];
     }
     if (live) *reinterpret_cast<uint4 *>(hs + 4 * ch) = __builtin_bit_cast(uint4, pr);
-    sum += __shfl_xor(sum, 1, 64);
-    sum += __shfl_xor(sum, 2, 64);
+    sum = xor_sum<1>(sum);
+    sum = xor_sum<2>(sum);
     if ((ch & 3) == 0 && live) hseg[ch >> 2] = sum;
   }
   __syncthreads();
@@ -433,19 +432,18 @@ __global__ __launch_bounds__(DT) void k_dec_c(DecodeArgs a) {
     }
   }
   // lanes of one row: both K halves (xor 1) and the eight unit groups (xor 8, 16, 32)
-  acc += __shfl_xor(acc, 1, 64);
-  acc += __shfl_xor(acc, 8, 64);
-  acc += __shfl_xor(acc, 16, 64);
-  acc += __shfl_xor(acc, 32, 64);
+  acc = xor_sum<1>(acc);
+  acc = xor_sum<8>(acc);
+  acc = xor_sum<16>(acc);
+  acc = xor_sum<32>(acc);
   if (lane < 8 && hh == 0) red[wave * 4 + r4] = acc;
   __syncthreads();
   if (tid < 4) {
     float y = 0.f;
 #pragma unroll
     for (int v = 0; v < DT / 64; ++v) y += red[v * 4 + tid];
-    const int row = 64 * b + 4 * t + tid;
-    if (a.residual) y += bf16_to_f32(a.residual[row]);
-    a.y[row] = f32_to_bf16(y);
+    if (a.residual) y += bf16_to_f32(resid);
+    a.y[orow] = f32_to_bf16(y);
   }
 }
 

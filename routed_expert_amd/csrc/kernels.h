@@ -128,8 +128,8 @@ struct DecodeArgs {
   uint16_t *y;                // [H]
   float *z;                   // [E] logits
   float *h;                   // [k+S, I] fp32
-  int32_t *ids_out;           // [k]
-  float *w_out;               // [k]
+  int32_t *sel_ids;           // [k] selected experts, rank order (largest logit first)
+  float *sel_z;               // [k] their logits
   int H, I, E, k, S;
   // when set, the layer reads RMSNorm(x) (unit gain, rounded to bf16) instead of x; the
   // residual is still the caller's (un-normalised) pointer

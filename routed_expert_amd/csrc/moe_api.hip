@@ -84,7 +84,7 @@ moe_status check_layer(const moe_layer *L) {
 
 // Workspace layout: the batch-1 decode buffers first, then the T-dependent region.
 struct Plan {
-  size_t dec_logits, dec_ids, dec_w, dec_h;
+  size_t dec_logits, dec_ids, dec_z, dec_h;
   size_t logits, logits2, planes, ids, w, blk, offsets, sorted, slot, slot_w, x16, tiles, ntiles,
       h, out,
       out_sh;
@@ -107,7 +107,7 @@ Plan make_plan(const moe_layer *L, int64_t T) {
   const size_t NB = (Tn + moe::kRouteBlock - 1) / moe::kRouteBlock;
   p.dec_logits = take(E * 4);
   p.dec_ids = take(k * 4);
-  p.dec_w = take(k * 4);
+  p.dec_z = take(k * 4);
   p.dec_h = take((k + S) * I * 4);
   const size_t tiles = (k * Tn + moe::kTileM - 1) / moe::kTileM + E +
                        (S ? (Tn + moe::kTileM - 1) / moe::kTileM : 0);
@@ -514,8 +514,8 @@ static moe_status decode_impl(const moe_layer *layer, const void *x, void *y,
     da.y = static_cast<uint16_t *>(y);
     da.z = at<float>(ws, p.dec_logits);
     da.h = at<float>(ws, p.dec_h);
-    da.ids_out = at<int32_t>(ws, p.dec_ids);
-    da.w_out = at<float>(ws, p.dec_w);
+    da.sel_ids = at<int32_t>(ws, p.dec_ids);
+    da.sel_z = at<float>(ws, p.dec_z);
     da.H = layer->hidden;
     da.I = layer->inter;
     da.E = layer->n_experts;
