@@ -60,7 +60,9 @@ typedef enum { MOE_ACT_F32 = 0, MOE_ACT_BF16 = 1 } moe_act_dtype;
  * Supported: 1 <= k <= 8, k <= E <= 256, S in {0,1}; H % 64 == 0, I % 64 == 0,
  * and for int4 additionally H % 256 == 0 and I % 128 == 0. Pointers to codes, tiled
  * arrays, fp32 weights, activations and the workspace must be 16-byte aligned; int4
- * scale and bias pointers 4-byte aligned. */
+ * scale and bias pointers 4-byte aligned. Int4 weights are rebuilt in fp16 on the GPU:
+ * every scale is 0 or has |scale| >= 2^-13, and scales, biases, weights, x and h stay
+ * below 65504 in magnitude (results are unspecified otherwise). */
 typedef struct {
   int32_t abi_version;  /* must be MOE_ABI_VERSION */
   int32_t hidden, inter, n_experts, top_k, n_shared;

@@ -93,6 +93,29 @@ MOE_DEV uint32_t and_or(uint32_t v, uint32_t mask, uint32_t bits) {
   return r;
 }
 
+// The same eight weights with one shift instead of three: the nibbles at bits 4..7 (and
+// 20..23) are masked in place, giving the fp16 pair (1024 + 16 q_lo, 1024 + 16 q_hi), and
+// are scaled by s / 16 (s2q) instead of s. 16 q (s / 16) equals q s exactly when s / 16 is
+// exact in fp16, which holds for bf16 scales with |s| >= 2^-13; the single rounding of the
+// fused multiply-add then gives the same bits as dequant8_pk.
+MOE_DEV uint4 dequant8_pk_q(uint32_t w, f16x2_t s2, f16x2_t s2q, f16x2_t b2) {
+  constexpr uint32_t kLo = 0x000F000Fu, kHi = 0x00F000F0u, kMagic = 0x64006400u;
+  const f16x2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+  const uint32_t u = w >> 8;
+  const uint32_t t0 = and_or(w, kLo, kMagic), t1 = and_or(w, kHi, kMagic);
+  const uint32_t t2 = and_or(u, kLo, kMagic), t3 = and_or(u, kHi, kMagic);
+  uint4 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(
+                                         __builtin_bit_cast(f16x2_t, t0) - k1024, s2, b2));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(
+                                         __builtin_bit_cast(f16x2_t, t1) - k1024, s2q, b2));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(
+                                         __builtin_bit_cast(f16x2_t, t2) - k1024, s2, b2));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(
+                                         __builtin_bit_cast(f16x2_t, t3) - k1024, s2q, b2));
+  return r;
+}
+
 MOE_DEV uint4 dequant8_pk(uint32_t w, f16x2_t s2, f16x2_t b2) {
   constexpr uint32_t kMask = 0x000F000Fu, kMagic = 0x64006400u;
   const f16x2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};

@@ -153,7 +153,7 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
   // half a step early and without a barrier; only the activation rows, which all four
   // waves load together, wait for the step barrier.
   uint32_t w0[4], w1[4];
-  f16x2_t s0, b0, s1, b1;
+  f16x2_t s0, b0, s1, b1, s0q, s1q;
   const int bn = lane & 31, bh = lane >> 5;
 #define MOE_READ_B(step)                                                                \
   do {                                                                                  \
@@ -169,6 +169,8 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
     b0 = f16_pair_from_bf16((uint16_t)(sb0_ >> 16));                                    \
     s1 = f16_pair_from_bf16((uint16_t)sb1_);                                            \
     b1 = f16_pair_from_bf16((uint16_t)(sb1_ >> 16));                                    \
+    s0q = s0 * f16x2_t{(_Float16)0.0625f, (_Float16)0.0625f};                           \
+    s1q = s1 * f16x2_t{(_Float16)0.0625f, (_Float16)0.0625f};                           \
     w0[0] = q0_.x; w0[1] = q0_.y; w0[2] = q0_.z; w0[3] = q0_.w;                         \
     w1[0] = q1_.x; w1[1] = q1_.y; w1[2] = q1_.z; w1[3] = q1_.w;                         \
   } while (0)
@@ -183,8 +185,8 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
   else
     wait_vmcnt<0>();
   MOE_READ_B(0);
-  f16x8_t bc0 = __builtin_bit_cast(f16x8_t, dequant8_pk(w0[0], s0, b0));
-  f16x8_t bc1 = __builtin_bit_cast(f16x8_t, dequant8_pk(w1[0], s1, b1));
+  f16x8_t bc0 = __builtin_bit_cast(f16x8_t, dequant8_pk_q(w0[0], s0, s0q, b0));
+  f16x8_t bc1 = __builtin_bit_cast(f16x8_t, dequant8_pk_q(w1[0], s1, s1q, b1));
   for (int st = 0; st < nsteps; ++st) {
     // every wave's loads of step st have landed (each wave waited for its own before its
     // mid-step read of step st's codes), and every wave is done with the stage step st+2
@@ -212,8 +214,8 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
       if (kk == 0 && st + 2 < nsteps) MOE_ISSUE(st + 2);
       if (kk < 3) {
         // next substep's weights while the MFMAs above run
-        bc0 = __builtin_bit_cast(f16x8_t, dequant8_pk(w0[kk + 1], s0, b0));
-        bc1 = __builtin_bit_cast(f16x8_t, dequant8_pk(w1[kk + 1], s1, b1));
+        bc0 = __builtin_bit_cast(f16x8_t, dequant8_pk_q(w0[kk + 1], s0, s0q, b0));
+        bc1 = __builtin_bit_cast(f16x8_t, dequant8_pk_q(w1[kk + 1], s1, s1q, b1));
         // A wave issues in order: interleave the dequantisation (and the next fragments'
         // LDS reads) between the MFMAs so the vector ALU works in the matrix unit's shadow
         // instead of after the last MFMA of the substep.
@@ -235,8 +237,8 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
           wait_vmcnt<0>();
         }
         MOE_READ_B(st + 1);
-        bc0 = __builtin_bit_cast(f16x8_t, dequant8_pk(w0[0], s0, b0));
-        bc1 = __builtin_bit_cast(f16x8_t, dequant8_pk(w1[0], s1, b1));
+        bc0 = __builtin_bit_cast(f16x8_t, dequant8_pk_q(w0[0], s0, s0q, b0));
+        bc1 = __builtin_bit_cast(f16x8_t, dequant8_pk_q(w1[0], s1, s1q, b1));
       }
     }
   }
