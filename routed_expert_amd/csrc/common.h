@@ -254,11 +254,13 @@ constexpr int kTopkScratch = 64 + 4 * kMaxTopK + kMaxTopK;  // uint64 entries pe
 // read as -inf, experts >= E excluded). The order is (logit desc, id asc), encoded in one
 // 64-bit key: float key in the high word, ~id in the low word. Each lane sorts its four
 // keys; the k best elements lie in the k lanes whose heads rank highest, so the wave
-// ranks the 64 heads, gathers those lanes' 4k keys and ranks them. Every lane receives
-// the k ids in ascending id order and their weights: softmax over the selected logits.
+// ranks the 64 heads, gathers those lanes' 4k keys and ranks them. Lane j < k then takes
+// the j-th largest: it returns its expert id, its position among the k ids in ascending
+// id order, and its weight, the softmax over the selected logits (hardware exp2; the
+// denominator is summed over the k lanes in a fixed order). Needs E >= k.
 // scratch: kTopkScratch uint64 entries of LDS private to the calling wave (16-B aligned).
-MOE_DEV void wave_topk(const float v[4], int E, int k, uint64_t *scratch, int ids[kMaxTopK],
-                       float w[kMaxTopK]) {
+MOE_DEV void wave_topk(const float v[4], int E, int k, uint64_t *scratch, int &id_out,
+                       int &pos_out, float &w_out) {
   const int lane = threadIdx.x & 63;
   uint64_t key[4];
 #pragma unroll
@@ -279,6 +281,7 @@ MOE_DEV void wave_topk(const float v[4], int E, int k, uint64_t *scratch, int id
 #undef MOE_CSWAP
   uint64_t *heads = scratch, *cand = scratch + 64, *best = scratch + 64 + 4 * kMaxTopK;
   heads[lane] = key[0];
+  if (lane < 4 * kMaxTopK) cand[lane] = 0ull;  // unused candidate slots rank last
   wave_lds_sync();
   int r = 0;
 #pragma unroll 8
@@ -291,47 +294,49 @@ MOE_DEV void wave_topk(const float v[4], int E, int k, uint64_t *scratch, int id
     for (int c = 0; c < 4; ++c) cand[4 * r + c] = key[c];
   }
   wave_lds_sync();
-  const int nc = 4 * k;
-  if (lane < nc) {
-    const uint64_t mine = cand[lane];
+  {
+    const uint64_t mine = cand[lane & (4 * kMaxTopK - 1)];
     int r2 = 0;
-    for (int q = 0; q < nc; ++q) r2 += cand[q] > mine;
-    if (r2 < k) best[r2] = mine;
+#pragma unroll
+    for (int q = 0; q < 4 * kMaxTopK; q += 2) {
+      const ulonglong2 c2 = *reinterpret_cast<const ulonglong2 *>(cand + q);
+      r2 += (c2.x > mine) + (c2.y > mine);
+    }
+    if (lane < 4 * kMaxTopK && mine != 0ull && r2 < k) best[r2] = mine;
   }
   wave_lds_sync();
-  int sel[kMaxTopK];
-  float val[kMaxTopK];
+  // lane j < k: the j-th largest key; every such lane reads all k winners (same order)
+  uint64_t win[kMaxTopK];
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    if (j >= k) break;
-    const uint64_t b = best[j];
-    sel[j] = (int)(0xFFFFFFFFu - (uint32_t)b);
-    val[j] = key_float((uint32_t)(b >> 32));
+  for (int q = 0; q < kMaxTopK; q += 2) {
+    const ulonglong2 b2 = *reinterpret_cast<const ulonglong2 *>(best + q);
+    win[q] = b2.x;
+    win[q + 1] = b2.y;
   }
   wave_lds_sync();  // scratch may be reused by the caller's next token
-  float ex[kMaxTopK], denom = 0.f;
+  uint64_t mw = win[0];
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    if (j >= k) break;
-    ex[j] = val[0] == -INFINITY ? 1.0f : expf(val[j] - val[0]);
-    denom += ex[j];
-  }
+  for (int q = 1; q < kMaxTopK; ++q)
+    if (q == lane) mw = win[q];
+  const int id = (int)(0xFFFFFFFFu - (uint32_t)mw);
+  const float top = key_float((uint32_t)(win[0] >> 32));
+  float den = 0.f, mine = 0.f;
+  int pos = 0;
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    if (j >= k) break;
-    int rk = 0;
-#pragma unroll
-    for (int q = 0; q < kMaxTopK; ++q) {
-      if (q >= k) break;
-      rk += sel[q] < sel[j] ? 1 : 0;
+  for (int q = 0; q < kMaxTopK; ++q) {
+    if (q < k) {
+      const float vq = key_float((uint32_t)(win[q] >> 32));
+      // exp(v - top) from the hardware exp2; top == -inf only when every logit is -inf
+      const float ex = top == -INFINITY ? 1.0f
+                                        : __builtin_amdgcn_exp2f((vq - top) * 1.4426950408889634f);
+      den += ex;
+      if (q == lane) mine = ex;
+      pos += (int)(0xFFFFFFFFu - (uint32_t)win[q]) < id ? 1 : 0;
     }
-#pragma unroll
-    for (int q = 0; q < kMaxTopK; ++q)
-      if (q == rk) {
-        ids[q] = sel[j];
-        w[q] = ex[j] / denom;
-      }
   }
+  id_out = id;
+  pos_out = pos;
+  w_out = mine / den;
 }
 
 }  // namespace moe

@@ -228,6 +228,7 @@ __global__ __launch_bounds__(256) void k_router_f32(const float *__restrict__ x,
 
 // ---- top-k, one wave per token; per-block histogram by device atomics -----------------
 // Workgroup = 4 waves = 4 tokens. blk_cnt[t / 64][e] was zeroed by the router kernel.
+template <bool kTwoHalves>
 __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ z,
                                               const float *__restrict__ z2, int T, int E, int k,
                                               int32_t *__restrict__ ids,
@@ -237,27 +238,25 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ z,
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
-  float v[4];
+  // all loads leave before the first use (experts past E read the last one and are masked)
+  float v[4], v2[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const int e = lane + kWave * c;
-    v[c] = e < E ? (z2 ? z[(size_t)t * E + e] + z2[(size_t)t * E + e] : z[(size_t)t * E + e])
-                 : -INFINITY;
+    const size_t i = (size_t)t * E + min(lane + kWave * c, E - 1);
+    v[c] = z[i];
+    v2[c] = kTwoHalves ? z2[i] : 0.f;
   }
-  int sel[kMaxTopK];
-  float sw[kMaxTopK];
-  wave_topk(v, E, k, s_topk[wave], sel, sw);
-  int id = 0;
-  float weight = 0.f;
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j)
-    if (j == lane) {
-      id = sel[j];
-      weight = sw[j];
-    }
+  for (int c = 0; c < 4; ++c) {
+    if (kTwoHalves) v[c] += v2[c];
+    if (lane + kWave * c >= E) v[c] = -INFINITY;
+  }
+  int id, pos;
+  float weight;
+  wave_topk(v, E, k, s_topk[wave], id, pos, weight);
   if (lane < k) {
-    ids[(size_t)t * k + lane] = id;
-    w[(size_t)t * k + lane] = weight;
+    ids[(size_t)t * k + pos] = id;
+    w[(size_t)t * k + pos] = weight;
     atomicAdd(&blk_cnt[(size_t)(t / kRouteBlock) * E + id], 1);
   }
 }
@@ -411,8 +410,12 @@ hipError_t launch_route_prefill(const RouteArgs &a, hipStream_t s) {
     MOE_LAUNCH("k_router_f32", k_router_f32, g1, dim3(256), 0, s,
                static_cast<const float *>(a.x), a.router_w, a.router_b, a.logits, a.blk,
                (int)a.T, a.H, a.E);
-  MOE_LAUNCH("k_topk", k_topk, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, s, a.logits,
-             a.bf16 ? a.logits2 : nullptr, (int)a.T, a.E, a.k, a.ids, a.w, a.blk);
+  if (a.bf16)
+    MOE_LAUNCH("k_topk", k_topk<true>, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, s,
+               a.logits, a.logits2, (int)a.T, a.E, a.k, a.ids, a.w, a.blk);
+  else
+    MOE_LAUNCH("k_topk", k_topk<false>, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, s,
+               a.logits, nullptr, (int)a.T, a.E, a.k, a.ids, a.w, a.blk);
   MOE_LAUNCH("k_scan", k_scan, dim3(1), dim3(256), 0, s, a.blk, NB, a.E, (int)a.T, a.k, a.S,
              a.offsets, a.counts_user, a.offsets_user, a.tiles, a.n_tiles);
   MOE_LAUNCH("k_scatter", k_scatter, dim3(NB), dim3(256), 0, s, a.ids, (int)a.T, a.E, a.k,
