@@ -4,8 +4,8 @@
 // "Optimizing On-Device Inference for Apple Silicon", section "Reduce intermediate
 // and state traffic": each expert's output projection is combined with its routing
 // score and with the shared-expert result. In the prefill path the down GEMM writes each
-// routed slot's output already scaled by its routing weight (fp16, slot order) and the
-// shared expert's output in fp32 (token order); this kernel gathers a token's rows in a
+// routed slot's output already scaled by its routing weight and the shared expert's
+// output after them (slots kT + t), all fp16; this kernel gathers a token's rows in a
 // fixed order (shared first, then ascending expert id) and sums them in fp32, so the
 // result is deterministic.
 #include "common.h"
@@ -25,11 +25,11 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
     const size_t o = (size_t)t * H + c;
     float acc[8];
-    if (a.out_sh) {
-      const float4 *p = reinterpret_cast<const float4 *>(a.out_sh + o);
-      const float4 u = p[0], v = p[1];
-      acc[0] = u.x; acc[1] = u.y; acc[2] = u.z; acc[3] = u.w;
-      acc[4] = v.x; acc[5] = v.y; acc[6] = v.z; acc[7] = v.w;
+    if (a.S) {
+      const uint4 v =
+          *reinterpret_cast<const uint4 *>(a.out + ((size_t)k * a.T + t) * H + c);
+      acc[0] = f16lo(v.x); acc[1] = f16hi(v.x); acc[2] = f16lo(v.y); acc[3] = f16hi(v.y);
+      acc[4] = f16lo(v.z); acc[5] = f16hi(v.z); acc[6] = f16lo(v.w); acc[7] = f16hi(v.w);
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = 0.f;

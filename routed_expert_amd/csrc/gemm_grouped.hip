@@ -22,10 +22,10 @@
 //   gate/up: weight rows = gate rows i0 + 32w .. +32 and the matching up rows, so the gate
 //            and up accumulators of a (row, i) sit in the same lane and SwiGLU is applied
 //            in registers; h is written in slot order [slots, I] fp16.
-//   down:    weight rows = output columns n0 + 64w .. +64. A routed slot's row is scaled
-//            by its routing weight and written fp16 in slot order; the shared expert's
-//            rows are written fp32 in token order (section "Reduce intermediate and state
-//            traffic": the output projection is combined with the routing score).
+//   down:    weight rows = output columns n0 + 64w .. +64. Every row is written fp16 in
+//            slot order: a routed slot's row scaled by its routing weight, a shared-expert
+//            slot's row as it is (section "Reduce intermediate and state traffic": the
+//            output projection is combined with the routing score).
 // MFMA K order: lane (n, half) of a B operand holds the 8 K of substep kk at
 // 32*half + 8*kk (inside that chunk in the order 0,4,1,5,2,6,3,7 in which the packed
 // dequantisation produces them), so over the 4 substeps a lane covers 32 consecutive K =
@@ -273,12 +273,13 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
       *reinterpret_cast<uint4 *>(a.h16 + (size_t)(slot0 + rr) * a.I + n_tile * (BNW / 2) +
                                  8 * (tid & 15)) =
           *reinterpret_cast<const uint4 *>(ht + rr * HP + 8 * (tid & 15));
-  } else if (e < a.E) {
-    // routed rows, pre-weighted by their routing weight: rows x 256 columns fp16
+  } else {
+    // rows x 256 columns fp16 in slot order: a routed slot pre-weighted by its routing
+    // weight, a shared-expert slot (weight 1) as it is
     constexpr int OP = BNW + 8;
     _Float16 *ot = reinterpret_cast<_Float16 *>(smem);
     float *sw = reinterpret_cast<float *>(smem + BM * OP * 2);
-    if (tid < BM) sw[tid] = tid < nvalid ? a.slot_w[slot0 + tid] : 0.f;
+    if (tid < BM) sw[tid] = tid < nvalid ? (e < a.E ? a.slot_w[slot0 + tid] : 1.0f) : 0.f;
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < MB; ++m)
@@ -294,20 +295,6 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
       *reinterpret_cast<uint4 *>(a.out + (size_t)(slot0 + rr) * a.H + n_tile * BNW +
                                  8 * (tid & 31)) =
           *reinterpret_cast<const uint4 *>(ot + rr * OP + 8 * (tid & 31));
-  } else {
-    // shared expert: fp32 in token order; each store instruction writes 128 contiguous
-    // bytes of a row already
-    const int n = n_tile * BNW + 64 * wave + col;
-#pragma unroll
-    for (int m = 0; m < MB; ++m)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 32 * m + (r >> 2) * 8 + rq4 + (r & 3);
-        if (row >= nvalid) continue;
-        const size_t t = (size_t)(row0 + row);
-        a.out_sh[t * a.H + n] = acc[m][0][r];
-        a.out_sh[t * a.H + n + 32] = acc[m][1][r];
-      }
   }
 }
 

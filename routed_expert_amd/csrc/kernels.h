@@ -85,16 +85,16 @@ struct GroupedArgs {
   int H, I, E, k;
   ExpertWeights wt;
   uint16_t *h16;   // [(k+S) T, I] fp16, slot order
-  uint16_t *out;   // [k T, H] fp16, routed slots, already scaled by the routing weight
-  float *out_sh;   // [T, H] fp32, shared expert output in token order
+  uint16_t *out;   // [(k+S) T, H] fp16, slot order: routed slots already scaled by the
+                   // routing weight, then the shared expert's slots (token order)
 };
 hipError_t launch_grouped_gateup(const GroupedArgs &a, hipStream_t s);
 hipError_t launch_grouped_down(const GroupedArgs &a, hipStream_t s);
 
 // Weighted combine of the slot-ordered expert outputs back to token order.
 struct CombineArgs {
-  const uint16_t *out;       // [k T, H] fp16, weighted routed outputs
-  const float *out_sh;       // [T, H] fp32 shared-expert output (null if S == 0)
+  const uint16_t *out;       // [(k+S) T, H] fp16: weighted routed outputs, then the shared
+                             // expert's rows in token order
   const int32_t *slot_of;    // [T, k]
   const uint16_t *residual;  // [T, H] or null
   uint16_t *y;               // [T, H]

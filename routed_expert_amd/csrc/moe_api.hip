@@ -86,8 +86,7 @@ moe_status check_layer(const moe_layer *L) {
 struct Plan {
   size_t dec_logits, dec_ids, dec_z, dec_h;
   size_t logits, logits2, planes, ids, w, blk, offsets, sorted, slot, slot_w, x16, tiles, ntiles,
-      h, out,
-      out_sh;
+      h, out;
   size_t total;
   int max_tiles;
 };
@@ -127,11 +126,10 @@ Plan make_plan(const moe_layer *L, int64_t T) {
     p.slot_w = take(k * Tn * 4);
     p.x16 = take(Tn * H * 2);
     p.h = take((k + S) * Tn * I * 2);
-    p.out = take(k * Tn * H * 2);
-    p.out_sh = take(S * Tn * H * 4);
+    p.out = take((k + S) * Tn * H * 2);
   } else {
     p.h = take((k + S) * Tn * I * 4);
-    p.slot_w = p.x16 = p.out = p.out_sh = off;
+    p.slot_w = p.x16 = p.out = off;
   }
   p.total = off;
   return p;
@@ -431,14 +429,12 @@ static moe_status prefill_impl(const moe_layer *layer, const void *x, int64_t T,
     ga.wt = wt;
     ga.h16 = at<uint16_t>(ws, p.h);
     ga.out = at<uint16_t>(ws, p.out);
-    ga.out_sh = layer->n_shared ? at<float>(ws, p.out_sh) : nullptr;
     if ((e = moe::launch_grouped_gateup(ga, s)) != hipSuccess)
       return hip_fail(e, "moe_prefill gate/up");
     if ((e = moe::launch_grouped_down(ga, s)) != hipSuccess)
       return hip_fail(e, "moe_prefill down");
     moe::CombineArgs ca{};
     ca.out = ga.out;
-    ca.out_sh = ga.out_sh;
     ca.slot_of = ra.slot_of;
     ca.residual = static_cast<const uint16_t *>(residual);
     ca.y = static_cast<uint16_t *>(y);
