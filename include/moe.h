@@ -30,7 +30,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum {
   MOE_OK = 0,
@@ -72,8 +72,9 @@ typedef struct {
   const void *w13_q, *w13_s, *w13_b;
   const void *w2_q, *w2_s, *w2_b;
   const void *w13_t, *w13_tsb, *w2_t, *w2_tsb;
-  /* bf16 bit patterns [3, E, H]: router_w split exactly into three bf16 planes (hi, mid,
-   * lo; their sum is the fp32 weight), written by moe_pack_weights, or NULL. When set, the
+  /* fp16 bit patterns [2, E, H]: router_w split into two fp16 planes, hi = fp16(w) and
+   * lo = fp16((w - hi) * 2048), so w = hi + lo / 2048 to about 22 bits (router weights must
+   * be below 65504 in magnitude); written by moe_pack_weights, or NULL. When set, the
    * prefill router reads it instead of splitting router_w on every call. */
   const void *router_planes;
 } moe_layer;
@@ -119,7 +120,7 @@ moe_status moe_pack_bytes(const moe_layer *layer, size_t *bytes);
  * 32j..32j+31; W2 block j: rows 64j..64j+63) and steps of 64 along K:
  *   *_t    uint8 [E+S][R/64][K/64][64 rows][32 bytes]  (the row's 32 code bytes of the step)
  *   *_tsb  bf16  [E+S][R/64][ceil(K/256)][64 rows][4 groups][scale, bias]  (zero padded)
- * and the router's three bf16 planes (router_planes).
+ * and the router's two fp16 planes (router_planes).
  * Stream-ordered like every call; dst must not overlap the source arrays. */
 moe_status moe_pack_weights(const moe_layer *layer, void *dst, size_t dst_bytes,
                             moe_layer *packed, void *stream);

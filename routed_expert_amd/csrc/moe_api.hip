@@ -113,7 +113,7 @@ Plan make_plan(const moe_layer *L, int64_t T) {
   p.max_tiles = (int)tiles;
   p.logits = take(Tn * E * 4);
   p.logits2 = take(L->act_dtype == MOE_ACT_BF16 ? Tn * E * 4 : 0);
-  p.planes = take(L->act_dtype == MOE_ACT_BF16 ? 3 * E * H * 2 : 0);
+  p.planes = take(L->act_dtype == MOE_ACT_BF16 ? 2 * E * H * 2 : 0);
   p.ids = take(Tn * k * 4);
   p.w = take(Tn * k * 4);
   p.blk = take(NB * E * 4);
@@ -187,7 +187,7 @@ PackPlan pack_plan(const moe_layer *L) {
   p.w2_tsb = off;
   off += align256(moe::tiled_sb_bytes(n, H, I));
   p.planes = off;
-  off += align256((size_t)3 * L->n_experts * H * 2);
+  off += align256((size_t)2 * L->n_experts * H * 2);
   p.total = off;
   return p;
 }

@@ -18,9 +18,12 @@
 namespace moe {
 
 // ---- router logits for many tokens: z[T,E] = x[T,H] W[E,H]^T + b --------------------------
-// bf16 activations: MFMA with the fp32 router weights split into three bf16 planes
-// (w = hi + mid + lo to ~24 mantissa bits); x is exact in bf16, every product is exact in
-// fp32 and the MFMA accumulates in fp32, so the logits carry fp32-class error.
+// bf16 activations: MFMA in fp16 with the fp32 router weights split into two fp16 planes,
+// hi = fp16(w) and lo = fp16((w - hi) * 2^11), so w = hi + lo * 2^-11 to 22 bits (the lo
+// plane is scaled to stay clear of fp16 subnormals). x converts exactly to fp16 (inside the
+// fp16 range), every product is exact in fp32, and the two planes accumulate separately in
+// fp32 before z = acc_hi + 2^-11 acc_lo, so the logits carry fp32-class error. Two planes
+// instead of three bf16 ones: the kernel is bound by the LDS traffic of the weight planes.
 // Tile: 64 tokens x 64 experts per workgroup, K in steps of 64; 4 waves in 2x2, each one
 // 32x32 accumulator. Side jobs: the fp16 copy of x for the expert GEMMs (expert tile 0,
 // chunks in kChunkOrder) and zeroing this token block's histogram row (the top-k kernel
@@ -29,32 +32,28 @@ namespace {
 constexpr int RP = 64 + 8;  // LDS row pitch (elements)
 }
 
-MOE_DEV void split3(float w, uint16_t &hi, uint16_t &mid, uint16_t &lo) {
-  const __bf16 h = (__bf16)w;
-  const float r1 = w - (float)h;
-  const __bf16 m = (__bf16)r1;
-  const float r2 = r1 - (float)m;
+constexpr float kLoScale = 2048.0f;  // lo plane = fp16((w - hi) * 2^11)
+
+MOE_DEV void split2(float w, uint16_t &hi, uint16_t &lo) {
+  const _Float16 h = (_Float16)w;
   hi = __builtin_bit_cast(uint16_t, h);
-  mid = __builtin_bit_cast(uint16_t, m);
-  lo = __builtin_bit_cast(uint16_t, (__bf16)r2);
+  lo = __builtin_bit_cast(uint16_t, (_Float16)((w - (float)h) * kLoScale));
 }
 
-// Router weights split into three bf16 planes [3][E][H]: once by moe_pack_weights for a
-// packed layer, else on every call into the workspace.
+// Router weights split into two fp16 planes [2][E][H] (hi, lo; natural element order):
+// once by moe_pack_weights for a packed layer, else on every call into the workspace.
 __global__ __launch_bounds__(256) void k_router_split(const float *__restrict__ W, size_t n,
                                                       uint16_t *__restrict__ planes) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n / 4;
        i += (size_t)gridDim.x * 256) {
     const float4 f = reinterpret_cast<const float4 *>(W)[i];
     const float v[4] = {f.x, f.y, f.z, f.w};
-    uint16_t h[4], m[4], l[4];
+    uint16_t h[4], l[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) split3(v[q], h[q], m[q], l[q]);
+    for (int q = 0; q < 4; ++q) split2(v[q], h[q], l[q]);
     reinterpret_cast<uint2 *>(planes)[i] =
         make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
     reinterpret_cast<uint2 *>(planes + n)[i] =
-        make_uint2(m[0] | ((uint32_t)m[1] << 16), m[2] | ((uint32_t)m[3] << 16));
-    reinterpret_cast<uint2 *>(planes + 2 * n)[i] =
         make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
   }
 }
@@ -68,7 +67,7 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t *__restrict_
                                                      int32_t *__restrict__ blk_cnt, int T,
                                                      int H, int E) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][64 * RP];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][3][64 * RP];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][2][64 * RP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
@@ -81,7 +80,7 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t *__restrict_
   const int t = t0 + lr, e = e0 + lr;
   const int frow = lane & 31, fk = (lane >> 5) * 8;
   const size_t plane = (size_t)E * H;
-  uint4 ra[2], rb[3][2];
+  uint4 ra[2], rb[2][2];
   auto gload = [&](int k0) {
     ra[0] = ra[1] = make_uint4(0, 0, 0, 0);
     if (t < T) {
@@ -90,7 +89,7 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t *__restrict_
       ra[1] = p[1];
     }
 #pragma unroll
-    for (int pl = 0; pl < 3; ++pl) {
+    for (int pl = 0; pl < 2; ++pl) {
       rb[pl][0] = rb[pl][1] = make_uint4(0, 0, 0, 0);
       if (e < E) {
         const uint4 *p =
@@ -101,11 +100,14 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t *__restrict_
     }
   };
   auto lstore = [&](int buf, int k0) {
+    // x as fp16 (natural order; exact inside the fp16 range)
     uint4 *pa = reinterpret_cast<uint4 *>(&As[buf][lr * RP + lc]);
-    pa[0] = ra[0];
-    pa[1] = ra[1];
+    pa[0] = make_uint4(bf16x2_to_f16x2(ra[0].x), bf16x2_to_f16x2(ra[0].y),
+                       bf16x2_to_f16x2(ra[0].z), bf16x2_to_f16x2(ra[0].w));
+    pa[1] = make_uint4(bf16x2_to_f16x2(ra[1].x), bf16x2_to_f16x2(ra[1].y),
+                       bf16x2_to_f16x2(ra[1].z), bf16x2_to_f16x2(ra[1].w));
 #pragma unroll
-    for (int pl = 0; pl < 3; ++pl) {
+    for (int pl = 0; pl < 2; ++pl) {
       uint4 *pb = reinterpret_cast<uint4 *>(&Bs[buf][pl][lr * RP + lc]);
       pb[0] = rb[pl][0];
       pb[1] = rb[pl][1];
@@ -117,7 +119,7 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t *__restrict_
       q[1] = bf16x8_to_f16x8_chunk(ra[1]);
     }
   };
-  f32x16_t acc = {};
+  f32x16_t acc_h = {}, acc_l = {};
   gload(kbase);
   lstore(0, kbase);
   __syncthreads();
@@ -128,14 +130,14 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t *__restrict_
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int ko = kk * 16 + fk;
-      const bf16x8_t av =
-          *reinterpret_cast<const bf16x8_t *>(&As[cur][(wm * 32 + frow) * RP + ko]);
-#pragma unroll
-      for (int pl = 0; pl < 3; ++pl) {
-        const bf16x8_t bv =
-            *reinterpret_cast<const bf16x8_t *>(&Bs[cur][pl][(wn * 32 + frow) * RP + ko]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
-      }
+      const f16x8_t av =
+          *reinterpret_cast<const f16x8_t *>(&As[cur][(wm * 32 + frow) * RP + ko]);
+      const f16x8_t bh =
+          *reinterpret_cast<const f16x8_t *>(&Bs[cur][0][(wn * 32 + frow) * RP + ko]);
+      const f16x8_t bl =
+          *reinterpret_cast<const f16x8_t *>(&Bs[cur][1][(wn * 32 + frow) * RP + ko]);
+      acc_h = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bh, acc_h, 0, 0, 0);
+      acc_l = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bl, acc_l, 0, 0, 0);
     }
     if (st + 1 < nsteps) lstore(cur ^ 1, kbase + (st + 1) * 64);
     __syncthreads();
@@ -146,10 +148,11 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t *__restrict_
   for (int r = 0; r < 16; ++r) {
     const int tt = t0 + wm * 32 + (r >> 2) * 8 + rq4 + (r & 3);
     if (tt < T && ee < E) {
+      const float v = __builtin_fmaf(acc_l[r], 1.0f / kLoScale, acc_h[r]);
       if (blockIdx.z == 0)
-        z[(size_t)tt * E + ee] = acc[r] + (bias ? bias[ee] : 0.f);
+        z[(size_t)tt * E + ee] = v + (bias ? bias[ee] : 0.f);
       else
-        z2[(size_t)tt * E + ee] = acc[r];
+        z2[(size_t)tt * E + ee] = v;
     }
   }
 }

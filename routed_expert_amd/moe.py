@@ -18,7 +18,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4
 W_F32, W_INT4_G64 = 0, 1
 ACT_F32, ACT_BF16 = 0, 1

@@ -138,7 +138,7 @@ def test_pack_size_and_argument_errors(M):
     E1, H, I = 257, 2048, 512
     codes = E1 * 2 * I * H // 2 + E1 * H * I // 2
     sb = E1 * (2 * I // 64) * (H // 256) * 64 * 16 + E1 * (H // 64) * (I // 256) * 64 * 16
-    planes = 3 * (E1 - 1) * H * 2   # the router split into three bf16 planes
+    planes = 2 * (E1 - 1) * H * 2   # the router split into two fp16 planes
     assert n.value == codes + sb + planes
     out = M.MoeLayer()
     dst = ctypes.c_void_p(0x1000000)

@@ -291,11 +291,16 @@ def test_pack_weights_layout(M, H, I):
         got_sb = buf[sp - base: sp - base + 2 * want_sb.size].view(np.uint16)
         assert np.array_equal(got_q, want_q)
         assert np.array_equal(got_sb, want_sb)
-    # router planes: hi + mid + lo == the fp32 weight exactly, each plane a bf16 value
+    # router planes: hi = fp16(w), lo = fp16((w - hi) * 2048), so hi + lo / 2048 is w to
+    # 2^-22 relative (2^-25 absolute where w is an fp16 subnormal)
     E = layer.n_experts
-    planes = buf[d.router_planes - base: d.router_planes - base + 3 * E * H * 2].view(np.uint16)
-    pf = synth.bf16_bits_to_f32(planes).astype(np.float64).reshape(3, E, H)
-    assert np.array_equal(pf.sum(0), layer.router_w.astype(np.float64))
+    planes = buf[d.router_planes - base: d.router_planes - base + 2 * E * H * 2].view(np.float16)
+    hi, lo = planes.reshape(2, E, H)
+    w = layer.router_w
+    assert np.array_equal(hi, w.astype(np.float16))
+    assert np.array_equal(lo, ((w - hi.astype(np.float32)) * 2048).astype(np.float16))
+    err = np.abs(hi.astype(np.float64) + lo.astype(np.float64) / 2048 - w.astype(np.float64))
+    assert np.all(err <= 2.0 ** -22 * np.abs(w) + 2.0 ** -25)
 
 
 def test_prefill_small_layer_padded_scale_blocks(M):
