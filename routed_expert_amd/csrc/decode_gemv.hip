@@ -332,6 +332,13 @@ __global__ __launch_bounds__(DT) void k_dec_c(DecodeArgs a) {
   __shared__ float red[DT / 64 * 4];
   const int w = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int k = a.k, nslot = a.k + a.S;
+  // token blockIdx.y (the small-T path runs one grid row per token)
+  const int tok = blockIdx.y;
+  const int32_t *sel_ids = a.sel_ids + (size_t)tok * k;
+  const float *sel_z = a.sel_z + (size_t)tok * k;
+  const float *hbase = a.h + (size_t)tok * nslot * DI;
+  const uint16_t *residual = a.residual ? a.residual + (size_t)tok * DH : nullptr;
+  uint16_t *yrow = a.y + (size_t)tok * DH;
   // three independent loads leave together: the routing (ids and logits of the winners),
   // h of all k+1 experts (two 8-element chunks per thread), then -- once the ids are known
   // -- the W2 rows; the routing weights are formed and h is converted into LDS while the W2
@@ -339,21 +346,21 @@ __global__ __launch_bounds__(DT) void k_dec_c(DecodeArgs a) {
   // (the loads are unconditional, with indices clamped into range, so that no branch makes
   // the compiler wait for one before issuing the next)
   const int tq = tid < k ? tid : 0;
-  const int my_id = a.sel_ids[tq];
-  const float my_z = a.sel_z[tq];
+  const int my_id = sel_ids[tq];
+  const float my_z = sel_z[tq];
   // output rows 64b + 4t .. +4; the residual of row 64b + 4t + tid % 4 (used by threads
   // 0..3; y stands in when there is no residual, read before it is written)
   const int b = w >> 4, t = w & 15;
   const int orow = 64 * b + 4 * t + (tid & 3);
-  const uint16_t resid = (a.residual ? a.residual : a.y)[orow];
+  const uint16_t resid = (residual ? residual : yrow)[orow];
   const int nch = nslot * DI / 8;
   static_assert(kSlots * DI / 8 <= 2 * DT, "h of all slots must fit two chunks per thread");
   float4 hv[2][2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int ch = min(tid + q * DT, nch - 1);
-    hv[q][0] = reinterpret_cast<const float4 *>(a.h)[2 * ch];
-    hv[q][1] = reinterpret_cast<const float4 *>(a.h)[2 * ch + 1];
+    hv[q][0] = reinterpret_cast<const float4 *>(hbase)[2 * ch];
+    hv[q][1] = reinterpret_cast<const float4 *>(hbase)[2 * ch + 1];
   }
   if (tid < kSlots) {
     s_ids[tid] = tid < k ? min(max(my_id, 0), a.E - 1) : a.E;
@@ -379,11 +386,13 @@ __global__ __launch_bounds__(DT) void k_dec_c(DecodeArgs a) {
     sb[i] = *reinterpret_cast<const uint4 *>(a.wt.w2_tsb + (blk * (kNS2 / 4) + (st >> 2)) * 512 +
                                              8 * (4 * t + r4));
   }
-  // routing weights: softmax over the selected logits, s_z[0] the largest; the shared
-  // expert (slot k) has weight 1
+  // routing weights: softmax over the selected logits, s_z[0] the largest (or, on the
+  // small-T path, the weights themselves); the shared expert (slot k) has weight 1
   if (tid < kSlots) {
     float wj = 1.0f;
-    if (tid < k) {
+    if (tid < k && a.sel_is_w) {
+      wj = s_z[tid];
+    } else if (tid < k) {
       const float top = s_z[0];
       float den = 0.f, mine = 0.f;
 #pragma unroll
@@ -442,13 +451,229 @@ __global__ __launch_bounds__(DT) void k_dec_c(DecodeArgs a) {
     float y = 0.f;
 #pragma unroll
     for (int v = 0; v < DT / 64; ++v) y += red[v * 4 + tid];
-    if (a.residual) y += bf16_to_f32(resid);
-    a.y[orow] = f32_to_bf16(y);
+    if (residual) y += bf16_to_f32(resid);
+    yrow[orow] = f32_to_bf16(y);
+  }
+}
+
+// ---- small-T path: 2 <= T <= kSmallT tokens of one layer, three kernels like decode -------
+// Section "Optimize the one-row weight path" carried to a few rows: each selected expert's
+// weights are read once for all the tokens that chose it, so the bytes grow with the union
+// of the tokens' experts, not with T. The prefill pipeline (routing tables, tile map,
+// grouped GEMMs, combine) costs a fixed ~60 us at such T.
+//   SA  one workgroup per expert e: router row e read once, dot products with every token.
+//   SB  every workgroup redoes the T top-k's (wave t takes token t), builds the union of the
+//       selected experts (ascending id, plus the shared expert) with a token mask per
+//       expert, then walks units (expert, 16 gate + 16 up rows) w, w + 256, ...: one load of
+//       the unit's codes serves every token in its mask. h[t][j] lands in the slot j of the
+//       expert in token t's ascending id list (the shared expert in slot k).
+//   SC  the decode output kernel, one grid row per token, with the weights from SB.
+
+// SA: z[t][e] for the T tokens; thread i holds router weights 4i .. 4i+3.
+__global__ __launch_bounds__(DT) void k_st_a(DecodeArgs a) {
+  __shared__ float red[kSmallT][DT / 64];
+  const int e = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int T = a.T;
+  // every load leaves before the first use (tokens past T re-read the last one)
+  const float4 wr = reinterpret_cast<const float4 *>(a.router_w + (size_t)e * DH)[tid];
+  const float braw = (a.router_b ? a.router_b : a.router_w)[e];
+  uint2 xb[kSmallT];
+#pragma unroll
+  for (int i = 0; i < kSmallT; ++i)
+    xb[i] = reinterpret_cast<const uint2 *>(a.x + (size_t)min(i, T - 1) * DH)[tid];
+#pragma unroll
+  for (int i = 0; i < kSmallT; ++i) {
+    if (i < T) {
+      float d = wr.x * bf16lo(xb[i].x);
+      d = __builtin_fmaf(wr.y, bf16hi(xb[i].x), d);
+      d = __builtin_fmaf(wr.z, bf16lo(xb[i].y), d);
+      d = __builtin_fmaf(wr.w, bf16hi(xb[i].y), d);
+      d = wave_sum_dpp(d);
+      if (lane == 0) red[i][wave] = d;
+    }
+  }
+  __syncthreads();
+  if (tid < T) {
+    float s = 0.f;
+#pragma unroll
+    for (int v = 0; v < DT / 64; ++v) s += red[tid][v];
+    a.z[(size_t)tid * a.E + e] = s + (a.router_b ? braw : 0.f);
+  }
+}
+
+// SB: top-k of every token, the union of their experts, then the gate/up units.
+__global__ __launch_bounds__(DT) void k_st_b(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) f16x2_t xs[kSmallT][DH / 2];
+  __shared__ float xseg[kSmallT][DH / 32];
+  __shared__ __attribute__((aligned(16))) uint64_t s_topk[kSmallT][kTopkScratch];
+  __shared__ int s_ids[kSmallT][kMaxTopK];
+  __shared__ int s_list[kMaxExperts + 1];
+  __shared__ uint32_t s_mask[kMaxExperts + 1], s_jtab[kMaxExperts + 1];
+  __shared__ int s_wtot[4];
+  __shared__ float red[2][kSmallT][DT / 64 * 32];
+  const int w = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int T = a.T, E = a.E, k = a.k;
+  // loads: wave t's token logits (lane l: experts l, l+64, l+128, l+192; past E the last
+  // expert, masked by the top-k) and every token's x (chunk ch = tid + DT q of the T x 256
+  // chunks; past them the last chunk again, not stored)
+  const int tw = min(wave, T - 1);
+  float zv[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) zv[c] = a.z[(size_t)tw * E + min(lane + 64 * c, E - 1)];
+  constexpr int kXQ = kSmallT * (DH / 8) / DT;
+  uint4 xr[kXQ];
+#pragma unroll
+  for (int q = 0; q < kXQ; ++q) {
+    const int ch = min(tid + DT * q, T * (DH / 8) - 1);
+    xr[q] = reinterpret_cast<const uint4 *>(a.x)[ch];
+  }
+  // x -> fp16 pairs (v[8c + p], v[8c + p + 4]) and 32-element segment sums, per token
+#pragma unroll
+  for (int q = 0; q < kXQ; ++q) {
+    const int ch = tid + DT * q;
+    const bool live = ch < T * (DH / 8);
+    const int ti = ch / (DH / 8), c = ch % (DH / 8);
+    const uint32_t wd[4] = {xr[q].x, xr[q].y, xr[q].z, xr[q].w};
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16lo(wd[i]);
+      v[2 * i + 1] = bf16hi(wd[i]);
+    }
+    float sum = 0.f;
+    f16x2_t pr[4];
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      pr[pp] = f16x2_t{(_Float16)v[pp], (_Float16)v[pp + 4]};
+      sum += (float)pr[pp][0] + (float)pr[pp][1];
+    }
+    if (live) *reinterpret_cast<uint4 *>(&xs[ti][4 * c]) = __builtin_bit_cast(uint4, pr);
+    sum = xor_sum<1>(sum);
+    sum = xor_sum<2>(sum);
+    if ((c & 3) == 0 && live) xseg[ti][c >> 2] = sum;
+  }
+  // top-k: wave t < T takes token t (ids in ascending order, weights from the softmax)
+  if (wave < T) {
+    int id, pos;
+    float wt;
+    wave_topk(zv, E, k, s_topk[wave], id, pos, wt);
+    if (lane < k) {
+      s_ids[wave][pos] = id;
+      if (w == 0) {
+        a.sel_ids[(size_t)wave * k + pos] = id;
+        a.sel_z[(size_t)wave * k + pos] = wt;
+      }
+    }
+  }
+  __syncthreads();
+  // the union: thread e < 256 gathers the tokens that chose expert e (mask) and the slot of
+  // e in each token's list (4 bits per token); a workgroup scan packs the experts in
+  // ascending id order
+  uint32_t mask = 0, jt = 0;
+  if (tid < kMaxExperts) {
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j)
+        if (j < k && s_ids[t][j] == tid) {
+          mask |= 1u << t;
+          jt |= (uint32_t)j << (4 * t);
+        }
+  }
+  const bool nz = tid < kMaxExperts && mask != 0;
+  const uint64_t bal = __ballot(nz);
+  const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                               __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+  if (lane == 0 && wave < 4) s_wtot[wave] = __popcll(bal);
+  __syncthreads();
+  int base = 0, nu = 0;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    base += v < wave ? s_wtot[v] : 0;
+    nu += s_wtot[v];
+  }
+  if (nz) {
+    s_list[base + before] = tid;
+    s_mask[base + before] = mask;
+    s_jtab[base + before] = jt;
+  }
+  if (tid == 0 && a.S) {
+    // the shared expert: every token, slot k
+    s_list[nu] = E;
+    s_mask[nu] = (1u << T) - 1;
+    uint32_t all = 0;
+    for (int t = 0; t < T; ++t) all |= (uint32_t)k << (4 * t);
+    s_jtab[nu] = all;
+  }
+  __syncthreads();
+  const int nunits = (nu + a.S) * (2 * kNB13);
+  // units u = w, w + G, ...: expert u / 32, W13 block (u / 2) % 16, half u % 2; wave v takes
+  // K steps 4v .. 4v+3 of the unit's 32 rows (lanes 0..31 gate rows, 32..63 up rows; lane:
+  // row (l % 32) / 2, K half l % 2), as in the decode kernel. The next unit's codes load
+  // while this one computes (past the last unit this unit is loaded again and unused).
+  const bool up = lane >= 32;
+  const int r16 = (lane & 31) >> 1, hh = lane & 1;
+  auto unit_load = [&](int u, uint4 (&c)[4], uint4 &sb) {
+    const int ex = u >> 5, b = (u >> 1) & 15, f = u & 1;
+    const size_t blk = (size_t)s_list[ex] * kNB13 + b;
+    const uint8_t *tq = a.wt.w13_t + (blk * kNS13 + 4 * wave) * 2048 + (up ? 1024 : 0) +
+                        512 * f + 16 * (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = *reinterpret_cast<const uint4 *>(tq + i * 2048);
+    sb = *reinterpret_cast<const uint4 *>(
+        a.wt.w13_tsb + (blk * (kNS13 / 4) + wave) * 512 + 8 * ((up ? 32 : 0) + 16 * f + r16));
+  };
+  const int G = gridDim.x;
+  uint4 c[4], sb, cn[4], sbn;
+  unit_load(min(w, nunits - 1), c, sb);
+  int par = 0;
+  for (int u = w; u < nunits; u += G) {
+    unit_load(min(u + G, nunits - 1), cn, sbn);
+    const int ex = u >> 5, b = (u >> 1) & 15, f = u & 1;
+    const uint32_t m = s_mask[ex], jt = s_jtab[ex];
+#pragma unroll
+    for (int t = 0; t < kSmallT; ++t) {
+      if ((m >> t) & 1) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int st = 4 * wave + i;
+          acc += group_dot(dot_codes(c[i], xs[t], 8 * st + 4 * hh), word_of(sb, i),
+                           xseg[t][2 * st + hh]);
+        }
+        acc = xor_sum<1>(acc);
+        if (hh == 0) red[par][t][wave * 32 + (up ? 16 : 0) + r16] = acc;
+      }
+    }
+    __syncthreads();
+    {
+      const int t = tid >> 4, r = tid & 15;
+      if (t < kSmallT && ((m >> t) & 1)) {
+        float gs = 0.f, us = 0.f;
+#pragma unroll
+        for (int v = 0; v < DT / 64; ++v) {
+          gs += red[par][t][v * 32 + r];
+          us += red[par][t][v * 32 + 16 + r];
+        }
+        const int j = (jt >> (4 * t)) & 15;
+        a.h[((size_t)t * (k + a.S) + j) * DI + 32 * b + 16 * f + r] = silu(gs) * us;
+      }
+    }
+    par ^= 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = cn[i];
+    sb = sbn;
   }
 }
 
 bool decode_gemv_supported(int H, int I, int E, int k, int S, bool int4) {
   return int4 && H == DH && I == DI && E <= 256 && k + S <= kSlots;
+}
+
+hipError_t launch_small_t(const DecodeArgs &a, hipStream_t s) {
+  MOE_LAUNCH("k_st_a", k_st_a, dim3(a.E), dim3(DT), 0, s, a);
+  MOE_LAUNCH("k_st_b", k_st_b, dim3(DWG), dim3(DT), 0, s, a);
+  MOE_LAUNCH("k_dec_c", k_dec_c, dim3(kDownWG, a.T), dim3(DT), 0, s, a);
+  return hipSuccess;
 }
 
 hipError_t launch_decode_gemv(const DecodeArgs &a, hipStream_t s) {

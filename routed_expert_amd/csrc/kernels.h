@@ -119,7 +119,9 @@ struct TokenArgs {
 };
 hipError_t launch_token_experts(const TokenArgs &a, hipStream_t s);
 
-// Batch-1 layer in three kernels (hidden 2048, intermediate 512, int4).
+// Batch-1 layer in three kernels (hidden 2048, intermediate 512, int4); the same kernels'
+// small-T variant takes T <= kSmallT tokens.
+constexpr int kSmallT = 8;
 struct DecodeArgs {
   const uint16_t *x;          // [H] bf16
   const float *router_w, *router_b;
@@ -128,8 +130,12 @@ struct DecodeArgs {
   uint16_t *y;                // [H]
   float *z;                   // [E] logits
   float *h;                   // [k+S, I] fp32
-  int32_t *sel_ids;           // [k] selected experts, rank order (largest logit first)
-  float *sel_z;               // [k] their logits
+  int32_t *sel_ids;           // [k] selected experts, rank order (largest logit first);
+                              // small-T: [T, k] in ascending id order
+  float *sel_z;               // [k] their logits; small-T: [T, k] their routing weights
+  int T;                      // tokens (small-T path; 1 for decode): x [T,H], z [T,E],
+                              // h [T,k+S,I], y and residual [T,H]
+  int sel_is_w;               // sel_z holds routing weights, not logits
   int H, I, E, k, S;
   // when set, the layer reads RMSNorm(x) (unit gain, rounded to bf16) instead of x; the
   // residual is still the caller's (un-normalised) pointer
@@ -138,6 +144,7 @@ struct DecodeArgs {
 };
 bool decode_gemv_supported(int H, int I, int E, int k, int S, bool int4);
 hipError_t launch_decode_gemv(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_small_t(const DecodeArgs &a, hipStream_t s);
 
 hipError_t launch_rmsnorm(const void *h, int64_t T, int H, float eps, bool bf16, void *out,
                           hipStream_t s);

@@ -84,7 +84,7 @@ moe_status check_layer(const moe_layer *L) {
 
 // Workspace layout: the batch-1 decode buffers first, then the T-dependent region.
 struct Plan {
-  size_t dec_logits, dec_ids, dec_z, dec_h;
+  size_t dec_logits, dec_ids, dec_z, dec_h, st_z, st_ids, st_w, st_h;
   size_t logits, logits2, planes, ids, w, blk, offsets, sorted, slot, slot_w, x16, tiles, ntiles,
       h, out;
   size_t total;
@@ -108,6 +108,12 @@ Plan make_plan(const moe_layer *L, int64_t T) {
   p.dec_ids = take(k * 4);
   p.dec_z = take(k * 4);
   p.dec_h = take((k + S) * I * 4);
+  // small-T path (2 .. kSmallT tokens)
+  const size_t Ts = Tn < (size_t)moe::kSmallT ? Tn : (size_t)moe::kSmallT;
+  p.st_z = take(Ts * E * 4);
+  p.st_ids = take(Ts * k * 4);
+  p.st_w = take(Ts * k * 4);
+  p.st_h = take(Ts * (k + S) * I * 4);
   const size_t tiles = (k * Tn + moe::kTileM - 1) / moe::kTileM + E +
                        (S ? (Tn + moe::kTileM - 1) / moe::kTileM : 0);
   p.max_tiles = (int)tiles;
@@ -399,9 +405,36 @@ moe_status moe_route(const moe_layer *layer, const void *x, int64_t T, const moe
 }
 
 // The layer for T >= 1 tokens after validation; p is the workspace plan for T tokens.
+static bool decode_fast(const moe_layer *layer);
+
 static moe_status prefill_impl(const moe_layer *layer, const void *x, int64_t T, void *y,
                                const void *residual, const moe_route_out *route_out, void *ws,
                                const Plan &p, hipStream_t s) {
+  if (!route_out && T <= moe::kSmallT && decode_fast(layer)) {
+    // a few tokens: the decode kernels' three-kernel structure, weights read once per
+    // selected expert (no routing tables, tile map or grouped GEMMs)
+    moe::DecodeArgs da{};
+    da.x = static_cast<const uint16_t *>(x);
+    da.router_w = layer->router_w;
+    da.router_b = layer->router_b;
+    da.wt = weights_of(layer);
+    da.residual = static_cast<const uint16_t *>(residual);
+    da.y = static_cast<uint16_t *>(y);
+    da.z = at<float>(ws, p.st_z);
+    da.h = at<float>(ws, p.st_h);
+    da.sel_ids = at<int32_t>(ws, p.st_ids);
+    da.sel_z = at<float>(ws, p.st_w);
+    da.sel_is_w = 1;
+    da.T = (int)T;
+    da.H = layer->hidden;
+    da.I = layer->inter;
+    da.E = layer->n_experts;
+    da.k = layer->top_k;
+    da.S = layer->n_shared;
+    const hipError_t e = moe::launch_small_t(da, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_prefill (small T)");
+    return MOE_OK;
+  }
   moe::RouteArgs ra = route_args(layer, x, T);
   route_targets(ra, p, ws, route_out);
   const bool int4 = layer->w_format == MOE_W_INT4_G64;
@@ -517,6 +550,7 @@ static moe_status decode_impl(const moe_layer *layer, const void *x, void *y,
     da.E = layer->n_experts;
     da.k = layer->top_k;
     da.S = layer->n_shared;
+    da.T = 1;
     da.norm = norm_eps >= 0.f;
     da.eps = norm_eps;
     if ((e = moe::launch_decode_gemv(da, s)) != hipSuccess) return hip_fail(e, "moe_decode");
