@@ -506,9 +506,9 @@ __global__ __launch_bounds__(DT) void k_st_b(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) f16x2_t xs[kSmallT][DH / 2];
   __shared__ float xseg[kSmallT][DH / 32];
   __shared__ __attribute__((aligned(16))) uint64_t s_topk[kSmallT][kTopkScratch];
-  __shared__ int s_ids[kSmallT][kMaxTopK];
   __shared__ int s_list[kMaxExperts + 1];
   __shared__ uint32_t s_mask[kMaxExperts + 1], s_jtab[kMaxExperts + 1];
+  __shared__ uint32_t m_raw[kMaxExperts], jt_raw[kMaxExperts];
   __shared__ int s_wtot[4];
   __shared__ float red[2][kSmallT][DT / 64 * 32];
   const int w = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -552,13 +552,18 @@ __global__ __launch_bounds__(DT) void k_st_b(DecodeArgs a) {
     sum = xor_sum<2>(sum);
     if ((c & 3) == 0 && live) xseg[ti][c >> 2] = sum;
   }
-  // top-k: wave t < T takes token t (ids in ascending order, weights from the softmax)
+  if (tid < kMaxExperts) m_raw[tid] = jt_raw[tid] = 0;
+  __syncthreads();
+  // top-k: wave t < T takes token t (ids in ascending order, weights from the softmax);
+  // each winner marks its expert with the token's bit and its slot (LDS bitwise ORs, so
+  // the result does not depend on their order)
   if (wave < T) {
     int id, pos;
     float wt;
     wave_topk(zv, E, k, s_topk[wave], id, pos, wt);
     if (lane < k) {
-      s_ids[wave][pos] = id;
+      atomicOr(&m_raw[id], 1u << wave);
+      atomicOr(&jt_raw[id], (uint32_t)pos << (4 * wave));
       if (w == 0) {
         a.sel_ids[(size_t)wave * k + pos] = id;
         a.sel_z[(size_t)wave * k + pos] = wt;
@@ -566,19 +571,11 @@ __global__ __launch_bounds__(DT) void k_st_b(DecodeArgs a) {
     }
   }
   __syncthreads();
-  // the union: thread e < 256 gathers the tokens that chose expert e (mask) and the slot of
-  // e in each token's list (4 bits per token); a workgroup scan packs the experts in
-  // ascending id order
-  uint32_t mask = 0, jt = 0;
-  if (tid < kMaxExperts) {
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j)
-        if (j < k && s_ids[t][j] == tid) {
-          mask |= 1u << t;
-          jt |= (uint32_t)j << (4 * t);
-        }
-  }
+  // the union: expert e's token mask and its slot in each token's list (4 bits per
+  // token); a workgroup scan packs the chosen experts in ascending id order (after the
+  // shared expert)
+  const uint32_t mask = tid < kMaxExperts ? m_raw[tid] : 0u;
+  const uint32_t jt = tid < kMaxExperts ? jt_raw[tid] : 0u;
   const bool nz = tid < kMaxExperts && mask != 0;
   const uint64_t bal = __ballot(nz);
   const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
@@ -591,53 +588,58 @@ __global__ __launch_bounds__(DT) void k_st_b(DecodeArgs a) {
     base += v < wave ? s_wtot[v] : 0;
     nu += s_wtot[v];
   }
+  // the shared expert (every token, slot k) comes first: its units carry all T tokens, so
+  // they start with everyone else's first units instead of trailing at the end
+  const int sh = a.S;
   if (nz) {
-    s_list[base + before] = tid;
-    s_mask[base + before] = mask;
-    s_jtab[base + before] = jt;
+    s_list[sh + base + before] = tid;
+    s_mask[sh + base + before] = mask;
+    s_jtab[sh + base + before] = jt;
   }
-  if (tid == 0 && a.S) {
-    // the shared expert: every token, slot k
-    s_list[nu] = E;
-    s_mask[nu] = (1u << T) - 1;
+  if (tid == 0 && sh) {
+    s_list[0] = E;
+    s_mask[0] = (1u << T) - 1;
     uint32_t all = 0;
     for (int t = 0; t < T; ++t) all |= (uint32_t)k << (4 * t);
-    s_jtab[nu] = all;
+    s_jtab[0] = all;
   }
   __syncthreads();
   const int nunits = (nu + a.S) * (2 * kNB13);
   // units u = w, w + G, ...: expert u / 32, W13 block (u / 2) % 16, half u % 2; wave v takes
   // K steps 4v .. 4v+3 of the unit's 32 rows (lanes 0..31 gate rows, 32..63 up rows; lane:
-  // row (l % 32) / 2, K half l % 2), as in the decode kernel. The next unit's codes load
-  // while this one computes (past the last unit this unit is loaded again and unused).
+  // row (l % 32) / 2, K half l % 2), as in the decode kernel.
   const bool up = lane >= 32;
   const int r16 = (lane & 31) >> 1, hh = lane & 1;
-  auto unit_load = [&](int u, uint4 (&c)[4], uint4 &sb) {
+  struct Unit {
+    uint4 c0, c1, c2, c3, sb;
+  };
+  auto unit_load = [&](int u) {
     const int ex = u >> 5, b = (u >> 1) & 15, f = u & 1;
     const size_t blk = (size_t)s_list[ex] * kNB13 + b;
     const uint8_t *tq = a.wt.w13_t + (blk * kNS13 + 4 * wave) * 2048 + (up ? 1024 : 0) +
                         512 * f + 16 * (lane & 31);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) c[i] = *reinterpret_cast<const uint4 *>(tq + i * 2048);
-    sb = *reinterpret_cast<const uint4 *>(
+    Unit d;
+    d.c0 = *reinterpret_cast<const uint4 *>(tq);
+    d.c1 = *reinterpret_cast<const uint4 *>(tq + 2048);
+    d.c2 = *reinterpret_cast<const uint4 *>(tq + 2 * 2048);
+    d.c3 = *reinterpret_cast<const uint4 *>(tq + 3 * 2048);
+    d.sb = *reinterpret_cast<const uint4 *>(
         a.wt.w13_tsb + (blk * (kNS13 / 4) + wave) * 512 + 8 * ((up ? 32 : 0) + 16 * f + r16));
+    return d;
   };
-  const int G = gridDim.x;
-  uint4 c[4], sb, cn[4], sbn;
-  unit_load(min(w, nunits - 1), c, sb);
   int par = 0;
-  for (int u = w; u < nunits; u += G) {
-    unit_load(min(u + G, nunits - 1), cn, sbn);
+  auto unit_compute = [&](int u, const Unit &d) {
     const int ex = u >> 5, b = (u >> 1) & 15, f = u & 1;
     const uint32_t m = s_mask[ex], jt = s_jtab[ex];
-#pragma unroll
+    const uint4 cc[4] = {d.c0, d.c1, d.c2, d.c3};
+#pragma unroll 1
     for (int t = 0; t < kSmallT; ++t) {
       if ((m >> t) & 1) {
         float acc = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int st = 4 * wave + i;
-          acc += group_dot(dot_codes(c[i], xs[t], 8 * st + 4 * hh), word_of(sb, i),
+          acc += group_dot(dot_codes(cc[i], xs[t], 8 * st + 4 * hh), word_of(d.sb, i),
                            xseg[t][2 * st + hh]);
         }
         acc = xor_sum<1>(acc);
@@ -645,23 +647,33 @@ __global__ __launch_bounds__(DT) void k_st_b(DecodeArgs a) {
       }
     }
     __syncthreads();
-    {
-      const int t = tid >> 4, r = tid & 15;
-      if (t < kSmallT && ((m >> t) & 1)) {
-        float gs = 0.f, us = 0.f;
+    const int t = tid >> 4, r = tid & 15;
+    if (t < kSmallT && ((m >> t) & 1)) {
+      float gs = 0.f, us = 0.f;
 #pragma unroll
-        for (int v = 0; v < DT / 64; ++v) {
-          gs += red[par][t][v * 32 + r];
-          us += red[par][t][v * 32 + 16 + r];
-        }
-        const int j = (jt >> (4 * t)) & 15;
-        a.h[((size_t)t * (k + a.S) + j) * DI + 32 * b + 16 * f + r] = silu(gs) * us;
+      for (int v = 0; v < DT / 64; ++v) {
+        gs += red[par][t][v * 32 + r];
+        us += red[par][t][v * 32 + 16 + r];
       }
+      const int j = (jt >> (4 * t)) & 15;
+      a.h[((size_t)t * (k + a.S) + j) * DI + 32 * b + 16 * f + r] = silu(gs) * us;
     }
     par ^= 1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) c[i] = cn[i];
-    sb = sbn;
+  };
+  // units run two ahead: while unit u computes, the loads of units u + G and u + 2G are in
+  // flight (past the last unit the last one is loaded again, unused). Three register sets,
+  // each reloaded right after its unit is computed, so no set is ever copied (a copy would
+  // wait for its loads).
+  const int G = gridDim.x, last = nunits - 1;
+  Unit d0 = unit_load(min(w, last)), d1 = unit_load(min(w + G, last)),
+       d2 = unit_load(min(w + 2 * G, last));
+  for (int u = w; u < nunits; u += 3 * G) {
+    unit_compute(u, d0);
+    d0 = unit_load(min(u + 3 * G, last));
+    if (u + G < nunits) unit_compute(u + G, d1);
+    d1 = unit_load(min(u + 4 * G, last));
+    if (u + 2 * G < nunits) unit_compute(u + 2 * G, d2);
+    d2 = unit_load(min(u + 5 * G, last));
   }
 }
 
