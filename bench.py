@@ -15,7 +15,8 @@ dominant kernel's roofline (durations from HIP events on its stream) and the CPU
 oracle's throughput on a bounded sample of the decode tokens.
 
 Also: a stack of 40 such layers (pre-norm residual blocks) with batch-1 decode of 256
-tokens and a 32,768-token prompt in chunks of 4096 tokens.
+tokens and a 32,768-token prompt in chunks of 4096 tokens; and moe_prefill with 2, 4 and
+8 tokens (the small-T kernels) over the 20 layer copies.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-prefill]
                        [--no-stack]
@@ -253,6 +254,56 @@ def bench_prefill(moe, torch, synth, dev, layer_host, reps=20):
 STACK_LAYERS, STACK_DECODE_TOKENS, STACK_PROMPT, STACK_CHUNK = 40, 256, 32768, 4096
 
 
+def bench_small_t(moe, torch, synth, dev, Ts=(2, 4, 8), calls=40, reps=10):
+    """moe_prefill with a few tokens (no routing output requested: the small-T kernels),
+    graph replays over the 20 cache-cold layer copies. Bytes per call: the router, every
+    expert in the union of the tokens' selections (read once) plus the shared expert, x, y;
+    the union size comes from the GPU's own routing of the same tokens."""
+    import numpy as np
+    layers = gpu_copies(moe, torch, synth, dev)
+    res = {}
+    for T in Ts:
+        x = moe.bf16_from_bits(synth.prefill_x(T, seed=3), dev)
+        ws = moe.workspace(layers[0], T, dev)
+        y = torch.empty_like(x)
+
+        def call(i):
+            moe.moe_prefill(layers[i % N_COPIES], x, y=y, ws=ws)
+
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(3):
+                call(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(calls):
+                call(i)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) * 1000 / (reps * calls)
+        del g
+        # union of the experts these tokens select (same layer copy 0 routing)
+        buf = moe.route_buffers(layers[0], T, dev)
+        moe.moe_route(layers[0], x, out=buf)
+        torch.cuda.synchronize()
+        n_union = len(np.unique(buf["topk_ids"].cpu().numpy()))
+        nbytes = E * H * 4 + (n_union + S) * sum(expert_bytes()) + 2 * T * H * 2
+        res[str(T)] = {"us_per_call": us, "tokens_per_s": T / (us * 1e-6),
+                       "union_experts": n_union, "bytes_per_call": nbytes,
+                       "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    return res
+
+
 def bench_stack(moe, torch, synth, dev, eps=1e-6):
     """40 layers of the decode shape (18.3 GB of int4 weights, plus their tiled copies)
     resident in HBM, as pre-norm residual blocks: batch-1 decode of 256 tokens, and a
@@ -435,6 +486,8 @@ def main():
         out["prefill_skewed"] = bench_prefill(moe, torch, synth, dev, synth.skewed_layer(0))
     if not args.no_stack:
         out["stack_40"] = bench_stack(moe, torch, synth, dev)
+    if not args.no_prefill:
+        out["small_T"] = bench_small_t(moe, torch, synth, dev)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(synth)
     print(json.dumps(out), flush=True)
