@@ -46,14 +46,14 @@ def check(layer, xb, y, min_sure=None):
     assert rel_err(got[sure], ref[sure]) <= BF16_TOL, rel_err(got[sure], ref[sure])
 
 
-@pytest.mark.parametrize("T", [2, 3, 5, 8])
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 8])
 def test_small_t_full_width(M, big, T):
     layer, dl = big
     announce(f"moe_prefill int4 H=2048 E=256 k=8 S=1 T={T}")
     xb = synth.prefill_x(T, seed=40 + T)
     y = M.moe_prefill(dl, M.bf16_from_bits(xb, DEV))
     torch.cuda.synchronize()
-    check(layer, xb, y)
+    check(layer, xb, y, min_sure=T if T == 1 else None)
 
 
 def test_small_t_residual_alias_and_determinism(M, big):
