@@ -12,7 +12,8 @@
  *     are DEVICE pointers; moe_layer / moe_route_out structs and `bytes` are HOST.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Calls
  *     only enqueue work on it: they never synchronise the host and never copy device
- *     memory to the host, so a whole layer can be captured into a HIP graph.
+ *     memory to the host, so a whole layer can be captured into a HIP graph (the one
+ *     exception is the host-routing ablation, which exists to measure exactly that).
  *   - The caller owns all memory (inputs, outputs, weights, workspace). The library
  *     never allocates or frees device memory.
  *   - Errors are detected on the host before anything is enqueued (except MOE_E_HIP,
@@ -151,6 +152,45 @@ moe_status moe_prefill(const moe_layer *layer, const void *x, int64_t T, void *y
  * x, y, residual: [1, H] of act_dtype; residual may be NULL and may alias y. */
 moe_status moe_decode(const moe_layer *layer, const void *x, void *y, const void *residual,
                       void *ws, size_t ws_bytes, void *stream);
+
+/* Ablations of the prefill path: the rejected designs of "Optimizing On-Device Inference
+ * for Apple Silicon", section "Optimize sparse expert computation", rebuilt on the same
+ * kernels so that each differs from the product path in one mechanism only. Every variant
+ * computes exactly what moe_prefill computes for T > 8 (the grouped-GEMM path, which the
+ * variants take for every T), so y is bit-identical to it:
+ *   MOE_ABL_NONE              the grouped-GEMM path unchanged (the control)
+ *   MOE_ABL_SEPARATE_DEQUANT  "Dequantize weights during matrix multiplication", its
+ *       ablation: a separate pass expands the int4 weights of every expert that received
+ *       rows (and the shared expert) into fp16 arrays in the workspace, and the GEMMs read
+ *       those back instead of dequantising tiles on chip
+ *   MOE_ABL_HOST_ROUTING      "Keep expert routing on the GPU", its ablation: the GPU stops
+ *       after the router and top-k; the host reads the ids back, builds the histogram,
+ *       offsets, per-block bases and tile map, uploads them and only then enqueues the
+ *       scatter and the GEMMs. This variant synchronises `stream` twice and copies
+ *       between host and device, unlike every other call, so it cannot be captured
+ *   MOE_ABL_TILE_64           "Match tile size to expert load", its ablation: tiles of at
+ *       most 64 rows, whatever the load
+ *   MOE_ABL_FIXED_TILE        tiles of 128 rows of which every one multiplies all 128 rows'
+ *       worth of blocks, however few rows it holds (no load adaptivity at all)
+ *   MOE_ABL_TILE_128          tiles of at most 128 rows whatever the load (the per-call
+ *       height choice off; each expert's last tile still only as high as its rows need)
+ * Int4 layers only (MOE_E_UNSUPPORTED otherwise), tiled weights required. Arguments as
+ * moe_prefill; the workspace must hold moe_ablation_workspace_bytes for the same variant
+ * (for MOE_ABL_SEPARATE_DEQUANT that includes 2 bytes per expert weight). */
+typedef enum {
+  MOE_ABL_NONE = 0,
+  MOE_ABL_SEPARATE_DEQUANT = 1,
+  MOE_ABL_HOST_ROUTING = 2,
+  MOE_ABL_TILE_64 = 3,
+  MOE_ABL_FIXED_TILE = 4,
+  MOE_ABL_TILE_128 = 5
+} moe_ablation;
+
+moe_status moe_ablation_workspace_bytes(const moe_layer *layer, int64_t max_tokens,
+                                        int32_t variant, size_t *bytes);
+moe_status moe_prefill_ablation(const moe_layer *layer, int32_t variant, const void *x, int64_t T,
+                                void *y, const void *residual, void *ws, size_t ws_bytes,
+                                void *stream);
 
 /* Workspace bytes for moe_stack_forward with chunks of up to chunk_tokens rows. */
 moe_status moe_stack_workspace_bytes(const moe_layer *layers, int32_t n_layers,

@@ -12,7 +12,13 @@ constexpr int kGroup = 64;        // int4 quantisation group (weights per scale/
 constexpr int kRouteBlock = 64;   // tokens per routing block (histogram granularity)
 constexpr int kMaxTopK = 8;
 constexpr int kMaxExperts = 256;
-constexpr int kTileM = 128;       // rows of a grouped-GEMM tile
+constexpr int kTileM = 128;       // rows of a grouped-GEMM tile (the tallest)
+constexpr int kGemmSlots = 512;   // grouped-GEMM workgroups resident at once (256 CUs x 2)
+// 32-row blocks per resident gate/up workgroup slot of one N tile (I / 128 N tiles)
+inline int gemm_fill(int I) {
+  const int n = I >= 256 ? I / 128 : 1;
+  return kGemmSlots / n > 0 ? kGemmSlots / n : 1;
+}
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));

@@ -50,6 +50,12 @@ constexpr int kStageBytes = kABytes + kBBytes;
 // 4 groups x {scale, bias}) into a 2-slot ring.
 constexpr int kSSlot = 4 * 1024;
 constexpr int kSmemBytes = kStages * kStageBytes + 2 * kSSlot;  // 80 KB: two workgroups per CU
+// Expanded-weight variant (separate dequantisation pass, an ablation): each wave's B operand
+// of a step is 8 KB of fp16 instead of 2 KB of codes, so a stage is 48 KB and the 144 KB
+// ring leaves room for one workgroup per CU.
+constexpr int kXBBytes = 4 * 8 * 1024;
+constexpr int kXStageBytes = kABytes + kXBBytes;
+constexpr int kXSmemBytes = kStages * kXStageBytes;
 }  // namespace
 
 MOE_DEV f16x2_t f16_pair_from_bf16(uint16_t v) {
@@ -65,9 +71,13 @@ MOE_DEV void wait_vmcnt() {
 // One tile: rows [row0, row0 + nvalid) of group e, weight rows of N tile n_tile. MB is the
 // number of 32-row blocks holding valid rows (1..4); blocks past them are neither loaded nor
 // multiplied, so a group's last, partial tile costs MFMA work in proportion to its rows.
-template <bool kGateUp, int MB>
+// kX: B operands come ready-made from the expanded fp16 weights (launch_expand) instead of
+// being dequantised from the codes; every other step is the same, and so are the results.
+template <bool kGateUp, int MB, bool kX>
 MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, int nvalid,
                           int n_tile) {
+  constexpr int kSB = kX ? kXStageBytes : kStageBytes;  // bytes of one ring stage
+  constexpr int kLB = kX ? 8 : 2;  // B loads per wave and step (besides the scale blocks)
   const int gbase = a.offsets[e];
   const int slot0 = gbase + row0;
   const int K = kGateUp ? a.H : a.I;
@@ -106,6 +116,11 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
                       ((size_t)e * nb + blk) * ns * 2048 + 16 * lane;
   const uint16_t *tsb = (kGateUp ? a.wt.w13_tsb : a.wt.w2_tsb) +
                         ((size_t)e * nb + blk) * ns4 * 512 + 8 * lane;
+  // expanded weights: the same block's 8 KB of fp16 per K step, 1 KB per (column block,
+  // substep), lane l's 8 values at 16 l
+  const uint8_t *txq = kX ? reinterpret_cast<const uint8_t *>(kGateUp ? a.w13_x : a.w2_x) +
+                                ((size_t)e * nb + blk) * ns * 8192 + 16 * lane
+                          : nullptr;
 
   // The direct-to-LDS loads and the step barrier are issued as inline assembly: the
   // compiler cannot tell the ring stages apart and would wait for every load in flight
@@ -123,20 +138,27 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %0, off"         \
                :: "v"(gptr), "s"(lds) : "memory", "m0")
   // issue the direct-to-LDS loads of K step `step` (MB + 2 memory instructions per wave,
-  // one more on every fourth step, which fetches the scales and biases of four steps)
+  // one more on every fourth step, which fetches the scales and biases of four steps;
+  // expanded weights: MB + 8)
 #define MOE_ISSUE(step)                                                                 \
   do {                                                                                  \
-    const uint32_t base_ = smem_lds + ((step) % kStages) * kStageBytes;                 \
+    const uint32_t base_ = smem_lds + ((step) % kStages) * kSB;                         \
     const int k0_ = (step) * BK;                                                        \
     _Pragma("unroll") for (int j = 0; j < MB; ++j)                                      \
       MOE_DMA16(asrc[j] + k0_, base_ + (wave_u + 4 * j) * 1024);                        \
-    const uint32_t bb_ = base_ + kABytes + wave_u * 2048;                               \
-    MOE_DMA16(tq + (size_t)(step) * 2048, bb_);                                         \
-    MOE_DMA16(tq + (size_t)(step) * 2048 + 1024, bb_ + 1024);                           \
-    if (((step) & 3) == 0) {                                                            \
-      const uint32_t sb_ =                                                              \
-          smem_lds + kStages * kStageBytes + (((step) >> 2) & 1) * kSSlot + wave_u * 1024; \
-      MOE_DMA16(tsb + (size_t)((step) >> 2) * 512, sb_);                                \
+    if constexpr (kX) {                                                                 \
+      const uint32_t bb_ = base_ + kABytes + wave_u * 8192;                             \
+      _Pragma("unroll") for (int q = 0; q < 8; ++q)                                     \
+        MOE_DMA16(txq + (size_t)(step) * 8192 + q * 1024, bb_ + q * 1024);              \
+    } else {                                                                            \
+      const uint32_t bb_ = base_ + kABytes + wave_u * 2048;                             \
+      MOE_DMA16(tq + (size_t)(step) * 2048, bb_);                                       \
+      MOE_DMA16(tq + (size_t)(step) * 2048 + 1024, bb_ + 1024);                         \
+      if (((step) & 3) == 0) {                                                          \
+        const uint32_t sb_ = smem_lds + kStages * kStageBytes + (((step) >> 2) & 1) * kSSlot + \
+                             wave_u * 1024;                                             \
+        MOE_DMA16(tsb + (size_t)((step) >> 2) * 512, sb_);                              \
+      }                                                                                 \
     }                                                                                   \
   } while (0)
 
@@ -154,7 +176,14 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
   // waves load together, wait for the step barrier.
   uint32_t w0[4], w1[4];
   f16x2_t s0, b0, s1, b1, s0q, s1q;
+  uint4 bx[8];  // expanded weights: the step's B operands, [column block][substep]
   const int bn = lane & 31, bh = lane >> 5;
+#define MOE_READ_BX(step)                                                               \
+  do {                                                                                  \
+    const uint8_t *bsrc_ = smem + ((step) % kStages) * kSB + kABytes + wave * 8192 + 16 * lane; \
+    _Pragma("unroll") for (int q = 0; q < 8; ++q)                                       \
+      bx[q] = *reinterpret_cast<const uint4 *>(bsrc_ + q * 1024);                       \
+  } while (0)
 #define MOE_READ_B(step)                                                                \
   do {                                                                                  \
     const uint8_t *bsrc_ = smem + ((step) % kStages) * kStageBytes + kABytes + wave * 2048 + \
@@ -179,20 +208,34 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   MOE_ISSUE(0);
   if (nsteps > 1) MOE_ISSUE(1);
-  // step 0's own loads: everything after them is step 1's (MB + 2 loads, step 1 is odd)
+  // step 0's own loads: everything after them is step 1's (MB + kLB loads, step 1 is odd)
   if (nsteps > 1)
-    wait_vmcnt<MB + 2>();
+    wait_vmcnt<MB + kLB>();
   else
     wait_vmcnt<0>();
-  MOE_READ_B(0);
-  f16x8_t bc0 = __builtin_bit_cast(f16x8_t, dequant8_pk_q(w0[0], s0, s0q, b0));
-  f16x8_t bc1 = __builtin_bit_cast(f16x8_t, dequant8_pk_q(w1[0], s1, s1q, b1));
+  // B operands of substep kk of the step whose codes (or expanded weights) are loaded
+#define MOE_B_OPS(kk)                                                                   \
+  do {                                                                                  \
+    if constexpr (kX) {                                                                 \
+      bc0 = __builtin_bit_cast(f16x8_t, bx[(kk)]);                                      \
+      bc1 = __builtin_bit_cast(f16x8_t, bx[4 + (kk)]);                                  \
+    } else {                                                                            \
+      bc0 = __builtin_bit_cast(f16x8_t, dequant8_pk_q(w0[(kk)], s0, s0q, b0));          \
+      bc1 = __builtin_bit_cast(f16x8_t, dequant8_pk_q(w1[(kk)], s1, s1q, b1));          \
+    }                                                                                   \
+  } while (0)
+  f16x8_t bc0, bc1;
+  if constexpr (kX)
+    MOE_READ_BX(0);
+  else
+    MOE_READ_B(0);
+  MOE_B_OPS(0);
   for (int st = 0; st < nsteps; ++st) {
     // every wave's loads of step st have landed (each wave waited for its own before its
     // mid-step read of step st's codes), and every wave is done with the stage step st+2
     // will reuse
     asm volatile("s_barrier" ::: "memory");
-    const uint8_t *arow = smem + (st % kStages) * kStageBytes + arow_l * 128;
+    const uint8_t *arow = smem + (st % kStages) * kSB + arow_l * 128;
     // A fragments are double-buffered: substep kk+1's are read while kk's MFMAs run
     f16x8_t av[2][MB];
 #pragma unroll
@@ -214,34 +257,39 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
       if (kk == 0 && st + 2 < nsteps) MOE_ISSUE(st + 2);
       if (kk < 3) {
         // next substep's weights while the MFMAs above run
-        bc0 = __builtin_bit_cast(f16x8_t, dequant8_pk_q(w0[kk + 1], s0, s0q, b0));
-        bc1 = __builtin_bit_cast(f16x8_t, dequant8_pk_q(w1[kk + 1], s1, s1q, b1));
+        MOE_B_OPS(kk + 1);
         // A wave issues in order: interleave the dequantisation (and the next fragments'
         // LDS reads) between the MFMAs so the vector ALU works in the matrix unit's shadow
         // instead of after the last MFMA of the substep.
+        if constexpr (!kX) {
 #pragma unroll
-        for (int i = 0; i < 2 * MB; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // 1 MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, (40 + 2 * MB - 1) / (2 * MB), 0);  // VALU
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                   // 1 LDS read
+          for (int i = 0; i < 2 * MB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // 1 MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, (40 + 2 * MB - 1) / (2 * MB), 0);  // VALU
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                   // 1 LDS read
+          }
         }
       } else if (st + 1 < nsteps) {
         // the next step's codes and its first substep's weights, before its barrier, once
         // this wave's loads of step st+1 have landed (only step st+2's are younger)
         if (st + 2 < nsteps) {
-          if (((st + 2) & 3) == 0)
+          if (!kX && ((st + 2) & 3) == 0)
             wait_vmcnt<MB + 3>();
           else
-            wait_vmcnt<MB + 2>();
+            wait_vmcnt<MB + kLB>();
         } else {
           wait_vmcnt<0>();
         }
-        MOE_READ_B(st + 1);
-        bc0 = __builtin_bit_cast(f16x8_t, dequant8_pk_q(w0[0], s0, s0q, b0));
-        bc1 = __builtin_bit_cast(f16x8_t, dequant8_pk_q(w1[0], s1, s1q, b1));
+        if constexpr (kX)
+          MOE_READ_BX(st + 1);
+        else
+          MOE_READ_B(st + 1);
+        MOE_B_OPS(0);
       }
     }
   }
+#undef MOE_B_OPS
+#undef MOE_READ_BX
 #undef MOE_READ_B
 #undef MOE_ISSUE
 #undef MOE_DMA16
@@ -298,10 +346,8 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
   }
 }
 
-template <bool kGateUp>
-__global__ __launch_bounds__(256, 2) void k_grouped(GroupedArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
-
+template <bool kGateUp, bool kX>
+MOE_DEV void grouped_body(const GroupedArgs &a, uint8_t *smem) {
   // XCD-aware tile order: workgroup ids are dealt round-robin over the 8 XCDs; this map
   // gives each XCD all N tiles of one M tile back to back, so the activation rows of a
   // tile are fetched into that XCD's L2 once.
@@ -310,14 +356,66 @@ __global__ __launch_bounds__(256, 2) void k_grouped(GroupedArgs a) {
   const int n_tile = j % nN, m_tile = (j / nN) * 8 + xcd;
   if (m_tile >= *a.n_tiles) return;
   const int2 tile = a.tiles[m_tile];
-  const int e = tile.x, row0 = tile.y;
-  const int nvalid = min(BM, a.offsets[e + 1] - a.offsets[e] - row0);
-  switch ((nvalid + 31) >> 5) {
-    case 1: grouped_tile<kGateUp, 1>(a, smem, e, row0, nvalid, n_tile); break;
-    case 2: grouped_tile<kGateUp, 2>(a, smem, e, row0, nvalid, n_tile); break;
-    case 3: grouped_tile<kGateUp, 3>(a, smem, e, row0, nvalid, n_tile); break;
-    default: grouped_tile<kGateUp, 4>(a, smem, e, row0, nvalid, n_tile); break;
+  const int e = tile.x & 0xFFFF, row0 = tile.y, nvalid = tile.x >> 16;
+  // load-adaptive height: only the 32-row blocks that hold rows (all four when fixed)
+  switch (a.fixed_mb ? 4 : (nvalid + 31) >> 5) {
+    case 1: grouped_tile<kGateUp, 1, kX>(a, smem, e, row0, nvalid, n_tile); break;
+    case 2: grouped_tile<kGateUp, 2, kX>(a, smem, e, row0, nvalid, n_tile); break;
+    case 3: grouped_tile<kGateUp, 3, kX>(a, smem, e, row0, nvalid, n_tile); break;
+    default: grouped_tile<kGateUp, 4, kX>(a, smem, e, row0, nvalid, n_tile); break;
   }
+}
+
+template <bool kGateUp>
+__global__ __launch_bounds__(256, 2) void k_grouped(GroupedArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+  grouped_body<kGateUp, false>(a, smem);
+}
+
+template <bool kGateUp>
+__global__ __launch_bounds__(256, 1) void k_grouped_x(GroupedArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kXSmemBytes];
+  grouped_body<kGateUp, true>(a, smem);
+}
+
+// ---- separate dequantisation pass (ablation) -------------------------------------------
+// One workgroup per (64-row block, K step) of one expert: thread (kk, l) expands the code
+// word of substep kk of lane l for both column blocks with the same packed dequantisation
+// the GEMM runs in registers, so the expanded operands are bit-identical to the fused ones.
+// Experts that received no rows are skipped (the shared expert always has T rows).
+template <bool kGateUp>
+__global__ __launch_bounds__(256) void k_expand(GroupedArgs a) {
+  const int e = blockIdx.y;
+  if (e < a.E && a.offsets[e + 1] == a.offsets[e]) return;
+  const int K = kGateUp ? a.H : a.I;
+  const int nb = kGateUp ? 2 * a.I / 64 : a.H / 64;
+  const int ns = K / BK, ns4 = (ns + 3) / 4;
+  const int blk = blockIdx.x / ns, st = blockIdx.x % ns;
+  const int kk = threadIdx.x >> 6, lane = threadIdx.x & 63, bn = lane & 31, bh = lane >> 5;
+  const uint8_t *tq = (kGateUp ? a.wt.w13_t : a.wt.w2_t) +
+                      (((size_t)e * nb + blk) * ns + st) * 2048 + 32 * bn + 16 * bh + 4 * kk;
+  const uint16_t *tsb = (kGateUp ? a.wt.w13_tsb : a.wt.w2_tsb) +
+                        (((size_t)e * nb + blk) * ns4 + st / 4) * 512 + 8 * bn + 2 * (st & 3);
+  uint16_t *dst = const_cast<uint16_t *>(kGateUp ? a.w13_x : a.w2_x) +
+                  (((size_t)e * nb + blk) * ns + st) * 4096 + kk * 512 + 8 * lane;
+  const f16x2_t q16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const uint32_t w = *reinterpret_cast<const uint32_t *>(tq + c * 1024);
+    const f16x2_t sc = f16_pair_from_bf16(tsb[256 * c]), bi = f16_pair_from_bf16(tsb[256 * c + 1]);
+    *reinterpret_cast<uint4 *>(dst + c * 2048) = dequant8_pk_q(w, sc, sc * q16, bi);
+  }
+}
+
+size_t expanded_bytes(int n_mat, int rows, int K) { return (size_t)n_mat * rows * K * 2; }
+
+hipError_t launch_expand(const GroupedArgs &a, hipStream_t s) {
+  const unsigned ne = (unsigned)(a.E + (a.S ? 1 : 0));
+  MOE_LAUNCH("k_expand_gateup", (k_expand<true>), dim3((2 * a.I / 64) * (a.H / BK), ne),
+             dim3(256), 0, s, a);
+  MOE_LAUNCH("k_expand_down", (k_expand<false>), dim3((a.H / 64) * (a.I / BK), ne), dim3(256),
+             0, s, a);
+  return hipSuccess;
 }
 
 static unsigned grouped_grid(int max_tiles, int nN) {
@@ -326,14 +424,20 @@ static unsigned grouped_grid(int max_tiles, int nN) {
 }
 
 hipError_t launch_grouped_gateup(const GroupedArgs &a, hipStream_t s) {
-  MOE_LAUNCH("k_grouped_gateup", (k_grouped<true>),
-             dim3(grouped_grid(a.max_tiles, a.I / (BNW / 2))), dim3(256), 0, s, a);
+  const dim3 g(grouped_grid(a.max_tiles, a.I / (BNW / 2)));
+  if (a.w13_x)
+    MOE_LAUNCH("k_grouped_gateup_x", (k_grouped_x<true>), g, dim3(256), 0, s, a);
+  else
+    MOE_LAUNCH("k_grouped_gateup", (k_grouped<true>), g, dim3(256), 0, s, a);
   return hipSuccess;
 }
 
 hipError_t launch_grouped_down(const GroupedArgs &a, hipStream_t s) {
-  MOE_LAUNCH("k_grouped_down", (k_grouped<false>), dim3(grouped_grid(a.max_tiles, a.H / BNW)),
-             dim3(256), 0, s, a);
+  const dim3 g(grouped_grid(a.max_tiles, a.H / BNW));
+  if (a.w2_x)
+    MOE_LAUNCH("k_grouped_down_x", (k_grouped_x<false>), g, dim3(256), 0, s, a);
+  else
+    MOE_LAUNCH("k_grouped_down", (k_grouped<false>), g, dim3(256), 0, s, a);
   return hipSuccess;
 }
 

@@ -29,6 +29,7 @@ struct RouteArgs {
   const float *router_w, *router_b;
   int64_t T;
   int H, E, k, S;
+  int I = 0;              // expert intermediate size (sizes the tile-height choice)
   float *logits;          // [T, E] (decode: [E])
   float *logits2;         // [T, E] second half of the reduction (bf16 path)
   uint16_t *router_planes;  // [3, E, H] bf16 split of the router weights (bf16 path)
@@ -45,9 +46,16 @@ struct RouteArgs {
   uint16_t *x16;          // [T, H] fp16 copy of x for the MFMA path (or null)
   int2 *tiles;            // [max tiles]: (group, first row)
   int32_t *n_tiles;       // [1]
+  int tile_shift = 0;     // grouped-GEMM tile height: 0 = chosen from the load on the GPU,
+                          // else fixed at 2^tile_shift rows (5..7)
 };
 
 hipError_t launch_route_prefill(const RouteArgs &a, hipStream_t s);
+// the two halves of launch_route_prefill: router, top-k and the per-block histogram; then
+// the scan into offsets, block bases and tile map (skipped when the host wrote them) and
+// the stable scatter
+hipError_t launch_route_topk(const RouteArgs &a, hipStream_t s);
+hipError_t launch_route_group(const RouteArgs &a, bool scan, hipStream_t s);
 
 struct ExpertWeights {
   const uint8_t *w13_q, *w2_q;     // int4 codes, interchange layout
@@ -78,7 +86,7 @@ struct GroupedArgs {
   const int32_t *sorted_tok;  // [k T]
   const float *slot_w;        // [k T]
   const int32_t *offsets;     // [E + 2]
-  const int2 *tiles;
+  const int2 *tiles;          // (group | rows << 16, first row) per tile
   const int32_t *n_tiles;
   int max_tiles;
   int64_t T;
@@ -87,9 +95,20 @@ struct GroupedArgs {
   uint16_t *h16;   // [(k+S) T, I] fp16, slot order
   uint16_t *out;   // [(k+S) T, H] fp16, slot order: routed slots already scaled by the
                    // routing weight, then the shared expert's slots (token order)
+  // Ablation switches (moe_prefill_ablation); the product path leaves them unset.
+  int fixed_mb = 0;        // every tile multiplies all four 32-row blocks
+  int S = 0;               // shared experts (launch_expand only)
+  // fp16 weights expanded by launch_expand (tiled order, see expanded_bytes); when set, the
+  // GEMMs read them instead of the int4 codes
+  const uint16_t *w13_x = nullptr, *w2_x = nullptr;
 };
 hipError_t launch_grouped_gateup(const GroupedArgs &a, hipStream_t s);
 hipError_t launch_grouped_down(const GroupedArgs &a, hipStream_t s);
+// Separate dequantisation pass: every expert that received rows (and the shared expert)
+// expanded to fp16, [E+S][R/64][K/64][2 column blocks][4 substeps][64 lanes][8], the B
+// operand registers of the grouped GEMM in the order it reads them.
+size_t expanded_bytes(int n_mat, int rows, int K);
+hipError_t launch_expand(const GroupedArgs &a, hipStream_t s);
 
 // Weighted combine of the slot-ordered expert outputs back to token order.
 struct CombineArgs {

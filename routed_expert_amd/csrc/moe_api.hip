@@ -93,7 +93,23 @@ struct Plan {
 
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
-Plan make_plan(const moe_layer *L, int64_t T) {
+// Tiles of r rows that k routed assignments per token plus the shared expert's T rows can
+// need: every expert's rows in full tiles plus one partial tile.
+size_t tile_bound(const moe_layer *L, size_t Tn, size_t r) {
+  const size_t k = L->top_k, E = L->n_experts;
+  return (k * Tn + r - 1) / r + E + (L->n_shared ? (Tn + r - 1) / r : 0);
+}
+
+// Tile-map entries for tile height 2^tile_shift, or (0) the height the scan picks from the
+// load: 128 rows, or 64 / 32 rows only while the rows fill fewer than 4 * fill 32-row
+// blocks, and then there are fewer tiles than blocks.
+size_t max_tiles_for(const moe_layer *L, size_t Tn, int tile_shift) {
+  if (tile_shift > 0) return tile_bound(L, Tn, (size_t)1 << tile_shift);
+  const size_t small = std::min(tile_bound(L, Tn, 32), (size_t)4 * moe::gemm_fill(L->inter));
+  return std::max(tile_bound(L, Tn, moe::kTileM), small);
+}
+
+Plan make_plan(const moe_layer *L, int64_t T, int tile_shift = 0) {
   Plan p{};
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -114,8 +130,7 @@ Plan make_plan(const moe_layer *L, int64_t T) {
   p.st_ids = take(Ts * k * 4);
   p.st_w = take(Ts * k * 4);
   p.st_h = take(Ts * (k + S) * I * 4);
-  const size_t tiles = (k * Tn + moe::kTileM - 1) / moe::kTileM + E +
-                       (S ? (Tn + moe::kTileM - 1) / moe::kTileM : 0);
+  const size_t tiles = max_tiles_for(L, Tn, tile_shift);
   p.max_tiles = (int)tiles;
   p.logits = take(Tn * E * 4);
   p.logits2 = take(L->act_dtype == MOE_ACT_BF16 ? Tn * E * 4 : 0);
@@ -243,6 +258,7 @@ moe::RouteArgs route_args(const moe_layer *L, const void *x, int64_t T) {
   a.E = L->n_experts;
   a.k = L->top_k;
   a.S = L->n_shared;
+  a.I = L->inter;
   if (a.bf16 && L->router_planes) {
     a.router_planes = const_cast<uint16_t *>(static_cast<const uint16_t *>(L->router_planes));
     a.planes_ready = true;
@@ -404,6 +420,50 @@ moe_status moe_route(const moe_layer *layer, const void *x, int64_t T, const moe
   return MOE_OK;
 }
 
+// Grouped GEMMs of an int4 layer over the routing in ra (tables already on the device).
+static moe::GroupedArgs grouped_args(const moe_layer *layer, const moe::RouteArgs &ra, void *ws,
+                                     const Plan &p) {
+  moe::GroupedArgs ga{};
+  ga.x16 = ra.x16;
+  ga.sorted_tok = ra.sorted_tok;
+  ga.slot_w = ra.slot_w;
+  ga.offsets = ra.offsets;
+  ga.tiles = ra.tiles;
+  ga.n_tiles = ra.n_tiles;
+  ga.max_tiles = p.max_tiles;
+  ga.T = ra.T;
+  ga.H = layer->hidden;
+  ga.I = layer->inter;
+  ga.E = layer->n_experts;
+  ga.k = layer->top_k;
+  ga.S = layer->n_shared;
+  ga.wt = weights_of(layer);
+  ga.h16 = at<uint16_t>(ws, p.h);
+  ga.out = at<uint16_t>(ws, p.out);
+  return ga;
+}
+
+// gate/up GEMM, down GEMM and the weighted combine into y
+static moe_status run_grouped(const moe_layer *layer, const moe::GroupedArgs &ga,
+                              const moe::RouteArgs &ra, const void *residual, void *y,
+                              hipStream_t s) {
+  hipError_t e;
+  if ((e = moe::launch_grouped_gateup(ga, s)) != hipSuccess)
+    return hip_fail(e, "moe_prefill gate/up");
+  if ((e = moe::launch_grouped_down(ga, s)) != hipSuccess) return hip_fail(e, "moe_prefill down");
+  moe::CombineArgs ca{};
+  ca.out = ga.out;
+  ca.slot_of = ra.slot_of;
+  ca.residual = static_cast<const uint16_t *>(residual);
+  ca.y = static_cast<uint16_t *>(y);
+  ca.T = ra.T;
+  ca.H = layer->hidden;
+  ca.k = layer->top_k;
+  ca.S = layer->n_shared;
+  if ((e = moe::launch_combine(ca, s)) != hipSuccess) return hip_fail(e, "moe_prefill combine");
+  return MOE_OK;
+}
+
 // The layer for T >= 1 tokens after validation; p is the workspace plan for T tokens.
 static bool decode_fast(const moe_layer *layer);
 
@@ -446,36 +506,8 @@ static moe_status prefill_impl(const moe_layer *layer, const void *x, int64_t T,
   if (e != hipSuccess) return hip_fail(e, "moe_prefill route");
   const moe::ExpertWeights wt = weights_of(layer);
   if (int4) {
-    moe::GroupedArgs ga{};
-    ga.x16 = ra.x16;
-    ga.sorted_tok = ra.sorted_tok;
-    ga.slot_w = ra.slot_w;
-    ga.offsets = ra.offsets;
-    ga.tiles = ra.tiles;
-    ga.n_tiles = ra.n_tiles;
-    ga.max_tiles = p.max_tiles;
-    ga.T = T;
-    ga.H = layer->hidden;
-    ga.I = layer->inter;
-    ga.E = layer->n_experts;
-    ga.k = layer->top_k;
-    ga.wt = wt;
-    ga.h16 = at<uint16_t>(ws, p.h);
-    ga.out = at<uint16_t>(ws, p.out);
-    if ((e = moe::launch_grouped_gateup(ga, s)) != hipSuccess)
-      return hip_fail(e, "moe_prefill gate/up");
-    if ((e = moe::launch_grouped_down(ga, s)) != hipSuccess)
-      return hip_fail(e, "moe_prefill down");
-    moe::CombineArgs ca{};
-    ca.out = ga.out;
-    ca.slot_of = ra.slot_of;
-    ca.residual = static_cast<const uint16_t *>(residual);
-    ca.y = static_cast<uint16_t *>(y);
-    ca.T = T;
-    ca.H = layer->hidden;
-    ca.k = layer->top_k;
-    ca.S = layer->n_shared;
-    if ((e = moe::launch_combine(ca, s)) != hipSuccess) return hip_fail(e, "moe_prefill combine");
+    moe::GroupedArgs ga = grouped_args(layer, ra, ws, p);
+    return run_grouped(layer, ga, ra, residual, y, s);
   } else {
     moe::TokenArgs ta{};
     ta.bf16 = false;
@@ -515,6 +547,185 @@ moe_status moe_prefill(const moe_layer *layer, const void *x, int64_t T, void *y
   Plan p;
   if ((st = check_ws(layer, T, ws, ws_bytes, &p))) return st;
   return prefill_impl(layer, x, T, y, residual, route_out, ws, p, static_cast<hipStream_t>(stream));
+}
+
+// ---- ablations of the prefill path ------------------------------------------------------
+namespace {
+
+// Tile height of a variant: fixed (log2 rows) or 0, the product's choice from the load.
+int abl_shift(int variant) {
+  switch (variant) {
+    case MOE_ABL_TILE_64: return 6;
+    case MOE_ABL_TILE_128:
+    case MOE_ABL_FIXED_TILE: return 7;
+    default: return 0;
+  }
+}
+
+// Workspace of moe_prefill_ablation: a prefill plan sized for the variant's tiles, one
+// contiguous block of routing tables the host can upload in one copy, and (separate
+// dequantisation) the expanded fp16 weights.
+struct AblPlan {
+  Plan p;
+  size_t tab, tab_bytes, x13, x2, total;
+  size_t tab_offsets, tab_ntiles, tab_tiles, tab_blk;  // int32 word offsets inside tab
+};
+
+AblPlan abl_plan(const moe_layer *L, int64_t T, int variant) {
+  AblPlan a{};
+  a.p = make_plan(L, T, abl_shift(variant));
+  const size_t E = L->n_experts, Tn = (size_t)(T > 0 ? T : 1);
+  const size_t NB = (Tn + moe::kRouteBlock - 1) / moe::kRouteBlock;
+  a.tab_offsets = 0;
+  a.tab_ntiles = E + 2;
+  a.tab_tiles = (E + 3 + 1) & ~size_t(1);  // int2 entries start on an even word
+  a.tab_blk = a.tab_tiles + 2 * (size_t)a.p.max_tiles;
+  a.tab_bytes = (a.tab_blk + NB * E) * 4;
+  size_t off = a.p.total;
+  a.tab = off;
+  off += align256(a.tab_bytes);
+  a.x13 = a.x2 = off;
+  if (variant == MOE_ABL_SEPARATE_DEQUANT) {
+    const int n = L->n_experts + L->n_shared;
+    a.x13 = off;
+    off += align256(moe::expanded_bytes(n, 2 * L->inter, L->hidden));
+    a.x2 = off;
+    off += align256(moe::expanded_bytes(n, L->hidden, L->inter));
+  }
+  a.total = off;
+  return a;
+}
+
+// Host copy of the device scan (k_scan): per-block bases, offsets, the tile height (fixed
+// or chosen from the load by the same rule) and the tile map in the same order and
+// encoding (full tiles, the shared expert's full tiles, partial tiles by height, the
+// shared expert's partial tile), from the top-k ids read back from the device.
+int host_tables(const std::vector<int32_t> &ids, int64_t T, int E, int k, int S, int I,
+                int tile_shift, const AblPlan &ap, std::vector<int32_t> &tab) {
+  const int64_t NB = (T + moe::kRouteBlock - 1) / moe::kRouteBlock;
+  tab.assign(ap.tab_bytes / 4, 0);
+  int32_t *blk = tab.data() + ap.tab_blk;
+  std::vector<int64_t> run(E, 0);
+  for (int64_t b = 0; b < NB; ++b) {
+    int32_t *row = blk + b * E;
+    for (int e = 0; e < E; ++e) row[e] = (int32_t)run[e];
+    const int64_t t1 = std::min<int64_t>(T, (b + 1) * moe::kRouteBlock);
+    for (int64_t i = b * moe::kRouteBlock * k; i < t1 * k; ++i) {
+      if (ids[i] < 0 || ids[i] >= E) return -1;
+      ++run[ids[i]];
+    }
+  }
+  int32_t *off = tab.data() + ap.tab_offsets;
+  int64_t acc = 0;
+  for (int e = 0; e < E; ++e) {
+    off[e] = (int32_t)acc;
+    acc += run[e];
+  }
+  off[E] = (int32_t)acc;
+  off[E + 1] = (int32_t)(acc + (S ? T : 0));
+  if (tile_shift <= 0) {
+    int64_t nblk = S ? (T + 31) / 32 : 0;
+    for (int e = 0; e < E; ++e) nblk += (run[e] + 31) / 32;
+    const int fill = moe::gemm_fill(I);
+    tile_shift = nblk >= 4 * fill ? 7 : nblk >= 2 * fill ? 6 : 5;
+  }
+  const int64_t tr = int64_t(1) << tile_shift;
+  int2 *tiles = reinterpret_cast<int2 *>(tab.data() + ap.tab_tiles);
+  auto tile = [](int g, int64_t rows, int64_t r0) { return make_int2(g | (int)rows << 16, (int)r0); };
+  int n = 0;
+  for (int e = 0; e < E; ++e)
+    for (int64_t r = 0; r + tr <= run[e]; r += tr) tiles[n++] = tile(e, tr, r);
+  if (S)
+    for (int64_t r = 0; r + tr <= T; r += tr) tiles[n++] = tile(E, tr, r);
+  for (int mb = 4; mb >= 1; --mb)
+    for (int e = 0; e < E; ++e) {
+      const int64_t rem = run[e] % tr;
+      if (rem && (rem + 31) / 32 == mb) tiles[n++] = tile(e, rem, run[e] - rem);
+    }
+  if (S && T % tr) tiles[n++] = tile(E, T % tr, T - T % tr);
+  tab[ap.tab_ntiles] = n;
+  return n;
+}
+
+}  // namespace
+
+moe_status moe_ablation_workspace_bytes(const moe_layer *layer, int64_t max_tokens,
+                                        int32_t variant, size_t *bytes) {
+  g_err.clear();
+  moe_status st = check_layer(layer);
+  if (st) return st;
+  if (!bytes) return fail(MOE_E_INVALID, "bytes is NULL");
+  if (variant < MOE_ABL_NONE || variant > MOE_ABL_TILE_128)
+    return fail(MOE_E_INVALID, "unknown ablation %d", variant);
+  if (max_tokens < 0 || max_tokens > kMaxTokens)
+    return fail(MOE_E_INVALID, "max_tokens %lld out of range", (long long)max_tokens);
+  *bytes = abl_plan(layer, max_tokens, variant).total;
+  return MOE_OK;
+}
+
+moe_status moe_prefill_ablation(const moe_layer *layer, int32_t variant, const void *x, int64_t T,
+                                void *y, const void *residual, void *ws, size_t ws_bytes,
+                                void *stream) {
+  g_err.clear();
+  moe_status st = check_layer(layer);
+  if (st) return st;
+  if (variant < MOE_ABL_NONE || variant > MOE_ABL_TILE_128)
+    return fail(MOE_E_INVALID, "unknown ablation %d", variant);
+  if (layer->w_format != MOE_W_INT4_G64)
+    return fail(MOE_E_UNSUPPORTED, "ablations cover the int4 grouped-GEMM path only");
+  if (T < 0 || T > kMaxTokens) return fail(MOE_E_INVALID, "T %lld out of range", (long long)T);
+  if (T == 0) return MOE_OK;
+  if (!x || !y || !aligned16(x) || !aligned16(y))
+    return fail(MOE_E_INVALID, "x and y must be non-NULL and 16-byte aligned");
+  if (residual && !aligned16(residual)) return fail(MOE_E_INVALID, "residual misaligned");
+  if ((st = check_tiled(layer))) return st;
+  const AblPlan ap = abl_plan(layer, T, variant);
+  if (!ws || !aligned16(ws)) return fail(MOE_E_INVALID, "workspace NULL or misaligned");
+  if (ws_bytes < ap.total)
+    return fail(MOE_E_WORKSPACE, "workspace %zu bytes < %zu needed for T=%lld, ablation %d",
+                ws_bytes, ap.total, (long long)T, variant);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const Plan &p = ap.p;
+  moe::RouteArgs ra = route_args(layer, x, T);
+  route_targets(ra, p, ws, nullptr);
+  ra.slot_w = at<float>(ws, p.slot_w);
+  ra.x16 = at<uint16_t>(ws, p.x16);
+  ra.tile_shift = abl_shift(variant);
+  hipError_t e;
+  int host_tiles = -1;
+  if (variant == MOE_ABL_HOST_ROUTING) {
+    // the GPU stops after top-k; the host reads the ids, builds the tables and uploads them
+    if ((e = moe::launch_route_topk(ra, s)) != hipSuccess) return hip_fail(e, "ablation route");
+    std::vector<int32_t> ids((size_t)T * layer->top_k), tab;
+    if ((e = hipMemcpyAsync(ids.data(), ra.ids, ids.size() * 4, hipMemcpyDeviceToHost, s)) ||
+        (e = hipStreamSynchronize(s)))
+      return hip_fail(e, "ablation: reading the top-k ids");
+    host_tiles = host_tables(ids, T, layer->n_experts, layer->top_k, layer->n_shared,
+                             layer->inter, ra.tile_shift, ap, tab);
+    if (host_tiles < 0) return fail(MOE_E_HIP, "ablation: top-k ids out of range");
+    int32_t *dtab = at<int32_t>(ws, ap.tab);
+    if ((e = hipMemcpyAsync(dtab, tab.data(), ap.tab_bytes, hipMemcpyHostToDevice, s)) ||
+        (e = hipStreamSynchronize(s)))  // tab is host memory local to this call
+      return hip_fail(e, "ablation: uploading the routing tables");
+    ra.offsets = dtab + ap.tab_offsets;
+    ra.n_tiles = dtab + ap.tab_ntiles;
+    ra.tiles = reinterpret_cast<int2 *>(dtab + ap.tab_tiles);
+    ra.blk = dtab + ap.tab_blk;
+    if ((e = moe::launch_route_group(ra, false, s)) != hipSuccess)
+      return hip_fail(e, "ablation scatter");
+  } else if ((e = moe::launch_route_prefill(ra, s)) != hipSuccess) {
+    return hip_fail(e, "ablation route");
+  }
+  moe::GroupedArgs ga = grouped_args(layer, ra, ws, p);
+  // grid: the bound for the variant's tile heights, or exactly the tiles the host listed
+  if (host_tiles >= 0) ga.max_tiles = host_tiles;
+  ga.fixed_mb = variant == MOE_ABL_FIXED_TILE;
+  if (variant == MOE_ABL_SEPARATE_DEQUANT) {
+    ga.w13_x = at<uint16_t>(ws, ap.x13);
+    ga.w2_x = at<uint16_t>(ws, ap.x2);
+    if ((e = moe::launch_expand(ga, s)) != hipSuccess) return hip_fail(e, "ablation dequant pass");
+  }
+  return run_grouped(layer, ga, ra, residual, y, s);
 }
 
 // One token after validation; p is a workspace plan for at least one token.

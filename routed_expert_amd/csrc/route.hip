@@ -292,8 +292,8 @@ __global__ __launch_bounds__(256) void k_scan(int32_t *__restrict__ blk_cnt, int
                                               int32_t *__restrict__ counts_user,
                                               int32_t *__restrict__ offsets_user,
                                               int2 *__restrict__ tiles,
-                                              int32_t *__restrict__ n_tiles) {
-  __shared__ int sc[4];
+                                              int32_t *__restrict__ n_tiles, int tsh_fixed,
+                                              int fill) {
   const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
@@ -309,48 +309,64 @@ __global__ __launch_bounds__(256) void k_scan(int32_t *__restrict__ blk_cnt, int
       }
     }
   }
-  const int incl = block_scan_incl(run, sc);
-  const int off = incl - run;
-  // Tile map in descending order of work (the GEMM workgroups start in index order, so the
-  // long tiles go first and the short ones fill the end): every full 128-row tile (routed
-  // experts in order, then the shared expert), then the partial tiles by their number of
-  // 32-row blocks, 4 down to 1. One 64-bit scan places them all: bits [0, 21) count full
-  // tiles, 9-bit fields at 21 + 9q count partial tiles of 4 - q blocks.
-  const int nfull = run >> 7, mb = ((run & 127) + 31) >> 5;
-  const uint64_t packed = (uint64_t)nfull | (mb ? (1ull << (21 + 9 * (4 - mb))) : 0ull);
+  // one scan gives the offsets (low word) and the number of 32-row blocks the experts'
+  // rows fill (high word)
   __shared__ uint64_t sc64[4];
+  const uint64_t rb = (uint64_t)run | ((uint64_t)((run + 31) >> 5) << 32);
+  const uint64_t rincl = block_scan_incl(rb, sc64);
+  const int off = (int)((rincl - rb) & 0xFFFFFFFFu);
+  __shared__ uint64_t rtot[1];
+  if (e == 255) rtot[0] = rincl;
+  __syncthreads();
+  const int nassign = (int)(rtot[0] & 0xFFFFFFFFu);
+  // Tile height of this call, from the load ("Match tile size to expert load"): while the
+  // rows fill at least 4 * fill blocks (fill = 32-row blocks per resident gate/up
+  // workgroup slot of one N tile), 128-row tiles; with fewer, a 128-row tile would outlast
+  // the rest of the grid, so 64 rows (at least 2 * fill blocks) or 32. Callers may fix it.
+  int tsh = tsh_fixed;
+  if (tsh <= 0) {
+    const int nblk = (int)(rtot[0] >> 32) + (S ? (T + 31) >> 5 : 0);
+    tsh = nblk >= 4 * fill ? 7 : nblk >= 2 * fill ? 6 : 5;
+  }
+  // Tile map in descending order of work (the GEMM workgroups start in index order, so the
+  // long tiles go first and the short ones fill the end): every full tile of 2^tsh rows
+  // (routed experts in order, then the shared expert), then the partial tiles by their
+  // number of 32-row blocks, 4 down to 1: each expert's last tile is only as high as its
+  // remaining rows need. One 64-bit scan places them all: bits [0, 22) count full tiles,
+  // 9-bit fields at 22 + 9q count partial tiles of 4 - q blocks. A tile entry is
+  // (group | rows << 16, first row).
+  const int trows = 1 << tsh;
+  const int rem = run & (trows - 1);
+  const int nfull = run >> tsh, mb = (rem + 31) >> 5;
+  const uint64_t packed = (uint64_t)nfull | (mb ? (1ull << (22 + 9 * (4 - mb))) : 0ull);
   const uint64_t pincl = block_scan_incl(packed, sc64);
   const uint64_t pexcl = pincl - packed;
-  __shared__ int totals[1];
   __shared__ uint64_t ptot[1];
-  if (e == 255) {
-    totals[0] = incl;
-    ptot[0] = pincl;
-  }
+  if (e == 255) ptot[0] = pincl;
   __syncthreads();
-  const int nassign = totals[0];
   const uint64_t tot = ptot[0];
-  const int nfull_tot = (int)(tot & 0x1FFFFF);
-  const int sh_full = S ? T >> 7 : 0, sh_rem = S ? (T & 127) : 0;
+  const int nfull_tot = (int)(tot & 0x3FFFFF);
+  const int sh_full = S ? T >> tsh : 0, sh_rem = S ? (T & (trows - 1)) : 0;
   int bstart[4];
   bstart[0] = nfull_tot + sh_full;
 #pragma unroll
-  for (int q = 1; q < 4; ++q) bstart[q] = bstart[q - 1] + (int)((tot >> (21 + 9 * (q - 1))) & 0x1FF);
-  const int npart = bstart[3] + (int)((tot >> (21 + 27)) & 0x1FF);
+  for (int q = 1; q < 4; ++q) bstart[q] = bstart[q - 1] + (int)((tot >> (22 + 9 * (q - 1))) & 0x1FF);
+  const int npart = bstart[3] + (int)((tot >> (22 + 27)) & 0x1FF);
   if (e < E) {
     offsets[e] = off;
     if (counts_user) counts_user[e] = run;
     if (offsets_user) offsets_user[e] = off;
-    const int f0 = (int)(pexcl & 0x1FFFFF);
-    for (int i = 0; i < nfull; ++i) tiles[f0 + i] = make_int2(e, i * kTileM);
+    const int f0 = (int)(pexcl & 0x3FFFFF);
+    for (int i = 0; i < nfull; ++i) tiles[f0 + i] = make_int2(e | trows << 16, i * trows);
     if (mb) {
       const int q = 4 - mb;
-      tiles[bstart[q] + (int)((pexcl >> (21 + 9 * q)) & 0x1FF)] = make_int2(e, nfull * kTileM);
+      tiles[bstart[q] + (int)((pexcl >> (22 + 9 * q)) & 0x1FF)] =
+          make_int2(e | rem << 16, nfull * trows);
     }
   }
-  for (int i = e; i < sh_full; i += 256) tiles[nfull_tot + i] = make_int2(E, i * kTileM);
+  for (int i = e; i < sh_full; i += 256) tiles[nfull_tot + i] = make_int2(E | trows << 16, i * trows);
   if (e == 0) {
-    if (sh_rem) tiles[npart] = make_int2(E, sh_full * kTileM);
+    if (sh_rem) tiles[npart] = make_int2(E | sh_rem << 16, sh_full * trows);
     offsets[E] = nassign;
     offsets[E + 1] = nassign + (S ? T : 0);
     if (offsets_user) offsets_user[E] = nassign;
@@ -397,7 +413,7 @@ hipError_t launch_router_split(const float *W, size_t n, uint16_t *planes, hipSt
   return hipSuccess;
 }
 
-hipError_t launch_route_prefill(const RouteArgs &a, hipStream_t s) {
+hipError_t launch_route_topk(const RouteArgs &a, hipStream_t s) {
   const int NB = (int)((a.T + kRouteBlock - 1) / kRouteBlock);
   const dim3 g1((unsigned)NB, (unsigned)((a.E + 63) / 64));
   if (a.bf16) {
@@ -419,11 +435,24 @@ hipError_t launch_route_prefill(const RouteArgs &a, hipStream_t s) {
   else
     MOE_LAUNCH("k_topk", k_topk<false>, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, s,
                a.logits, nullptr, (int)a.T, a.E, a.k, a.ids, a.w, a.blk);
-  MOE_LAUNCH("k_scan", k_scan, dim3(1), dim3(256), 0, s, a.blk, NB, a.E, (int)a.T, a.k, a.S,
-             a.offsets, a.counts_user, a.offsets_user, a.tiles, a.n_tiles);
+  return hipSuccess;
+}
+
+hipError_t launch_route_group(const RouteArgs &a, bool scan, hipStream_t s) {
+  const int NB = (int)((a.T + kRouteBlock - 1) / kRouteBlock);
+  if (scan)
+    MOE_LAUNCH("k_scan", k_scan, dim3(1), dim3(256), 0, s, a.blk, NB, a.E, (int)a.T, a.k, a.S,
+               a.offsets, a.counts_user, a.offsets_user, a.tiles, a.n_tiles, a.tile_shift,
+               gemm_fill(a.I));
   MOE_LAUNCH("k_scatter", k_scatter, dim3(NB), dim3(256), 0, s, a.ids, (int)a.T, a.E, a.k,
              a.offsets, a.blk, a.w, a.sorted_tok, a.slot_of, a.slot_w);
   return hipSuccess;
+}
+
+hipError_t launch_route_prefill(const RouteArgs &a, hipStream_t s) {
+  const hipError_t e = launch_route_topk(a, s);
+  if (e != hipSuccess) return e;
+  return launch_route_group(a, true, s);
 }
 
 }  // namespace moe

@@ -26,7 +26,13 @@ ACT_F32, ACT_BF16 = 0, 1
 EXPORTS = ("moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_pack_bytes",
            "moe_pack_weights", "moe_route", "moe_prefill", "moe_decode",
            "moe_stack_workspace_bytes", "moe_stack_forward", "moe_rmsnorm",
-           "moe_profile_enable", "moe_profile_query", "moe_profile_reset")
+           "moe_profile_enable", "moe_profile_query", "moe_profile_reset",
+           "moe_ablation_workspace_bytes", "moe_prefill_ablation")
+(ABL_NONE, ABL_SEPARATE_DEQUANT, ABL_HOST_ROUTING, ABL_TILE_64, ABL_FIXED_TILE,
+ ABL_TILE_128) = range(6)
+ABLATIONS = {"none": ABL_NONE, "separate_dequant": ABL_SEPARATE_DEQUANT,
+             "host_routing": ABL_HOST_ROUTING, "tile_64": ABL_TILE_64,
+             "fixed_tile": ABL_FIXED_TILE, "tile_128": ABL_TILE_128}
 
 
 class MoeLayer(ctypes.Structure):
@@ -96,6 +102,8 @@ def lib():
         "moe_profile_query": ([ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                ctypes.POINTER(I64)], ctypes.c_int),
         "moe_profile_reset": ([], ctypes.c_int),
+        "moe_ablation_workspace_bytes": ([P, I64, I32, ctypes.POINTER(SZ)], ctypes.c_int),
+        "moe_prefill_ablation": ([P, I32, P, I64, P, P, P, SZ, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -256,6 +264,28 @@ def moe_decode(layer: DeviceLayer, x: torch.Tensor, y=None, residual=None, ws=No
     y = torch.empty_like(x) if y is None else y
     _check("moe_decode", lib().moe_decode(layer.ref, _ptr(x), _ptr(y), _ptr(residual),
                                           _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+def ablation_workspace(layer: DeviceLayer, max_tokens: int, variant: int,
+                       device="cuda") -> torch.Tensor:
+    n = ctypes.c_size_t(0)
+    _check("moe_ablation_workspace_bytes",
+           lib().moe_ablation_workspace_bytes(layer.ref, int(max_tokens), int(variant),
+                                              ctypes.byref(n)))
+    return torch.zeros(n.value, dtype=torch.uint8, device=device)
+
+
+def moe_prefill_ablation(layer: DeviceLayer, x: torch.Tensor, variant: int, y=None,
+                         residual=None, ws=None, stream=None) -> torch.Tensor:
+    """The prefill path with one mechanism replaced by the pages' rejected design
+    (ABL_* constants); the result is bit-identical to moe_prefill's grouped path."""
+    T = x.shape[0]
+    ws = ablation_workspace(layer, max(T, 1), variant, x.device) if ws is None else ws
+    y = torch.empty_like(x) if y is None else y
+    _check("moe_prefill_ablation",
+           lib().moe_prefill_ablation(layer.ref, int(variant), _ptr(x), T, _ptr(y),
+                                      _ptr(residual), _ptr(ws), ws.numel(), _stream(stream)))
     return y
 
 

@@ -180,3 +180,38 @@ def test_profile_controls_without_records(M):
     M.profile_reset()
     M.profile_enable(False)
     assert M.profile_query("k_grouped_gateup") == (0.0, 0)
+
+
+def test_ablation_workspace_and_argument_errors(M):
+    L = M.lib()
+    layer = fake_layer(M)
+    ref = ctypes.byref(layer)
+    sizes = {}
+    for name, v in M.ABLATIONS.items():
+        n = ctypes.c_size_t(0)
+        assert L.moe_ablation_workspace_bytes(ref, 4096, v, ctypes.byref(n)) == M.OK
+        sizes[name] = n.value
+    # every variant needs at least the product workspace; the separate dequantisation pass
+    # adds the expanded fp16 weights: 2 bytes per weight of all E+S experts
+    _, base = ws_bytes(M, layer, 4096)
+    assert min(sizes.values()) >= base
+    E1, H, I = 257, 2048, 512
+    assert sizes["separate_dequant"] - sizes["none"] >= E1 * 3 * H * I * 2
+    n = ctypes.c_size_t(0)
+    assert L.moe_ablation_workspace_bytes(ref, 16, 6, ctypes.byref(n)) == M.E_INVALID
+    assert L.moe_ablation_workspace_bytes(ref, 16, -1, ctypes.byref(n)) == M.E_INVALID
+    x, y, ws = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), ctypes.c_void_p(0x300000)
+    need = sizes["separate_dequant"]
+    assert L.moe_prefill_ablation(ref, 9, x, 64, y, None, ws, need, None) == M.E_INVALID
+    assert "ablation" in L.moe_last_error().decode()
+    assert L.moe_prefill_ablation(ref, M.ABL_SEPARATE_DEQUANT, x, 4096, y, None, ws,
+                                  sizes["none"], None) == M.E_WORKSPACE
+    assert L.moe_prefill_ablation(ref, M.ABL_TILE_64, None, 4, y, None, ws, need,
+                                  None) == M.E_INVALID
+    assert L.moe_prefill_ablation(ref, M.ABL_NONE, x, 0, y, None, ws, need, None) == M.OK
+    f32 = fake_layer(M, w_format=M.W_F32, act_dtype=M.ACT_F32)
+    assert L.moe_prefill_ablation(ctypes.byref(f32), M.ABL_NONE, x, 4, y, None, ws, need,
+                                  None) == M.E_UNSUPPORTED
+    bare = fake_layer(M, w13_t=None)
+    assert L.moe_prefill_ablation(ctypes.byref(bare), M.ABL_NONE, x, 4, y, None, ws, need,
+                                  None) == M.E_INVALID
