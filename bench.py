@@ -471,13 +471,23 @@ def profile_run(moe, torch, synth, dev, what):
         y = torch.empty((1, H), dtype=torch.bfloat16, device=dev)
         for i in range(200):
             moe.moe_decode(layers[i % N_COPIES], xs[i % 64:i % 64 + 1], y=y, ws=ws)
+    elif what == "prefill_separate_dequant":
+        # the separate-dequantisation ablation (expansion pass + GEMMs on fp16 weights)
+        dl = moe.DeviceLayer.from_host(synth.decode_layer(0), dev)
+        x = moe.bf16_from_bits(synth.prefill_x(4096, seed=2), dev)
+        ws = moe.ablation_workspace(dl, 4096, moe.ABL_SEPARATE_DEQUANT, dev)
+        y = torch.empty_like(x)
+        for _ in range(60):
+            moe.moe_prefill_ablation(dl, x, moe.ABL_SEPARATE_DEQUANT, y=y, ws=ws)
     else:
         layer = synth.skewed_layer(0) if what == "prefill_skewed" else synth.decode_layer(0)
         dl = moe.DeviceLayer.from_host(layer, dev)
         x = moe.bf16_from_bits(synth.prefill_x(4096, seed=2), dev)
         ws = moe.workspace(dl, 4096, dev)
         y = torch.empty_like(x)
-        for _ in range(10):
+        # 200 calls (about 75 ms): the averages are dominated by the steady clock, not by
+        # the slower first tens of milliseconds after the GPU was idle
+        for _ in range(200):
             moe.moe_prefill(dl, x, y=y, ws=ws)
     torch.cuda.synchronize()
     print(f"profile run done: {what}", flush=True)
@@ -491,7 +501,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-stack", action="store_true")
-    ap.add_argument("--profile", choices=["decode", "prefill_uniform", "prefill_skewed"],
+    ap.add_argument("--profile", choices=["decode", "prefill_uniform", "prefill_skewed",
+                                          "prefill_separate_dequant"],
                     help="fixed work for rocprofv3 instead of the benchmark")
     args = ap.parse_args()
     if args.gpus != 1:
