@@ -1,4 +1,5 @@
-"""CPU oracle of the routed-expert MoE layer (plain C, fp64), with a ctypes wrapper.
+"""CPU oracle of the routed-expert MoE layer and of grouped-query decode attention (plain
+C, fp64), with a ctypes wrapper.
 
 TEST INFRASTRUCTURE ONLY. Only the test suite, the package smoke check and the
 benchmark's CPU-baseline leg may import this module. The product path (the HIP
@@ -7,7 +8,8 @@ library and its binding) never imports, links or runs it, and shares no code wit
 Source of the arithmetic: "Optimizing On-Device Inference for Apple Silicon"
 (sections "Qwen creates three distinct workload shapes", "Dequantize weights during
 matrix multiplication", "Keep expert routing on the GPU", "Reduce intermediate and
-state traffic"); the readings taken where the page is silent are listed in
+state traffic"; attention: "Qwen creates three distinct workload shapes" and "Read the
+attention cache efficiently"); the readings taken where the page is silent are listed in
 ``moe_oracle.c``.
 
 Pinning: every function here is checked in ``tests/test_oracle_pins.py`` against
@@ -68,6 +70,7 @@ def _load():
             "oracle_expert": [P, I32, P, P],
             "oracle_moe": [P, P, I64, P, ctypes.c_int],
             "oracle_rmsnorm": [P, I64, I32, D, P],
+            "oracle_attn_decode": [P, P, P, I32, I32, I32, I64, I64, D, P],
         }
         for name, args in sigs.items():
             fn = getattr(_lib, name)
@@ -199,4 +202,20 @@ def rmsnorm(h, eps: float = 1e-6) -> np.ndarray:
     T, H = h.shape
     out = np.empty_like(h)
     _check(_load().oracle_rmsnorm(h.ctypes.data, T, H, eps, out.ctypes.data), "rmsnorm")
+    return out
+
+
+def attn_decode(q, k, v, n_q: int, n_kv: int, scale: float) -> np.ndarray:
+    """Decode attention of one token (fp64). q [n_q, D] (bf16 bits or floats); k, v bf16 bit
+    patterns [n_kv, ctx, D]. Returns out [n_q, D] float64."""
+    q = to_f64(q)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    n_kv_, ctx, D = k.shape
+    if n_kv_ != n_kv or v.shape != k.shape or q.shape != (n_q, D):
+        raise ValueError("attention shapes do not match")
+    out = np.empty((n_q, D), dtype=np.float64)
+    _check(_load().oracle_attn_decode(q.ctypes.data, k.ctypes.data, v.ctypes.data, n_q, n_kv,
+                                      D, ctx, ctx * D, float(scale), out.ctypes.data),
+           "attn_decode")
     return out

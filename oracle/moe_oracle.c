@@ -281,3 +281,45 @@ int oracle_rmsnorm(const double *h, int64_t T, int32_t H, double eps, double *ou
   }
   return 0;
 }
+
+/* Decode attention of one query token over a KV cache, grouped-query form ("Optimizing
+ * On-Device Inference for Apple Silicon", sections "Qwen creates three distinct workload
+ * shapes" -- query heads share key-value heads, eight to one -- and "Read the attention
+ * cache efficiently"). Readings where the page is silent: query head h reads key-value
+ * head h / (n_q / n_kv) (consecutive heads share one); scores are scale * q.k; the
+ * weights are the softmax over all ctx cached positions. The largest score is subtracted
+ * before exponentiating, which leaves the softmax unchanged in exact arithmetic.
+ *   q    [n_q, D] fp64;  k, v  bf16 bit patterns, head g's row t at g * head_stride + t * D
+ *   out  [n_q, D] fp64 */
+int oracle_attn_decode(const double *q, const uint16_t *k, const uint16_t *v, int32_t n_q,
+                       int32_t n_kv, int32_t D, int64_t ctx, int64_t head_stride, double scale,
+                       double *out) {
+  if (!q || !k || !v || !out || n_q <= 0 || n_kv <= 0 || n_q % n_kv || D <= 0 || ctx <= 0 ||
+      head_stride < ctx * D)
+    return -1;
+  const int32_t G = n_q / n_kv;
+  double *s = (double *)malloc((size_t)ctx * sizeof(double));
+  if (!s) return -1;
+  for (int32_t h = 0; h < n_q; ++h) {
+    const int64_t base = (int64_t)(h / G) * head_stride;
+    double m = -INFINITY;
+    for (int64_t t = 0; t < ctx; ++t) {
+      double dot = 0.0;
+      for (int32_t d = 0; d < D; ++d) dot += q[(int64_t)h * D + d] * bf16_to_double(k[base + t * D + d]);
+      s[t] = scale * dot;
+      if (s[t] > m) m = s[t];
+    }
+    double z = 0.0;
+    for (int64_t t = 0; t < ctx; ++t) {
+      s[t] = exp(s[t] - m);
+      z += s[t];
+    }
+    for (int32_t d = 0; d < D; ++d) {
+      double acc = 0.0;
+      for (int64_t t = 0; t < ctx; ++t) acc += s[t] * bf16_to_double(v[base + t * D + d]);
+      out[(int64_t)h * D + d] = acc / z;
+    }
+  }
+  free(s);
+  return 0;
+}

@@ -76,6 +76,12 @@ int oracle_moe(const oracle_layer *L, const double *x, int64_t T, double *y, int
 /* RMSNorm with unit gain: out[t] = h[t] / sqrt(mean(h[t]^2) + eps). */
 int oracle_rmsnorm(const double *h, int64_t T, int32_t H, double eps, double *out);
 
+/* Decode attention of one token: out[h] = softmax_t(scale * q[h].k[g, t]) v[g, t] with
+ * g = h / (n_q / n_kv); k and v bf16 bit patterns, head g's row t at g * head_stride + t * D. */
+int oracle_attn_decode(const double *q, const uint16_t *k, const uint16_t *v, int32_t n_q,
+                       int32_t n_kv, int32_t D, int64_t ctx, int64_t head_stride, double scale,
+                       double *out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -166,3 +166,32 @@ def prefill_x(T: int = 4096, hidden: int = 2048, seed: int = 2) -> np.ndarray:
 
 def skewed_layer(seed: int = 0, gamma: float = 0.7) -> Layer:
     return make_int4_layer(seed, router_bias=zipf_router_bias(gamma=gamma))
+
+
+# ---- decode attention inputs ---------------------------------------------------------------
+# Grouped-query attention of the model's full-attention layers: 16 query heads, two key-value
+# heads (eight query heads per KV head), 256 values per head, bf16 cache.
+ATTN_Q_HEADS, ATTN_KV_HEADS, ATTN_HEAD_DIM = 16, 2, 256
+
+
+def attn_inputs(ctx: int, seed: int = 0, n_q: int = ATTN_Q_HEADS, n_kv: int = ATTN_KV_HEADS,
+                D: int = ATTN_HEAD_DIM, n_hot: int = 16, hot_score: float = 8.0):
+    """One decode token's query and a KV cache of ctx positions, as bf16 bit patterns:
+    q [n_q, D], k and v [n_kv, ctx, D]. Draw order per seed: q, k, v ~ N(0, 1), then the
+    n_hot "hot" positions per KV head (without replacement). A hot key is the mean of its
+    group's queries scaled so that that mean query scores hot_score against it at scale
+    1/sqrt(D), so the softmax has a few dominant positions over a flat background, as
+    attention over a long context does."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((n_q, D), dtype=np.float32)
+    k = rng.standard_normal((n_kv, ctx, D), dtype=np.float32)
+    v = rng.standard_normal((n_kv, ctx, D), dtype=np.float32)
+    qb = f32_to_bf16_bits(q)
+    qf = bf16_bits_to_f32(qb).astype(np.float64)
+    G = n_q // n_kv
+    scale = 1.0 / np.sqrt(D)
+    for g in range(n_kv):
+        hot = rng.choice(ctx, size=min(n_hot, ctx), replace=False)
+        qbar = qf[g * G:(g + 1) * G].mean(axis=0)
+        k[g, hot] = (hot_score / (scale * float(qbar @ qbar)) * qbar).astype(np.float32)
+    return qb, f32_to_bf16_bits(k), f32_to_bf16_bits(v)

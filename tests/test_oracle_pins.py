@@ -327,3 +327,100 @@ def test_rmsnorm_constant_row_and_torch(oracle_lib):
     h = rng_x(28, 5, 96).astype(np.float64)
     ref = torch.nn.functional.rms_norm(torch.as_tensor(h), (96,), eps=1e-6).numpy()
     np.testing.assert_allclose(oracle.rmsnorm(h, 1e-6), ref, rtol=1e-13)
+
+
+# ---- decode attention ------------------------------------------------------------------
+# What it computes: per query head, the softmax-weighted average of its key-value head's
+# cached values, weights from the scaled query-key scores; eight query heads share one KV
+# head ("Qwen creates three distinct workload shapes", "Read the attention cache
+# efficiently"). Readings: consecutive query heads share a KV head; scale 1/sqrt(D).
+
+def _attn_rand(seed, n_kv, ctx, D, n_q):
+    rng = np.random.default_rng(seed)
+    q = bf16(rng.standard_normal((n_q, D)))
+    k = bf16(rng.standard_normal((n_kv, ctx, D)))
+    v = bf16(rng.standard_normal((n_kv, ctx, D)))
+    return q, k, v
+
+
+def test_attn_single_position_returns_its_value():
+    q, k, v = _attn_rand(1, 2, 1, 16, 4)
+    out = oracle.attn_decode(q, k, v, 4, 2, 0.25)
+    vf = synth.bf16_bits_to_f32(v).astype(np.float64)
+    for h in range(4):
+        assert np.array_equal(out[h], vf[h // 2, 0])
+
+
+def test_attn_equal_keys_give_the_mean_value():
+    # identical keys: every score equal, softmax uniform, output = plain mean of the values
+    q, k, v = _attn_rand(2, 2, 37, 16, 8)
+    k[:] = k[:, :1]
+    out = oracle.attn_decode(q, k, v, 8, 2, 0.25)
+    vf = synth.bf16_bits_to_f32(v).astype(np.float64)
+    for h in range(8):
+        np.testing.assert_allclose(out[h], vf[h // 4].mean(axis=0), rtol=0, atol=1e-13)
+
+
+def test_attn_dominant_key_selects_its_value():
+    q, k, v = _attn_rand(3, 1, 50, 16, 2)
+    qf = synth.bf16_bits_to_f32(q).astype(np.float64)
+    k[0, 17] = bf16(40.0 * qf.mean(axis=0))   # score tens of units above every other
+    out = oracle.attn_decode(q, k, v, 2, 1, 1.0)
+    vf = synth.bf16_bits_to_f32(v).astype(np.float64)
+    for h in range(2):
+        np.testing.assert_allclose(out[h], vf[0, 17], rtol=0, atol=1e-9)
+
+
+def test_attn_matches_torch_sdpa_with_grouped_heads():
+    # the library's scaled-dot-product attention on the CPU in fp64, KV heads expanded so
+    # that query head h reads KV head h // G
+    n_q, n_kv, D, ctx = 8, 2, 32, 53
+    q, k, v = _attn_rand(4, n_kv, ctx, D, n_q)
+    scale = 0.37
+    out = oracle.attn_decode(q, k, v, n_q, n_kv, scale)
+    f = lambda a: torch.as_tensor(synth.bf16_bits_to_f32(a).astype(np.float64))
+    G = n_q // n_kv
+    kk = f(k).repeat_interleave(G, dim=0)[None]           # [1, n_q, ctx, D]
+    vv = f(v).repeat_interleave(G, dim=0)[None]
+    qq = f(q)[None, :, None, :]                           # [1, n_q, 1, D]
+    ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, scale=scale)
+    np.testing.assert_allclose(out, ref[0, :, 0].numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_attn_heads_read_only_their_kv_head():
+    n_q, n_kv, D, ctx = 6, 3, 16, 20
+    q, k, v = _attn_rand(5, n_kv, ctx, D, n_q)
+    base = oracle.attn_decode(q, k, v, n_q, n_kv, 0.25)
+    v2 = v.copy()
+    v2[1] = bf16(np.full((ctx, D), 3.0))                  # change KV head 1 only
+    out = oracle.attn_decode(q, k, v2, n_q, n_kv, 0.25)
+    assert np.array_equal(out[[0, 1, 4, 5]], base[[0, 1, 4, 5]])
+    np.testing.assert_allclose(out[[2, 3]], 3.0, rtol=0, atol=1e-12)
+
+
+def test_attn_is_invariant_to_reordering_positions():
+    q, k, v = _attn_rand(6, 2, 41, 16, 4)
+    perm = np.random.default_rng(7).permutation(41)
+    a = oracle.attn_decode(q, k, v, 4, 2, 0.3)
+    b = oracle.attn_decode(q, k[:, perm], v[:, perm], 4, 2, 0.3)
+    np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-14)
+
+
+def test_attn_brute_force_two_positions():
+    # closed form for two positions: w1 = 1 / (1 + exp(s0 - s1)), out = (1 - w1) v0 + w1 v1
+    q, k, v = _attn_rand(8, 1, 2, 8, 1)
+    scale = 0.5
+    qf, kf, vf = (synth.bf16_bits_to_f32(a).astype(np.float64) for a in (q, k, v))
+    s0, s1 = scale * qf[0] @ kf[0, 0], scale * qf[0] @ kf[0, 1]
+    w1 = 1.0 / (1.0 + np.exp(s0 - s1))
+    out = oracle.attn_decode(q, k, v, 1, 1, scale)
+    np.testing.assert_allclose(out[0], (1 - w1) * vf[0, 0] + w1 * vf[0, 1], rtol=1e-13)
+
+
+def test_attn_inputs_recipe_has_hot_positions():
+    q, k, v = synth.attn_inputs(300, seed=1)
+    assert q.shape == (16, 256) and k.shape == (2, 300, 256) and v.shape == k.shape
+    qf = synth.bf16_bits_to_f32(q).astype(np.float64)
+    kf = synth.bf16_bits_to_f32(k).astype(np.float64)
+    s = np.einsum("hd,htd->ht", qf.reshape(2, 8, 256).mean(axis=1), kf) / 16.0
+    assert (s > 6).sum(axis=1).tolist() == [16, 16] and np.abs(s[s < 6]).max() < 6
