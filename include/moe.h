@@ -192,6 +192,32 @@ moe_status moe_prefill_ablation(const moe_layer *layer, int32_t variant, const v
                                 void *y, const void *residual, void *ws, size_t ws_bytes,
                                 void *stream);
 
+/* Decode attention of one token over a grouped-query KV cache ("Optimizing On-Device
+ * Inference for Apple Silicon", sections "Qwen creates three distinct workload shapes" and
+ * "Read the attention cache efficiently"):
+ *     out[h] = sum_t softmax_t(scale * q[h] . k[g, t]) v[g, t],   g = h / (n_q / n_kv)
+ * over t = 0 .. ctx-1. The query heads sharing a KV head are packed into one workgroup,
+ * which loads each cached row once for all of them; the cache is split into equal blocks
+ * processed in parallel and merged (fp32 scores, softmax and sums).
+ *   q    bf16 [n_q, head_dim]
+ *   k, v bf16 caches: KV head g's row t at element g * kv_head_stride + t * head_dim
+ *        (kv_head_stride >= ctx * head_dim, a multiple of 8)
+ *   out  bf16 [n_q, head_dim]
+ * Supported: head_dim == 256, n_q / n_kv in {1, 2, 4, 8}, 1 <= ctx <= 2^31. Pointers
+ * 16-byte aligned; ws holds moe_attn_workspace_bytes(n_q, max_ctx >= ctx) bytes. */
+moe_status moe_attn_workspace_bytes(int32_t n_q, int32_t n_kv, int32_t head_dim, int64_t max_ctx,
+                                    size_t *bytes);
+moe_status moe_attn_decode(const void *q, const void *k_cache, const void *v_cache, int32_t n_q,
+                           int32_t n_kv, int32_t head_dim, int64_t ctx, int64_t kv_head_stride,
+                           float scale, void *out, void *ws, size_t ws_bytes, void *stream);
+/* The page's ablation of the packing: one workgroup per query head, so each cached row is
+ * loaded once per query head ("Pack query heads to reuse KV rows"); the same blocks and the
+ * same arithmetic per head, so out is bit-identical to moe_attn_decode. */
+moe_status moe_attn_decode_unpacked(const void *q, const void *k_cache, const void *v_cache,
+                                    int32_t n_q, int32_t n_kv, int32_t head_dim, int64_t ctx,
+                                    int64_t kv_head_stride, float scale, void *out, void *ws,
+                                    size_t ws_bytes, void *stream);
+
 /* Workspace bytes for moe_stack_forward with chunks of up to chunk_tokens rows. */
 moe_status moe_stack_workspace_bytes(const moe_layer *layers, int32_t n_layers,
                                      int64_t chunk_tokens, size_t *bytes);

@@ -168,4 +168,24 @@ hipError_t launch_small_t(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_rmsnorm(const void *h, int64_t T, int H, float eps, bool bf16, void *out,
                           hipStream_t s);
 
+// Decode attention of one token over a grouped-query KV cache (bf16, head dimension 256).
+constexpr int kAttnMaxSlots = 512;  // workgroups the cache blocks are spread over, at most
+struct AttnArgs {
+  const uint16_t *q;          // [n_q, 256] bf16
+  const uint16_t *k, *v;      // head g's row t at g * head_stride + t * 256 (bf16)
+  int64_t head_stride;        // elements
+  int64_t ctx;                // cached positions (>= 1)
+  int64_t tps;                // positions per block (multiple of 32)
+  int n_split;                // blocks
+  int n_q, G;                 // query heads, query heads per KV head
+  float scale_log2;           // score scale times log2(e)
+  float *part_acc;            // [n_split, n_q, 256] unnormalised block sums
+  float *part_m, *part_l;     // [n_split, n_q] block maxima (exp2 domain) and sums
+  uint16_t *out;              // [n_q, 256] bf16
+};
+bool attn_supported(int n_q, int n_kv, int D);
+void attn_plan(int64_t ctx, int n_groups, int *n_split, int64_t *tps);
+// heads_per_group: G (query heads of a KV head share a workgroup) or 1 (one per head)
+hipError_t launch_attn_decode(const AttnArgs &a, int heads_per_group, hipStream_t s);
+
 }  // namespace moe

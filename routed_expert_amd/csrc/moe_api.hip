@@ -861,6 +861,83 @@ moe_status moe_stack_forward(const moe_layer *layers, int32_t n_layers, void *h,
   return MOE_OK;
 }
 
+// ---- decode attention ---------------------------------------------------------------------
+namespace {
+size_t attn_ws_bytes(int32_t n_q, int64_t max_ctx) {
+  int ns;
+  int64_t tps;
+  moe::attn_plan(max_ctx, 1, &ns, &tps);  // one head group bounds the block count
+  return (size_t)ns * n_q * (256 + 2) * 4;
+}
+
+moe_status attn_impl(const void *q, const void *k, const void *v, int32_t n_q, int32_t n_kv,
+                     int32_t D, int64_t ctx, int64_t stride, float scale, void *out, void *ws,
+                     size_t ws_bytes, void *stream, bool packed) {
+  g_err.clear();
+  if (!moe::attn_supported(n_q, n_kv, D))
+    return fail(MOE_E_UNSUPPORTED, "attention needs head_dim 256 and n_q / n_kv in {1,2,4,8}");
+  if (ctx < 1 || ctx > (int64_t(1) << 31)) return fail(MOE_E_INVALID, "ctx %lld out of range",
+                                                       (long long)ctx);
+  if (stride < ctx * D || stride % 8)
+    return fail(MOE_E_INVALID, "kv_head_stride must be >= ctx * head_dim and a multiple of 8");
+  if (!q || !k || !v || !out || !ws)
+    return fail(MOE_E_INVALID, "q, k_cache, v_cache, out and ws must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(ws))
+    return fail(MOE_E_INVALID, "attention pointers must be 16-byte aligned");
+  if (!(scale == scale)) return fail(MOE_E_INVALID, "scale is NaN");
+  const int G = n_q / n_kv;
+  const int hp = packed ? G : 1;
+  moe::AttnArgs a{};
+  moe::attn_plan(ctx, n_kv, &a.n_split, &a.tps);  // the packed path's blocks, for both
+  const size_t need = (size_t)a.n_split * n_q * (D + 2) * 4;
+  if (ws_bytes < need)
+    return fail(MOE_E_WORKSPACE, "workspace %zu bytes < %zu needed for ctx=%lld", ws_bytes, need,
+                (long long)ctx);
+  a.q = static_cast<const uint16_t *>(q);
+  a.k = static_cast<const uint16_t *>(k);
+  a.v = static_cast<const uint16_t *>(v);
+  a.head_stride = stride;
+  a.ctx = ctx;
+  a.n_q = n_q;
+  a.G = G;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.part_acc = static_cast<float *>(ws);
+  a.part_m = a.part_acc + (size_t)a.n_split * n_q * D;
+  a.part_l = a.part_m + (size_t)a.n_split * n_q;
+  a.out = static_cast<uint16_t *>(out);
+  const hipError_t e = moe::launch_attn_decode(a, hp, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "moe_attn_decode");
+  return MOE_OK;
+}
+}  // namespace
+
+moe_status moe_attn_workspace_bytes(int32_t n_q, int32_t n_kv, int32_t head_dim, int64_t max_ctx,
+                                    size_t *bytes) {
+  g_err.clear();
+  if (!bytes) return fail(MOE_E_INVALID, "bytes is NULL");
+  if (!moe::attn_supported(n_q, n_kv, head_dim))
+    return fail(MOE_E_UNSUPPORTED, "attention needs head_dim 256 and n_q / n_kv in {1,2,4,8}");
+  if (max_ctx < 1 || max_ctx > (int64_t(1) << 31))
+    return fail(MOE_E_INVALID, "max_ctx %lld out of range", (long long)max_ctx);
+  *bytes = attn_ws_bytes(n_q, max_ctx);
+  return MOE_OK;
+}
+
+moe_status moe_attn_decode(const void *q, const void *k_cache, const void *v_cache, int32_t n_q,
+                           int32_t n_kv, int32_t head_dim, int64_t ctx, int64_t kv_head_stride,
+                           float scale, void *out, void *ws, size_t ws_bytes, void *stream) {
+  return attn_impl(q, k_cache, v_cache, n_q, n_kv, head_dim, ctx, kv_head_stride, scale, out, ws,
+                   ws_bytes, stream, true);
+}
+
+moe_status moe_attn_decode_unpacked(const void *q, const void *k_cache, const void *v_cache,
+                                    int32_t n_q, int32_t n_kv, int32_t head_dim, int64_t ctx,
+                                    int64_t kv_head_stride, float scale, void *out, void *ws,
+                                    size_t ws_bytes, void *stream) {
+  return attn_impl(q, k_cache, v_cache, n_q, n_kv, head_dim, ctx, kv_head_stride, scale, out, ws,
+                   ws_bytes, stream, false);
+}
+
 moe_status moe_rmsnorm(const void *h, int64_t T, int32_t hidden, float eps, int32_t act_dtype,
                        void *out, void *stream) {
   g_err.clear();

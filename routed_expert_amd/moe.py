@@ -27,7 +27,8 @@ EXPORTS = ("moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_pack
            "moe_pack_weights", "moe_route", "moe_prefill", "moe_decode",
            "moe_stack_workspace_bytes", "moe_stack_forward", "moe_rmsnorm",
            "moe_profile_enable", "moe_profile_query", "moe_profile_reset",
-           "moe_ablation_workspace_bytes", "moe_prefill_ablation")
+           "moe_ablation_workspace_bytes", "moe_prefill_ablation",
+           "moe_attn_workspace_bytes", "moe_attn_decode", "moe_attn_decode_unpacked")
 (ABL_NONE, ABL_SEPARATE_DEQUANT, ABL_HOST_ROUTING, ABL_TILE_64, ABL_FIXED_TILE,
  ABL_TILE_128) = range(6)
 ABLATIONS = {"none": ABL_NONE, "separate_dequant": ABL_SEPARATE_DEQUANT,
@@ -104,6 +105,11 @@ def lib():
         "moe_profile_reset": ([], ctypes.c_int),
         "moe_ablation_workspace_bytes": ([P, I64, I32, ctypes.POINTER(SZ)], ctypes.c_int),
         "moe_prefill_ablation": ([P, I32, P, I64, P, P, P, SZ, P], ctypes.c_int),
+        "moe_attn_workspace_bytes": ([I32, I32, I32, I64, ctypes.POINTER(SZ)], ctypes.c_int),
+        "moe_attn_decode": ([P, P, P, I32, I32, I32, I64, I64, ctypes.c_float, P, P, SZ, P],
+                            ctypes.c_int),
+        "moe_attn_decode_unpacked": ([P, P, P, I32, I32, I32, I64, I64, ctypes.c_float, P, P,
+                                      SZ, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -287,6 +293,38 @@ def moe_prefill_ablation(layer: DeviceLayer, x: torch.Tensor, variant: int, y=No
            lib().moe_prefill_ablation(layer.ref, int(variant), _ptr(x), T, _ptr(y),
                                       _ptr(residual), _ptr(ws), ws.numel(), _stream(stream)))
     return y
+
+
+def attn_workspace(n_q: int, n_kv: int, head_dim: int, max_ctx: int,
+                   device="cuda") -> torch.Tensor:
+    n = ctypes.c_size_t(0)
+    _check("moe_attn_workspace_bytes",
+           lib().moe_attn_workspace_bytes(int(n_q), int(n_kv), int(head_dim), int(max_ctx),
+                                          ctypes.byref(n)))
+    return torch.empty(n.value, dtype=torch.uint8, device=device)
+
+
+def moe_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, ctx=None,
+                    scale=None, out=None, ws=None, packed: bool = True,
+                    stream=None) -> torch.Tensor:
+    """Decode attention of one token. q [n_q, D] bf16; k_cache, v_cache [n_kv, cap, D] bf16
+    (contiguous; the first ctx positions are attended, ctx defaults to cap); scale defaults
+    to 1 / sqrt(D). Returns out [n_q, D] bf16."""
+    n_q, D = q.shape
+    n_kv, cap, D2 = k_cache.shape
+    if D2 != D or v_cache.shape != k_cache.shape:
+        raise ValueError("q / cache shapes do not match")
+    if not (q.is_contiguous() and k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("q and the caches must be contiguous")
+    ctx = cap if ctx is None else int(ctx)
+    scale = D ** -0.5 if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    ws = attn_workspace(n_q, n_kv, D, ctx, q.device) if ws is None else ws
+    fn = lib().moe_attn_decode if packed else lib().moe_attn_decode_unpacked
+    _check("moe_attn_decode", fn(_ptr(q), _ptr(k_cache), _ptr(v_cache), n_q, n_kv, D, ctx,
+                                 cap * D, ctypes.c_float(scale), _ptr(out), _ptr(ws),
+                                 ws.numel(), _stream(stream)))
+    return out
 
 
 def moe_rmsnorm(h: torch.Tensor, eps: float = 1e-6, out=None, stream=None) -> torch.Tensor:

@@ -215,3 +215,27 @@ def test_ablation_workspace_and_argument_errors(M):
     bare = fake_layer(M, w13_t=None)
     assert L.moe_prefill_ablation(ctypes.byref(bare), M.ABL_NONE, x, 4, y, None, ws, need,
                                   None) == M.E_INVALID
+
+
+def test_attention_argument_errors_before_any_launch(M):
+    L = M.lib()
+    n = ctypes.c_size_t(0)
+    assert L.moe_attn_workspace_bytes(16, 2, 256, 131072, ctypes.byref(n)) == M.OK
+    need = n.value
+    assert need >= 256 * 16 * 258 * 4
+    assert L.moe_attn_workspace_bytes(16, 2, 128, 1000, ctypes.byref(n)) == M.E_UNSUPPORTED
+    assert L.moe_attn_workspace_bytes(12, 4, 256, 1000, ctypes.byref(n)) == M.E_UNSUPPORTED
+    assert L.moe_attn_workspace_bytes(16, 2, 256, 0, ctypes.byref(n)) == M.E_INVALID
+    q, k, v, o, ws = (ctypes.c_void_p(a) for a in (0x100000, 0x200000, 0x300000, 0x400000,
+                                                   0x500000))
+    f = ctypes.c_float(0.0625)
+    args = lambda ctx, stride, nbytes: (q, k, v, 16, 2, 256, ctx, stride, f, o, ws, nbytes, None)
+    assert L.moe_attn_decode(*args(4096, 4096 * 256, 100)) == M.E_WORKSPACE
+    assert L.moe_attn_decode(*args(0, 4096 * 256, need)) == M.E_INVALID
+    assert L.moe_attn_decode(*args(4096, 4095 * 256, need)) == M.E_INVALID   # stride < ctx*D
+    assert L.moe_attn_decode(q, k, v, 16, 2, 128, 64, 64 * 128, f, o, ws, need,
+                             None) == M.E_UNSUPPORTED
+    assert L.moe_attn_decode(q, None, v, 16, 2, 256, 64, 64 * 256, f, o, ws, need,
+                             None) == M.E_INVALID
+    assert L.moe_attn_decode_unpacked(ctypes.c_void_p(0x100008), k, v, 16, 2, 256, 64,
+                                      64 * 256, f, o, ws, need, None) == M.E_INVALID
