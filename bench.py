@@ -18,11 +18,13 @@ Also: a stack of 40 such layers (pre-norm residual blocks) with batch-1 decode o
 tokens and a 32,768-token prompt in chunks of 4096 tokens; moe_prefill with 2, 4 and
 8 tokens (the small-T kernels) over the 20 layer copies; and the prefill ablations
 (separate dequantisation pass, host-inspected routing, fixed tile heights) at 512, 2048
-and 4096 tokens beside the product path. Prefill timings start after about 80 ms of
-sustained calls, past the lower-clock spell that follows an idle GPU.
+and 4096 tokens beside the product path; grouped-query decode attention (16 query heads,
+2 KV heads, head dimension 256, bf16 cache) over 3,840 to 131,072 cached positions, packed
+and unpacked. Prefill timings start after about 80 ms of sustained calls, past the
+lower-clock spell that follows an idle GPU.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-prefill]
-                       [--no-stack]
+                       [--no-stack] [--no-attention]
 """
 import argparse
 import hashlib
@@ -274,6 +276,86 @@ PAGE_ABLATION_GAINS = {"separate_dequant": {"tokens": 512, "gain": 0.774},
                        "tile_64": {"tokens": 2048, "gain": 0.132, "note": "16- vs 32-row tile"}}
 
 
+ATTN_CTXS = (3840, 32768, 65536, 131072)
+
+
+def bench_attention(moe, torch, synth, dev, ctxs=ATTN_CTXS, rounds=5):
+    """Decode attention of one token (16 query heads, 2 KV heads, head dimension 256, bf16
+    cache) over caches of the given lengths. Cache-cold: enough seeded cache copies rotate
+    that together they exceed 1 GiB (several Infinity Caches); calls replay from HIP graphs.
+    Bytes per call = the K and V rows read (2 * 2 * ctx * 256 * 2) + q and out. Also the
+    unpacked variant (one workgroup per query head, the page's ablation) for its gain."""
+    import numpy as np
+    nq, nkv, D = synth.ATTN_Q_HEADS, synth.ATTN_KV_HEADS, synth.ATTN_HEAD_DIM
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    res = {}
+    for ctx in ctxs:
+        cache_bytes = 2 * nkv * ctx * D * 2
+        n = max(4, -(-(1 << 30) // cache_bytes))
+        ks = [torch.randn(nkv, ctx, D, device=dev, generator=gen).to(torch.bfloat16)
+              for _ in range(n)]
+        vs = [torch.randn(nkv, ctx, D, device=dev, generator=gen).to(torch.bfloat16)
+              for _ in range(n)]
+        q = torch.randn(nq, D, device=dev, generator=gen).to(torch.bfloat16)
+        out = torch.empty_like(q)
+        ws = moe.attn_workspace(nq, nkv, D, ctx, dev)
+        calls = n * max(1, 40 // n)
+        graphs = {}
+        for packed in (True, False):
+            def call(i, packed=packed):
+                moe.moe_attn_decode(q, ks[i % n], vs[i % n], out=out, ws=ws, packed=packed)
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                for i in range(3):
+                    call(i)
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(calls):
+                    call(i)
+            graphs[packed] = g
+        warm_up(graphs[True].replay)
+        us = {True: [], False: []}
+        for _ in range(rounds):
+            for packed, g in graphs.items():
+                ev0.record()
+                for _ in range(3):
+                    g.replay()
+                ev1.record()
+                torch.cuda.synchronize()
+                us[packed].append(ev0.elapsed_time(ev1) * 1e3 / (3 * calls))
+        del graphs
+        moe.profile_reset()
+        moe.profile_enable(True)
+        for i in range(2 * n):
+            moe.moe_attn_decode(q, ks[i % n], vs[i % n], out=out, ws=ws)
+        torch.cuda.synchronize()
+        moe.profile_enable(False)
+        kern = {}
+        for name in ("k_attn_split", "k_attn_combine"):
+            tot, cnt = moe.profile_query(name)
+            kern[name] = round(1e3 * tot / max(cnt, 1), 2)
+        moe.profile_reset()
+        t_p, t_u = float(np.median(us[True])), float(np.median(us[False]))
+        nbytes = cache_bytes + 2 * nq * D * 2
+        split_gbs = cache_bytes / (kern["k_attn_split"] * 1e-6) / 1e9
+        res[str(ctx)] = {"us_per_call": round(t_p, 2), "GB_s": round(nbytes / (t_p * 1e-6) / 1e9, 1),
+                         "hbm_frac": round(nbytes / (t_p * 1e-6) / 1e9 / HBM_PEAK_GBS, 3),
+                         "kernels_us": kern, "split_kernel_hbm_frac":
+                         round(split_gbs / HBM_PEAK_GBS, 3), "cache_copies": n,
+                         "unpacked_us_per_call": round(t_u, 2),
+                         "packing_gain": round(t_u / t_p - 1, 3)}
+        del ks, vs, ws
+        torch.cuda.empty_cache()
+    res["pages"] = {"gqa_packing_gain_e2e_32k": 0.238, "note": "whole-model decode, other hardware"}
+    return res
+
+
 def bench_ablations(moe, torch, synth, dev, Ts=(512, 2048, 4096), rounds=5, calls=20):
     """moe_prefill_ablation on the uniform-routing layer: the product path and each
     rejected design, rounds alternating over the variants after a warm-up; median
@@ -471,6 +553,20 @@ def profile_run(moe, torch, synth, dev, what):
         y = torch.empty((1, H), dtype=torch.bfloat16, device=dev)
         for i in range(200):
             moe.moe_decode(layers[i % N_COPIES], xs[i % 64:i % 64 + 1], y=y, ws=ws)
+    elif what == "attn_decode_32k":
+        # decode attention over a 32,768-position cache, 16 rotating copies (cache-cold)
+        nq, nkv, D, ctx = synth.ATTN_Q_HEADS, synth.ATTN_KV_HEADS, synth.ATTN_HEAD_DIM, 32768
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(5)
+        ks = [torch.randn(nkv, ctx, D, device=dev, generator=gen).to(torch.bfloat16)
+              for _ in range(16)]
+        vs = [torch.randn(nkv, ctx, D, device=dev, generator=gen).to(torch.bfloat16)
+              for _ in range(16)]
+        q = torch.randn(nq, D, device=dev, generator=gen).to(torch.bfloat16)
+        ws = moe.attn_workspace(nq, nkv, D, ctx, dev)
+        out = torch.empty_like(q)
+        for i in range(400):
+            moe.moe_attn_decode(q, ks[i % 16], vs[i % 16], out=out, ws=ws)
     elif what == "prefill_separate_dequant":
         # the separate-dequantisation ablation (expansion pass + GEMMs on fp16 weights)
         dl = moe.DeviceLayer.from_host(synth.decode_layer(0), dev)
@@ -501,8 +597,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--no-attention", action="store_true")
     ap.add_argument("--profile", choices=["decode", "prefill_uniform", "prefill_skewed",
-                                          "prefill_separate_dequant"],
+                                          "prefill_separate_dequant", "attn_decode_32k"],
                     help="fixed work for rocprofv3 instead of the benchmark")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -558,6 +655,8 @@ def main():
     if not args.no_prefill:
         out["small_T"] = bench_small_t(moe, torch, synth, dev)
         out["ablations"] = bench_ablations(moe, torch, synth, dev)
+    if not args.no_attention:
+        out["attention_decode"] = bench_attention(moe, torch, synth, dev)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(synth)
     print(json.dumps(out), flush=True)

@@ -99,10 +99,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_split(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
 
-  for (int64_t t0 = t_begin + wave * kAttnStep; t0 < t_end; t0 += kAttnWaves * kAttnStep) {
-    // every load of the step first (positions past the block repeat its last row and are
-    // masked out of the softmax)
-    uint4 kb[2][NJ], vb[16];
+  // K and V rows of the step at t0 (positions past the block repeat its last row and are
+  // masked out of the softmax). Every load of a step is issued before any is used; with two
+  // waves per SIMD one wave's loads are in flight while the other computes (issuing the
+  // next step's loads early measured slower: the prefetch past a block's end adds a
+  // memory round trip before the partial sums can be stored).
+  uint4 kb[2][NJ], vb[16];
+  auto load_k = [&](int64_t t0) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int64_t t = imin(t0 + 16 * hh + r, t_end - 1);
@@ -110,11 +113,17 @@ __global__ __launch_bounds__(256, 2) void k_attn_split(AttnArgs a) {
       for (int j = 0; j < NJ; ++j)
         kb[hh][j] = *reinterpret_cast<const uint4 *>(K + t * D + 32 * j + 8 * g);
     }
+  };
+  auto load_v = [&](int64_t t0) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int64_t t = imin(t0 + 2 * i + par, t_end - 1);
       vb[i] = *reinterpret_cast<const uint4 *>(V + t * D + 8 * c8);
     }
+  };
+  for (int64_t t0 = t_begin + wave * kAttnStep; t0 < t_end; t0 += kAttnWaves * kAttnStep) {
+    load_k(t0);
+    load_v(t0);
     // scores of positions t0 + r (c0) and t0 + 16 + r (c1) for heads 4 g + i
     f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -225,39 +234,69 @@ __global__ __launch_bounds__(256, 2) void k_attn_split(AttnArgs a) {
   }
 }
 
-// Merge of the blocks: grid (query heads, D / 64); four groups of 64 lanes walk the
-// blocks with a running maximum, then combine in LDS; out = sum / l in bf16.
+// Merge of the blocks: grid (query heads, D / 64). Thread (split lane sl, column quad dq)
+// requests the maxima, sums and 16-byte accumulator slices of its blocks s = sl + 16 i
+// (i < 32 covers 512 blocks) before using any, so the merge costs one round trip; the
+// head's maximum M comes from LDS, each block is weighted by 2^(m_s - M), the 16 split
+// lanes are added in LDS, and out = sum / l in bf16.
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
-  constexpr int D = 256;
-  const int h = blockIdx.x, tid = threadIdx.x, sg = tid >> 6;
-  const int d = blockIdx.y * 64 + (tid & 63);
-  float M = kNegInf, L = 0.f, A = 0.f;
-  for (int s = sg; s < a.n_split; s += 4) {
+  constexpr int D = 256, NI = kAttnMaxSlots / 16;
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const int dq = tid & 15, sl = tid >> 4;
+  const int d0 = blockIdx.y * 64 + 4 * dq;
+  float ms[NI], ls[NI];
+  float4 vs[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int s = min(sl + 16 * i, a.n_split - 1);
     const size_t row = (size_t)s * a.n_q + h;
-    const float ms = a.part_m[row];
-    const float mn = fmaxf(M, ms);
-    const float f0 = __builtin_amdgcn_exp2f(M - mn), f1 = __builtin_amdgcn_exp2f(ms - mn);
-    L = L * f0 + a.part_l[row] * f1;
-    A = A * f0 + a.part_acc[row * D + d] * f1;
-    M = mn;
+    ms[i] = a.part_m[row];
+    ls[i] = a.part_l[row];
+    vs[i] = *reinterpret_cast<const float4 *>(a.part_acc + row * D + d0);
   }
-  __shared__ float sm[4][64], sl[4][64], sa[4][64];
-  sm[sg][tid & 63] = M;
-  sl[sg][tid & 63] = L;
-  sa[sg][tid & 63] = A;
+  __shared__ float red[256];
+  __shared__ __attribute__((aligned(16))) float4 sacc[16][16];
+  __shared__ float sl_l[16];
+  float mx = kNegInf;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) mx = fmaxf(mx, ms[i]);  // repeats of the last block are harmless
+  red[tid] = mx;
   __syncthreads();
-  if (sg == 0) {
-    float Mt = kNegInf;
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  float lp = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) Mt = fmaxf(Mt, sm[w][tid]);
-    float Lt = 0.f, At = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float f = __builtin_amdgcn_exp2f(sm[w][tid] - Mt);
-      Lt = __builtin_fmaf(f, sl[w][tid], Lt);
-      At = __builtin_fmaf(f, sa[w][tid], At);
+  for (int i = 0; i < NI; ++i) {
+    const float f = sl + 16 * i < a.n_split ? __builtin_amdgcn_exp2f(ms[i] - M) : 0.f;
+    lp = __builtin_fmaf(f, ls[i], lp);
+    acc.x = __builtin_fmaf(f, vs[i].x, acc.x);
+    acc.y = __builtin_fmaf(f, vs[i].y, acc.y);
+    acc.z = __builtin_fmaf(f, vs[i].z, acc.z);
+    acc.w = __builtin_fmaf(f, vs[i].w, acc.w);
+  }
+  sacc[sl][dq] = acc;
+  if (dq == 0) sl_l[sl] = lp;
+  __syncthreads();
+  if (tid < 16) {
+    float4 t = sacc[0][tid];
+    float L = sl_l[0];
+    for (int i = 1; i < 16; ++i) {
+      const float4 u = sacc[i][tid];
+      t.x += u.x;
+      t.y += u.y;
+      t.z += u.z;
+      t.w += u.w;
+      L += sl_l[i];
     }
-    a.out[(size_t)h * D + d] = f32_to_bf16(At / Lt);
+    const float inv = 1.0f / L;
+    uint2 o;
+    o.x = pack_bf16x2(t.x * inv, t.y * inv);
+    o.y = pack_bf16x2(t.z * inv, t.w * inv);
+    *reinterpret_cast<uint2 *>(a.out + (size_t)h * D + blockIdx.y * 64 + 4 * tid) = o;
   }
 }
 
