@@ -1,5 +1,5 @@
-"""CPU oracle of the routed-expert MoE layer and of grouped-query decode attention (plain
-C, fp64), with a ctypes wrapper.
+"""CPU oracle of the routed-expert MoE layer, of grouped-query decode attention and of the
+Gated DeltaNet recurrence (plain C, fp64), with a ctypes wrapper.
 
 TEST INFRASTRUCTURE ONLY. Only the test suite, the package smoke check and the
 benchmark's CPU-baseline leg may import this module. The product path (the HIP
@@ -9,7 +9,8 @@ Source of the arithmetic: "Optimizing On-Device Inference for Apple Silicon"
 (sections "Qwen creates three distinct workload shapes", "Dequantize weights during
 matrix multiplication", "Keep expert routing on the GPU", "Reduce intermediate and
 state traffic"; attention: "Qwen creates three distinct workload shapes" and "Read the
-attention cache efficiently"); the readings taken where the page is silent are listed in
+attention cache efficiently"; DeltaNet: "Qwen creates three distinct workload shapes" and
+"Keep recurrent state on chip"); the readings taken where the page is silent are listed in
 ``moe_oracle.c``.
 
 Pinning: every function here is checked in ``tests/test_oracle_pins.py`` against
@@ -71,6 +72,7 @@ def _load():
             "oracle_moe": [P, P, I64, P, ctypes.c_int],
             "oracle_rmsnorm": [P, I64, I32, D, P],
             "oracle_attn_decode": [P, P, P, I32, I32, I32, I64, I64, D, P],
+            "oracle_gdn_scan": [P, P, P, P, P, I64, I32, I32, I32, I32, P, P, ctypes.c_int],
         }
         for name, args in sigs.items():
             fn = getattr(_lib, name)
@@ -219,3 +221,26 @@ def attn_decode(q, k, v, n_q: int, n_kv: int, scale: float) -> np.ndarray:
                                       D, ctx, ctx * D, float(scale), out.ctypes.data),
            "attn_decode")
     return out
+
+
+def gdn_scan(q, k, v, alpha, beta, n_k: int, n_v: int, state0=None, nthreads: int = 0):
+    """Gated DeltaNet recurrence (fp64). q, k bf16 bits [T, n_k, d_k]; v bf16 bits
+    [T, n_v, d_v]; alpha, beta float32 [T, n_v]; state0 [n_v, d_v, d_k] or None (zeros).
+    Returns (out [T, n_v, d_v] float64, final state [n_v, d_v, d_k] float64)."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    alpha = np.ascontiguousarray(alpha, dtype=np.float32)
+    beta = np.ascontiguousarray(beta, dtype=np.float32)
+    T, nk_, d_k = q.shape
+    d_v = v.shape[2]
+    if nk_ != n_k or k.shape != q.shape or v.shape[:2] != (T, n_v) or alpha.shape != (T, n_v) \
+            or beta.shape != (T, n_v):
+        raise ValueError("DeltaNet shapes do not match")
+    state = np.zeros((n_v, d_v, d_k)) if state0 is None else np.array(state0, dtype=np.float64)
+    out = np.empty((T, n_v, d_v), dtype=np.float64)
+    _check(_load().oracle_gdn_scan(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                   alpha.ctypes.data, beta.ctypes.data, T, n_k, n_v, d_k, d_v,
+                                   state.ctypes.data, out.ctypes.data, int(nthreads)),
+           "gdn_scan")
+    return out, state

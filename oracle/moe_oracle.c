@@ -323,3 +323,61 @@ int oracle_attn_decode(const double *q, const uint16_t *k, const uint16_t *v, in
   free(s);
   return 0;
 }
+
+/* Gated DeltaNet recurrence over T tokens ("Optimizing On-Device Inference for Apple
+ * Silicon", sections "Qwen creates three distinct workload shapes" -- a learned gate decides
+ * how much of the fixed-size state to keep, a delta update writes the current token -- and
+ * "Keep recurrent state on chip": fp32 state and gate, bf16 queries and keys). Reading taken
+ * where the page gives no formula: the gated delta rule
+ *     S_t = alpha_t S_{t-1} + beta_t (v_t - alpha_t S_{t-1} k_t) k_t^T,   o_t = S_t q_t,
+ * with S of value head j a d_v x d_k matrix and value head j reading key head
+ * j / (n_v / n_k) for q and k.
+ *   q, k   bf16 bits [T, n_k, d_k];  v bf16 bits [T, n_v, d_v];  alpha, beta fp32 [T, n_v]
+ *   state  fp64 [n_v, d_v, d_k]: S_0 on entry, S_T on return;  out fp64 [T, n_v, d_v] */
+int oracle_gdn_scan(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *alpha,
+                    const float *beta, int64_t T, int32_t n_k, int32_t n_v, int32_t d_k,
+                    int32_t d_v, double *state, double *out, int nthreads) {
+  if (!q || !k || !v || !alpha || !beta || !state || !out || T < 0 || n_k <= 0 || n_v <= 0 ||
+      n_v % n_k || d_k <= 0 || d_v <= 0)
+    return -1;
+  const int32_t rep = n_v / n_k;
+  int failed = 0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+  for (int32_t j = 0; j < n_v; ++j) {
+    const int32_t kh = j / rep;
+    double *S = state + (int64_t)j * d_v * d_k;
+    double *kt = (double *)malloc((size_t)d_k * sizeof(double));
+    double *qt = (double *)malloc((size_t)d_k * sizeof(double));
+    if (!kt || !qt) {
+      failed = 1;
+      free(kt);
+      free(qt);
+      continue;
+    }
+    for (int64_t t = 0; t < T; ++t) {
+      const double a = alpha[t * n_v + j], b = beta[t * n_v + j];
+      for (int32_t e = 0; e < d_k; ++e) {
+        kt[e] = bf16_to_double(k[(t * n_k + kh) * d_k + e]);
+        qt[e] = bf16_to_double(q[(t * n_k + kh) * d_k + e]);
+      }
+      for (int32_t i = 0; i < d_v; ++i) {
+        double *row = S + (int64_t)i * d_k;
+        double sk = 0.0;
+        for (int32_t e = 0; e < d_k; ++e) sk += row[e] * kt[e];
+        const double c = b * (bf16_to_double(v[(t * n_v + j) * d_v + i]) - a * sk);
+        double o = 0.0;
+        for (int32_t e = 0; e < d_k; ++e) {
+          row[e] = a * row[e] + c * kt[e];
+          o += row[e] * qt[e];
+        }
+        out[(t * n_v + j) * d_v + i] = o;
+      }
+    }
+    free(kt);
+    free(qt);
+  }
+  return failed ? -1 : 0;
+}

@@ -82,6 +82,13 @@ int oracle_attn_decode(const double *q, const uint16_t *k, const uint16_t *v, in
                        int32_t n_kv, int32_t D, int64_t ctx, int64_t head_stride, double scale,
                        double *out);
 
+/* Gated DeltaNet recurrence: S_t = alpha_t S_{t-1} + beta_t (v_t - alpha_t S_{t-1} k_t) k_t^T,
+ * o_t = S_t q_t per value head (state fp64 [n_v, d_v, d_k], S_0 in, S_T out); q, k bf16 bits
+ * [T, n_k, d_k], v bf16 bits [T, n_v, d_v], alpha, beta [T, n_v]; out fp64 [T, n_v, d_v]. */
+int oracle_gdn_scan(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *alpha,
+                    const float *beta, int64_t T, int32_t n_k, int32_t n_v, int32_t d_k,
+                    int32_t d_v, double *state, double *out, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

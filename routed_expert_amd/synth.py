@@ -195,3 +195,31 @@ def attn_inputs(ctx: int, seed: int = 0, n_q: int = ATTN_Q_HEADS, n_kv: int = AT
         qbar = qf[g * G:(g + 1) * G].mean(axis=0)
         k[g, hot] = (hot_score / (scale * float(qbar @ qbar)) * qbar).astype(np.float32)
     return qb, f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+
+
+# ---- Gated DeltaNet inputs ------------------------------------------------------------------
+# Dimensions: 32 value heads and 16 key heads of 128 values each, so that one layer's fp32
+# state is 32 x 128 x 128 x 4 B = 2 MiB (a blockwise scan over 2K tokens in 32-token blocks
+# then reads and writes 256 MiB of state, the figure the page gives for its ablation).
+GDN_K_HEADS, GDN_V_HEADS, GDN_DK, GDN_DV = 16, 32, 128, 128
+
+
+def gdn_inputs(T: int, seed: int = 0, n_k: int = GDN_K_HEADS, n_v: int = GDN_V_HEADS,
+               d_k: int = GDN_DK, d_v: int = GDN_DV):
+    """Inputs of a Gated DeltaNet scan over T tokens. Draw order per seed: q, k, v ~ N(0, 1),
+    then the gate and write-strength logits ~ N(3, 1) and N(0, 1). q and k are L2-normalised
+    per (token, head) in fp32 (q further scaled by 1/sqrt(d_k)) and rounded to bf16; v is
+    bf16; alpha = sigmoid(N(3, 1)) (the state keeps about 95 % per token) and
+    beta = sigmoid(N(0, 1)) stay fp32. Returns (q, k [T, n_k, d_k], v [T, n_v, d_v] as bf16
+    bits; alpha, beta [T, n_v] float32)."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((T, n_k, d_k), dtype=np.float32)
+    k = rng.standard_normal((T, n_k, d_k), dtype=np.float32)
+    v = rng.standard_normal((T, n_v, d_v), dtype=np.float32)
+    ga = rng.standard_normal((T, n_v), dtype=np.float32) + 3.0
+    gb = rng.standard_normal((T, n_v), dtype=np.float32)
+    q /= np.linalg.norm(q, axis=-1, keepdims=True) * np.float32(np.sqrt(d_k))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    alpha = (1.0 / (1.0 + np.exp(-ga))).astype(np.float32)
+    beta = (1.0 / (1.0 + np.exp(-gb))).astype(np.float32)
+    return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v), alpha, beta

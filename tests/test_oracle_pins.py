@@ -424,3 +424,97 @@ def test_attn_inputs_recipe_has_hot_positions():
     kf = synth.bf16_bits_to_f32(k).astype(np.float64)
     s = np.einsum("hd,htd->ht", qf.reshape(2, 8, 256).mean(axis=1), kf) / 16.0
     assert (s > 6).sum(axis=1).tolist() == [16, 16] and np.abs(s[s < 6]).max() < 6
+
+
+# ---- Gated DeltaNet recurrence ---------------------------------------------------------
+# What it computes: a fixed-size matrix state per head, kept in part by a learned gate and
+# written by a delta update from the current token ("Qwen creates three distinct workload
+# shapes", "Keep recurrent state on chip"). Reading: the gated delta rule
+# S_t = alpha S_{t-1} + beta (v - alpha S_{t-1} k) k^T, o_t = S_t q_t.
+
+def _gdn_rand(seed, T, n_k, n_v, d_k, d_v):
+    rng = np.random.default_rng(seed)
+    q = bf16(rng.standard_normal((T, n_k, d_k)) * 0.3)
+    k = bf16(rng.standard_normal((T, n_k, d_k)) * 0.3)
+    v = bf16(rng.standard_normal((T, n_v, d_v)))
+    a = rng.uniform(0.5, 1.0, (T, n_v)).astype(np.float32)
+    b = rng.uniform(0.0, 1.0, (T, n_v)).astype(np.float32)
+    s0 = rng.standard_normal((n_v, d_v, d_k))
+    return q, k, v, a, b, s0
+
+
+def _f(bits):
+    return synth.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def test_gdn_keep_all_write_nothing_reads_the_initial_state():
+    q, k, v, a, b, s0 = _gdn_rand(1, 9, 2, 4, 8, 6)
+    out, st = oracle.gdn_scan(q, k, v, np.ones_like(a), np.zeros_like(b), 2, 4, s0)
+    qf = np.repeat(_f(q), 2, axis=1)                       # value head j reads key head j // 2
+    np.testing.assert_allclose(out, np.einsum("jde,tje->tjd", s0, qf), rtol=1e-13, atol=1e-13)
+    assert np.array_equal(st, s0)
+
+
+def test_gdn_zero_gate_forgets_the_past():
+    # alpha = 0: S_t = beta v_t k_t^T, so o_t = beta (k_t . q_t) v_t whatever came before
+    q, k, v, a, b, s0 = _gdn_rand(2, 7, 1, 2, 8, 5)
+    out, _ = oracle.gdn_scan(q, k, v, np.zeros_like(a), b, 1, 2, s0)
+    kq = np.einsum("te,te->t", _f(k)[:, 0], _f(q)[:, 0])
+    ref = b[:, :, None] * kq[:, None, None] * _f(v)
+    np.testing.assert_allclose(out, ref, rtol=1e-13, atol=1e-14)
+
+
+def test_gdn_full_write_recalls_the_value_under_its_key():
+    # beta = 1 with a unit key: S_t k_t = v_t exactly, whatever the state and gate were
+    T, d_k, d_v = 12, 8, 6
+    rng = np.random.default_rng(3)
+    k = np.zeros((T, 1, d_k), dtype=np.float32)
+    k[np.arange(T), 0, rng.integers(0, d_k, T)] = 1.0        # one-hot keys, exact in bf16
+    kb = bf16(k)
+    v = bf16(rng.standard_normal((T, 1, d_v)))
+    a = rng.uniform(0.3, 1.0, (T, 1)).astype(np.float32)
+    out, _ = oracle.gdn_scan(kb, kb, v, a, np.ones((T, 1), np.float32), 1, 1,
+                             rng.standard_normal((1, d_v, d_k)))
+    np.testing.assert_allclose(out, _f(v), rtol=0, atol=1e-14)
+
+
+def test_gdn_matches_the_literal_matrix_form():
+    # S_t = S_{t-1} (alpha (I - beta k k^T)) + beta v k^T, o = S q, with numpy matrices
+    T, n_k, n_v, d_k, d_v = 6, 1, 2, 5, 4
+    q, k, v, a, b, s0 = _gdn_rand(4, T, n_k, n_v, d_k, d_v)
+    out, st = oracle.gdn_scan(q, k, v, a, b, n_k, n_v, s0)
+    S = s0.copy()
+    for t in range(T):
+        kk, qq = _f(k)[t, 0], _f(q)[t, 0]
+        for j in range(n_v):
+            S[j] = S[j] @ (float(a[t, j]) * (np.eye(d_k) - float(b[t, j]) * np.outer(kk, kk))) \
+                + float(b[t, j]) * np.outer(_f(v)[t, j], kk)
+            np.testing.assert_allclose(out[t, j], S[j] @ qq, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(st, S, rtol=1e-12, atol=1e-13)
+
+
+def test_gdn_value_heads_read_their_key_head():
+    q, k, v, a, b, s0 = _gdn_rand(5, 5, 2, 4, 8, 3)
+    base, _ = oracle.gdn_scan(q, k, v, a, b, 2, 4, s0)
+    k2 = k.copy()
+    k2[:, 1] = bf16(np.full((5, 8), 0.25))                   # change key head 1 only
+    out, _ = oracle.gdn_scan(q, k2, v, a, b, 2, 4, s0)
+    assert np.array_equal(out[:, :2], base[:, :2])
+    assert not np.allclose(out[:, 2:], base[:, 2:])
+
+
+def test_gdn_scan_continues_from_its_final_state():
+    q, k, v, a, b, s0 = _gdn_rand(6, 20, 2, 4, 8, 6)
+    full, st_full = oracle.gdn_scan(q, k, v, a, b, 2, 4, s0)
+    o1, st1 = oracle.gdn_scan(q[:13], k[:13], v[:13], a[:13], b[:13], 2, 4, s0)
+    o2, st2 = oracle.gdn_scan(q[13:], k[13:], v[13:], a[13:], b[13:], 2, 4, st1)
+    assert np.array_equal(np.concatenate([o1, o2]), full) and np.array_equal(st2, st_full)
+
+
+def test_gdn_inputs_recipe():
+    q, k, v, a, b = synth.gdn_inputs(40, seed=1)
+    assert q.shape == (40, 16, 128) and v.shape == (40, 32, 128) and a.shape == (40, 32)
+    kn = np.linalg.norm(_f(k), axis=-1)
+    qn = np.linalg.norm(_f(q), axis=-1) * np.sqrt(128)
+    assert np.all(np.abs(kn - 1) < 1e-2) and np.all(np.abs(qn - 1) < 1e-2)
+    assert 0.85 < a.mean() < 0.99 and np.all((a > 0) & (a < 1)) and np.all((b > 0) & (b < 1))
