@@ -218,6 +218,23 @@ moe_status moe_attn_decode_unpacked(const void *q, const void *k_cache, const vo
                                     int64_t kv_head_stride, float scale, void *out, void *ws,
                                     size_t ws_bytes, void *stream);
 
+/* Gated DeltaNet recurrence over T tokens, state resident on chip for the whole scan
+ * ("Optimizing On-Device Inference for Apple Silicon", sections "Qwen creates three distinct
+ * workload shapes" and "Keep recurrent state on chip"), per value head j with key head
+ * kh = j / (n_v / n_k):
+ *     S_t = alpha_t S_{t-1} + beta_t (v_t - alpha_t S_{t-1} k_t) k_t^T,   o_t = S_t q_t
+ * (the gated delta rule; fp32 state and arithmetic, bf16 q, k, v, o).
+ *   q, k   bf16 [T, n_k, d_k]        v  bf16 [T, n_v, d_v]
+ *   alpha, beta  fp32 [T, n_v]       (gate and write strength of each token and head)
+ *   state  fp32 [n_v, d_v, d_k]      S_0 on entry, overwritten with S_T (a prompt chunk
+ *                                    continues from the previous chunk's state)
+ *   out    bf16 [T, n_v, d_v]
+ * Supported: d_k = d_v = 128, n_v a multiple of n_k, 0 <= T <= 2^24 (T = 0 leaves the state
+ * as it is). Pointers 16-byte aligned (alpha and beta 4). No workspace. */
+moe_status moe_gdn_scan(const void *q, const void *k, const void *v, const float *alpha,
+                        const float *beta, int64_t T, int32_t n_k, int32_t n_v, int32_t d_k,
+                        int32_t d_v, float *state, void *out, void *stream);
+
 /* Workspace bytes for moe_stack_forward with chunks of up to chunk_tokens rows. */
 moe_status moe_stack_workspace_bytes(const moe_layer *layers, int32_t n_layers,
                                      int64_t chunk_tokens, size_t *bytes);

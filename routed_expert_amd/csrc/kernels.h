@@ -188,4 +188,17 @@ void attn_plan(int64_t ctx, int n_groups, int *n_split, int64_t *tps);
 // heads_per_group: G (query heads of a KV head share a workgroup) or 1 (one per head)
 hipError_t launch_attn_decode(const AttnArgs &a, int heads_per_group, hipStream_t s);
 
+// Gated DeltaNet recurrence over T tokens (d_k = d_v = 128), state fp32 in and out.
+struct GdnArgs {
+  const uint16_t *q, *k;        // [T, n_k, 128] bf16
+  const uint16_t *v;            // [T, n_v, 128] bf16
+  const float *alpha, *beta;    // [T, n_v]
+  int64_t T;                    // >= 1
+  int n_k, n_v;
+  float *state;                 // [n_v, 128, 128]: S_0 in, S_T out
+  uint16_t *out;                // [T, n_v, 128] bf16
+};
+bool gdn_supported(int n_k, int n_v, int d_k, int d_v);
+hipError_t launch_gdn_scan(const GdnArgs &a, hipStream_t s);
+
 }  // namespace moe

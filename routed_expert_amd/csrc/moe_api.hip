@@ -938,6 +938,36 @@ moe_status moe_attn_decode_unpacked(const void *q, const void *k_cache, const vo
                    ws_bytes, stream, false);
 }
 
+moe_status moe_gdn_scan(const void *q, const void *k, const void *v, const float *alpha,
+                        const float *beta, int64_t T, int32_t n_k, int32_t n_v, int32_t d_k,
+                        int32_t d_v, float *state, void *out, void *stream) {
+  g_err.clear();
+  if (!moe::gdn_supported(n_k, n_v, d_k, d_v))
+    return fail(MOE_E_UNSUPPORTED, "DeltaNet scan needs d_k = d_v = 128 and n_v a multiple of n_k");
+  if (T < 0 || T > kMaxTokens) return fail(MOE_E_INVALID, "T %lld out of range", (long long)T);
+  if (!state) return fail(MOE_E_INVALID, "state must be non-NULL");
+  if (T == 0) return MOE_OK;  // the state stays S_0
+  if (!q || !k || !v || !alpha || !beta || !out)
+    return fail(MOE_E_INVALID, "q, k, v, alpha, beta and out must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(state) ||
+      ((uintptr_t)alpha & 3) || ((uintptr_t)beta & 3))
+    return fail(MOE_E_INVALID, "DeltaNet pointers misaligned");
+  moe::GdnArgs a{};
+  a.q = static_cast<const uint16_t *>(q);
+  a.k = static_cast<const uint16_t *>(k);
+  a.v = static_cast<const uint16_t *>(v);
+  a.alpha = alpha;
+  a.beta = beta;
+  a.T = T;
+  a.n_k = n_k;
+  a.n_v = n_v;
+  a.state = state;
+  a.out = static_cast<uint16_t *>(out);
+  const hipError_t e = moe::launch_gdn_scan(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "moe_gdn_scan");
+  return MOE_OK;
+}
+
 moe_status moe_rmsnorm(const void *h, int64_t T, int32_t hidden, float eps, int32_t act_dtype,
                        void *out, void *stream) {
   g_err.clear();

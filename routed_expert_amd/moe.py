@@ -28,7 +28,8 @@ EXPORTS = ("moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_pack
            "moe_stack_workspace_bytes", "moe_stack_forward", "moe_rmsnorm",
            "moe_profile_enable", "moe_profile_query", "moe_profile_reset",
            "moe_ablation_workspace_bytes", "moe_prefill_ablation",
-           "moe_attn_workspace_bytes", "moe_attn_decode", "moe_attn_decode_unpacked")
+           "moe_attn_workspace_bytes", "moe_attn_decode", "moe_attn_decode_unpacked",
+           "moe_gdn_scan")
 (ABL_NONE, ABL_SEPARATE_DEQUANT, ABL_HOST_ROUTING, ABL_TILE_64, ABL_FIXED_TILE,
  ABL_TILE_128) = range(6)
 ABLATIONS = {"none": ABL_NONE, "separate_dequant": ABL_SEPARATE_DEQUANT,
@@ -110,6 +111,7 @@ def lib():
                             ctypes.c_int),
         "moe_attn_decode_unpacked": ([P, P, P, I32, I32, I32, I64, I64, ctypes.c_float, P, P,
                                       SZ, P], ctypes.c_int),
+        "moe_gdn_scan": ([P, P, P, P, P, I64, I32, I32, I32, I32, P, P, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -324,6 +326,23 @@ def moe_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
     _check("moe_attn_decode", fn(_ptr(q), _ptr(k_cache), _ptr(v_cache), n_q, n_kv, D, ctx,
                                  cap * D, ctypes.c_float(scale), _ptr(out), _ptr(ws),
                                  ws.numel(), _stream(stream)))
+    return out
+
+
+def moe_gdn_scan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+                 beta: torch.Tensor, state: torch.Tensor, out=None, stream=None) -> torch.Tensor:
+    """Gated DeltaNet recurrence over T tokens. q, k [T, n_k, 128] bf16; v [T, n_v, 128] bf16;
+    alpha, beta [T, n_v] fp32; state [n_v, 128, 128] fp32 (updated in place to S_T).
+    Returns out [T, n_v, 128] bf16."""
+    T, n_k, d_k = q.shape
+    n_v, d_v = v.shape[1], v.shape[2]
+    for t in (q, k, v, alpha, beta, state):
+        if not t.is_contiguous():
+            raise ValueError("DeltaNet tensors must be contiguous")
+    out = torch.empty((T, n_v, d_v), dtype=torch.bfloat16, device=q.device) if out is None else out
+    _check("moe_gdn_scan", lib().moe_gdn_scan(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                              T, n_k, n_v, d_k, d_v, _ptr(state), _ptr(out),
+                                              _stream(stream)))
     return out
 
 

@@ -239,3 +239,16 @@ def test_attention_argument_errors_before_any_launch(M):
                              None) == M.E_INVALID
     assert L.moe_attn_decode_unpacked(ctypes.c_void_p(0x100008), k, v, 16, 2, 256, 64,
                                       64 * 256, f, o, ws, need, None) == M.E_INVALID
+
+
+def test_gdn_argument_errors_before_any_launch(M):
+    L = M.lib()
+    p = [ctypes.c_void_p(a) for a in (0x100000, 0x200000, 0x300000, 0x400000, 0x500000)]
+    st, out = ctypes.c_void_p(0x600000), ctypes.c_void_p(0x700000)
+    assert L.moe_gdn_scan(*p, 64, 16, 32, 64, 128, st, out, None) == M.E_UNSUPPORTED
+    assert L.moe_gdn_scan(*p, 64, 16, 24, 128, 128, st, out, None) == M.E_UNSUPPORTED
+    assert L.moe_gdn_scan(*p, -1, 16, 32, 128, 128, st, out, None) == M.E_INVALID
+    assert L.moe_gdn_scan(*p, 64, 16, 32, 128, 128, None, out, None) == M.E_INVALID
+    assert L.moe_gdn_scan(*p, 0, 16, 32, 128, 128, st, out, None) == M.OK   # empty: no-op
+    q_bad = ctypes.c_void_p(0x100008)
+    assert L.moe_gdn_scan(q_bad, *p[1:], 64, 16, 32, 128, 128, st, out, None) == M.E_INVALID
