@@ -26,9 +26,13 @@ namespace moe {
 namespace {
 constexpr int kGdnD = 128;      // d_k = d_v
 constexpr int kGdnChunk = 64;   // tokens staged per block
-constexpr int kGdnRows = 16;    // state rows per workgroup
+constexpr int kGdnLanes = 16;   // lanes per state row (32 measured slower: one more reduction step)
 
-MOE_DEV float row16_sum_g(float v) {
+// sum over the L lanes of an aligned group (xor 16 by permlane swap, the rest by DPP; the
+// rotation by 4 stands for xor 4 right after the xor-8 step)
+template <int L>
+MOE_DEV float group_sum_dpp(float v) {
+  if constexpr (L == 32) v = xor_sum<16>(v);
   v = xor_sum<8>(v);
   v = xor_sum<4>(v);
   v = xor_sum<2>(v);
@@ -36,33 +40,36 @@ MOE_DEV float row16_sum_g(float v) {
 }
 }  // namespace
 
+// L lanes per state row (EL = 128 / L values each), 64 / L rows per wave, RW rows per
+// workgroup of four waves; grid (128 / RW, value heads).
+template <int L>
 __global__ __launch_bounds__(256, 1) void k_gdn_scan(GdnArgs a) {
-  constexpr int D = kGdnD, C = kGdnChunk, R = kGdnRows;
-  const int j = blockIdx.y, i0 = blockIdx.x * R;
+  constexpr int D = kGdnD, C = kGdnChunk, EL = D / L, RW = 4 * (64 / L);
+  const int j = blockIdx.y, i0 = blockIdx.x * RW;
   const int kh = j / (a.n_v / a.n_k);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int g = lane >> 4, l16 = lane & 15;
-  const int rl = wave * 4 + g;  // this lane group's row inside the workgroup
+  const int g = lane / L, lr = lane % L;
+  const int rl = wave * (64 / L) + g;  // this lane group's row inside the workgroup
 
   __shared__ __attribute__((aligned(16))) float sK[C][D];
   __shared__ __attribute__((aligned(16))) float sQ[C][D];
-  __shared__ float sV[C][R];
-  __shared__ float sA[C], sB[C], sKQ[C];
-  __shared__ __attribute__((aligned(16))) uint16_t sO[C][R];
+  __shared__ float sV[C][RW];
+  __shared__ __attribute__((aligned(16))) float4 sS[C];  // alpha, beta, k . q, alpha beta
+  __shared__ __attribute__((aligned(16))) uint16_t sO[C][RW];
 
-  // the row's state, 8 values at d = 8 l16 .. +8
-  float *srow = a.state + ((size_t)j * D + i0 + rl) * D + 8 * l16;
-  float s[8];
-  {
-    const float4 x = *reinterpret_cast<const float4 *>(srow);
-    const float4 y = *reinterpret_cast<const float4 *>(srow + 4);
-    s[0] = x.x; s[1] = x.y; s[2] = x.z; s[3] = x.w;
-    s[4] = y.x; s[5] = y.y; s[6] = y.z; s[7] = y.w;
+  // the row's state, EL values at d = EL lr .. +EL
+  float *srow = a.state + ((size_t)j * D + i0 + rl) * D + EL * lr;
+  float s[EL];
+#pragma unroll
+  for (int e = 0; e < EL; e += 4) {
+    const float4 x = *reinterpret_cast<const float4 *>(srow + e);
+    s[e] = x.x; s[e + 1] = x.y; s[e + 2] = x.z; s[e + 3] = x.w;
   }
 
   // staging registers of one block: q and k (4 x 16 bytes each per thread), the block's v
-  // slice (threads 0..127) or alpha / beta (threads 128..255)
-  uint4 rq[4], rk[4], rv;
+  // slice (threads 0 .. 8 RW - 1: one 16-byte piece each), alpha (128..191), beta (192..255)
+  constexpr int VT = C * RW / 8;  // threads holding v
+  uint4 rq[4], rk[4], rv = {0, 0, 0, 0};
   float rab = 0.f;
   auto fetch = [&](int64_t t0) {
 #pragma unroll
@@ -73,11 +80,11 @@ __global__ __launch_bounds__(256, 1) void k_gdn_scan(GdnArgs a) {
       rq[i] = *reinterpret_cast<const uint4 *>(a.q + off);
       rk[i] = *reinterpret_cast<const uint4 *>(a.k + off);
     }
-    if (tid < 128) {
-      const int tt = tid >> 1;
+    if (tid < VT) {
+      const int tt = tid / (RW / 8), part = tid % (RW / 8);
       const int64_t t = t0 + tt < a.T ? t0 + tt : a.T - 1;
-      rv = *reinterpret_cast<const uint4 *>(a.v + ((size_t)t * a.n_v + j) * D + i0 + 8 * (tid & 1));
-    } else {
+      rv = *reinterpret_cast<const uint4 *>(a.v + ((size_t)t * a.n_v + j) * D + i0 + 8 * part);
+    } else if (tid >= 128) {
       const int tt = (tid - 128) & 63;
       const int64_t t = t0 + tt < a.T ? t0 + tt : a.T - 1;
       rab = (tid < 192 ? a.alpha : a.beta)[(size_t)t * a.n_v + j];
@@ -104,15 +111,10 @@ __global__ __launch_bounds__(256, 1) void k_gdn_scan(GdnArgs a) {
       widen(rq[i], &sQ[tt][8 * part]);
       widen(rk[i], &sK[tt][8 * part]);
     }
-    if (tid < 128) {
-      float tmp[8];
-      widen(rv, tmp);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sV[tid >> 1][8 * (tid & 1) + e] = tmp[e];
-    } else if (tid < 192) {
-      sA[tid - 128] = rab;
-    } else {
-      sB[tid - 192] = rab;
+    if (tid < VT) {
+      widen(rv, &sV[tid / (RW / 8)][8 * (tid % (RW / 8))]);
+    } else if (tid >= 128) {
+      reinterpret_cast<float *>(&sS[(tid - 128) & 63])[tid < 192 ? 0 : 1] = rab;
     }
     __syncthreads();
     {
@@ -123,46 +125,80 @@ __global__ __launch_bounds__(256, 1) void k_gdn_scan(GdnArgs a) {
       for (int e = 0; e < 32; ++e) p = __builtin_fmaf(sK[tt][32 * part + e], sQ[tt][32 * part + e], p);
       p = xor_sum<1>(p);
       p = xor_sum<2>(p);
-      if (part == 0) sKQ[tt] = p;
+      if (part == 0) {
+        float *sc = reinterpret_cast<float *>(&sS[tt]);
+        sc[2] = p;
+        sc[3] = sc[0] * sc[1];
+      }
     }
     __syncthreads();
     if (c + 1 < nch) fetch(t0 + C);  // in flight while this block is scanned
 
-#pragma unroll 2
-    for (int tt = 0; tt < nt; ++tt) {
-      const float4 k0 = *reinterpret_cast<const float4 *>(&sK[tt][8 * l16]);
-      const float4 k1 = *reinterpret_cast<const float4 *>(&sK[tt][8 * l16 + 4]);
-      const float4 q0 = *reinterpret_cast<const float4 *>(&sQ[tt][8 * l16]);
-      const float4 q1 = *reinterpret_cast<const float4 *>(&sQ[tt][8 * l16 + 4]);
-      const float kv[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-      const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-      float pb0 = s[0] * kv[0], pb1 = s[1] * kv[1], pa0 = s[0] * qv[0], pa1 = s[1] * qv[1];
+    // Token tt + 1's operands are requested from LDS before token tt's dependent chain
+    // runs (two register sets in turn, indices clamped so every read is unconditional):
+    // one LDS round trip per token is hidden behind the chain instead of three waited on.
+    struct Tok {
+      float kv[EL], qv[EL];
+      float4 sc;  // alpha, beta, k . q, alpha beta
+      float vr;
+    };
+    auto ld = [&](int tt) {
+      Tok t;
 #pragma unroll
-      for (int e = 2; e < 8; e += 2) {
-        pb0 = __builtin_fmaf(s[e], kv[e], pb0);
-        pb1 = __builtin_fmaf(s[e + 1], kv[e + 1], pb1);
-        pa0 = __builtin_fmaf(s[e], qv[e], pa0);
-        pa1 = __builtin_fmaf(s[e + 1], qv[e + 1], pa1);
+      for (int e = 0; e < EL; e += 4) {
+        const float4 k4 = *reinterpret_cast<const float4 *>(&sK[tt][EL * lr + e]);
+        const float4 q4 = *reinterpret_cast<const float4 *>(&sQ[tt][EL * lr + e]);
+        t.kv[e] = k4.x; t.kv[e + 1] = k4.y; t.kv[e + 2] = k4.z; t.kv[e + 3] = k4.w;
+        t.qv[e] = q4.x; t.qv[e + 1] = q4.y; t.qv[e + 2] = q4.z; t.qv[e + 3] = q4.w;
       }
-      const float b = row16_sum_g(pb0 + pb1);
-      const float av = row16_sum_g(pa0 + pa1);
-      const float al = sA[tt], be = sB[tt];
-      const float cc = be * (sV[tt][rl] - al * b);
-      const float o = __builtin_fmaf(al, av, cc * sKQ[tt]);
+      t.sc = sS[tt];
+      t.vr = sV[tt][rl];
+      return t;
+    };
+    auto step = [&](const Tok &t, int tt) {
+      float pb0 = s[0] * t.kv[0], pb1 = s[1] * t.kv[1];
+      float pa0 = s[0] * t.qv[0], pa1 = s[1] * t.qv[1];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s[e] = __builtin_fmaf(cc, kv[e], al * s[e]);
-      if (l16 == 0) sO[tt][rl] = f32_to_bf16(o);
+      for (int e = 2; e < EL; e += 2) {
+        pb0 = __builtin_fmaf(s[e], t.kv[e], pb0);
+        pb1 = __builtin_fmaf(s[e + 1], t.kv[e + 1], pb1);
+        pa0 = __builtin_fmaf(s[e], t.qv[e], pa0);
+        pa1 = __builtin_fmaf(s[e + 1], t.qv[e + 1], pa1);
+      }
+      const float b = group_sum_dpp<L>(pb0 + pb1);
+      const float av = group_sum_dpp<L>(pa0 + pa1);
+      const float cc = __builtin_fmaf(-t.sc.w, b, t.sc.y * t.vr);  // beta (v - alpha b)
+      const float o = __builtin_fmaf(t.sc.x, av, cc * t.sc.z);
+#pragma unroll
+      for (int e = 0; e < EL; ++e) s[e] = __builtin_fmaf(cc, t.kv[e], t.sc.x * s[e]);
+      sO[tt][rl] = f32_to_bf16(o);  // every lane of the row stores the same value
+    };
+    // Both steps of a pair run unconditionally (a load under a branch is waited for where
+    // the branch joins): a token past the block's end gets alpha = 1, beta = 0, which leaves
+    // the state exactly as it is, and its output lands in an unused row of the staging.
+    // (the scheduling barriers keep the next token's reads ahead of the current chain; left
+    // alone, the scheduler issues them halfway through it, too late to hide their latency)
+    Tok ta = ld(0);
+    for (int tt = 0; tt < nt; tt += 2) {
+      Tok tb = ld(tt + 1 < C ? tt + 1 : C - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      step(ta, tt);
+      ta = ld(tt + 2 < C ? tt + 2 : C - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (tt + 1 >= nt) tb.sc = float4{1.f, 0.f, 0.f, 0.f};  // alpha 1, beta 0
+      step(tb, tt + 1 < C ? tt + 1 : C - 1);
     }
     __syncthreads();
-    // the block's outputs: per token, this workgroup's 16 rows are 32 contiguous bytes
-    if (tid < 2 * nt) {
-      const int tt = tid >> 1, h = tid & 1;
+    // the block's outputs: per token, this workgroup's RW rows are contiguous
+    if (tid < nt * (RW / 8)) {
+      const int tt = tid / (RW / 8), h = tid % (RW / 8);
       *reinterpret_cast<uint4 *>(a.out + ((size_t)(t0 + tt) * a.n_v + j) * D + i0 + 8 * h) =
           *reinterpret_cast<const uint4 *>(&sO[tt][8 * h]);
     }
   }
-  *reinterpret_cast<float4 *>(srow) = float4{s[0], s[1], s[2], s[3]};
-  *reinterpret_cast<float4 *>(srow + 4) = float4{s[4], s[5], s[6], s[7]};
+#pragma unroll
+  for (int e = 0; e < EL; e += 4)
+    *reinterpret_cast<float4 *>(srow + e) = float4{s[e], s[e + 1], s[e + 2], s[e + 3]};
 }
 
 bool gdn_supported(int n_k, int n_v, int d_k, int d_v) {
@@ -170,8 +206,9 @@ bool gdn_supported(int n_k, int n_v, int d_k, int d_v) {
 }
 
 hipError_t launch_gdn_scan(const GdnArgs &a, hipStream_t s) {
-  MOE_LAUNCH("k_gdn_scan", k_gdn_scan, dim3(kGdnD / kGdnRows, (unsigned)a.n_v), dim3(256), 0, s,
-             a);
+  constexpr int RW = 4 * (64 / kGdnLanes);
+  MOE_LAUNCH("k_gdn_scan", k_gdn_scan<kGdnLanes>, dim3(kGdnD / RW, (unsigned)a.n_v), dim3(256), 0,
+             s, a);
   return hipSuccess;
 }
 
