@@ -20,11 +20,12 @@ tokens and a 32,768-token prompt in chunks of 4096 tokens; moe_prefill with 2, 4
 (separate dequantisation pass, host-inspected routing, fixed tile heights) at 512, 2048
 and 4096 tokens beside the product path; grouped-query decode attention (16 query heads,
 2 KV heads, head dimension 256, bf16 cache) over 3,840 to 131,072 cached positions, packed
-and unpacked. Prefill timings start after about 80 ms of sustained calls, past the
+and unpacked; the Gated DeltaNet prompt scan of one layer (2,048 and 8,192 tokens, 32 value
+heads, fp32 state in registers). Prefill timings start after about 80 ms of sustained calls, past the
 lower-clock spell that follows an idle GPU.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-prefill]
-                       [--no-stack] [--no-attention]
+                       [--no-stack] [--no-attention] [--no-gdn]
 """
 import argparse
 import hashlib
@@ -39,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (packed FMA), TFLOP/s
 H, I, E, K_TOP, S = 2048, 512, 256, 8, 1
 N_COPIES = 20
 N_TOKENS = 1000
@@ -356,6 +358,56 @@ def bench_attention(moe, torch, synth, dev, ctxs=ATTN_CTXS, rounds=5):
     return res
 
 
+GDN_TS = (2048, 8192)
+
+
+def synth_gdn_dims():
+    from routed_expert_amd import synth
+    return synth.GDN_K_HEADS, synth.GDN_V_HEADS, synth.GDN_DK, synth.GDN_DV
+
+
+def gdn_flops_per_token():
+    """Algorithmic fp32 FLOP of the DeltaNet recurrence per token (all value heads): per
+    state row two dot products with k and q and the update alpha S + c k, 6 d_k FLOP."""
+    _, n_v, d_k, d_v = synth_gdn_dims()
+    return 6 * d_k * d_v * n_v
+
+
+def bench_gdn(moe, torch, synth, dev, Ts=GDN_TS, reps=10):
+    """Gated DeltaNet prompt scan of one layer (16 key / 32 value heads of 128, fp32 state
+    from zero). Time per call after a warm-up; FLOP/s against the fp32 vector peak; bytes
+    per call for reference (q, k, v, gates in, o out, the state read and written once)."""
+    res = {}
+    n_k, n_v, d_k, d_v = synth_gdn_dims()
+    for T in Ts:
+        q, k, v, a, b = synth.gdn_inputs(T, seed=3)
+        qd, kd, vd = (moe.bf16_from_bits(x, dev) for x in (q, k, v))
+        ad, bd = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+        st = torch.zeros((n_v, d_v, d_k), dtype=torch.float32, device=dev)
+        out = torch.empty((T, n_v, d_v), dtype=torch.bfloat16, device=dev)
+        fn = lambda: moe.moe_gdn_scan(qd, kd, vd, ad, bd, st, out=out)
+        warm_up(fn)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        flops = gdn_flops_per_token() * T
+        nbytes = T * (2 * n_k * d_k * 2 + n_v * d_v * 2 * 2 + n_v * 8) + 2 * n_v * d_v * d_k * 4
+        res[str(T)] = {"us_per_call": round(us, 1), "ns_per_token": round(us * 1e3 / T, 1),
+                       "tflops": round(flops / (us * 1e-6) / 1e12, 2),
+                       "alu_frac": round(flops / (us * 1e-6) / 1e12 / FP32_VECTOR_PEAK_TFLOPS, 3),
+                       "bytes_per_call": nbytes}
+        del qd, kd, vd, ad, bd, st, out
+        torch.cuda.empty_cache()
+    res["bound"] = "alu"
+    res["peak_tflops"] = FP32_VECTOR_PEAK_TFLOPS
+    return res
+
+
 def bench_ablations(moe, torch, synth, dev, Ts=(512, 2048, 4096), rounds=5, calls=20):
     """moe_prefill_ablation on the uniform-routing layer: the product path and each
     rejected design, rounds alternating over the variants after a warm-up; median
@@ -567,6 +619,15 @@ def profile_run(moe, torch, synth, dev, what):
         out = torch.empty_like(q)
         for i in range(400):
             moe.moe_attn_decode(q, ks[i % 16], vs[i % 16], out=out, ws=ws)
+    elif what == "gdn_scan_2k":
+        # one DeltaNet layer's scan of a 2,048-token prompt (32 value heads), 20 calls
+        q, k, v, a, b = synth.gdn_inputs(2048, seed=3)
+        qd, kd, vd = (moe.bf16_from_bits(x, dev) for x in (q, k, v))
+        ad, bd = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+        st = torch.zeros((synth.GDN_V_HEADS, synth.GDN_DV, synth.GDN_DK), dtype=torch.float32,
+                         device=dev)
+        for _ in range(20):
+            moe.moe_gdn_scan(qd, kd, vd, ad, bd, st)
     elif what == "prefill_separate_dequant":
         # the separate-dequantisation ablation (expansion pass + GEMMs on fp16 weights)
         dl = moe.DeviceLayer.from_host(synth.decode_layer(0), dev)
@@ -598,8 +659,10 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-stack", action="store_true")
     ap.add_argument("--no-attention", action="store_true")
+    ap.add_argument("--no-gdn", action="store_true")
     ap.add_argument("--profile", choices=["decode", "prefill_uniform", "prefill_skewed",
-                                          "prefill_separate_dequant", "attn_decode_32k"],
+                                          "prefill_separate_dequant", "attn_decode_32k",
+                                          "gdn_scan_2k"],
                     help="fixed work for rocprofv3 instead of the benchmark")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -657,6 +720,8 @@ def main():
         out["ablations"] = bench_ablations(moe, torch, synth, dev)
     if not args.no_attention:
         out["attention_decode"] = bench_attention(moe, torch, synth, dev)
+    if not args.no_gdn:
+        out["gdn_scan"] = bench_gdn(moe, torch, synth, dev)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(synth)
     print(json.dumps(out), flush=True)
