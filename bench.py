@@ -368,9 +368,10 @@ def synth_gdn_dims():
 
 def gdn_flops_per_token():
     """Algorithmic fp32 FLOP of the DeltaNet recurrence per token (all value heads): per
-    state row two dot products with k and q and the update alpha S + c k, 6 d_k FLOP."""
+    state row two dot products with k and q (2 d_k each) and the update alpha S + c k
+    (3 d_k), 7 d_k FLOP."""
     _, n_v, d_k, d_v = synth_gdn_dims()
-    return 6 * d_k * d_v * n_v
+    return 7 * d_k * d_v * n_v
 
 
 def bench_gdn(moe, torch, synth, dev, Ts=GDN_TS, reps=10):
