@@ -41,11 +41,14 @@ MOE_DEV float group_sum_dpp(float v) {
 }  // namespace
 
 // L lanes per state row (EL = 128 / L values each), 64 / L rows per wave, RW rows per
-// workgroup of four waves; grid (128 / RW, value heads).
+// workgroup of four waves; grid (value heads, 128 / RW). Workgroup ids are dealt over the 8
+// XCDs round-robin, so with the head as the fast grid index all row blocks of a head run on
+// one XCD and its q and k are fetched into that XCD's L2 once (head-major order put them
+// on eight XCDs and read the inputs about four times over from memory).
 template <int L>
 __global__ __launch_bounds__(256, 1) void k_gdn_scan(GdnArgs a) {
   constexpr int D = kGdnD, C = kGdnChunk, EL = D / L, RW = 4 * (64 / L);
-  const int j = blockIdx.y, i0 = blockIdx.x * RW;
+  const int j = blockIdx.x, i0 = blockIdx.y * RW;
   const int kh = j / (a.n_v / a.n_k);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane / L, lr = lane % L;
@@ -207,7 +210,7 @@ bool gdn_supported(int n_k, int n_v, int d_k, int d_v) {
 
 hipError_t launch_gdn_scan(const GdnArgs &a, hipStream_t s) {
   constexpr int RW = 4 * (64 / kGdnLanes);
-  MOE_LAUNCH("k_gdn_scan", k_gdn_scan<kGdnLanes>, dim3(kGdnD / RW, (unsigned)a.n_v), dim3(256), 0,
+  MOE_LAUNCH("k_gdn_scan", k_gdn_scan<kGdnLanes>, dim3((unsigned)a.n_v, kGdnD / RW), dim3(256), 0,
              s, a);
   return hipSuccess;
 }
