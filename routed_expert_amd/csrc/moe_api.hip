@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -884,7 +885,7 @@ moe_status attn_impl(const void *q, const void *k, const void *v, int32_t n_q, i
     return fail(MOE_E_INVALID, "q, k_cache, v_cache, out and ws must be non-NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(ws))
     return fail(MOE_E_INVALID, "attention pointers must be 16-byte aligned");
-  if (!(scale == scale)) return fail(MOE_E_INVALID, "scale is NaN");
+  if (!std::isfinite(scale)) return fail(MOE_E_INVALID, "scale must be finite");
   const int G = n_q / n_kv;
   const int hp = packed ? G : 1;
   moe::AttnArgs a{};

@@ -233,6 +233,9 @@ def test_attention_argument_errors_before_any_launch(M):
     assert L.moe_attn_decode(*args(4096, 4096 * 256, 100)) == M.E_WORKSPACE
     assert L.moe_attn_decode(*args(0, 4096 * 256, need)) == M.E_INVALID
     assert L.moe_attn_decode(*args(4096, 4095 * 256, need)) == M.E_INVALID   # stride < ctx*D
+    inf = ctypes.c_float(float("inf"))
+    assert L.moe_attn_decode(q, k, v, 16, 2, 256, 64, 64 * 256, inf, o, ws, need,
+                             None) == M.E_INVALID
     assert L.moe_attn_decode(q, k, v, 16, 2, 128, 64, 64 * 128, f, o, ws, need,
                              None) == M.E_UNSUPPORTED
     assert L.moe_attn_decode(q, None, v, 16, 2, 256, 64, 64 * 256, f, o, ws, need,
