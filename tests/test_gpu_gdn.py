@@ -58,7 +58,7 @@ def run(M, T, seed, n_k=16, n_v=32, state0=None):
     return out, st, ref_o, ref_s
 
 
-@pytest.mark.parametrize("T", [1, 63, 64, 65, 200, 2048])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 200, 2048, 8192])
 def test_gdn_scan_model_shape(M, T):
     announce(f"moe_gdn_scan 16 key / 32 value heads x 128, T={T}")
     check(*run(M, T, seed=T))
