@@ -579,9 +579,28 @@ def cpu_baseline(synth):
                     break
     except OSError:
         pass
-    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} decode tokens (seeds 1000000..{1000000 + n - 1}) through layer "
-                      f"copy 0, full layer per token, fp64, {dt:.1f} s on {cpu}"}
+    res = {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{n} decode tokens (seeds 1000000..{1000000 + n - 1}) through layer "
+                     f"copy 0, full layer per token, fp64, {dt:.1f} s on {cpu}"}
+    # the oracle beside the other two workloads (bounded samples of their benchmark shapes)
+    ctx = 32768
+    q, k, v = synth.attn_inputs(ctx, seed=5)
+    t0 = time.perf_counter()
+    oracle.attn_decode(q, k, v, synth.ATTN_Q_HEADS, synth.ATTN_KV_HEADS, synth.ATTN_HEAD_DIM ** -0.5)
+    dt_a = time.perf_counter() - t0
+    res["attention_decode"] = {"value": 1.0 / dt_a, "unit": "calls/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"one decode token over {ctx} cached positions, 16 query "
+                                         f"/ 2 KV heads of 256, fp64, {dt_a:.2f} s"}
+    T = 2048
+    gq, gk, gv, ga, gb = synth.gdn_inputs(T, seed=3)
+    t0 = time.perf_counter()
+    oracle.gdn_scan(gq, gk, gv, ga, gb, synth.GDN_K_HEADS, synth.GDN_V_HEADS, nthreads=threads)
+    dt_g = time.perf_counter() - t0
+    res["gdn_scan"] = {"value": T / dt_g, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                       "sample": f"one DeltaNet layer over a {T}-token prompt (32 value heads "
+                                 f"of 128), fp64, {dt_g:.2f} s"}
+    return res
 
 
 COPY_BYTES = 256 << 20
