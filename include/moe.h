@@ -235,6 +235,20 @@ moe_status moe_gdn_scan(const void *q, const void *k, const void *v, const float
                         const float *beta, int64_t T, int32_t n_k, int32_t n_v, int32_t d_k,
                         int32_t d_v, float *state, void *out, void *stream);
 
+/* The same recurrence in its chunked form: tokens in chunks of 32; a first kernel forms, for
+ * every chunk at once, the factors that depend on the inputs only (the WY factors of the
+ * chunk's product of (I - beta k k^T) terms, the values they map to, the gate products and
+ * the query-key products); a second walks the chunks in order with the state in registers,
+ * so the sequential chain is T / 32 chunk steps instead of T token steps. Arguments as
+ * moe_gdn_scan plus a workspace of moe_gdn_chunked_workspace_bytes (about 40 KB per value
+ * head and chunk); results agree with moe_gdn_scan to fp32 rounding. */
+moe_status moe_gdn_chunked_workspace_bytes(int64_t max_tokens, int32_t n_k, int32_t n_v,
+                                           int32_t d_k, int32_t d_v, size_t *bytes);
+moe_status moe_gdn_scan_chunked(const void *q, const void *k, const void *v, const float *alpha,
+                                const float *beta, int64_t T, int32_t n_k, int32_t n_v,
+                                int32_t d_k, int32_t d_v, float *state, void *out, void *ws,
+                                size_t ws_bytes, void *stream);
+
 /* Workspace bytes for moe_stack_forward with chunks of up to chunk_tokens rows. */
 moe_status moe_stack_workspace_bytes(const moe_layer *layers, int32_t n_layers,
                                      int64_t chunk_tokens, size_t *bytes);

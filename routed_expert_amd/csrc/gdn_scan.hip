@@ -204,6 +204,269 @@ __global__ __launch_bounds__(256, 1) void k_gdn_scan(GdnArgs a) {
     *reinterpret_cast<float4 *>(srow + e) = float4{s[e], s[e + 1], s[e + 2], s[e + 3]};
 }
 
+// ---- chunked form ------------------------------------------------------------------------
+// Tokens in chunks of 32 (r = 0..31 inside a chunk, S the state before it). The gate
+// products R[i][r] = prod_{i<j<=r} alpha_j (R[r][r] = 1) and gam_r = prod_{j<=r} alpha_j are
+// formed as products, never as ratios. With G[i][r] = k_i . k_r and M[i][r] = k_i . q_r:
+//   W_r = beta_r (k_r - sum_{i<r} G[i][r] W_i)                (the WY factors of prod (I - b k k^T))
+//   U_r = beta_r (v_r - sum_{i<r} R[i][r] G[i][r] U_i)
+// and then, per state row s (a row of S):
+//   P_i = s . W_i,  Qs_r = s . q_r
+//   o_r = gam_r (Qs_r - sum_{i<=r} M[i][r] P_i) + sum_{i<=r} R[i][r] M[i][r] U_i[row]
+//   s  <- gam_31 s + sum_i (R[i][31] U_i[row] - gam_31 P_i) k_i
+// W, U and the chunk's coefficient tables depend on the inputs only, so k_gdn_prep forms
+// them for every chunk at once; k_gdn_chunks then walks the chunks in order with the state
+// in registers. Tokens past the end get alpha = 1, beta = 0 and zero q, k, v.
+namespace {
+constexpr int kCk = 32;                                 // tokens per chunk
+constexpr int kCkFloats = 2 * kCk * kGdnD + 2 * kCk * kCk + 2 * kCk;  // per (head, chunk)
+constexpr int kPad = kGdnD + 4;                          // LDS row stride (bank spread)
+}  // namespace
+
+size_t gdn_chunk_ws_bytes(int64_t T, int n_v) {
+  return (size_t)((T + kCk - 1) / kCk) * n_v * kCkFloats * 4;
+}
+
+// one workgroup per (value head, chunk): W, U, A1 = M (i <= r), A2 = R M (i <= r),
+// e_i = R[i][31], gam_r
+__global__ __launch_bounds__(256) void k_gdn_prep(GdnArgs a) {
+  constexpr int D = kGdnD, C = kCk;
+  const int j = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+  const int kh = j / (a.n_v / a.n_k);
+  const int64_t t0 = (int64_t)c * C;
+  __shared__ __attribute__((aligned(16))) float sK[C][kPad];
+  __shared__ __attribute__((aligned(16))) float sQ[C][kPad];
+  __shared__ __attribute__((aligned(16))) float sV[C][kPad];
+  __shared__ float sG[C][C + 1], sM[C][C + 1], sR[C][C + 1];
+  __shared__ float sAl[C], sBe[C], sGam[C];
+  // inputs: 32 rows x 16 pieces of 8 values for each of q, k, v
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int f = tid + 256 * i, r = f >> 4, part = f & 15;
+    const int64_t t = t0 + r;
+    uint4 uq = {0, 0, 0, 0}, uk = {0, 0, 0, 0}, uv = {0, 0, 0, 0};
+    if (t < a.T) {
+      const size_t off = ((size_t)t * a.n_k + kh) * D + 8 * part;
+      uq = *reinterpret_cast<const uint4 *>(a.q + off);
+      uk = *reinterpret_cast<const uint4 *>(a.k + off);
+      uv = *reinterpret_cast<const uint4 *>(a.v + ((size_t)t * a.n_v + j) * D + 8 * part);
+    }
+    const uint32_t wq[4] = {uq.x, uq.y, uq.z, uq.w}, wk[4] = {uk.x, uk.y, uk.z, uk.w},
+                   wv[4] = {uv.x, uv.y, uv.z, uv.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sQ[r][8 * part + 2 * e] = bf16lo(wq[e]);
+      sQ[r][8 * part + 2 * e + 1] = bf16hi(wq[e]);
+      sK[r][8 * part + 2 * e] = bf16lo(wk[e]);
+      sK[r][8 * part + 2 * e + 1] = bf16hi(wk[e]);
+      sV[r][8 * part + 2 * e] = bf16lo(wv[e]);
+      sV[r][8 * part + 2 * e + 1] = bf16hi(wv[e]);
+    }
+  }
+  if (tid < C) {
+    const int64_t t = t0 + tid;
+    sAl[tid] = t < a.T ? a.alpha[(size_t)t * a.n_v + j] : 1.f;
+    sBe[tid] = t < a.T ? a.beta[(size_t)t * a.n_v + j] : 0.f;
+  }
+  __syncthreads();
+  // G and M: 2 x 32 x 32 dot products of 128, eight per thread
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const int d = tid + 256 * m, which = d >> 10, i = (d >> 5) & 31, r = d & 31;
+    const float *x = sK[i], *y = which ? sQ[r] : sK[r];
+    float p0 = 0.f, p1 = 0.f;
+#pragma unroll 8
+    for (int e = 0; e < D; e += 2) {
+      p0 = __builtin_fmaf(x[e], y[e], p0);
+      p1 = __builtin_fmaf(x[e + 1], y[e + 1], p1);
+    }
+    (which ? sM : sG)[i][r] = p0 + p1;
+  }
+  // gate products: R[i][r] for r >= i (zero below), gam_r
+  if (tid < C) {
+    float run = 1.f;
+    for (int r = 0; r < C; ++r) {
+      if (r > tid) run *= sAl[r];
+      sR[tid][r] = r >= tid ? run : 0.f;
+    }
+  } else if (tid == C) {
+    float g = 1.f;
+    for (int r = 0; r < C; ++r) {
+      g *= sAl[r];
+      sGam[r] = g;
+    }
+  }
+  __syncthreads();
+  float *ws = a.ws + ((size_t)j * a.nch + c) * kCkFloats;
+  {
+    // forward substitution, one column per thread: W (threads 0..127), U (128..255)
+    const int col = tid & 127, isU = tid >> 7;
+    float x[C];
+#pragma unroll
+    for (int r = 0; r < C; ++r) {
+      float acc = isU ? sV[r][col] : sK[r][col];
+#pragma unroll
+      for (int i = 0; i < r; ++i) {
+        const float g = isU ? sR[i][r] * sG[i][r] : sG[i][r];
+        acc = __builtin_fmaf(-g, x[i], acc);
+      }
+      x[r] = sBe[r] * acc;
+    }
+    float *dst = ws + (isU ? C * D : 0) + col;
+#pragma unroll
+    for (int r = 0; r < C; ++r) dst[r * D] = x[r];
+  }
+  // coefficient tables
+  float *A1 = ws + 2 * C * D, *A2 = A1 + C * C, *E = A2 + C * C, *Gm = E + C;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int f = tid + 256 * m, i = f >> 5, r = f & 31;
+    const float mm = i <= r ? sM[i][r] : 0.f;
+    A1[f] = mm;
+    A2[f] = mm * sR[i][r];
+  }
+  if (tid < C) {
+    E[tid] = sR[tid][C - 1];
+    Gm[tid] = sGam[tid];
+  }
+}
+
+// grid (value heads, 8 row slices of 16), the chunks in order; layout of the register scan
+// (one state row per 16-lane DPP row, 8 values per lane)
+__global__ __launch_bounds__(256, 1) void k_gdn_chunks(GdnArgs a) {
+  constexpr int D = kGdnD, C = kCk, R = 16, EL = 8;
+  const int j = blockIdx.x, i0 = blockIdx.y * R;
+  const int kh = j / (a.n_v / a.n_k);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, lr = lane & 15;
+  const int rl = wave * 4 + g;  // state row of this lane group
+
+  __shared__ __attribute__((aligned(16))) float sW[C][kPad];
+  __shared__ __attribute__((aligned(16))) float sQ[C][kPad];
+  __shared__ __attribute__((aligned(16))) float sK[C][kPad];
+  __shared__ float sU[C][R];
+  __shared__ float sA1[C][C], sA2[C][C], sE[C], sGm[C];
+  __shared__ __attribute__((aligned(16))) uint16_t sO[C][R];
+
+  float *srow = a.state + ((size_t)j * D + i0 + rl) * D + EL * lr;
+  float s[EL];
+  {
+    const float4 x = *reinterpret_cast<const float4 *>(srow);
+    const float4 y = *reinterpret_cast<const float4 *>(srow + 4);
+    s[0] = x.x; s[1] = x.y; s[2] = x.z; s[3] = x.w;
+    s[4] = y.x; s[5] = y.y; s[6] = y.z; s[7] = y.w;
+  }
+  for (int c = 0; c < a.nch; ++c) {
+    const int64_t t0 = (int64_t)c * C;
+    const int n = (int)(a.T - t0 < C ? a.T - t0 : C);
+    const float *ws = a.ws + ((size_t)j * a.nch + c) * kCkFloats;
+    __syncthreads();  // the previous chunk's tables and outputs are consumed
+    // stage: W (fp32), q and k of the key head (bf16 -> fp32), U of this slice, the tables
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int f = tid + 256 * m, r = f >> 5, part = f & 31;
+      *reinterpret_cast<float4 *>(&sW[r][4 * part]) =
+          *reinterpret_cast<const float4 *>(ws + r * D + 4 * part);
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int f = tid + 256 * m, r = f >> 4, part = f & 15;
+      const int64_t t = t0 + r < a.T ? t0 + r : a.T - 1;
+      const size_t off = ((size_t)t * a.n_k + kh) * D + 8 * part;
+      const uint4 uq = *reinterpret_cast<const uint4 *>(a.q + off);
+      const uint4 uk = *reinterpret_cast<const uint4 *>(a.k + off);
+      const uint32_t wq[4] = {uq.x, uq.y, uq.z, uq.w}, wk[4] = {uk.x, uk.y, uk.z, uk.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sQ[r][8 * part + 2 * e] = bf16lo(wq[e]);
+        sQ[r][8 * part + 2 * e + 1] = bf16hi(wq[e]);
+        sK[r][8 * part + 2 * e] = bf16lo(wk[e]);
+        sK[r][8 * part + 2 * e + 1] = bf16hi(wk[e]);
+      }
+    }
+    if (tid < 128) {
+      const int r = tid >> 2, part = tid & 3;
+      *reinterpret_cast<float4 *>(&sU[r][4 * part]) =
+          *reinterpret_cast<const float4 *>(ws + C * D + r * D + i0 + 4 * part);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int f = tid + 256 * m;
+      (&sA1[0][0])[f] = ws[2 * C * D + f];
+      (&sA2[0][0])[f] = ws[2 * C * D + C * C + f];
+    }
+    if (tid < C) {
+      sE[tid] = ws[2 * C * D + 2 * C * C + tid];
+      sGm[tid] = ws[2 * C * D + 2 * C * C + C + tid];
+    }
+    __syncthreads();
+    // P_i = s . W_i and Qs_r = s . q_r for the 32 tokens, reduced over the row's 16 lanes
+    float P[C], Qs[C];
+#pragma unroll
+    for (int r = 0; r < C; ++r) {
+      const float4 w0 = *reinterpret_cast<const float4 *>(&sW[r][EL * lr]);
+      const float4 w1 = *reinterpret_cast<const float4 *>(&sW[r][EL * lr + 4]);
+      const float4 q0 = *reinterpret_cast<const float4 *>(&sQ[r][EL * lr]);
+      const float4 q1 = *reinterpret_cast<const float4 *>(&sQ[r][EL * lr + 4]);
+      float pw = s[0] * w0.x, pq = s[0] * q0.x;
+      pw = __builtin_fmaf(s[1], w0.y, pw); pq = __builtin_fmaf(s[1], q0.y, pq);
+      pw = __builtin_fmaf(s[2], w0.z, pw); pq = __builtin_fmaf(s[2], q0.z, pq);
+      pw = __builtin_fmaf(s[3], w0.w, pw); pq = __builtin_fmaf(s[3], q0.w, pq);
+      pw = __builtin_fmaf(s[4], w1.x, pw); pq = __builtin_fmaf(s[4], q1.x, pq);
+      pw = __builtin_fmaf(s[5], w1.y, pw); pq = __builtin_fmaf(s[5], q1.y, pq);
+      pw = __builtin_fmaf(s[6], w1.z, pw); pq = __builtin_fmaf(s[6], q1.z, pq);
+      pw = __builtin_fmaf(s[7], w1.w, pw); pq = __builtin_fmaf(s[7], q1.w, pq);
+      P[r] = group_sum_dpp<16>(pw);
+      Qs[r] = group_sum_dpp<16>(pq);
+    }
+    // outputs: lane lr takes tokens 2 lr and 2 lr + 1 of this row
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 2 * lr + h;
+      float acc1 = 0.f, acc2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < C; ++i) {
+        acc1 = __builtin_fmaf(sA1[i][r], P[i], acc1);
+        acc2 = __builtin_fmaf(sA2[i][r], sU[i][rl], acc2);
+      }
+      float qsr = Qs[0];
+#pragma unroll
+      for (int i = 1; i < C; ++i) qsr = r == i ? Qs[i] : qsr;
+      sO[r][rl] = f32_to_bf16(__builtin_fmaf(sGm[r], qsr - acc1, acc2));
+    }
+    // state: s <- gam_31 s + sum_i (e_i U_i - gam_31 P_i) k_i
+    const float gl = sGm[C - 1];
+#pragma unroll
+    for (int e = 0; e < EL; ++e) s[e] *= gl;
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      const float ci = __builtin_fmaf(sE[i], sU[i][rl], -gl * P[i]);
+      const float4 k0 = *reinterpret_cast<const float4 *>(&sK[i][EL * lr]);
+      const float4 k1 = *reinterpret_cast<const float4 *>(&sK[i][EL * lr + 4]);
+      s[0] = __builtin_fmaf(ci, k0.x, s[0]); s[1] = __builtin_fmaf(ci, k0.y, s[1]);
+      s[2] = __builtin_fmaf(ci, k0.z, s[2]); s[3] = __builtin_fmaf(ci, k0.w, s[3]);
+      s[4] = __builtin_fmaf(ci, k1.x, s[4]); s[5] = __builtin_fmaf(ci, k1.y, s[5]);
+      s[6] = __builtin_fmaf(ci, k1.z, s[6]); s[7] = __builtin_fmaf(ci, k1.w, s[7]);
+    }
+    __syncthreads();
+    if (tid < 2 * n) {
+      const int r = tid >> 1, h = tid & 1;
+      *reinterpret_cast<uint4 *>(a.out + ((size_t)(t0 + r) * a.n_v + j) * D + i0 + 8 * h) =
+          *reinterpret_cast<const uint4 *>(&sO[r][8 * h]);
+    }
+  }
+  *reinterpret_cast<float4 *>(srow) = float4{s[0], s[1], s[2], s[3]};
+  *reinterpret_cast<float4 *>(srow + 4) = float4{s[4], s[5], s[6], s[7]};
+}
+
+hipError_t launch_gdn_chunked(const GdnArgs &a, hipStream_t s) {
+  MOE_LAUNCH("k_gdn_prep", k_gdn_prep, dim3((unsigned)a.n_v, (unsigned)a.nch), dim3(256), 0, s,
+             a);
+  MOE_LAUNCH("k_gdn_chunks", k_gdn_chunks, dim3((unsigned)a.n_v, kGdnD / 16), dim3(256), 0, s,
+             a);
+  return hipSuccess;
+}
+
 bool gdn_supported(int n_k, int n_v, int d_k, int d_v) {
   return n_k > 0 && n_v > 0 && n_v % n_k == 0 && d_k == kGdnD && d_v == kGdnD;
 }

@@ -197,8 +197,12 @@ struct GdnArgs {
   int n_k, n_v;
   float *state;                 // [n_v, 128, 128]: S_0 in, S_T out
   uint16_t *out;                // [T, n_v, 128] bf16
+  float *ws = nullptr;          // chunked form: per (value head, chunk) factors and tables
+  int nch = 0;                  // chunks of 32 tokens
 };
 bool gdn_supported(int n_k, int n_v, int d_k, int d_v);
 hipError_t launch_gdn_scan(const GdnArgs &a, hipStream_t s);
+size_t gdn_chunk_ws_bytes(int64_t T, int n_v);
+hipError_t launch_gdn_chunked(const GdnArgs &a, hipStream_t s);
 
 }  // namespace moe

@@ -969,6 +969,55 @@ moe_status moe_gdn_scan(const void *q, const void *k, const void *v, const float
   return MOE_OK;
 }
 
+moe_status moe_gdn_chunked_workspace_bytes(int64_t max_tokens, int32_t n_k, int32_t n_v,
+                                           int32_t d_k, int32_t d_v, size_t *bytes) {
+  g_err.clear();
+  if (!bytes) return fail(MOE_E_INVALID, "bytes is NULL");
+  if (!moe::gdn_supported(n_k, n_v, d_k, d_v))
+    return fail(MOE_E_UNSUPPORTED, "DeltaNet scan needs d_k = d_v = 128 and n_v a multiple of n_k");
+  if (max_tokens < 0 || max_tokens > kMaxTokens)
+    return fail(MOE_E_INVALID, "max_tokens %lld out of range", (long long)max_tokens);
+  *bytes = moe::gdn_chunk_ws_bytes(max_tokens, n_v);
+  return MOE_OK;
+}
+
+moe_status moe_gdn_scan_chunked(const void *q, const void *k, const void *v, const float *alpha,
+                                const float *beta, int64_t T, int32_t n_k, int32_t n_v,
+                                int32_t d_k, int32_t d_v, float *state, void *out, void *ws,
+                                size_t ws_bytes, void *stream) {
+  g_err.clear();
+  if (!moe::gdn_supported(n_k, n_v, d_k, d_v))
+    return fail(MOE_E_UNSUPPORTED, "DeltaNet scan needs d_k = d_v = 128 and n_v a multiple of n_k");
+  if (T < 0 || T > kMaxTokens) return fail(MOE_E_INVALID, "T %lld out of range", (long long)T);
+  if (!state) return fail(MOE_E_INVALID, "state must be non-NULL");
+  if (T == 0) return MOE_OK;  // the state stays S_0
+  if (!q || !k || !v || !alpha || !beta || !out || !ws)
+    return fail(MOE_E_INVALID, "q, k, v, alpha, beta, out and ws must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(state) ||
+      !aligned16(ws) || ((uintptr_t)alpha & 3) || ((uintptr_t)beta & 3))
+    return fail(MOE_E_INVALID, "DeltaNet pointers misaligned");
+  const size_t need = moe::gdn_chunk_ws_bytes(T, n_v);
+  if (ws_bytes < need)
+    return fail(MOE_E_WORKSPACE, "workspace %zu bytes < %zu needed for T=%lld", ws_bytes, need,
+                (long long)T);
+  moe::GdnArgs a{};
+  a.q = static_cast<const uint16_t *>(q);
+  a.k = static_cast<const uint16_t *>(k);
+  a.v = static_cast<const uint16_t *>(v);
+  a.alpha = alpha;
+  a.beta = beta;
+  a.T = T;
+  a.n_k = n_k;
+  a.n_v = n_v;
+  a.state = state;
+  a.out = static_cast<uint16_t *>(out);
+  a.ws = static_cast<float *>(ws);
+  a.nch = (int)((T + 31) / 32);
+  const hipError_t e = moe::launch_gdn_chunked(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "moe_gdn_scan_chunked");
+  return MOE_OK;
+}
+
 moe_status moe_rmsnorm(const void *h, int64_t T, int32_t hidden, float eps, int32_t act_dtype,
                        void *out, void *stream) {
   g_err.clear();

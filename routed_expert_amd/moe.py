@@ -29,7 +29,7 @@ EXPORTS = ("moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_pack
            "moe_profile_enable", "moe_profile_query", "moe_profile_reset",
            "moe_ablation_workspace_bytes", "moe_prefill_ablation",
            "moe_attn_workspace_bytes", "moe_attn_decode", "moe_attn_decode_unpacked",
-           "moe_gdn_scan")
+           "moe_gdn_scan", "moe_gdn_chunked_workspace_bytes", "moe_gdn_scan_chunked")
 (ABL_NONE, ABL_SEPARATE_DEQUANT, ABL_HOST_ROUTING, ABL_TILE_64, ABL_FIXED_TILE,
  ABL_TILE_128) = range(6)
 ABLATIONS = {"none": ABL_NONE, "separate_dequant": ABL_SEPARATE_DEQUANT,
@@ -112,6 +112,10 @@ def lib():
         "moe_attn_decode_unpacked": ([P, P, P, I32, I32, I32, I64, I64, ctypes.c_float, P, P,
                                       SZ, P], ctypes.c_int),
         "moe_gdn_scan": ([P, P, P, P, P, I64, I32, I32, I32, I32, P, P, P], ctypes.c_int),
+        "moe_gdn_chunked_workspace_bytes": ([I64, I32, I32, I32, I32, ctypes.POINTER(SZ)],
+                                            ctypes.c_int),
+        "moe_gdn_scan_chunked": ([P, P, P, P, P, I64, I32, I32, I32, I32, P, P, P, SZ, P],
+                                 ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -343,6 +347,31 @@ def moe_gdn_scan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch
     _check("moe_gdn_scan", lib().moe_gdn_scan(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                               T, n_k, n_v, d_k, d_v, _ptr(state), _ptr(out),
                                               _stream(stream)))
+    return out
+
+
+def gdn_chunked_workspace(T: int, n_k: int, n_v: int, device="cuda") -> torch.Tensor:
+    n = ctypes.c_size_t(0)
+    _check("moe_gdn_chunked_workspace_bytes",
+           lib().moe_gdn_chunked_workspace_bytes(int(T), n_k, n_v, 128, 128, ctypes.byref(n)))
+    return torch.empty(n.value, dtype=torch.uint8, device=device)
+
+
+def moe_gdn_scan_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+                         beta: torch.Tensor, state: torch.Tensor, out=None, ws=None,
+                         stream=None) -> torch.Tensor:
+    """moe_gdn_scan in its chunked form (32-token chunks; workspace as gdn_chunked_workspace)."""
+    T, n_k, d_k = q.shape
+    n_v, d_v = v.shape[1], v.shape[2]
+    for t in (q, k, v, alpha, beta, state):
+        if not t.is_contiguous():
+            raise ValueError("DeltaNet tensors must be contiguous")
+    out = torch.empty((T, n_v, d_v), dtype=torch.bfloat16, device=q.device) if out is None else out
+    ws = gdn_chunked_workspace(max(T, 1), n_k, n_v, q.device) if ws is None else ws
+    _check("moe_gdn_scan_chunked",
+           lib().moe_gdn_scan_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), T, n_k,
+                                      n_v, d_k, d_v, _ptr(state), _ptr(out), _ptr(ws),
+                                      ws.numel(), _stream(stream)))
     return out
 
 

@@ -48,32 +48,39 @@ def check(out, st, ref_o, ref_s):
     assert np.abs(s - ref_s).max() <= 1e-4 * srms, float(np.abs(s - ref_s).max() / srms)
 
 
-def run(M, T, seed, n_k=16, n_v=32, state0=None):
+def run(M, T, seed, n_k=16, n_v=32, state0=None, chunked=False):
     q, k, v, a, b = synth.gdn_inputs(T, seed=seed, n_k=n_k, n_v=n_v)
     s0 = np.zeros((n_v, 128, 128), np.float32) if state0 is None else state0.astype(np.float32)
     st = torch.from_numpy(s0.copy()).to(DEV)
-    out = M.moe_gdn_scan(*dev_inputs(M, q, k, v, a, b), st)
+    scan = M.moe_gdn_scan_chunked if chunked else M.moe_gdn_scan
+    out = scan(*dev_inputs(M, q, k, v, a, b), st)
     torch.cuda.synchronize()
     ref_o, ref_s = oracle.gdn_scan(q, k, v, a, b, n_k, n_v, s0.astype(np.float64))
     return out, st, ref_o, ref_s
 
 
-@pytest.mark.parametrize("T", [1, 63, 64, 65, 200, 2048, 8192])
-def test_gdn_scan_model_shape(M, T):
-    announce(f"moe_gdn_scan 16 key / 32 value heads x 128, T={T}")
-    check(*run(M, T, seed=T))
+FORMS = [False, True]  # token by token (moe_gdn_scan), chunked (moe_gdn_scan_chunked)
 
 
-def test_gdn_scan_from_a_nonzero_state(M):
-    announce("moe_gdn_scan T=300 from a random initial state")
+@pytest.mark.parametrize("chunked", FORMS)
+@pytest.mark.parametrize("T", [1, 31, 32, 33, 63, 64, 65, 200, 2048, 8192])
+def test_gdn_scan_model_shape(M, T, chunked):
+    announce(f"moe_gdn_scan{'_chunked' if chunked else ''} 16 key / 32 value heads x 128, T={T}")
+    check(*run(M, T, seed=T, chunked=chunked))
+
+
+@pytest.mark.parametrize("chunked", FORMS)
+def test_gdn_scan_from_a_nonzero_state(M, chunked):
+    announce(f"moe_gdn_scan{'_chunked' if chunked else ''} T=300 from a random initial state")
     s0 = np.random.default_rng(9).standard_normal((32, 128, 128)) * 0.5
-    check(*run(M, 300, seed=9, state0=s0))
+    check(*run(M, 300, seed=9, state0=s0, chunked=chunked))
 
 
+@pytest.mark.parametrize("chunked", FORMS)
 @pytest.mark.parametrize("n_k,n_v", [(4, 4), (1, 8), (8, 24)])
-def test_gdn_scan_other_head_counts(M, n_k, n_v):
-    announce(f"moe_gdn_scan {n_k} key / {n_v} value heads, T=150")
-    check(*run(M, 150, seed=n_k + n_v, n_k=n_k, n_v=n_v))
+def test_gdn_scan_other_head_counts(M, n_k, n_v, chunked):
+    announce(f"moe_gdn_scan{'_chunked' if chunked else ''} {n_k} key / {n_v} value heads, T=150")
+    check(*run(M, 150, seed=n_k + n_v, n_k=n_k, n_v=n_v, chunked=chunked))
 
 
 def test_gdn_scan_continues_bit_for_bit(M):
