@@ -386,23 +386,30 @@ def bench_gdn(moe, torch, synth, dev, Ts=GDN_TS, reps=10):
         ad, bd = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
         st = torch.zeros((n_v, d_v, d_k), dtype=torch.float32, device=dev)
         out = torch.empty((T, n_v, d_v), dtype=torch.bfloat16, device=dev)
+        ws = moe.gdn_chunked_workspace(T, n_k, n_v, dev)
         fn = lambda: moe.moe_gdn_scan(qd, kd, vd, ad, bd, st, out=out)
+        fc = lambda: moe.moe_gdn_scan_chunked(qd, kd, vd, ad, bd, st, out=out, ws=ws)
         warm_up(fn)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
+
+        def timed(f):
+            e0.record()
+            for _ in range(reps):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / reps
+
+        us = timed(fn)
+        us_chunked = timed(fc)
         flops = gdn_flops_per_token() * T
         nbytes = T * (2 * n_k * d_k * 2 + n_v * d_v * 2 * 2 + n_v * 8) + 2 * n_v * d_v * d_k * 4
         res[str(T)] = {"us_per_call": round(us, 1), "ns_per_token": round(us * 1e3 / T, 1),
                        "tflops": round(flops / (us * 1e-6) / 1e12, 2),
                        "alu_frac": round(flops / (us * 1e-6) / 1e12 / FP32_VECTOR_PEAK_TFLOPS, 3),
-                       "bytes_per_call": nbytes}
-        del qd, kd, vd, ad, bd, st, out
+                       "bytes_per_call": nbytes, "chunked_us_per_call": round(us_chunked, 1)}
+        del qd, kd, vd, ad, bd, st, out, ws
         torch.cuda.empty_cache()
     res["bound"] = "alu"
     res["peak_tflops"] = FP32_VECTOR_PEAK_TFLOPS

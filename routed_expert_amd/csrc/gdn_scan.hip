@@ -237,7 +237,7 @@ __global__ __launch_bounds__(256) void k_gdn_prep(GdnArgs a) {
   __shared__ __attribute__((aligned(16))) float sK[C][kPad];
   __shared__ __attribute__((aligned(16))) float sQ[C][kPad];
   __shared__ __attribute__((aligned(16))) float sV[C][kPad];
-  __shared__ float sG[C][C + 1], sM[C][C + 1], sR[C][C + 1];
+  __shared__ float sG[C][C + 1], sM[C][C + 1], sR[C][C + 1], sGU[C][C + 1];
   __shared__ float sAl[C], sBe[C], sGam[C];
   // inputs: 32 rows x 16 pieces of 8 values for each of q, k, v
 #pragma unroll
@@ -273,12 +273,16 @@ __global__ __launch_bounds__(256) void k_gdn_prep(GdnArgs a) {
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
     const int d = tid + 256 * m, which = d >> 10, i = (d >> 5) & 31, r = d & 31;
-    const float *x = sK[i], *y = which ? sQ[r] : sK[r];
+    const float4 *x = reinterpret_cast<const float4 *>(sK[i]);
+    const float4 *y = reinterpret_cast<const float4 *>(which ? sQ[r] : sK[r]);
     float p0 = 0.f, p1 = 0.f;
 #pragma unroll 8
-    for (int e = 0; e < D; e += 2) {
-      p0 = __builtin_fmaf(x[e], y[e], p0);
-      p1 = __builtin_fmaf(x[e + 1], y[e + 1], p1);
+    for (int e = 0; e < D / 4; ++e) {
+      const float4 u = x[e], w = y[e];
+      p0 = __builtin_fmaf(u.x, w.x, p0);
+      p1 = __builtin_fmaf(u.y, w.y, p1);
+      p0 = __builtin_fmaf(u.z, w.z, p0);
+      p1 = __builtin_fmaf(u.w, w.w, p1);
     }
     (which ? sM : sG)[i][r] = p0 + p1;
   }
@@ -297,6 +301,8 @@ __global__ __launch_bounds__(256) void k_gdn_prep(GdnArgs a) {
     }
   }
   __syncthreads();
+  for (int f = tid; f < C * C; f += 256) sGU[f >> 5][f & 31] = sR[f >> 5][f & 31] * sG[f >> 5][f & 31];
+  __syncthreads();
   float *ws = a.ws + ((size_t)j * a.nch + c) * kCkFloats;
   {
     // forward substitution, one column per thread: W (threads 0..127), U (128..255)
@@ -307,7 +313,7 @@ __global__ __launch_bounds__(256) void k_gdn_prep(GdnArgs a) {
       float acc = isU ? sV[r][col] : sK[r][col];
 #pragma unroll
       for (int i = 0; i < r; ++i) {
-        const float g = isU ? sR[i][r] * sG[i][r] : sG[i][r];
+        const float g = isU ? sGU[i][r] : sG[i][r];
         acc = __builtin_fmaf(-g, x[i], acc);
       }
       x[r] = sBe[r] * acc;
@@ -316,11 +322,11 @@ __global__ __launch_bounds__(256) void k_gdn_prep(GdnArgs a) {
 #pragma unroll
     for (int r = 0; r < C; ++r) dst[r * D] = x[r];
   }
-  // coefficient tables
+  // coefficient tables, token-major: A1[r][i] = M[i][r], A2[r][i] = R[i][r] M[i][r] (i <= r)
   float *A1 = ws + 2 * C * D, *A2 = A1 + C * C, *E = A2 + C * C, *Gm = E + C;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const int f = tid + 256 * m, i = f >> 5, r = f & 31;
+    const int f = tid + 256 * m, r = f >> 5, i = f & 31;
     const float mm = i <= r ? sM[i][r] : 0.f;
     A1[f] = mm;
     A2[f] = mm * sR[i][r];
@@ -344,8 +350,13 @@ __global__ __launch_bounds__(256, 1) void k_gdn_chunks(GdnArgs a) {
   __shared__ __attribute__((aligned(16))) float sW[C][kPad];
   __shared__ __attribute__((aligned(16))) float sQ[C][kPad];
   __shared__ __attribute__((aligned(16))) float sK[C][kPad];
-  __shared__ float sU[C][R];
-  __shared__ float sA1[C][C], sA2[C][C], sE[C], sGm[C];
+  __shared__ __attribute__((aligned(16))) float sU[R][C + 4];    // U_i[row], row-major
+  __shared__ __attribute__((aligned(16))) float sA1[C][C + 4];   // [r][i]
+  __shared__ __attribute__((aligned(16))) float sA2[C][C + 4];
+  __shared__ __attribute__((aligned(16))) float sP[R][C + 4];    // P_i of each row
+  __shared__ __attribute__((aligned(16))) float sQs[R][C + 4];   // Qs_r of each row
+  __shared__ __attribute__((aligned(16))) float sE[C];
+  __shared__ float sGm[C];
   __shared__ __attribute__((aligned(16))) uint16_t sO[C][R];
 
   float *srow = a.state + ((size_t)j * D + i0 + rl) * D + EL * lr;
@@ -356,26 +367,52 @@ __global__ __launch_bounds__(256, 1) void k_gdn_chunks(GdnArgs a) {
     s[0] = x.x; s[1] = x.y; s[2] = x.z; s[3] = x.w;
     s[4] = y.x; s[5] = y.y; s[6] = y.z; s[7] = y.w;
   }
-  for (int c = 0; c < a.nch; ++c) {
-    const int64_t t0 = (int64_t)c * C;
-    const int n = (int)(a.T - t0 < C ? a.T - t0 : C);
+  // staging registers of one chunk (loaded a chunk ahead, stored to LDS after the scan)
+  float4 rW0, rW1, rW2, rW3, rA1, rA2, rU;  // named, not an array (an array went to scratch)
+  uint4 rq[2], rk[2];
+  float rEG = 0.f;
+  auto fetch = [&](int c) {
     const float *ws = a.ws + ((size_t)j * a.nch + c) * kCkFloats;
-    __syncthreads();  // the previous chunk's tables and outputs are consumed
-    // stage: W (fp32), q and k of the key head (bf16 -> fp32), U of this slice, the tables
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    const int64_t t0 = (int64_t)c * C;
+    auto ldw = [&](int m) {
       const int f = tid + 256 * m, r = f >> 5, part = f & 31;
-      *reinterpret_cast<float4 *>(&sW[r][4 * part]) =
-          *reinterpret_cast<const float4 *>(ws + r * D + 4 * part);
-    }
+      return *reinterpret_cast<const float4 *>(ws + r * D + 4 * part);
+    };
+    rW0 = ldw(0);
+    rW1 = ldw(1);
+    rW2 = ldw(2);
+    rW3 = ldw(3);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const int f = tid + 256 * m, r = f >> 4, part = f & 15;
       const int64_t t = t0 + r < a.T ? t0 + r : a.T - 1;
       const size_t off = ((size_t)t * a.n_k + kh) * D + 8 * part;
-      const uint4 uq = *reinterpret_cast<const uint4 *>(a.q + off);
-      const uint4 uk = *reinterpret_cast<const uint4 *>(a.k + off);
-      const uint32_t wq[4] = {uq.x, uq.y, uq.z, uq.w}, wk[4] = {uk.x, uk.y, uk.z, uk.w};
+      rq[m] = *reinterpret_cast<const uint4 *>(a.q + off);
+      rk[m] = *reinterpret_cast<const uint4 *>(a.k + off);
+    }
+    rA1 = *reinterpret_cast<const float4 *>(ws + 2 * C * D + 4 * tid);
+    rA2 = *reinterpret_cast<const float4 *>(ws + 2 * C * D + C * C + 4 * tid);
+    {
+      // U_i[i0 .. i0+15] for the 32 tokens: 128 pieces of 4 (threads 0..127)
+      const int i = (tid & 127) >> 2, part = tid & 3;
+      rU = *reinterpret_cast<const float4 *>(ws + C * D + i * D + i0 + 4 * part);
+    }
+    if (tid < 2 * C) rEG = ws[2 * C * D + 2 * C * C + tid];
+  };
+  auto stage = [&]() {
+    auto stw = [&](int m, float4 w) {
+      const int f = tid + 256 * m, r = f >> 5, part = f & 31;
+      *reinterpret_cast<float4 *>(&sW[r][4 * part]) = w;
+    };
+    stw(0, rW0);
+    stw(1, rW1);
+    stw(2, rW2);
+    stw(3, rW3);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int f = tid + 256 * m, r = f >> 4, part = f & 15;
+      const uint32_t wq[4] = {rq[m].x, rq[m].y, rq[m].z, rq[m].w};
+      const uint32_t wk[4] = {rk[m].x, rk[m].y, rk[m].z, rk[m].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         sQ[r][8 * part + 2 * e] = bf16lo(wq[e]);
@@ -384,25 +421,31 @@ __global__ __launch_bounds__(256, 1) void k_gdn_chunks(GdnArgs a) {
         sK[r][8 * part + 2 * e + 1] = bf16hi(wk[e]);
       }
     }
+    *reinterpret_cast<float4 *>(&sA1[tid >> 3][4 * (tid & 7)]) = rA1;
+    *reinterpret_cast<float4 *>(&sA2[tid >> 3][4 * (tid & 7)]) = rA2;
     if (tid < 128) {
-      const int r = tid >> 2, part = tid & 3;
-      *reinterpret_cast<float4 *>(&sU[r][4 * part]) =
-          *reinterpret_cast<const float4 *>(ws + C * D + r * D + i0 + 4 * part);
+      const int i = tid >> 2, part = tid & 3;
+      sU[4 * part][i] = rU.x;
+      sU[4 * part + 1][i] = rU.y;
+      sU[4 * part + 2][i] = rU.z;
+      sU[4 * part + 3][i] = rU.w;
     }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int f = tid + 256 * m;
-      (&sA1[0][0])[f] = ws[2 * C * D + f];
-      (&sA2[0][0])[f] = ws[2 * C * D + C * C + f];
-    }
-    if (tid < C) {
-      sE[tid] = ws[2 * C * D + 2 * C * C + tid];
-      sGm[tid] = ws[2 * C * D + 2 * C * C + C + tid];
-    }
+    if (tid < C) sE[tid] = rEG;
+    else if (tid < 2 * C) sGm[tid - C] = rEG;
+  };
+
+  fetch(0);
+  for (int c = 0; c < a.nch; ++c) {
+    const int64_t t0 = (int64_t)c * C;
+    const int n = (int)(a.T - t0 < C ? a.T - t0 : C);
+    __syncthreads();  // the previous chunk's tables and outputs are consumed
+    stage();
     __syncthreads();
-    // P_i = s . W_i and Qs_r = s . q_r for the 32 tokens, reduced over the row's 16 lanes
-    float P[C], Qs[C];
-#pragma unroll
+    if (c + 1 < a.nch) fetch(c + 1);  // in flight during this chunk
+    // P_i = s . W_i and Qs_r = s . q_r, reduced over the row's 16 lanes; lane (r & 15)
+    // keeps token r's pair in LDS (partial unrolling: fully unrolled, the scheduler hoists
+    // every token's reads and runs out of registers)
+#pragma unroll 4
     for (int r = 0; r < C; ++r) {
       const float4 w0 = *reinterpret_cast<const float4 *>(&sW[r][EL * lr]);
       const float4 w1 = *reinterpret_cast<const float4 *>(&sW[r][EL * lr + 4]);
@@ -416,37 +459,53 @@ __global__ __launch_bounds__(256, 1) void k_gdn_chunks(GdnArgs a) {
       pw = __builtin_fmaf(s[5], w1.y, pw); pq = __builtin_fmaf(s[5], q1.y, pq);
       pw = __builtin_fmaf(s[6], w1.z, pw); pq = __builtin_fmaf(s[6], q1.z, pq);
       pw = __builtin_fmaf(s[7], w1.w, pw); pq = __builtin_fmaf(s[7], q1.w, pq);
-      P[r] = group_sum_dpp<16>(pw);
-      Qs[r] = group_sum_dpp<16>(pq);
+      pw = group_sum_dpp<16>(pw);
+      pq = group_sum_dpp<16>(pq);
+      if (lr == (r & 15)) {
+        sP[rl][r] = pw;
+        sQs[rl][r] = pq;
+      }
     }
-    // outputs: lane lr takes tokens 2 lr and 2 lr + 1 of this row
+    wave_lds_sync();  // each row's P and Qs come from its own wave
+    // outputs: lane lr takes tokens lr and lr + 16 of this row
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int r = 2 * lr + h;
+      const int r = lr + 16 * h;
       float acc1 = 0.f, acc2 = 0.f;
-#pragma unroll
-      for (int i = 0; i < C; ++i) {
-        acc1 = __builtin_fmaf(sA1[i][r], P[i], acc1);
-        acc2 = __builtin_fmaf(sA2[i][r], sU[i][rl], acc2);
+#pragma unroll 2
+      for (int i = 0; i < C; i += 4) {
+        const float4 a1 = *reinterpret_cast<const float4 *>(&sA1[r][i]);
+        const float4 a2 = *reinterpret_cast<const float4 *>(&sA2[r][i]);
+        const float4 pp = *reinterpret_cast<const float4 *>(&sP[rl][i]);
+        const float4 uu = *reinterpret_cast<const float4 *>(&sU[rl][i]);
+        acc1 = __builtin_fmaf(a1.x, pp.x, acc1); acc2 = __builtin_fmaf(a2.x, uu.x, acc2);
+        acc1 = __builtin_fmaf(a1.y, pp.y, acc1); acc2 = __builtin_fmaf(a2.y, uu.y, acc2);
+        acc1 = __builtin_fmaf(a1.z, pp.z, acc1); acc2 = __builtin_fmaf(a2.z, uu.z, acc2);
+        acc1 = __builtin_fmaf(a1.w, pp.w, acc1); acc2 = __builtin_fmaf(a2.w, uu.w, acc2);
       }
-      float qsr = Qs[0];
-#pragma unroll
-      for (int i = 1; i < C; ++i) qsr = r == i ? Qs[i] : qsr;
-      sO[r][rl] = f32_to_bf16(__builtin_fmaf(sGm[r], qsr - acc1, acc2));
+      sO[r][rl] = f32_to_bf16(__builtin_fmaf(sGm[r], sQs[rl][r] - acc1, acc2));
     }
     // state: s <- gam_31 s + sum_i (e_i U_i - gam_31 P_i) k_i
     const float gl = sGm[C - 1];
 #pragma unroll
     for (int e = 0; e < EL; ++e) s[e] *= gl;
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-      const float ci = __builtin_fmaf(sE[i], sU[i][rl], -gl * P[i]);
+    auto upd = [&](float ci, int i) {
       const float4 k0 = *reinterpret_cast<const float4 *>(&sK[i][EL * lr]);
       const float4 k1 = *reinterpret_cast<const float4 *>(&sK[i][EL * lr + 4]);
       s[0] = __builtin_fmaf(ci, k0.x, s[0]); s[1] = __builtin_fmaf(ci, k0.y, s[1]);
       s[2] = __builtin_fmaf(ci, k0.z, s[2]); s[3] = __builtin_fmaf(ci, k0.w, s[3]);
       s[4] = __builtin_fmaf(ci, k1.x, s[4]); s[5] = __builtin_fmaf(ci, k1.y, s[5]);
       s[6] = __builtin_fmaf(ci, k1.z, s[6]); s[7] = __builtin_fmaf(ci, k1.w, s[7]);
+    };
+#pragma unroll 2
+    for (int i = 0; i < C; i += 4) {
+      const float4 pp = *reinterpret_cast<const float4 *>(&sP[rl][i]);
+      const float4 uu = *reinterpret_cast<const float4 *>(&sU[rl][i]);
+      const float4 ee = *reinterpret_cast<const float4 *>(&sE[i]);
+      upd(__builtin_fmaf(ee.x, uu.x, -gl * pp.x), i);
+      upd(__builtin_fmaf(ee.y, uu.y, -gl * pp.y), i + 1);
+      upd(__builtin_fmaf(ee.z, uu.z, -gl * pp.z), i + 2);
+      upd(__builtin_fmaf(ee.w, uu.w, -gl * pp.w), i + 3);
     }
     __syncthreads();
     if (tid < 2 * n) {
