@@ -255,3 +255,21 @@ def test_gdn_argument_errors_before_any_launch(M):
     assert L.moe_gdn_scan(*p, 0, 16, 32, 128, 128, st, out, None) == M.OK   # empty: no-op
     q_bad = ctypes.c_void_p(0x100008)
     assert L.moe_gdn_scan(q_bad, *p[1:], 64, 16, 32, 128, 128, st, out, None) == M.E_INVALID
+
+
+def test_gdn_chunked_workspace_and_argument_errors(M):
+    L = M.lib()
+    n = ctypes.c_size_t(0)
+    assert L.moe_gdn_chunked_workspace_bytes(2048, 16, 32, 128, 128, ctypes.byref(n)) == M.OK
+    # 64 chunks x 32 heads x (two 32 x 128 factor blocks, two 32 x 32 tables, 2 x 32) floats
+    assert n.value == 64 * 32 * (2 * 32 * 128 + 2 * 32 * 32 + 64) * 4
+    need = n.value
+    assert L.moe_gdn_chunked_workspace_bytes(2048, 16, 32, 64, 128, ctypes.byref(n)) == \
+        M.E_UNSUPPORTED
+    p = [ctypes.c_void_p(a) for a in (0x100000, 0x200000, 0x300000, 0x400000, 0x500000)]
+    st, out, ws = ctypes.c_void_p(0x600000), ctypes.c_void_p(0x700000), ctypes.c_void_p(0x800000)
+    assert L.moe_gdn_scan_chunked(*p, 2048, 16, 32, 128, 128, st, out, ws, need - 1,
+                                  None) == M.E_WORKSPACE
+    assert L.moe_gdn_scan_chunked(*p, 2048, 16, 32, 128, 128, st, out, None, need,
+                                  None) == M.E_INVALID
+    assert L.moe_gdn_scan_chunked(*p, 0, 16, 32, 128, 128, st, out, ws, 0, None) == M.OK
