@@ -647,14 +647,18 @@ def profile_run(moe, torch, synth, dev, what):
         for i in range(400):
             moe.moe_attn_decode(q, ks[i % 16], vs[i % 16], out=out, ws=ws)
     elif what == "gdn_scan_2k":
-        # one DeltaNet layer's scan of a 2,048-token prompt (32 value heads), 20 calls
+        # one DeltaNet layer's scan of a 2,048-token prompt (32 value heads), 20 calls of the
+        # token scan, then 20 of the chunked form
         q, k, v, a, b = synth.gdn_inputs(2048, seed=3)
         qd, kd, vd = (moe.bf16_from_bits(x, dev) for x in (q, k, v))
         ad, bd = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
         st = torch.zeros((synth.GDN_V_HEADS, synth.GDN_DV, synth.GDN_DK), dtype=torch.float32,
                          device=dev)
+        ws = moe.gdn_chunked_workspace(2048, synth.GDN_K_HEADS, synth.GDN_V_HEADS, dev)
         for _ in range(20):
             moe.moe_gdn_scan(qd, kd, vd, ad, bd, st)
+        for _ in range(20):
+            moe.moe_gdn_scan_chunked(qd, kd, vd, ad, bd, st, ws=ws)
     elif what == "prefill_separate_dequant":
         # the separate-dequantisation ablation (expansion pass + GEMMs on fp16 weights)
         dl = moe.DeviceLayer.from_host(synth.decode_layer(0), dev)
