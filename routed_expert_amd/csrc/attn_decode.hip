@@ -234,69 +234,92 @@ __global__ __launch_bounds__(256, 2) void k_attn_split(AttnArgs a) {
   }
 }
 
-// Merge of the blocks: grid (query heads, D / 64). Thread (split lane sl, column quad dq)
-// requests the maxima, sums and 16-byte accumulator slices of its blocks s = sl + 16 i
-// (i < 32 covers 512 blocks) before using any, so the merge costs one round trip; the
-// head's maximum M comes from LDS, each block is weighted by 2^(m_s - M), the 16 split
-// lanes are added in LDS, and out = sum / l in bf16.
+// Merge of the blocks: grid (query heads, D / 16), 256 threads. Thread (split lane sl < 64,
+// column quad cq < 4) requests the maxima, sums and 16-byte accumulator slices of its
+// blocks s = sl + 64 i, i < NI = ceil(blocks / 64), before using any, so the merge costs one
+// memory round trip and no load repeats another; the head's maximum M is a wave reduction
+// and four LDS words, each block is weighted by 2^(m_s - M), the split lanes are added in a
+// fixed order (within the wave, then over the four waves), and out = sum / l in bf16.
+template <int NI>
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
-  constexpr int D = 256, NI = kAttnMaxSlots / 16;
-  const int h = blockIdx.x, tid = threadIdx.x;
-  const int dq = tid & 15, sl = tid >> 4;
-  const int d0 = blockIdx.y * 64 + 4 * dq;
+  constexpr int D = 256;
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cq = lane & 3, sl = (wave << 4) | (lane >> 2);
+  const int d0 = blockIdx.y * 16 + 4 * cq;
   float ms[NI], ls[NI];
   float4 vs[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int s = min(sl + 16 * i, a.n_split - 1);
+    const int s = min(sl + 64 * i, a.n_split - 1);
     const size_t row = (size_t)s * a.n_q + h;
     ms[i] = a.part_m[row];
     ls[i] = a.part_l[row];
     vs[i] = *reinterpret_cast<const float4 *>(a.part_acc + row * D + d0);
   }
-  __shared__ float red[256];
-  __shared__ __attribute__((aligned(16))) float4 sacc[16][16];
-  __shared__ float sl_l[16];
+  __shared__ float wmax[4];
+  __shared__ __attribute__((aligned(16))) float4 sacc[4][4];
+  __shared__ float swl[4];
   float mx = kNegInf;
 #pragma unroll
   for (int i = 0; i < NI; ++i) mx = fmaxf(mx, ms[i]);  // repeats of the last block are harmless
-  red[tid] = mx;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
-    __syncthreads();
+  // lanes of one column quad differ in lane bits 2..5
+  mx = fmaxf(mx, __uint_as_float(xor_peer_dpp<8>(__float_as_uint(mx))));
+  mx = fmaxf(mx, __uint_as_float(xor_peer_dpp<4>(__float_as_uint(mx))));  // rotation: ok after 8
+  {
+    const uint32_t u = __float_as_uint(mx);
+    const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    mx = fmaxf(__uint_as_float((uint32_t)p16[0]), __uint_as_float((uint32_t)p16[1]));
+    const uint32_t w = __float_as_uint(mx);
+    const auto p32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    mx = fmaxf(__uint_as_float((uint32_t)p32[0]), __uint_as_float((uint32_t)p32[1]));
   }
-  const float M = red[0];
+  if (lane == 0) wmax[wave] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   float4 acc = {0.f, 0.f, 0.f, 0.f};
   float lp = 0.f;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const float f = sl + 16 * i < a.n_split ? __builtin_amdgcn_exp2f(ms[i] - M) : 0.f;
+    const float f = sl + 64 * i < a.n_split ? __builtin_amdgcn_exp2f(ms[i] - M) : 0.f;
     lp = __builtin_fmaf(f, ls[i], lp);
     acc.x = __builtin_fmaf(f, vs[i].x, acc.x);
     acc.y = __builtin_fmaf(f, vs[i].y, acc.y);
     acc.z = __builtin_fmaf(f, vs[i].z, acc.z);
     acc.w = __builtin_fmaf(f, vs[i].w, acc.w);
   }
-  sacc[sl][dq] = acc;
-  if (dq == 0) sl_l[sl] = lp;
+  auto quad_sum = [](float v) {  // over the 16 lanes of one column quad, order 32, 16, 8, 4
+    v = xor_sum<32>(v);
+    v = xor_sum<16>(v);
+    v = xor_sum<8>(v);
+    return xor_sum<4>(v);
+  };
+  acc.x = quad_sum(acc.x);
+  acc.y = quad_sum(acc.y);
+  acc.z = quad_sum(acc.z);
+  acc.w = quad_sum(acc.w);
+  lp = quad_sum(lp);
+  if (lane < 4) {
+    sacc[wave][cq] = acc;
+    if (cq == 0) swl[wave] = lp;
+  }
   __syncthreads();
-  if (tid < 16) {
+  if (tid < 4) {
     float4 t = sacc[0][tid];
-    float L = sl_l[0];
-    for (int i = 1; i < 16; ++i) {
-      const float4 u = sacc[i][tid];
+    float L = swl[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      const float4 u = sacc[w][tid];
       t.x += u.x;
       t.y += u.y;
       t.z += u.z;
       t.w += u.w;
-      L += sl_l[i];
+      L += swl[w];
     }
     const float inv = 1.0f / L;
     uint2 o;
     o.x = pack_bf16x2(t.x * inv, t.y * inv);
     o.y = pack_bf16x2(t.z * inv, t.w * inv);
-    *reinterpret_cast<uint2 *>(a.out + (size_t)h * D + blockIdx.y * 64 + 4 * tid) = o;
+    *reinterpret_cast<uint2 *>(a.out + (size_t)h * D + blockIdx.y * 16 + 4 * tid) = o;
   }
 }
 
@@ -328,8 +351,16 @@ hipError_t launch_attn_decode(const AttnArgs &a, int heads_per_group, hipStream_
     case 8: MOE_LAUNCH("k_attn_split", k_attn_split<8>, grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
-  MOE_LAUNCH("k_attn_combine", k_attn_combine, dim3((unsigned)a.n_q, 256 / 64), dim3(256), 0, s,
-             a);
+  const dim3 cgrid((unsigned)a.n_q, 256 / 16);
+  static_assert(kAttnMaxSlots <= 8 * 64, "k_attn_combine takes at most 8 blocks per lane");
+  if (a.n_split <= 64)
+    MOE_LAUNCH("k_attn_combine", k_attn_combine<1>, cgrid, dim3(256), 0, s, a);
+  else if (a.n_split <= 128)
+    MOE_LAUNCH("k_attn_combine", k_attn_combine<2>, cgrid, dim3(256), 0, s, a);
+  else if (a.n_split <= 256)
+    MOE_LAUNCH("k_attn_combine", k_attn_combine<4>, cgrid, dim3(256), 0, s, a);
+  else
+    MOE_LAUNCH("k_attn_combine", k_attn_combine<8>, cgrid, dim3(256), 0, s, a);
   return hipSuccess;
 }
 
