@@ -144,16 +144,18 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t *__restrict_
   }
   const int col = lane & 31, rq4 = (lane >> 5) * 4;
   const int ee = e0 + wn * 32 + col;
+  // the bias is read once and resolved before the stores' branches: a load first used
+  // inside them makes every store wait for all memory operations in flight
+  float bv = 0.f;
+  if (blockIdx.z == 0 && bias) bv = bias[min(ee, E - 1)];
+  asm volatile("" ::"v"(bv));
+  const bool first_half = blockIdx.z == 0;
+  float *zo = first_half ? z : z2;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int tt = t0 + wm * 32 + (r >> 2) * 8 + rq4 + (r & 3);
-    if (tt < T && ee < E) {
-      const float v = __builtin_fmaf(acc_l[r], 1.0f / kLoScale, acc_h[r]);
-      if (blockIdx.z == 0)
-        z[(size_t)tt * E + ee] = v + (bias ? bias[ee] : 0.f);
-      else
-        z2[(size_t)tt * E + ee] = v;
-    }
+    const float v = __builtin_fmaf(acc_l[r], 1.0f / kLoScale, acc_h[r]);
+    if (tt < T && ee < E) zo[(size_t)tt * E + ee] = first_half ? v + bv : v;
   }
 }
 
@@ -217,6 +219,12 @@ __global__ __launch_bounds__(256) void k_router_f32(const float *__restrict__ x,
     }
     __syncthreads();
   }
+  // the biases are read once, outside the stores' branches (a load first used inside them
+  // would make every store wait for memory)
+  float bj[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) bj[j] = bias ? bias[min(e0 + tx * 4 + j, E - 1)] : 0.f;
+  asm volatile("" ::"v"(bj[0]), "v"(bj[1]), "v"(bj[2]), "v"(bj[3]));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int t = t0 + ty * 4 + i;
@@ -224,7 +232,7 @@ __global__ __launch_bounds__(256) void k_router_f32(const float *__restrict__ x,
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = e0 + tx * 4 + j;
-      if (e < E) z[(size_t)t * E + e] = acc[i][j] + (bias ? bias[e] : 0.f);
+      if (e < E) z[(size_t)t * E + e] = acc[i][j] + bj[j];
     }
   }
 }
