@@ -75,6 +75,16 @@ def test_attn_other_groupings(M, n_q, n_kv):
     check(out, oracle.attn_decode(q, k, v, n_q, n_kv, 1 / 16))
 
 
+@pytest.mark.parametrize("n_q,n_kv,ctx,blocks", [(16, 2, 12000, 94), (4, 1, 50000, 391),
+                                                  (16, 2, 9000, 71)])
+def test_attn_merge_widths(M, n_q, n_kv, ctx, blocks):
+    # the merge takes ceil(blocks / 64) partials per lane: 2 at 94 and 71 blocks, 8 at 391
+    # (one KV head may use up to 512 blocks)
+    announce(f"moe_attn_decode {n_q}/{n_kv}/256 ctx={ctx} ({blocks} blocks)")
+    q, k, v, out = run(M, ctx, seed=ctx, n_q=n_q, n_kv=n_kv)
+    check(out, oracle.attn_decode(q, k, v, n_q, n_kv, 1 / 16))
+
+
 @pytest.mark.parametrize("ctx", [500, 40000])
 def test_attn_unpacked_is_bit_identical(M, ctx):
     announce(f"moe_attn_decode_unpacked vs packed ctx={ctx}")
