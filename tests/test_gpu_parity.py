@@ -187,6 +187,19 @@ def test_prefill_skewed_4096(M, skewed):
     assert err <= BF16_TOL, err
 
 
+def test_prefill_skewed_ragged_1000(M, skewed):
+    # the router bias with a token count that is not a multiple of 64 (the last routing
+    # block holds 40 tokens, the router's last 128-token tile 104): every token's routing
+    # against the oracle, outputs on sampled tokens including the tail
+    layer, dl = skewed
+    T = 1000
+    announce(f"moe_prefill int4 T={T} Zipf(1.1)-skewed routing, x seed 5")
+    g, unsure, err, _ = _prefill_big(M, layer, dl, 5, T=T, n_sample=64)
+    assert g["counts"].sum() == 8 * T
+    assert unsure <= 10
+    assert err <= BF16_TOL, err
+
+
 def test_prefill_ragged_12000(M, big):
     # one call well past the benchmark size whose token count is not a multiple of 64:
     # 188 count blocks, the last one half full, and a tile map of about 860 tiles
