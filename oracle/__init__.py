@@ -80,6 +80,8 @@ def _load():
             fn.restype = ctypes.c_int
         _lib.oracle_bf16_to_f64.argtypes = [P, I64, P]
         _lib.oracle_bf16_to_f64.restype = None
+        _lib.oracle_round_bf16.argtypes = [P, I64, P]
+        _lib.oracle_round_bf16.restype = None
     return _lib
 
 
@@ -205,6 +207,21 @@ def rmsnorm(h, eps: float = 1e-6) -> np.ndarray:
     out = np.empty_like(h)
     _check(_load().oracle_rmsnorm(h.ctypes.data, T, H, eps, out.ctypes.data), "rmsnorm")
     return out
+
+
+def round_bf16(x) -> np.ndarray:
+    """Nearest bf16 of each value (ties to even, one rounding from the exact value);
+    returns uint16 bit patterns of the same shape."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().oracle_round_bf16(x.ctypes.data, x.size, out.ctypes.data)
+    return out
+
+
+def stack_layer_input(h, eps: float = 1e-6) -> np.ndarray:
+    """What one layer of the stack reads: RMSNorm (unit gain) of the residual stream h,
+    rounded to bf16 (bit patterns)."""
+    return round_bf16(rmsnorm(h, eps))
 
 
 def attn_decode(q, k, v, n_q: int, n_kv: int, scale: float) -> np.ndarray:

@@ -282,6 +282,30 @@ int oracle_rmsnorm(const double *h, int64_t T, int32_t H, double eps, double *ou
   return 0;
 }
 
+/* Round to the nearest bf16 value, ties to even (8 significant bits; below 2^-126 the
+ * bf16 subnormal grid of spacing 2^-133). The stack of layers rounds each normalised row
+ * to the activation dtype before the layer reads it; this is that rounding, done once
+ * from the exact value. Every step below is exact in double except the one nearbyint. */
+static uint16_t round_bf16_one(double v) {
+  if (isnan(v)) return 0x7FC0;
+  double r;
+  if (fabs(v) < 0x1p-126) {
+    r = nearbyint(v * 0x1p133) * 0x1p-133;
+  } else {
+    int e;
+    const double m = frexp(v, &e); /* v = m 2^e, 0.5 <= |m| < 1 */
+    r = ldexp(nearbyint(ldexp(m, 8)), e - 8);
+  }
+  const float f = (float)r; /* exact (or +-inf past the bf16 range) */
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return (uint16_t)(u >> 16);
+}
+
+void oracle_round_bf16(const double *src, int64_t n, uint16_t *dst) {
+  for (int64_t i = 0; i < n; ++i) dst[i] = round_bf16_one(src[i]);
+}
+
 /* Decode attention of one query token over a KV cache, grouped-query form ("Optimizing
  * On-Device Inference for Apple Silicon", sections "Qwen creates three distinct workload
  * shapes" -- query heads share key-value heads, eight to one -- and "Read the attention
@@ -343,8 +367,8 @@ int oracle_gdn_scan(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
   const int32_t rep = n_v / n_k;
   int failed = 0;
 #ifdef _OPENMP
-  if (nthreads > 0) omp_set_num_threads(nthreads);
-#pragma omp parallel for schedule(dynamic, 1)
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
 #endif
   for (int32_t j = 0; j < n_v; ++j) {
     const int32_t kh = j / rep;
@@ -352,6 +376,9 @@ int oracle_gdn_scan(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
     double *kt = (double *)malloc((size_t)d_k * sizeof(double));
     double *qt = (double *)malloc((size_t)d_k * sizeof(double));
     if (!kt || !qt) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
       failed = 1;
       free(kt);
       free(qt);

@@ -76,6 +76,10 @@ int oracle_moe(const oracle_layer *L, const double *x, int64_t T, double *y, int
 /* RMSNorm with unit gain: out[t] = h[t] / sqrt(mean(h[t]^2) + eps). */
 int oracle_rmsnorm(const double *h, int64_t T, int32_t H, double eps, double *out);
 
+/* Round each value to the nearest bf16, ties to even (one rounding from the exact value);
+ * returns bf16 bit patterns. */
+void oracle_round_bf16(const double *src, int64_t n, uint16_t *dst);
+
 /* Decode attention of one token: out[h] = softmax_t(scale * q[h].k[g, t]) v[g, t] with
  * g = h / (n_q / n_kv); k and v bf16 bit patterns, head g's row t at g * head_stride + t * D. */
 int oracle_attn_decode(const double *q, const uint16_t *k, const uint16_t *v, int32_t n_q,

@@ -343,6 +343,67 @@ def _attn_rand(seed, n_kv, ctx, D, n_q):
     return q, k, v
 
 
+def _bf16_neighbours(v):
+    """The two bf16 values bracketing float64 v (brute force over the bit patterns of the
+    float32 truncation and its successor), as float64."""
+    f = np.float32(v)
+    if abs(float(f)) > abs(v):  # float32 rounding went away from zero: step back
+        f = np.nextafter(f, np.float32(0.0))
+    lo_bits = (np.array([f], np.float32).view(np.uint32)[0] >> 16).astype(np.uint32)
+    lo = float((np.array([lo_bits << 16], np.uint32)).view(np.float32)[0])
+    hi = float((np.array([(lo_bits + 1) << 16], np.uint32)).view(np.float32)[0])
+    return (lo, int(lo_bits)), (hi, int(lo_bits) + 1)
+
+
+def test_round_bf16_matches_torch_on_float32_values(oracle_lib):
+    # torch rounds float32 to bf16 to nearest, ties to even: for values that are exact in
+    # float32 that is the single rounding the oracle must reproduce (normal, subnormal,
+    # both signs, exact bf16 values and exact midpoints included)
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.standard_normal(4000),
+                        rng.standard_normal(500) * 1e-39,          # bf16 subnormals
+                        rng.standard_normal(500) * 1e30,
+                        [0.0, -0.0, 1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 3.0e38]])
+    x = x.astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.round_bf16(x.astype(np.float64))
+    assert np.array_equal(got, want)
+    # the two exact midpoints above round to the even neighbour
+    assert got[-3] == 0x3F80 and got[-2] == 0x3F82
+
+
+def test_round_bf16_brute_force_nearest_on_float64(oracle_lib):
+    # values that are not float32: the result is the nearer of the two bracketing bf16
+    # values, the even one on an exact tie (no detour through float32)
+    rng = np.random.default_rng(12)
+    vals = rng.standard_normal(3000) * np.exp(rng.uniform(-20, 20, 3000))
+    got = oracle.round_bf16(vals)
+    for v, g in zip(vals, got):
+        (lo, lb), (hi, hb) = _bf16_neighbours(abs(v))
+        d_lo, d_hi = abs(v) - lo, hi - abs(v)
+        assert d_lo >= 0 and d_hi >= 0
+        want = lb if (d_lo < d_hi or (d_lo == d_hi and lb % 2 == 0)) else hb
+        assert (int(g) & 0x7FFF) == want and (int(g) >> 15) == (v < 0)
+    # a value just above a midpoint whose float32 rounding lands exactly on the midpoint:
+    # rounding through float32 would tie to the even (lower) neighbour, the exact value
+    # rounds up
+    mid = 1.0 + 2.0 ** -8                     # between 1.0 (0x3F80) and 1 + 2^-7 (0x3F81)
+    v = mid + 2.0 ** -40
+    assert float(np.float32(v)) == mid
+    assert oracle.round_bf16(np.array([v]))[0] == 0x3F81
+    assert oracle.round_bf16(np.array([mid]))[0] == 0x3F80
+
+
+def test_stack_layer_input_constant_row(oracle_lib):
+    # RMSNorm of a constant row c is c / sqrt(c^2 + eps) in every element, then one
+    # rounding to bf16
+    c, eps = 0.75, 1e-6
+    h = synth.f32_to_bf16_bits(np.full((2, 64), c, np.float32))
+    want = oracle.round_bf16(np.full((2, 64), c / np.sqrt(c * c + eps)))
+    assert np.array_equal(oracle.stack_layer_input(h, eps), want)
+    assert np.all(want == 0x3F80)              # 0.99999911 rounds to 1.0
+
+
 def test_attn_single_position_returns_its_value():
     q, k, v = _attn_rand(1, 2, 1, 16, 4)
     out = oracle.attn_decode(q, k, v, 4, 2, 0.25)
