@@ -61,9 +61,13 @@ typedef enum { MOE_ACT_F32 = 0, MOE_ACT_BF16 = 1 } moe_act_dtype;
  * Supported: 1 <= k <= 8, k <= E <= 256, S in {0,1}; H % 64 == 0, I % 64 == 0,
  * and for int4 additionally H % 256 == 0 and I % 128 == 0. Pointers to codes, tiled
  * arrays, fp32 weights, activations and the workspace must be 16-byte aligned; int4
- * scale and bias pointers 4-byte aligned. Int4 weights are rebuilt in fp16 on the GPU:
- * every scale is 0 or has |scale| >= 2^-13, and scales, biases, weights, x and h stay
- * below 65504 in magnitude (results are unspecified otherwise). */
+ * scale and bias pointers 4-byte aligned. Int4 weights are rebuilt in fp16 on the GPU
+ * (prefill path): scales, biases, weights, x and h must stay below 65504 in magnitude
+ * (results are unspecified otherwise). A weight is rebuilt as the fp16 rounding of the exact
+ * scale * code + bias when its group's scale is 0 or |scale| >= 2^-13 and its bias is 0 or
+ * |bias| >= 2^-14; in a group outside that range the rebuilt weight carries an extra
+ * absolute error of at most 2^-17 (fp16 subnormals). The decode kernels use the scales and
+ * biases in fp32 and have no such range. */
 typedef struct {
   int32_t abi_version;  /* must be MOE_ABI_VERSION */
   int32_t hidden, inter, n_experts, top_k, n_shared;
@@ -133,11 +137,12 @@ moe_status moe_pack_weights(const moe_layer *layer, void *dst, size_t dst_bytes,
 moe_status moe_route(const moe_layer *layer, const void *x, int64_t T,
                      const moe_route_out *out, void *ws, size_t ws_bytes, void *stream);
 
-/* Whole layer for T >= 1 tokens (prefill path): routing as moe_route, then for int4
- * (tiled weights required, see moe_pack_weights) a grouped gate/up GEMM with SwiGLU, a
- * grouped down GEMM (int4 codes dequantised to fp16 in registers, fp16 MFMA, fp32
- * accumulation) and a weighted combine
- * back to token order. y[t] = shared(x_t) + sum_j w[t,j] expert_{ids[t,j]}(x_t)
+/* Whole layer for T >= 1 tokens (prefill path; "Optimizing On-Device Inference for Apple
+ * Silicon", sections "Prefill: reuse weights and keep routing on the GPU", "Dequantize
+ * weights during matrix multiplication" and "Match tile size to expert load"): routing as
+ * moe_route, then for int4 (tiled weights required, see moe_pack_weights) a grouped
+ * gate/up GEMM with SwiGLU, a grouped down GEMM (int4 codes dequantised to fp16 in
+ * registers, fp16 MFMA, fp32 accumulation) and a weighted combine back to token order. y[t] = shared(x_t) + sum_j w[t,j] expert_{ids[t,j]}(x_t)
  * (+ residual[t]). x, y, residual: [T, H] of act_dtype; residual may be NULL and may
  * alias y. route_out may be NULL; when given it receives the routing results.
  * Results are deterministic: identical inputs give identical bytes. */
@@ -256,8 +261,9 @@ moe_status moe_stack_workspace_bytes(const moe_layer *layers, int32_t n_layers,
 /* A stack of n_layers MoE layers (host array of descriptors) as pre-norm residual
  * blocks, applied in place to h [T, H]:
  *     for l = 0 .. n_layers-1:   h <- h + MoE_l(RMSNorm(h))
- * with RMSNorm of unit gain in fp32 arithmetic (eps as given; the normalised rows are
- * rounded to the activation dtype before the layer reads them). Rows are processed in
+ * with RMSNorm of unit gain in fp64 arithmetic (eps as given), each normalised value
+ * rounded once to the activation dtype (bf16: to nearest, ties to even) before the layer
+ * reads it; router and experts read the same rounded row. Rows are processed in
  * chunks of at most chunk_tokens, each chunk through every layer, all reusing one
  * workspace of moe_stack_workspace_bytes ("Bound temporary memory with prompt chunking");
  * every layer is independent per token, so the chunk size does not change the result.
@@ -268,7 +274,8 @@ moe_status moe_stack_forward(const moe_layer *layers, int32_t n_layers, void *h,
                              void *stream);
 
 /* RMSNorm with unit gain for stacking layers: out[t] = h[t] / sqrt(mean(h[t]^2) + eps),
- * fp32 arithmetic. h, out: [T, H] of act_dtype (may alias). */
+ * fp64 arithmetic, each value rounded once to act_dtype (bf16: to nearest, ties to even);
+ * the normalisation moe_stack_forward applies. h, out: [T, H] of act_dtype (may alias). */
 moe_status moe_rmsnorm(const void *h, int64_t T, int32_t hidden, float eps, int32_t act_dtype,
                        void *out, void *stream);
 

@@ -57,34 +57,39 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   }
 }
 
-// out[t] = h[t] / sqrt(mean(h[t]^2) + eps); one workgroup per row, fp32 arithmetic.
-// h and out may alias: every element is read and written by the same thread.
+// out[t] = h[t] / sqrt(mean(h[t]^2) + eps); one workgroup of 512 threads per row, fp64
+// arithmetic rounded once to the output dtype (bf16: round to nearest even from the fp64
+// value). Thread t takes elements 4t .. 4t+3 of each 2048-element stretch, the layout of the
+// fused decode normalisation, so both give the same bits. h and out may alias: every
+// element is read and written by the same thread.
 template <bool kBf16>
-__global__ __launch_bounds__(256) void k_rmsnorm(const void *h, int H, float eps, void *out) {
-  __shared__ float part[4];
+__global__ __launch_bounds__(512) void k_rmsnorm(const void *h, int H, float eps, void *out) {
+  __shared__ double red8[8];
   const size_t base = (size_t)blockIdx.x * H;
   const int tid = threadIdx.x;
   auto ld = [&](int c) {
-    return kBf16 ? bf16_to_f32(static_cast<const uint16_t *>(h)[base + c])
-                 : static_cast<const float *>(h)[base + c];
+    return kBf16 ? (double)bf16_to_f32(static_cast<const uint16_t *>(h)[base + c])
+                 : (double)static_cast<const float *>(h)[base + c];
   };
-  float ss = 0.f;
-  for (int c = tid; c < H; c += 256) {
-    const float v = ld(c);
-    ss = __builtin_fmaf(v, v, ss);
-  }
-  ss = wave_sum(ss);
-  if ((tid & 63) == 0) part[tid >> 6] = ss;
-  __syncthreads();
-  const float total = (part[0] + part[1]) + (part[2] + part[3]);
-  const float inv = 1.0f / sqrtf(total / (float)H + eps);
-  for (int c = tid; c < H; c += 256) {
-    const float v = ld(c) * inv;
-    if (kBf16)
-      static_cast<uint16_t *>(out)[base + c] = f32_to_bf16(v);
-    else
-      static_cast<float *>(out)[base + c] = v;
-  }
+  double ss = 0.0;
+  for (int c0 = 4 * tid; c0 < H; c0 += 2048)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (c0 + i < H) {
+        const double v = ld(c0 + i);
+        ss = __builtin_fma(v, v, ss);
+      }
+  const double inv = row_inv_rms_f64(ss, H, (double)eps, red8);
+  for (int c0 = 4 * tid; c0 < H; c0 += 2048)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (c0 + i < H) {
+        const double v = ld(c0 + i) * inv;
+        if (kBf16)
+          static_cast<uint16_t *>(out)[base + c0 + i] = f64_to_bf16_rne(v);
+        else
+          static_cast<float *>(out)[base + c0 + i] = (float)v;
+      }
 }
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s) {
@@ -95,9 +100,9 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t s) {
 hipError_t launch_rmsnorm(const void *h, int64_t T, int H, float eps, bool bf16, void *out,
                           hipStream_t s) {
   if (bf16)
-    MOE_LAUNCH("k_rmsnorm", k_rmsnorm<true>, dim3((unsigned)T), dim3(256), 0, s, h, H, eps, out);
+    MOE_LAUNCH("k_rmsnorm", k_rmsnorm<true>, dim3((unsigned)T), dim3(512), 0, s, h, H, eps, out);
   else
-    MOE_LAUNCH("k_rmsnorm", k_rmsnorm<false>, dim3((unsigned)T), dim3(256), 0, s, h, H, eps,
+    MOE_LAUNCH("k_rmsnorm", k_rmsnorm<false>, dim3((unsigned)T), dim3(512), 0, s, h, H, eps,
                out);
   return hipSuccess;
 }

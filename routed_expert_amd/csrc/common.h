@@ -39,6 +39,25 @@ MOE_DEV uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Round a double to the nearest bf16, ties to even, in one step (no detour through fp32):
+// the mantissa is cut at 7 explicit bits with the usual carry trick on the integer bits,
+// which is exact; below 2^-126 the bf16 subnormal grid (spacing 2^-133) applies, past the
+// bf16 range the result is +-inf. The rounded value has at most 8 significant bits, so the
+// conversion to fp32 that extracts its top half is exact.
+MOE_DEV uint16_t f64_to_bf16_rne(double v) {
+  uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint64_t mag = u & 0x7FFFFFFFFFFFFFFFull;
+  if (mag > 0x7FF0000000000000ull) return 0x7FC0;                        // NaN
+  if (mag >= 0x47F0000000000000ull) return (uint16_t)((u >> 48) & 0x8000u) | 0x7F80u;  // >= 2^128
+  if (mag < 0x3810000000000000ull) {                                     // |v| < 2^-126
+    const double r = __builtin_rint(v * 0x1p133) * 0x1p-133;
+    return (uint16_t)(__float_as_uint((float)r) >> 16);
+  }
+  u += 0x00000FFFFFFFFFFFull + ((u >> 45) & 1ull);
+  u &= ~0x00001FFFFFFFFFFFull;
+  return (uint16_t)(__float_as_uint((float)__longlong_as_double((long long)u)) >> 16);
+}
+
 // Round to nearest even fp16 (v_cvt_pk_f16_f32). Values outside the fp16 range
 // become +-inf; callers keep operands inside it.
 MOE_DEV uint32_t pack_f16x2(float lo, float hi) {
@@ -234,6 +253,29 @@ MOE_DEV uint32_t wave_max_u32(uint32_t v) {
 
 MOE_DEV uint32_t wave_min_u32(uint32_t v) {
   return wave_reduce_u32(v, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
+
+// Sum over a workgroup of 512 threads of each thread's fp64 partial, in one fixed order:
+// xor butterfly inside each wave (every lane ends with the same bits), then the eight wave
+// totals in wave order. red8 holds 8 doubles of LDS. Every thread returns the total.
+MOE_DEV double block512_sum_f64(double v, double *red8) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  if ((threadIdx.x & 63) == 0) red8[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double t = red8[0];
+#pragma unroll
+  for (int w = 1; w < 8; ++w) t += red8[w];
+  return t;
+}
+
+// 1 / sqrt(mean of squares + eps) of a row of H values in fp64. Thread t of the 512 owns
+// elements 4t .. 4t+3 of every 2048-element stretch (its partial is the fma chain over them in
+// index order), so a kernel that holds those four elements of an H = 2048 row per thread gets
+// the same bits as the RMSNorm kernel.
+MOE_DEV double row_inv_rms_f64(double partial_ss, int H, double eps, double *red8) {
+  const double total = block512_sum_f64(partial_ss, red8);
+  return 1.0 / sqrt(total / (double)H + eps);
 }
 
 // Order-preserving map of a float to an unsigned key (larger float, larger key).

@@ -90,40 +90,22 @@ MOE_DEV void stage_f16_pairs(const void *src, int n, f16x2_t *pairs, float *seg)
   }
 }
 
-// 1 / sqrt(mean(x^2) + eps) of the row, from each thread's partial sum of squares (all DT
-// threads call it; red8 holds DT / 64 floats of LDS).
-MOE_DEV float block_inv_rms(float ss, float eps, float *red8) {
-  ss = wave_sum_dpp(ss);
-  if ((threadIdx.x & 63) == 0) red8[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  float total = 0.f;
-#pragma unroll
-  for (int v = 0; v < DT / 64; ++v) total += red8[v];
-  return 1.0f / sqrtf(total / (float)DH + eps);
-}
-
-// The bf16 row x (normalised first when a.norm) as fp16 pairs in LDS plus its 32-element
-// segment sums (of the fp16 values): thread t < DH / 8 takes chunk t.
-MOE_DEV void stage_x(const DecodeArgs &a, f16x2_t *pairs, float *seg, float *red8) {
+// The bf16 layer input as fp16 pairs in LDS plus its 32-element segment sums (of the fp16
+// values): thread t < DH / 8 takes chunk t. With a.norm the input is the normalised row that
+// k_dec_a wrote (a.xn), else x itself.
+MOE_DEV void stage_x(const DecodeArgs &a, f16x2_t *pairs, float *seg) {
   const int tid = threadIdx.x;
   const bool live = tid < DH / 8;
+  const uint16_t *src = a.norm ? a.xn : a.x;
   float v[8] = {};
   if (live) {
-    const uint4 u = reinterpret_cast<const uint4 *>(a.x)[tid];
+    const uint4 u = reinterpret_cast<const uint4 *>(src)[tid];
     const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       v[2 * i] = bf16lo(wd[i]);
       v[2 * i + 1] = bf16hi(wd[i]);
     }
-  }
-  if (a.norm) {
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
-    const float inv = block_inv_rms(ss, a.eps, red8);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = bf16_to_f32(f32_to_bf16(v[i] * inv));
   }
   float sum = 0.f;
   f16x2_t pr[4];
@@ -272,11 +254,23 @@ __global__ __launch_bounds__(DT) void k_dec_a(DecodeArgs a) {
   const uint2 xb = reinterpret_cast<const uint2 *>(a.x)[tid];
   float xv[4] = {bf16lo(xb.x), bf16hi(xb.x), bf16lo(xb.y), bf16hi(xb.y)};
   if (a.norm) {
-    __shared__ float red8[DT / 64];
-    const float inv = block_inv_rms(xv[0] * xv[0] + xv[1] * xv[1] + xv[2] * xv[2] + xv[3] * xv[3],
-                                    a.eps, red8);
+    // RMSNorm of the stacked layer's input in fp64, rounded once to bf16: thread t holds
+    // elements 4t .. 4t+3, the layout of the RMSNorm kernel, so the bits are the same.
+    // Workgroup 0 stores the normalised row for the gate/up kernel.
+    __shared__ double red8[DT / 64];
+    double ss = 0.0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xv[i] = bf16_to_f32(f32_to_bf16(xv[i] * inv));
+    for (int i = 0; i < 4; ++i) ss = __builtin_fma((double)xv[i], (double)xv[i], ss);
+    const double inv = row_inv_rms_f64(ss, DH, (double)a.eps, red8);
+    uint16_t nb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      nb[i] = f64_to_bf16_rne((double)xv[i] * inv);
+      xv[i] = bf16_to_f32(nb[i]);
+    }
+    if (w == 0)
+      reinterpret_cast<uint2 *>(a.xn)[tid] =
+          make_uint2(nb[0] | ((uint32_t)nb[1] << 16), nb[2] | ((uint32_t)nb[3] << 16));
   }
   float d = wr.x * xv[0];
   d = __builtin_fmaf(wr.y, xv[1], d);
@@ -303,8 +297,7 @@ __global__ __launch_bounds__(DT) void k_dec_b(DecodeArgs a) {
   // the logit this thread ranks and its chunk of x leave together
   const int ze = 32 * (tid >> 6) + (tid & 31);
   const float zv = (w < DWG && ze < a.E) ? a.z[ze] : 0.f;
-  __shared__ float red8[DT / 64];
-  stage_x(a, xs, xseg, red8);
+  stage_x(a, xs, xseg);
   if (w >= DWG) {
     // the shared expert needs no routing: half block (b, f) of workgroup DWG + 2b + f
     const int b = (w - DWG) >> 1, f = (w - DWG) & 1;

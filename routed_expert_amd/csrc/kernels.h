@@ -32,7 +32,7 @@ struct RouteArgs {
   int I = 0;              // expert intermediate size (sizes the tile-height choice)
   float *logits;          // [T, E] (decode: [E])
   float *logits2;         // [T, E] second half of the reduction (bf16 path)
-  uint16_t *router_planes;  // [3, E, H] bf16 split of the router weights (bf16 path)
+  uint16_t *router_planes;  // [2, E, H] fp16 split of the router weights (bf16 path)
   bool planes_ready;        // router_planes already hold the split (packed layer)
   int32_t *ids;           // [T, k]
   float *w;               // [T, k]
@@ -156,10 +156,12 @@ struct DecodeArgs {
                               // h [T,k+S,I], y and residual [T,H]
   int sel_is_w;               // sel_z holds routing weights, not logits
   int H, I, E, k, S;
-  // when set, the layer reads RMSNorm(x) (unit gain, rounded to bf16) instead of x; the
-  // residual is still the caller's (un-normalised) pointer
+  // when set, the layer reads RMSNorm(x) (unit gain, fp64, rounded once to bf16) instead of
+  // x: k_dec_a forms it and stores it in xn [H] for k_dec_b; the residual is still the
+  // caller's (un-normalised) pointer
   int norm;
   float eps;
+  uint16_t *xn;
 };
 bool decode_gemv_supported(int H, int I, int E, int k, int S, bool int4);
 hipError_t launch_decode_gemv(const DecodeArgs &a, hipStream_t s);

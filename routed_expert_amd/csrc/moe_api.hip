@@ -85,7 +85,7 @@ moe_status check_layer(const moe_layer *L) {
 
 // Workspace layout: the batch-1 decode buffers first, then the T-dependent region.
 struct Plan {
-  size_t dec_logits, dec_ids, dec_z, dec_h, st_z, st_ids, st_w, st_h;
+  size_t dec_logits, dec_ids, dec_z, dec_h, dec_xn, st_z, st_ids, st_w, st_h;
   size_t logits, logits2, planes, ids, w, blk, offsets, sorted, slot, slot_w, x16, tiles, ntiles,
       h, out;
   size_t total;
@@ -125,6 +125,7 @@ Plan make_plan(const moe_layer *L, int64_t T, int tile_shift = 0) {
   p.dec_ids = take(k * 4);
   p.dec_z = take(k * 4);
   p.dec_h = take((k + S) * I * 4);
+  p.dec_xn = take(H * 2);
   // small-T path (2 .. kSmallT tokens)
   const size_t Ts = Tn < (size_t)moe::kSmallT ? Tn : (size_t)moe::kSmallT;
   p.st_z = take(Ts * E * 4);
@@ -765,6 +766,7 @@ static moe_status decode_impl(const moe_layer *layer, const void *x, void *y,
     da.T = 1;
     da.norm = norm_eps >= 0.f;
     da.eps = norm_eps;
+    da.xn = at<uint16_t>(ws, p.dec_xn);
     if ((e = moe::launch_decode_gemv(da, s)) != hipSuccess) return hip_fail(e, "moe_decode");
     return MOE_OK;
   }

@@ -273,3 +273,26 @@ def test_gdn_chunked_workspace_and_argument_errors(M):
     assert L.moe_gdn_scan_chunked(*p, 2048, 16, 32, 128, 128, st, out, None, need,
                                   None) == M.E_INVALID
     assert L.moe_gdn_scan_chunked(*p, 0, 16, 32, 128, 128, st, out, ws, 0, None) == M.OK
+
+
+def test_calls_without_a_device_return_hip_error(M):
+    """With no GPU present every call that passes the host checks fails at its first HIP
+    call with MOE_E_HIP and a message, instead of crashing (the addresses are never used)."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: the fake addresses would be dereferenced")
+    lib = M.lib()
+    L = fake_layer(M)
+    st, need = ws_bytes(M, L, 16)
+    assert st == 0
+    ws, x, y = ctypes.c_void_p(0x1000000), ctypes.c_void_p(0x2000000), ctypes.c_void_p(0x3000000)
+    calls = {
+        "moe_rmsnorm": lambda: lib.moe_rmsnorm(x, 4, 2048, ctypes.c_float(1e-6), M.ACT_BF16, y,
+                                               None),
+        "moe_decode": lambda: lib.moe_decode(ctypes.byref(L), x, y, None, ws, need, None),
+        "moe_prefill": lambda: lib.moe_prefill(ctypes.byref(L), x, 16, y, None, None, ws, need,
+                                               None),
+    }
+    for name, call in calls.items():
+        assert call() == M.E_HIP, name
+        assert lib.moe_last_error().decode(), name
