@@ -158,6 +158,19 @@ moe_status moe_prefill(const moe_layer *layer, const void *x, int64_t T, void *y
 moe_status moe_decode(const moe_layer *layer, const void *x, void *y, const void *residual,
                       void *ws, size_t ws_bytes, void *stream);
 
+/* moe_decode for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same kernels and results, with
+ * the library's own scratch memory in place of a caller workspace. The scratch is one static
+ * 4 MiB array per GPU that the library runs on, held from its first use on that GPU until
+ * the process ends; a layer whose one-token workspace (moe_workspace_bytes with
+ * max_tokens = 1) exceeds it is rejected with MOE_E_WORKSPACE before anything is enqueued.
+ * The call allocates nothing and needs nothing cleared in the scratch. Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (two streams, two threads)
+ * race and give undefined results; calls ordered on one stream are fine. Arguments as
+ * moe_decode. */
+moe_status moe_decode_noalloc(const moe_layer *layer, const void *x, void *y,
+                              const void *residual, void *stream);
+
 /* Ablations of the prefill path: the rejected designs of "Optimizing On-Device Inference
  * for Apple Silicon", section "Optimize sparse expert computation", rebuilt on the same
  * kernels so that each differs from the product path in one mechanism only. Every variant

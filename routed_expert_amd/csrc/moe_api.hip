@@ -808,6 +808,58 @@ moe_status moe_decode(const moe_layer *layer, const void *x, void *y, const void
   return decode_impl(layer, x, y, residual, ws, p, static_cast<hipStream_t>(stream));
 }
 
+}  // extern "C"
+
+// ---- decode without a caller workspace ------------------------------------------------------
+// Scratch memory of moe_decode_noalloc: one array per GPU, allocated by the loader with the
+// code object and held until the process ends. In host code `scratch` only names the symbol;
+// its device address on the current GPU comes from hipGetSymbolAddress (kept per device).
+namespace {
+constexpr size_t kNoallocScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<void *> g_scratch_ptr;  // index: HIP device id; nullptr until looked up
+
+moe_status scratch_on_current_device(void **ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "moe_decode_noalloc: hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((size_t)dev >= g_scratch_ptr.size()) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "moe_decode_noalloc: hipGetSymbolAddress");
+    if (!p) return fail(MOE_E_HIP, "moe_decode_noalloc: no device address for the scratch array");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+moe_status moe_decode_noalloc(const moe_layer *layer, const void *x, void *y,
+                              const void *residual, void *stream) {
+  g_err.clear();
+  moe_status st = check_layer(layer);
+  if (st) return st;
+  if (!x || !y || !aligned16(x) || !aligned16(y))
+    return fail(MOE_E_INVALID, "x and y must be non-NULL and 16-byte aligned");
+  if (residual && !aligned16(residual)) return fail(MOE_E_INVALID, "residual misaligned");
+  const Plan p = make_plan(layer, 1);
+  if (p.total > kNoallocScratchBytes)
+    return fail(MOE_E_WORKSPACE,
+                "moe_decode_noalloc: this layer needs %zu bytes of scratch, the library holds %zu "
+                "(use moe_decode with a workspace)",
+                p.total, kNoallocScratchBytes);
+  void *ws = nullptr;
+  if ((st = scratch_on_current_device(&ws))) return st;
+  return decode_impl(layer, x, y, residual, ws, p, static_cast<hipStream_t>(stream));
+}
+
 moe_status moe_stack_workspace_bytes(const moe_layer *layers, int32_t n_layers,
                                      int64_t chunk_tokens, size_t *bytes) {
   g_err.clear();

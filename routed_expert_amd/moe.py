@@ -24,7 +24,7 @@ W_F32, W_INT4_G64 = 0, 1
 ACT_F32, ACT_BF16 = 0, 1
 
 EXPORTS = ("moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_pack_bytes",
-           "moe_pack_weights", "moe_route", "moe_prefill", "moe_decode",
+           "moe_pack_weights", "moe_route", "moe_prefill", "moe_decode", "moe_decode_noalloc",
            "moe_stack_workspace_bytes", "moe_stack_forward", "moe_rmsnorm",
            "moe_profile_enable", "moe_profile_query", "moe_profile_reset",
            "moe_ablation_workspace_bytes", "moe_prefill_ablation",
@@ -97,6 +97,7 @@ def lib():
         "moe_route": ([P, P, I64, P, P, SZ, P], ctypes.c_int),
         "moe_prefill": ([P, P, I64, P, P, P, P, SZ, P], ctypes.c_int),
         "moe_decode": ([P, P, P, P, P, SZ, P], ctypes.c_int),
+        "moe_decode_noalloc": ([P, P, P, P, P], ctypes.c_int),
         "moe_stack_workspace_bytes": ([P, I32, I64, ctypes.POINTER(SZ)], ctypes.c_int),
         "moe_stack_forward": ([P, I32, P, I64, I64, ctypes.c_float, P, SZ, P], ctypes.c_int),
         "moe_rmsnorm": ([P, I64, I32, ctypes.c_float, I32, P, P], ctypes.c_int),
@@ -276,6 +277,15 @@ def moe_decode(layer: DeviceLayer, x: torch.Tensor, y=None, residual=None, ws=No
     y = torch.empty_like(x) if y is None else y
     _check("moe_decode", lib().moe_decode(layer.ref, _ptr(x), _ptr(y), _ptr(residual),
                                           _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+def moe_decode_noalloc(layer: DeviceLayer, x: torch.Tensor, y=None, residual=None,
+                       stream=None) -> torch.Tensor:
+    """moe_decode on the library's static scratch memory (no workspace argument)."""
+    y = torch.empty_like(x) if y is None else y
+    _check("moe_decode_noalloc", lib().moe_decode_noalloc(layer.ref, _ptr(x), _ptr(y),
+                                                          _ptr(residual), _stream(stream)))
     return y
 
 

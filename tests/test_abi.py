@@ -296,3 +296,19 @@ def test_calls_without_a_device_return_hip_error(M):
     for name, call in calls.items():
         assert call() == M.E_HIP, name
         assert lib.moe_last_error().decode(), name
+
+
+def test_decode_noalloc_rejects_layers_beyond_its_scratch(M):
+    """The no-allocation decode holds 4 MiB of scratch per GPU: a layer whose one-token
+    workspace is larger is refused on the host (nothing is launched, the addresses are never
+    used), one that fits passes the size check."""
+    lib = M.lib()
+    x, y = ctypes.c_void_p(0x2000000), ctypes.c_void_p(0x3000000)
+    wide = fake_layer(M, hidden=8192)
+    st, need = ws_bytes(M, wide, 1)
+    assert st == 0 and need > (4 << 20)
+    assert lib.moe_decode_noalloc(ctypes.byref(wide), x, y, None, None) == M.E_WORKSPACE
+    assert b"scratch" in lib.moe_last_error()
+    st, need = ws_bytes(M, fake_layer(M), 1)
+    assert st == 0 and need <= (4 << 20)
+    assert lib.moe_decode_noalloc(ctypes.byref(fake_layer(M)), x, None, None, None) == M.E_INVALID
