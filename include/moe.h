@@ -77,10 +77,13 @@ typedef struct {
   const void *w13_q, *w13_s, *w13_b;
   const void *w2_q, *w2_s, *w2_b;
   const void *w13_t, *w13_tsb, *w2_t, *w2_tsb;
-  /* fp16 bit patterns [2, E, H]: router_w split into two fp16 planes, hi = fp16(w) and
-   * lo = fp16((w - hi) * 2048), so w = hi + lo / 2048 to about 22 bits (router weights must
-   * be below 65504 in magnitude); written by moe_pack_weights, or NULL. When set, the
-   * prefill router reads it instead of splitting router_w on every call. */
+  /* router_w split into two fp16 planes, hi = fp16(w) and lo = fp16((w - hi) * 2048), so
+   * w = hi + lo / 2048 to about 22 bits (router weights must be below 65504 in magnitude),
+   * stored in the matrix-core operand order the prefill router loads directly:
+   *   fp16 [E_pad / 32][H / 16][2 planes][64 lanes][8]  (E_pad = E rounded up to 128)
+   * where lane l of (column block c, step s) holds expert 32c + l % 32 at positions
+   * 16s + 8 (l / 32) .. +7 of the row (zero past E). Written by moe_pack_weights, or NULL:
+   * then the prefill router splits router_w into the workspace on every call. */
   const void *router_planes;
 } moe_layer;
 

@@ -30,9 +30,8 @@ struct RouteArgs {
   int64_t T;
   int H, E, k, S;
   int I = 0;              // expert intermediate size (sizes the tile-height choice)
-  float *logits;          // [T, E] (decode: [E])
-  float *logits2;         // [T, E] second half of the reduction (bf16 path)
-  uint16_t *router_planes;  // [2, E, H] fp16 split of the router weights (bf16 path)
+  float *logits;          // fp32 path: [T, E]; bf16 path: kRouterParts partial sums [4][T, E]
+  uint16_t *router_planes;  // fp16 split of the router weights in B-fragment order (bf16 path)
   bool planes_ready;        // router_planes already hold the split (packed layer)
   int32_t *ids;           // [T, k]
   float *w;               // [T, k]
@@ -78,7 +77,10 @@ struct PackArgs {
 size_t tiled_code_bytes(int n_mat, int rows, int K);
 size_t tiled_sb_bytes(int n_mat, int rows, int K);
 hipError_t launch_pack(const PackArgs &a, hipStream_t s);
-hipError_t launch_router_split(const float *W, size_t n, uint16_t *planes, hipStream_t s);
+// The router's two fp16 planes in B-fragment order (see k_router_split); bytes for E experts.
+constexpr int kRouterParts = 4;  // partial logit arrays of the bf16 router (quarters of H)
+size_t router_frag_bytes(int E, int H);
+hipError_t launch_router_split(const float *W, int E, int H, uint16_t *planes, hipStream_t s);
 
 // Grouped int4 GEMMs of the prefill path (fp16 operands, fp32 accumulation).
 struct GroupedArgs {

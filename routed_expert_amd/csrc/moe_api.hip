@@ -86,7 +86,7 @@ moe_status check_layer(const moe_layer *L) {
 // Workspace layout: the batch-1 decode buffers first, then the T-dependent region.
 struct Plan {
   size_t dec_logits, dec_ids, dec_z, dec_h, dec_xn, st_z, st_ids, st_w, st_h;
-  size_t logits, logits2, planes, ids, w, blk, offsets, sorted, slot, slot_w, x16, tiles, ntiles,
+  size_t logits, planes, ids, w, blk, offsets, sorted, slot, slot_w, x16, tiles, ntiles,
       h, out;
   size_t total;
   int max_tiles;
@@ -134,9 +134,9 @@ Plan make_plan(const moe_layer *L, int64_t T, int tile_shift = 0) {
   p.st_h = take(Ts * (k + S) * I * 4);
   const size_t tiles = max_tiles_for(L, Tn, tile_shift);
   p.max_tiles = (int)tiles;
-  p.logits = take(Tn * E * 4);
-  p.logits2 = take(L->act_dtype == MOE_ACT_BF16 ? Tn * E * 4 : 0);
-  p.planes = take(L->act_dtype == MOE_ACT_BF16 ? 2 * E * H * 2 : 0);
+  const bool bf16 = L->act_dtype == MOE_ACT_BF16;
+  p.logits = take((bf16 ? moe::kRouterParts : 1) * Tn * E * 4);
+  p.planes = take(bf16 ? moe::router_frag_bytes((int)E, (int)H) : 0);
   p.ids = take(Tn * k * 4);
   p.w = take(Tn * k * 4);
   p.blk = take(NB * E * 4);
@@ -210,7 +210,7 @@ PackPlan pack_plan(const moe_layer *L) {
   p.w2_tsb = off;
   off += align256(moe::tiled_sb_bytes(n, H, I));
   p.planes = off;
-  off += align256((size_t)2 * L->n_experts * H * 2);
+  off += align256(moe::router_frag_bytes(L->n_experts, H));
   p.total = off;
   return p;
 }
@@ -271,7 +271,6 @@ moe::RouteArgs route_args(const moe_layer *L, const void *x, int64_t T) {
 // Routing results go to the caller's buffers when given, else to the workspace.
 void route_targets(moe::RouteArgs &a, const Plan &p, void *ws, const moe_route_out *ro) {
   a.logits = at<float>(ws, p.logits);
-  a.logits2 = at<float>(ws, p.logits2);
   if (!a.planes_ready) a.router_planes = at<uint16_t>(ws, p.planes);
   a.blk = at<int32_t>(ws, p.blk);
   a.offsets = at<int32_t>(ws, p.offsets);
@@ -390,7 +389,7 @@ moe_status moe_pack_weights(const moe_layer *layer, void *dst, size_t dst_bytes,
   a.t = at<uint8_t>(dst, pp.w2_t);
   a.tsb = at<uint16_t>(dst, pp.w2_tsb);
   if ((e = moe::launch_pack(a, s)) != hipSuccess) return hip_fail(e, "moe_pack_weights down");
-  if ((e = moe::launch_router_split(layer->router_w, (size_t)layer->n_experts * layer->hidden,
+  if ((e = moe::launch_router_split(layer->router_w, layer->n_experts, layer->hidden,
                                     at<uint16_t>(dst, pp.planes), s)) != hipSuccess)
     return hip_fail(e, "moe_pack_weights router");
   *packed = *layer;

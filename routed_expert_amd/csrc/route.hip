@@ -22,17 +22,19 @@ namespace moe {
 // hi = fp16(w) and lo = fp16((w - hi) * 2^11), so w = hi + lo * 2^-11 to 22 bits (the lo
 // plane is scaled to stay clear of fp16 subnormals). x converts exactly to fp16 (inside the
 // fp16 range), every product is exact in fp32, and the two planes accumulate separately in
-// fp32 before z = acc_hi + 2^-11 acc_lo, so the logits carry fp32-class error. Two planes
-// instead of three bf16 ones: the kernel is bound by the LDS traffic of the weight planes.
-// Tile: 64 tokens x 64 experts per workgroup, K in steps of 64; 4 waves in 2x2, each one
-// 32x32 accumulator. Side jobs: the fp16 copy of x for the expert GEMMs (expert tile 0,
-// chunks in kChunkOrder) and zeroing this token block's histogram row (the top-k kernel
-// adds into it).
-namespace {
-constexpr int RP = 64 + 8;  // LDS row pitch (elements)
-}
-
+// fp32 before z = acc_hi + 2^-11 acc_lo, so the logits carry fp32-class error.
+//
+// The planes are stored in MFMA B-operand order (router_frag_bytes), so that a wave loads its
+// weight fragments straight from memory into registers, 1 KB per load instruction: only x
+// goes through LDS, read by all four waves, and the LDS traffic per MFMA is a third of
+// staging both operands there. Tile: 64 tokens x 128 experts x a quarter of the reduction
+// axis per workgroup; wave w takes all 64 tokens x experts 32w .. 32w+31 (two 32x32
+// accumulators per plane). The four quarters of the reduction land in four partial logit
+// arrays that the top-k adds in a fixed order, so the sum is the same whatever runs first.
+// Side jobs: the fp16 copy of x for the expert GEMMs (expert tile 0, chunks in kChunkOrder)
+// and zeroing this token block's histogram row (the top-k kernel adds into it).
 constexpr float kLoScale = 2048.0f;  // lo plane = fp16((w - hi) * 2^11)
+constexpr int kRouterEPad = 128;     // experts per router tile; planes are zero-padded to it
 
 MOE_DEV void split2(float w, uint16_t &hi, uint16_t &lo) {
   const _Float16 h = (_Float16)w;
@@ -40,123 +42,157 @@ MOE_DEV void split2(float w, uint16_t &hi, uint16_t &lo) {
   lo = __builtin_bit_cast(uint16_t, (_Float16)((w - (float)h) * kLoScale));
 }
 
-// Router weights split into two fp16 planes [2][E][H] (hi, lo; natural element order):
-// once by moe_pack_weights for a packed layer, else on every call into the workspace.
-__global__ __launch_bounds__(256) void k_router_split(const float *__restrict__ W, size_t n,
+size_t router_frag_bytes(int E, int H) {
+  const size_t ep = (size_t)(E + kRouterEPad - 1) / kRouterEPad * kRouterEPad;
+  return 2 * ep * (size_t)H * 2;
+}
+
+// Router weights split into the two fp16 planes, in B-fragment order:
+//   [E_pad / 32 column blocks][H / 16 K steps][plane hi, lo][64 lanes][8 halves]
+// where lane l of (column block c, K step s) holds expert 32c + l % 32 at k = 16 s + 8 (l / 32)
+// .. +7 (the v_mfma_f32_32x32x16_f16 B operand layout); experts past E are zero. Written once
+// by moe_pack_weights, else on every call into the workspace. One thread per (c, s, lane).
+__global__ __launch_bounds__(256) void k_router_split(const float *__restrict__ W, int E, int H,
                                                       uint16_t *__restrict__ planes) {
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n / 4;
-       i += (size_t)gridDim.x * 256) {
-    const float4 f = reinterpret_cast<const float4 *>(W)[i];
-    const float v[4] = {f.x, f.y, f.z, f.w};
-    uint16_t h[4], l[4];
+  const int ep = (E + kRouterEPad - 1) / kRouterEPad * kRouterEPad;
+  const int ks = H / 16;
+  const int n = ep / 32 * ks * 64;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
+    const int lane = i & 63, cs = i >> 6, st = cs % ks, c = cs / ks;
+    const int e = 32 * c + (lane & 31), k = 16 * st + 8 * (lane >> 5);
+    float v[8] = {};
+    if (e < E) {
+      const float4 a = *reinterpret_cast<const float4 *>(W + (size_t)e * H + k);
+      const float4 b = *reinterpret_cast<const float4 *>(W + (size_t)e * H + k + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    uint16_t h[8], l[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) split2(v[q], h[q], l[q]);
-    reinterpret_cast<uint2 *>(planes)[i] =
-        make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
-    reinterpret_cast<uint2 *>(planes + n)[i] =
-        make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
+    for (int q = 0; q < 8; ++q) split2(v[q], h[q], l[q]);
+    uint4 hv, lv;
+    hv.x = h[0] | ((uint32_t)h[1] << 16); hv.y = h[2] | ((uint32_t)h[3] << 16);
+    hv.z = h[4] | ((uint32_t)h[5] << 16); hv.w = h[6] | ((uint32_t)h[7] << 16);
+    lv.x = l[0] | ((uint32_t)l[1] << 16); lv.y = l[2] | ((uint32_t)l[3] << 16);
+    lv.z = l[4] | ((uint32_t)l[5] << 16); lv.w = l[6] | ((uint32_t)l[7] << 16);
+    uint16_t *dst = planes + ((size_t)(c * ks + st) * 2) * 512 + 8 * lane;
+    *reinterpret_cast<uint4 *>(dst) = hv;
+    *reinterpret_cast<uint4 *>(dst + 512) = lv;
   }
 }
 
-__global__ __launch_bounds__(256) void k_router_mfma(const uint16_t *__restrict__ x,
-                                                     const uint16_t *__restrict__ planes,
-                                                     const float *__restrict__ bias,
-                                                     float *__restrict__ z,
-                                                     float *__restrict__ z2,
-                                                     uint16_t *__restrict__ x16,
-                                                     int32_t *__restrict__ blk_cnt, int T,
-                                                     int H, int E) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][64 * RP];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][2][64 * RP];
+// x tile in LDS: 64 rows x 64 fp16 of one K step, 16-byte chunk c of row r at chunk
+// c ^ ((r >> 1) & 7), so the A-operand reads (16 rows of a 32-row block, one chunk) hit
+// distinct banks.
+MOE_DEV int router_a_off(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 7)) << 3); }
+
+__global__ __launch_bounds__(256, 2) void k_router_mfma(const uint16_t *__restrict__ x,
+                                                        const uint16_t *__restrict__ planes,
+                                                        const float *__restrict__ bias,
+                                                        float *__restrict__ z,
+                                                        uint16_t *__restrict__ x16,
+                                                        int32_t *__restrict__ blk_cnt, int T,
+                                                        int H, int E) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][64 * 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-  // blockIdx.z takes one half of the reduction axis; the halves land in z and z2 and the
-  // top-k adds them (z + z2, bias in z), so the sum is the same whatever runs first
-  const int kbase = blockIdx.z * (H / 2);
-  if (tid < 64 && e0 + tid < E && blockIdx.z == 0) blk_cnt[(size_t)blockIdx.x * E + e0 + tid] = 0;
-  // loader: row lr (token / expert), 16 elements at column lc
-  const int lr = tid >> 2, lc = (tid & 3) * 16;
-  const int t = t0 + lr, e = e0 + lr;
-  const int frow = lane & 31, fk = (lane >> 5) * 8;
-  const size_t plane = (size_t)E * H;
-  uint4 ra[2], rb[2][2];
-  auto gload = [&](int k0) {
-    ra[0] = ra[1] = make_uint4(0, 0, 0, 0);
-    if (t < T) {
-      const uint4 *p = reinterpret_cast<const uint4 *>(x + (size_t)t * H + k0 + lc);
-      ra[0] = p[0];
-      ra[1] = p[1];
-    }
+  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * kRouterEPad, kq = blockIdx.z;
+  const int KQ = H / kRouterParts, kbase = kq * KQ, nsteps = KQ / 64, ks = H / 16;
+  if (blockIdx.y == 0 && kq == 0)
+    for (int e = tid; e < E; e += 256) blk_cnt[(size_t)blockIdx.x * E + e] = 0;
+  // x staging: thread t loads chunks 2 (t % 4), +1 (8 elements each) of row t / 4
+  const int lr = tid >> 2, lc = 2 * (tid & 3);
+  const bool row_ok = t0 + lr < T;
+  const uint16_t *xrow = x + (size_t)(row_ok ? t0 + lr : 0) * H + kbase + 8 * lc;
+  // this wave's weight fragments: column block (e0 + 32 wave) / 32, 8 KB per K step
+  const uint16_t *bsrc = planes + ((size_t)((e0 >> 5) + wave) * ks * 2) * 512 + 8 * lane;
+  uint4 ra[2];
+  uint4 bq[2][8];  // fragment sets of even and odd steps
+  auto load_a = [&](int st) {
+    const uint4 *p = reinterpret_cast<const uint4 *>(xrow + st * 64);
+    ra[0] = row_ok ? p[0] : make_uint4(0, 0, 0, 0);
+    ra[1] = row_ok ? p[1] : make_uint4(0, 0, 0, 0);
+  };
+  auto load_b = [&](int st, uint4 (&b)[8]) {
+    const uint4 *p = reinterpret_cast<const uint4 *>(bsrc + (size_t)((kbase + st * 64) >> 4) * 1024);
 #pragma unroll
-    for (int pl = 0; pl < 2; ++pl) {
-      rb[pl][0] = rb[pl][1] = make_uint4(0, 0, 0, 0);
-      if (e < E) {
-        const uint4 *p =
-            reinterpret_cast<const uint4 *>(planes + pl * plane + (size_t)e * H + k0 + lc);
-        rb[pl][0] = p[0];
-        rb[pl][1] = p[1];
+    for (int q = 0; q < 8; ++q) b[q] = p[q * 64];  // (K step 4 st + q / 2, plane q % 2)
+  };
+  auto store_a = [&](int st) {
+    uint16_t *as = As[st & 1];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint4 u = ra[h];
+      *reinterpret_cast<uint4 *>(as + router_a_off(lr, lc + h)) =
+          make_uint4(bf16x2_to_f16x2(u.x), bf16x2_to_f16x2(u.y), bf16x2_to_f16x2(u.z),
+                     bf16x2_to_f16x2(u.w));
+      if (x16 && blockIdx.y == 0 && row_ok)
+        *reinterpret_cast<uint4 *>(x16 + (size_t)(t0 + lr) * H + kbase + st * 64 + 8 * (lc + h)) =
+            bf16x8_to_f16x8_chunk(u);
+    }
+  };
+  f32x16_t acc_h[2] = {}, acc_l[2] = {};
+  const int arow = lane & 31, ahalf = lane >> 5;
+  auto compute = [&](int st, const uint4 (&b)[8]) {
+    const uint16_t *as = As[st & 1];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const f16x8_t bh = __builtin_bit_cast(f16x8_t, b[2 * kk]);
+      const f16x8_t bl = __builtin_bit_cast(f16x8_t, b[2 * kk + 1]);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const f16x8_t av = *reinterpret_cast<const f16x8_t *>(
+            as + router_a_off(32 * m + arow, 2 * kk + ahalf));
+        acc_h[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bh, acc_h[m], 0, 0, 0);
+        acc_l[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bl, acc_l[m], 0, 0, 0);
       }
     }
   };
-  auto lstore = [&](int buf, int k0) {
-    // x as fp16 (natural order; exact inside the fp16 range)
-    uint4 *pa = reinterpret_cast<uint4 *>(&As[buf][lr * RP + lc]);
-    pa[0] = make_uint4(bf16x2_to_f16x2(ra[0].x), bf16x2_to_f16x2(ra[0].y),
-                       bf16x2_to_f16x2(ra[0].z), bf16x2_to_f16x2(ra[0].w));
-    pa[1] = make_uint4(bf16x2_to_f16x2(ra[1].x), bf16x2_to_f16x2(ra[1].y),
-                       bf16x2_to_f16x2(ra[1].z), bf16x2_to_f16x2(ra[1].w));
-#pragma unroll
-    for (int pl = 0; pl < 2; ++pl) {
-      uint4 *pb = reinterpret_cast<uint4 *>(&Bs[buf][pl][lr * RP + lc]);
-      pb[0] = rb[pl][0];
-      pb[1] = rb[pl][1];
-    }
-    if (x16 && blockIdx.y == 0 && t < T) {
-      // fp16 copy of x for the expert GEMMs, each 8-element chunk in kChunkOrder
-      uint4 *q = reinterpret_cast<uint4 *>(x16 + (size_t)t * H + k0 + lc);
-      q[0] = bf16x8_to_f16x8_chunk(ra[0]);
-      q[1] = bf16x8_to_f16x8_chunk(ra[1]);
-    }
-  };
-  f32x16_t acc_h = {}, acc_l = {};
-  gload(kbase);
-  lstore(0, kbase);
+  // steps in pairs: even steps use x stage 0 and fragment set 0, odd steps stage 1 and set 1;
+  // the next step's x is stored while the current one computes (its stage was last read
+  // before the previous barrier), and each set is reloaded right after its step's MFMAs.
+  // (Fragments further ahead would need a third register set, which does not fit beside
+  // the accumulators at two workgroups per CU.)
+  load_a(0);
+  load_b(0, bq[0]);
+  store_a(0);
+  if (nsteps > 1) {
+    load_a(1);
+    load_b(1, bq[1]);
+  }
   __syncthreads();
-  const int nsteps = H / 2 / 64;
-  for (int st = 0; st < nsteps; ++st) {
-    const int cur = st & 1;
-    if (st + 1 < nsteps) gload(kbase + (st + 1) * 64);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int ko = kk * 16 + fk;
-      const f16x8_t av =
-          *reinterpret_cast<const f16x8_t *>(&As[cur][(wm * 32 + frow) * RP + ko]);
-      const f16x8_t bh =
-          *reinterpret_cast<const f16x8_t *>(&Bs[cur][0][(wn * 32 + frow) * RP + ko]);
-      const f16x8_t bl =
-          *reinterpret_cast<const f16x8_t *>(&Bs[cur][1][(wn * 32 + frow) * RP + ko]);
-      acc_h = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bh, acc_h, 0, 0, 0);
-      acc_l = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bl, acc_l, 0, 0, 0);
+  for (int st = 0; st < nsteps; st += 2) {
+    compute(st, bq[0]);
+    if (st + 1 < nsteps) store_a(st + 1);
+    if (st + 2 < nsteps) {
+      load_a(st + 2);
+      load_b(st + 2, bq[0]);
     }
-    if (st + 1 < nsteps) lstore(cur ^ 1, kbase + (st + 1) * 64);
+    __syncthreads();
+    if (st + 1 >= nsteps) break;
+    compute(st + 1, bq[1]);
+    if (st + 2 < nsteps) store_a(st + 2);
+    if (st + 3 < nsteps) {
+      load_a(st + 3);
+      load_b(st + 3, bq[1]);
+    }
     __syncthreads();
   }
-  const int col = lane & 31, rq4 = (lane >> 5) * 4;
-  const int ee = e0 + wn * 32 + col;
-  // the bias is read once and resolved before the stores' branches: a load first used
-  // inside them makes every store wait for all memory operations in flight
+  // 32x32 accumulator layout: lane l holds column l % 32, register r row 8 (r / 4) + 4 (l / 32)
+  // + r % 4 of the block. The bias is read once, outside the stores' branches (a load first
+  // used inside them would make every store wait for all memory operations in flight).
+  const int ee = e0 + 32 * wave + (lane & 31);
   float bv = 0.f;
-  if (blockIdx.z == 0 && bias) bv = bias[min(ee, E - 1)];
+  if (kq == 0 && bias) bv = bias[min(ee, E - 1)];
   asm volatile("" ::"v"(bv));
-  const bool first_half = blockIdx.z == 0;
-  float *zo = first_half ? z : z2;
+  float *zo = z + (size_t)kq * T * E;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int tt = t0 + wm * 32 + (r >> 2) * 8 + rq4 + (r & 3);
-    const float v = __builtin_fmaf(acc_l[r], 1.0f / kLoScale, acc_h[r]);
-    if (tt < T && ee < E) zo[(size_t)tt * E + ee] = first_half ? v + bv : v;
-  }
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tt = t0 + 32 * m + 8 * (r >> 2) + 4 * ahalf + (r & 3);
+      const float v = __builtin_fmaf(acc_l[m][r], 1.0f / kLoScale, acc_h[m][r]) + bv;
+      if (tt < T && ee < E) zo[(size_t)tt * E + ee] = v;
+    }
 }
 
 // fp32 activations (fp32-weight layers): plain fp32 FMA on the vector ALUs.
@@ -170,10 +206,8 @@ __global__ __launch_bounds__(256) void k_router_f32(const float *__restrict__ x,
   __shared__ float wsm[32][68];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-  // blockIdx.z takes one half of the reduction axis; the halves land in z and z2 and the
-  // top-k adds them (z + z2, bias in z), so the sum is the same whatever runs first
-  const int kbase = blockIdx.z * (H / 2);
-  if (tid < 64 && e0 + tid < E && blockIdx.z == 0) blk_cnt[(size_t)blockIdx.x * E + e0 + tid] = 0;
+  // 64 tokens x 64 experts over the whole reduction axis; zeroes this block's histogram slice
+  if (tid < 64 && e0 + tid < E) blk_cnt[(size_t)blockIdx.x * E + e0 + tid] = 0;
   const int lr = tid >> 2, lk = (tid & 3) * 8;
   float acc[4][4];
 #pragma unroll
@@ -239,9 +273,9 @@ __global__ __launch_bounds__(256) void k_router_f32(const float *__restrict__ x,
 
 // ---- top-k, one wave per token; per-block histogram by device atomics -----------------
 // Workgroup = 4 waves = 4 tokens. blk_cnt[t / 64][e] was zeroed by the router kernel.
-template <bool kTwoHalves>
-__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ z,
-                                              const float *__restrict__ z2, int T, int E, int k,
+// kParts partial logit arrays of [T, E] each, contiguous, added in index order.
+template <int kParts>
+__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ z, int T, int E, int k,
                                               int32_t *__restrict__ ids,
                                               float *__restrict__ w,
                                               int32_t *__restrict__ blk_cnt) {
@@ -250,16 +284,18 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ z,
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
   // all loads leave before the first use (experts past E read the last one and are masked)
-  float v[4], v2[4];
+  float p[kParts][4];
+#pragma unroll
+  for (int q = 0; q < kParts; ++q)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      p[q][c] = z[(size_t)q * T * E + (size_t)t * E + min(lane + kWave * c, E - 1)];
+  float v[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const size_t i = (size_t)t * E + min(lane + kWave * c, E - 1);
-    v[c] = z[i];
-    v2[c] = kTwoHalves ? z2[i] : 0.f;
-  }
+    v[c] = p[0][c];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    if (kTwoHalves) v[c] += v2[c];
+    for (int q = 1; q < kParts; ++q) v[c] += p[q][c];
     if (lane + kWave * c >= E) v[c] = -INFINITY;
   }
   int id, pos;
@@ -414,35 +450,33 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t *__restrict__ ids
 }
 
 // ---- launchers ------------------------------------------------------------------------------
-hipError_t launch_router_split(const float *W, size_t n, uint16_t *planes, hipStream_t s) {
-  MOE_LAUNCH("k_router_split", k_router_split,
-             dim3((unsigned)std::min<size_t>((n / 4 + 255) / 256, 2048)), dim3(256), 0, s, W, n,
-             planes);
+hipError_t launch_router_split(const float *W, int E, int H, uint16_t *planes, hipStream_t s) {
+  const int n = (E + kRouterEPad - 1) / kRouterEPad * kRouterEPad / 32 * (H / 16) * 64;
+  MOE_LAUNCH("k_router_split", k_router_split, dim3((unsigned)std::min((n + 255) / 256, 2048)),
+             dim3(256), 0, s, W, E, H, planes);
   return hipSuccess;
 }
 
 hipError_t launch_route_topk(const RouteArgs &a, hipStream_t s) {
   const int NB = (int)((a.T + kRouteBlock - 1) / kRouteBlock);
-  const dim3 g1((unsigned)NB, (unsigned)((a.E + 63) / 64));
   if (a.bf16) {
     if (!a.planes_ready) {
-      const hipError_t e = launch_router_split(a.router_w, (size_t)a.E * a.H, a.router_planes, s);
+      const hipError_t e = launch_router_split(a.router_w, a.E, a.H, a.router_planes, s);
       if (e != hipSuccess) return e;
     }
-    MOE_LAUNCH("k_router_mfma", k_router_mfma, dim3(g1.x, g1.y, 2), dim3(256), 0, s,
-               static_cast<const uint16_t *>(a.x), a.router_planes, a.router_b, a.logits,
-               a.logits2, a.x16, a.blk, (int)a.T, a.H, a.E);
+    MOE_LAUNCH("k_router_mfma", k_router_mfma,
+               dim3((unsigned)NB, (unsigned)((a.E + kRouterEPad - 1) / kRouterEPad), kRouterParts),
+               dim3(256), 0, s, static_cast<const uint16_t *>(a.x), a.router_planes, a.router_b,
+               a.logits, a.x16, a.blk, (int)a.T, a.H, a.E);
+    MOE_LAUNCH("k_topk", k_topk<kRouterParts>, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, s,
+               a.logits, (int)a.T, a.E, a.k, a.ids, a.w, a.blk);
+  } else {
+    MOE_LAUNCH("k_router_f32", k_router_f32, dim3((unsigned)NB, (unsigned)((a.E + 63) / 64)),
+               dim3(256), 0, s, static_cast<const float *>(a.x), a.router_w, a.router_b,
+               a.logits, a.blk, (int)a.T, a.H, a.E);
+    MOE_LAUNCH("k_topk", k_topk<1>, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, s, a.logits,
+               (int)a.T, a.E, a.k, a.ids, a.w, a.blk);
   }
-  else
-    MOE_LAUNCH("k_router_f32", k_router_f32, g1, dim3(256), 0, s,
-               static_cast<const float *>(a.x), a.router_w, a.router_b, a.logits, a.blk,
-               (int)a.T, a.H, a.E);
-  if (a.bf16)
-    MOE_LAUNCH("k_topk", k_topk<true>, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, s,
-               a.logits, a.logits2, (int)a.T, a.E, a.k, a.ids, a.w, a.blk);
-  else
-    MOE_LAUNCH("k_topk", k_topk<false>, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, s,
-               a.logits, nullptr, (int)a.T, a.E, a.k, a.ids, a.w, a.blk);
   return hipSuccess;
 }
 

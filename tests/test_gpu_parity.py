@@ -312,10 +312,17 @@ def test_pack_weights_layout(M, H, I):
         assert np.array_equal(got_q, want_q)
         assert np.array_equal(got_sb, want_sb)
     # router planes: hi = fp16(w), lo = fp16((w - hi) * 2048), so hi + lo / 2048 is w to
-    # 2^-22 relative (2^-25 absolute where w is an fp16 subnormal)
+    # 2^-22 relative (2^-25 absolute where w is an fp16 subnormal), stored in operand order
+    # [E_pad/32][H/16][plane][lane 64][8]: lane l of (c, s) holds expert 32c + l % 32 at
+    # k = 16 s + 8 (l // 32) .. +7, experts past E zero
     E = layer.n_experts
-    planes = buf[d.router_planes - base: d.router_planes - base + 2 * E * H * 2].view(np.float16)
-    hi, lo = planes.reshape(2, E, H)
+    ep = -(-E // 128) * 128
+    frag = buf[d.router_planes - base: d.router_planes - base + 2 * ep * H * 2].view(np.float16)
+    frag = frag.reshape(ep // 32, H // 16, 2, 2, 32, 8)       # c, s, plane, l//32, l%32, j
+    planes = frag.transpose(2, 0, 4, 1, 3, 5).reshape(2, ep, H)  # plane, expert, k
+    hi, lo = planes[0], planes[1]
+    assert np.all(hi[E:] == 0) and np.all(lo[E:] == 0)
+    hi, lo = hi[:E], lo[:E]
     w = layer.router_w
     assert np.array_equal(hi, w.astype(np.float16))
     assert np.array_equal(lo, ((w - hi.astype(np.float32)) * 2048).astype(np.float16))
