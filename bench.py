@@ -247,7 +247,7 @@ def bench_prefill(moe, torch, synth, dev, layer_host, reps=50):
     torch.cuda.synchronize()
     moe.profile_enable(False)
     kern = {}
-    for name in ("k_router_mfma", "k_topk", "k_scan", "k_scatter", "k_grouped_gateup",
+    for name in ("k_router_mfma", "k_topk", "k_group", "k_grouped_gateup", "k_shared_down_combine",
                  "k_grouped_down", "k_combine"):
         tot, n = moe.profile_query(name)
         kern[name] = {"avg_us": 1e3 * tot / max(n, 1), "launches": n}

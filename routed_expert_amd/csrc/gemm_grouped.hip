@@ -73,7 +73,10 @@ MOE_DEV void wait_vmcnt() {
 // multiplied, so a group's last, partial tile costs MFMA work in proportion to its rows.
 // kX: B operands come ready-made from the expanded fp16 weights (launch_expand) instead of
 // being dequantised from the codes; every other step is the same, and so are the results.
-template <bool kGateUp, int MB, bool kX>
+// kComb (down projection of the shared expert over token tiles only): instead of storing the
+// tile, the epilogue adds each token's k routed outputs (already weighted) in a fixed order and
+// the residual, and writes y in bf16 (the weighted combine, fused).
+template <bool kGateUp, int MB, bool kX, bool kComb = false>
 MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, int nvalid,
                           int n_tile) {
   constexpr int kSB = kX ? kXStageBytes : kStageBytes;  // bytes of one ring stage
@@ -311,6 +314,59 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
       *reinterpret_cast<uint4 *>(a.h16 + (size_t)(slot0 + rr) * a.I + n_tile * (BNW / 2) +
                                  8 * (tid & 15)) =
           *reinterpret_cast<const uint4 *>(ht + rr * HP + 8 * (tid & 15));
+  } else if (kComb) {
+    // y[t] = shared(x_t) + sum_j out[slot_of[t, j]] (+ residual[t]) over this tile's 256
+    // columns, fp32 in that order, bf16 out. The shared result goes through LDS in fp32, one
+    // 32-row block at a time; then thread (row rr, 8 columns) gathers the routed rows with
+    // 16-byte loads (all k requested together) and writes 16 bytes of y.
+    constexpr int SP = BNW + 4;
+    float *st = reinterpret_cast<float *>(smem);
+    const int k = a.k;
+    const int cc = 8 * (tid & 31), col0 = n_tile * BNW + cc;
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      __syncthreads();  // the previous block's reads of st are done
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = (r >> 2) * 8 + rq4 + (r & 3);
+        st[row * SP + 64 * wave + col] = acc[m][0][r];
+        st[row * SP + 64 * wave + 32 + col] = acc[m][1][r];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int pass = 0; pass < 4; ++pass) {
+        const int rr = 8 * pass + (tid >> 5), r_tile = 32 * m + rr;
+        if (r_tile >= nvalid) continue;
+        const int64_t t = row0 + r_tile;
+        const float4 s0 = *reinterpret_cast<const float4 *>(st + rr * SP + cc);
+        const float4 s1 = *reinterpret_cast<const float4 *>(st + rr * SP + cc + 4);
+        float v[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        uint4 o[kMaxTopK];
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) {
+          // unused ranks (j >= k) repeat the last one's load and are not added, so that every
+          // load is issued before the first is waited for
+          const int32_t slot = a.slot_of[t * k + min(j, k - 1)];
+          o[j] = *reinterpret_cast<const uint4 *>(a.out + (size_t)slot * a.H + col0);
+        }
+        uint4 rv = make_uint4(0, 0, 0, 0);
+        if (a.residual) rv = *reinterpret_cast<const uint4 *>(a.residual + (size_t)t * a.H + col0);
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) {
+          if (j >= k) break;
+          v[0] += f16lo(o[j].x); v[1] += f16hi(o[j].x); v[2] += f16lo(o[j].y);
+          v[3] += f16hi(o[j].y); v[4] += f16lo(o[j].z); v[5] += f16hi(o[j].z);
+          v[6] += f16lo(o[j].w); v[7] += f16hi(o[j].w);
+        }
+        if (a.residual) {
+          v[0] += bf16lo(rv.x); v[1] += bf16hi(rv.x); v[2] += bf16lo(rv.y); v[3] += bf16hi(rv.y);
+          v[4] += bf16lo(rv.z); v[5] += bf16hi(rv.z); v[6] += bf16lo(rv.w); v[7] += bf16hi(rv.w);
+        }
+        *reinterpret_cast<uint4 *>(a.y + (size_t)t * a.H + col0) =
+            make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                       pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+      }
+    }
   } else {
     // rows x 256 columns fp16 in slot order: a routed slot pre-weighted by its routing
     // weight, a shared-expert slot (weight 1) as it is
@@ -347,6 +403,8 @@ MOE_DEV void grouped_body(const GroupedArgs &a, uint8_t *smem) {
   if (m_tile >= *a.n_tiles) return;
   const int2 tile = a.tiles[m_tile];
   const int e = tile.x & 0xFFFF, row0 = tile.y, nvalid = tile.x >> 16;
+  // the shared expert's down projection runs in its own launch with the combine fused
+  if (!kGateUp && a.fused_combine && e == a.E) return;
   // load-adaptive height: only the 32-row blocks that hold rows (all four when fixed)
   switch (a.fixed_mb ? 4 : (nvalid + 31) >> 5) {
     case 1: grouped_tile<kGateUp, 1, kX>(a, smem, e, row0, nvalid, n_tile); break;
@@ -360,6 +418,23 @@ template <bool kGateUp>
 __global__ __launch_bounds__(256, 2) void k_grouped(GroupedArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
   grouped_body<kGateUp, false>(a, smem);
+}
+
+// Down projection of the shared expert with the weighted combine in its epilogue: token tiles
+// of 64 rows (the shared expert's slots kT + t), every N tile of 256 output columns. XCD-aware
+// order as in grouped_body. Runs after the routed down projection (stream order).
+__global__ __launch_bounds__(256, 2) void k_shared_down_combine(GroupedArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+  const int nN = a.H / BNW;
+  const int id = blockIdx.x, xcd = id & 7, j = id >> 3;
+  const int n_tile = j % nN, m_tile = (j / nN) * 8 + xcd;
+  const int row0 = 64 * m_tile;
+  if (row0 >= a.T) return;
+  const int nvalid = min(64, (int)(a.T - row0));
+  if (nvalid > 32)
+    grouped_tile<false, 2, false, true>(a, smem, a.E, row0, nvalid, n_tile);
+  else
+    grouped_tile<false, 1, false, true>(a, smem, a.E, row0, nvalid, n_tile);
 }
 
 template <bool kGateUp>
@@ -419,6 +494,13 @@ hipError_t launch_grouped_gateup(const GroupedArgs &a, hipStream_t s) {
     MOE_LAUNCH("k_grouped_gateup_x", (k_grouped_x<true>), g, dim3(256), 0, s, a);
   else
     MOE_LAUNCH("k_grouped_gateup", (k_grouped<true>), g, dim3(256), 0, s, a);
+  return hipSuccess;
+}
+
+hipError_t launch_shared_down_combine(const GroupedArgs &a, hipStream_t s) {
+  const int mt = (int)((a.T + 63) / 64);
+  const dim3 g((unsigned)((mt + 7) / 8 * 8 * (a.H / BNW)));
+  MOE_LAUNCH("k_shared_down_combine", k_shared_down_combine, g, dim3(256), 0, s, a);
   return hipSuccess;
 }
 

@@ -49,12 +49,13 @@ struct RouteArgs {
                           // else fixed at 2^tile_shift rows (5..7)
 };
 
+// Router, top-k and per-block histogram (launch_route_topk), then one kernel that forms the
+// group offsets and tile map and scatters the assignments (k_group).
 hipError_t launch_route_prefill(const RouteArgs &a, hipStream_t s);
-// the two halves of launch_route_prefill: router, top-k and the per-block histogram; then
-// the scan into offsets, block bases and tile map (skipped when the host wrote them) and
-// the stable scatter
 hipError_t launch_route_topk(const RouteArgs &a, hipStream_t s);
-hipError_t launch_route_group(const RouteArgs &a, bool scan, hipStream_t s);
+// The scatter alone, from offsets, per-block bases and tile map already in memory (the
+// host-routing ablation uploads them).
+hipError_t launch_route_scatter(const RouteArgs &a, hipStream_t s);
 
 struct ExpertWeights {
   const uint8_t *w13_q, *w2_q;     // int4 codes, interchange layout
@@ -96,7 +97,14 @@ struct GroupedArgs {
   ExpertWeights wt;
   uint16_t *h16;   // [(k+S) T, I] fp16, slot order
   uint16_t *out;   // [(k+S) T, H] fp16, slot order: routed slots already scaled by the
-                   // routing weight, then the shared expert's slots (token order)
+                   // routing weight, then the shared expert's slots (token order; not
+                   // written when the combine is fused)
+  // Weighted combine fused into the shared expert's down projection (S == 1): the routed
+  // down launch skips the shared expert's tiles and launch_shared_down_combine writes y.
+  int fused_combine = 0;
+  const int32_t *slot_of = nullptr;   // [T, k]
+  const uint16_t *residual = nullptr; // [T, H] bf16 or null
+  uint16_t *y = nullptr;              // [T, H] bf16
   // Ablation switches (moe_prefill_ablation); the product path leaves them unset.
   int fixed_mb = 0;        // every tile multiplies all four 32-row blocks
   int S = 0;               // shared experts (launch_expand only)
@@ -106,6 +114,7 @@ struct GroupedArgs {
 };
 hipError_t launch_grouped_gateup(const GroupedArgs &a, hipStream_t s);
 hipError_t launch_grouped_down(const GroupedArgs &a, hipStream_t s);
+hipError_t launch_shared_down_combine(const GroupedArgs &a, hipStream_t s);
 // Separate dequantisation pass: every expert that received rows (and the shared expert)
 // expanded to fp16, [E+S][R/64][K/64][2 column blocks][4 substeps][64 lanes][8], the B
 // operand registers of the grouped GEMM in the order it reads them.

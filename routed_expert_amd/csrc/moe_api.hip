@@ -451,6 +451,18 @@ static moe_status run_grouped(const moe_layer *layer, const moe::GroupedArgs &ga
   hipError_t e;
   if ((e = moe::launch_grouped_gateup(ga, s)) != hipSuccess)
     return hip_fail(e, "moe_prefill gate/up");
+  if (layer->n_shared) {
+    // the routed experts' down projection, then the shared expert's with the combine fused
+    moe::GroupedArgs gd = ga;
+    gd.fused_combine = 1;
+    gd.slot_of = ra.slot_of;
+    gd.residual = static_cast<const uint16_t *>(residual);
+    gd.y = static_cast<uint16_t *>(y);
+    if ((e = moe::launch_grouped_down(gd, s)) != hipSuccess) return hip_fail(e, "moe_prefill down");
+    if ((e = moe::launch_shared_down_combine(gd, s)) != hipSuccess)
+      return hip_fail(e, "moe_prefill shared down + combine");
+    return MOE_OK;
+  }
   if ((e = moe::launch_grouped_down(ga, s)) != hipSuccess) return hip_fail(e, "moe_prefill down");
   moe::CombineArgs ca{};
   ca.out = ga.out;
@@ -597,7 +609,7 @@ AblPlan abl_plan(const moe_layer *L, int64_t T, int variant) {
   return a;
 }
 
-// Host copy of the device scan (k_scan): per-block bases, offsets, the tile height (fixed
+// Host copy of the device scan (group_tables): per-block bases, offsets, the tile height (fixed
 // or chosen from the load by the same rule) and the tile map in the same order and
 // encoding (full tiles, the shared expert's full tiles, partial tiles by height, the
 // shared expert's partial tile), from the top-k ids read back from the device.
@@ -712,7 +724,7 @@ moe_status moe_prefill_ablation(const moe_layer *layer, int32_t variant, const v
     ra.n_tiles = dtab + ap.tab_ntiles;
     ra.tiles = reinterpret_cast<int2 *>(dtab + ap.tab_tiles);
     ra.blk = dtab + ap.tab_blk;
-    if ((e = moe::launch_route_group(ra, false, s)) != hipSuccess)
+    if ((e = moe::launch_route_scatter(ra, s)) != hipSuccess)
       return hip_fail(e, "ablation scatter");
   } else if ((e = moe::launch_route_prefill(ra, s)) != hipSuccess) {
     return hip_fail(e, "ablation route");

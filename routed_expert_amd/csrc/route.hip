@@ -327,32 +327,16 @@ MOE_DEV V block_scan_incl(V v, V *wtot) {
   return v + before;
 }
 
-// ---- counts, offsets, per-block bases and the tile map (one workgroup) -------------------
-// blk_cnt[b][e] becomes the number of assignments to e in blocks before b. offsets has
-// E+2 entries: routed experts, then the shared expert's slots [kT, kT+T).
-__global__ __launch_bounds__(256) void k_scan(int32_t *__restrict__ blk_cnt, int NB, int E,
-                                              int T, int k, int S,
-                                              int32_t *__restrict__ offsets,
-                                              int32_t *__restrict__ counts_user,
-                                              int32_t *__restrict__ offsets_user,
-                                              int2 *__restrict__ tiles,
-                                              int32_t *__restrict__ n_tiles, int tsh_fixed,
-                                              int fill) {
+// ---- counts, offsets and the tile map from the per-expert totals --------------------------
+// Called by all 256 threads of a workgroup; thread e < E passes run = the assignments to expert
+// e (others 0). Returns the exclusive prefix of run over the experts (the group offset of e).
+// With `write` set the workgroup also stores the offsets (E+2 entries: routed experts, then the
+// shared expert's slots [kT, kT+T)), the caller's counts and offsets, and the tile map.
+MOE_DEV int group_tables(int run, bool write, int E, int T, int S, int32_t *__restrict__ offsets,
+                         int32_t *__restrict__ counts_user, int32_t *__restrict__ offsets_user,
+                         int2 *__restrict__ tiles, int32_t *__restrict__ n_tiles, int tsh_fixed,
+                         int fill) {
   const int e = threadIdx.x;
-  int run = 0;
-  if (e < E) {
-    // 32 block counts per round: the loads of a round are issued together
-    for (int b0 = 0; b0 < NB; b0 += 32) {
-      int c[32];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) c[i] = b0 + i < NB ? blk_cnt[(size_t)(b0 + i) * E + e] : 0;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        if (b0 + i < NB) blk_cnt[(size_t)(b0 + i) * E + e] = run;
-        run += c[i];
-      }
-    }
-  }
   // one scan gives the offsets (low word) and the number of 32-row blocks the experts'
   // rows fill (high word)
   __shared__ uint64_t sc64[4];
@@ -384,6 +368,7 @@ __global__ __launch_bounds__(256) void k_scan(int32_t *__restrict__ blk_cnt, int
   const int nfull = run >> tsh, mb = (rem + 31) >> 5;
   const uint64_t packed = (uint64_t)nfull | (mb ? (1ull << (22 + 9 * (4 - mb))) : 0ull);
   const uint64_t pincl = block_scan_incl(packed, sc64);
+  if (!write) return off;
   const uint64_t pexcl = pincl - packed;
   __shared__ uint64_t ptot[1];
   if (e == 255) ptot[0] = pincl;
@@ -415,6 +400,60 @@ __global__ __launch_bounds__(256) void k_scan(int32_t *__restrict__ blk_cnt, int
     offsets[E + 1] = nassign + (S ? T : 0);
     if (offsets_user) offsets_user[E] = nassign;
     *n_tiles = npart + (sh_rem ? 1 : 0);
+  }
+  return off;
+}
+
+// Scan and scatter in one kernel, one workgroup per routing block of 64 tokens: thread e sums
+// the block counts of expert e over all blocks (its total) and over the blocks before this one
+// (its base), every workgroup forms the same offsets from the totals (same inputs, same
+// order), workgroup 0 also writes the tables, and the block's assignments are placed as in
+// k_scatter. The histogram is only read, so the workgroups need no ordering between them.
+__global__ __launch_bounds__(256) void k_group(const int32_t *__restrict__ blk_cnt,
+                                               const int32_t *__restrict__ ids,
+                                               const float *__restrict__ w, int NB, int E, int T,
+                                               int k, int S, int32_t *__restrict__ offsets,
+                                               int32_t *__restrict__ counts_user,
+                                               int32_t *__restrict__ offsets_user,
+                                               int2 *__restrict__ tiles,
+                                               int32_t *__restrict__ n_tiles, int tsh_fixed,
+                                               int fill, int32_t *__restrict__ sorted_tok,
+                                               int32_t *__restrict__ slot_of,
+                                               float *__restrict__ slot_w) {
+  __shared__ unsigned long long mask[kMaxExperts];
+  __shared__ int start[kMaxExperts];
+  const int b = blockIdx.x, t0 = b * kRouteBlock, tid = threadIdx.x;
+  int run = 0, base = 0;
+  if (tid < E) {
+    for (int b0 = 0; b0 < NB; b0 += 32) {
+      int c[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) c[i] = b0 + i < NB ? blk_cnt[(size_t)(b0 + i) * E + tid] : 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        base += b0 + i < b ? c[i] : 0;
+        run += c[i];
+      }
+    }
+  }
+  const int off = group_tables(run, b == 0, E, T, S, offsets, counts_user, offsets_user, tiles,
+                               n_tiles, tsh_fixed, fill);
+  start[tid] = off + base;
+  mask[tid] = 0ull;
+  __syncthreads();
+  const int nt = min(kRouteBlock, T - t0), na = nt * k;
+  for (int i = tid; i < na; i += 256) {
+    const int e = ids[(size_t)t0 * k + i];
+    atomicOr(&mask[e], 1ull << (i / k));
+  }
+  __syncthreads();
+  for (int i = tid; i < na; i += 256) {
+    const int tt = i / k, e = ids[(size_t)t0 * k + i];
+    const unsigned long long before = tt ? (mask[e] & (~0ull >> (64 - tt))) : 0ull;
+    const int slot = start[e] + __popcll(before);
+    sorted_tok[slot] = t0 + tt;
+    slot_of[(size_t)t0 * k + i] = slot;
+    if (slot_w) slot_w[slot] = w[(size_t)t0 * k + i];
   }
 }
 
@@ -480,12 +519,8 @@ hipError_t launch_route_topk(const RouteArgs &a, hipStream_t s) {
   return hipSuccess;
 }
 
-hipError_t launch_route_group(const RouteArgs &a, bool scan, hipStream_t s) {
+hipError_t launch_route_scatter(const RouteArgs &a, hipStream_t s) {
   const int NB = (int)((a.T + kRouteBlock - 1) / kRouteBlock);
-  if (scan)
-    MOE_LAUNCH("k_scan", k_scan, dim3(1), dim3(256), 0, s, a.blk, NB, a.E, (int)a.T, a.k, a.S,
-               a.offsets, a.counts_user, a.offsets_user, a.tiles, a.n_tiles, a.tile_shift,
-               gemm_fill(a.I));
   MOE_LAUNCH("k_scatter", k_scatter, dim3(NB), dim3(256), 0, s, a.ids, (int)a.T, a.E, a.k,
              a.offsets, a.blk, a.w, a.sorted_tok, a.slot_of, a.slot_w);
   return hipSuccess;
@@ -494,7 +529,11 @@ hipError_t launch_route_group(const RouteArgs &a, bool scan, hipStream_t s) {
 hipError_t launch_route_prefill(const RouteArgs &a, hipStream_t s) {
   const hipError_t e = launch_route_topk(a, s);
   if (e != hipSuccess) return e;
-  return launch_route_group(a, true, s);
+  const int NB = (int)((a.T + kRouteBlock - 1) / kRouteBlock);
+  MOE_LAUNCH("k_group", k_group, dim3(NB), dim3(256), 0, s, a.blk, a.ids, a.w, NB, a.E, (int)a.T,
+             a.k, a.S, a.offsets, a.counts_user, a.offsets_user, a.tiles, a.n_tiles, a.tile_shift,
+             gemm_fill(a.I), a.sorted_tok, a.slot_of, a.slot_w);
+  return hipSuccess;
 }
 
 }  // namespace moe
