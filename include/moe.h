@@ -295,6 +295,25 @@ moe_status moe_stack_forward(const moe_layer *layers, int32_t n_layers, void *h,
 moe_status moe_rmsnorm(const void *h, int64_t T, int32_t hidden, float eps, int32_t act_dtype,
                        void *out, void *stream);
 
+/* Measurement aids ("Optimizing On-Device Inference for Apple Silicon", section "Limits of
+ * further optimization": kernels are judged against the fastest rate measured for their own
+ * access pattern, besides the nominal peak). Neither computes anything of the layer.
+ *
+ * moe_decode_read_ceiling: the weight loads of one batch-1 decode kernel, from the same grid
+ * and addresses, with the arithmetic taken out. part 0: the router GEMV's (router rows; the
+ * router weights stand in for x); part 1: the gate/up kernel's (the experts ids[0..k-1], then
+ * the shared expert); part 2: the down kernel's (the same experts). ids: device int32 [k];
+ * sink: device uint32 [1], written only in the rare case a checksum equals a fixed word. The
+ * layer must take the batch-1 fast path (packed, hidden 2048, intermediate 512); otherwise
+ * MOE_E_UNSUPPORTED.
+ *
+ * moe_mfma_ceiling: a dense loop of v_mfma_f32_32x32x16_f16 on register operands over 512
+ * workgroups of four waves (two per CU, like the grouped GEMMs), iters x 8 per wave; *flops
+ * (host) receives the FLOP it executes. sink as above. */
+moe_status moe_decode_read_ceiling(const moe_layer *layer, const int32_t *ids, int32_t part,
+                                   uint32_t *sink, void *stream);
+moe_status moe_mfma_ceiling(int32_t iters, uint32_t *sink, double *flops, void *stream);
+
 /* Kernel timing for measurement tools. When enabled, every kernel the library launches
  * is dispatched with a start/stop HIP event pair bound to the dispatch itself
  * (hipExtLaunchKernel), on the kernel's stream. moe_profile_query() waits for the recorded

@@ -203,6 +203,20 @@ MOE_DEV void block_topk(float zv, int E, int k, uint64_t *K, uint64_t *cand) {
 // Expert id of a top-k key.
 MOE_DEV int key_id(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
 
+// Where a wave of a gate/up half block reads: lane l's 16 code bytes of K step 4v + i are at
+// codes + i * 2048, its four steps' {scale, bias} pairs at the returned sb pointer (see
+// gateup_half_block for the lane layout).
+MOE_DEV const uint8_t *w13_codes_at(const DecodeArgs &a, int e, int b, int f, int wave, int lane) {
+  const size_t blk = (size_t)e * kNB13 + b;
+  return a.wt.w13_t + (blk * kNS13 + 4 * wave) * 2048 + (lane >= 32 ? 1024 : 0) + 512 * f +
+         16 * (lane & 31);
+}
+MOE_DEV const uint16_t *w13_sb_at(const DecodeArgs &a, int e, int b, int f, int wave, int lane) {
+  const size_t blk = (size_t)e * kNB13 + b;
+  return a.wt.w13_tsb + (blk * (kNS13 / 4) + wave) * 512 +
+         8 * ((lane >= 32 ? 32 : 0) + 16 * f + ((lane & 31) >> 1));
+}
+
 // 16 gate + 16 up rows (rows 32b + 16f .. +16 of expert e's tiled block b) against the
 // staged x: wave v takes K steps 4v .. 4v+3, one 1 KB load per step (lanes 0..31 the gate
 // rows, 32..63 the up rows; lane: row (l % 32) / 2, K half l % 2). Writes silu(g) * u of
@@ -212,14 +226,11 @@ MOE_DEV void gateup_half_block(const DecodeArgs &a, int e, int b, int f, const f
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const bool up = lane >= 32;
   const int r16 = (lane & 31) >> 1, hh = lane & 1;
-  const size_t blk = (size_t)e * kNB13 + b;
-  const uint8_t *tq = a.wt.w13_t + (blk * kNS13 + 4 * wave) * 2048 + (up ? 1024 : 0) +
-                      512 * f + 16 * (lane & 31);
+  const uint8_t *tq = w13_codes_at(a, e, b, f, wave, lane);
   uint4 c[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) c[i] = *reinterpret_cast<const uint4 *>(tq + i * 2048);
-  const uint4 sb = *reinterpret_cast<const uint4 *>(
-      a.wt.w13_tsb + (blk * (kNS13 / 4) + wave) * 512 + 8 * ((up ? 32 : 0) + 16 * f + r16));
+  const uint4 sb = *reinterpret_cast<const uint4 *>(w13_sb_at(a, e, b, f, wave, lane));
   __syncthreads();  // x staged by the caller
   float acc = 0.f;
 #pragma unroll
@@ -317,6 +328,18 @@ __global__ __launch_bounds__(DT) void k_dec_b(DecodeArgs a) {
                     a.h + (size_t)j * DI + 32 * b + 16 * f);
 }
 
+// Where lane l reads unit (expert e, K step st) of output rows 64b + 4t .. +4 of the down
+// projection (lane: row (l % 8) / 2, K half l % 2): 16 code bytes, and the row's 16-byte
+// {scale, bias} entry holding four K steps.
+MOE_DEV const uint8_t *w2_codes_at(const DecodeArgs &a, int e, int b, int t, int st, int lane) {
+  const size_t blk = (size_t)e * kNB2 + b;
+  return a.wt.w2_t + (blk * kNS2 + st) * 2048 + 32 * (4 * t + ((lane & 7) >> 1)) + 16 * (lane & 1);
+}
+MOE_DEV const uint16_t *w2_sb_at(const DecodeArgs &a, int e, int b, int t, int st, int lane) {
+  const size_t blk = (size_t)e * kNB2 + b;
+  return a.wt.w2_tsb + (blk * (kNS2 / 4) + (st >> 2)) * 512 + 8 * (4 * t + ((lane & 7) >> 1));
+}
+
 __global__ __launch_bounds__(DT) void k_dec_c(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) f16x2_t hs[kSlots * DI / 2];
   __shared__ float hseg[kSlots * DI / 32];
@@ -373,11 +396,8 @@ __global__ __launch_bounds__(DT) void k_dec_c(DecodeArgs a) {
     // these loads stay in flight across the next barrier
     const int p = wave + (DT / 64) * i, u = 8 * p + ug, jj = min(u >> 3, nslot - 1),
               st = u & 7;
-    const size_t blk = (size_t)s_ids[jj] * kNB2 + b;
-    c[i] = *reinterpret_cast<const uint4 *>(a.wt.w2_t + (blk * kNS2 + st) * 2048 +
-                                            32 * (4 * t + r4) + 16 * hh);
-    sb[i] = *reinterpret_cast<const uint4 *>(a.wt.w2_tsb + (blk * (kNS2 / 4) + (st >> 2)) * 512 +
-                                             8 * (4 * t + r4));
+    c[i] = *reinterpret_cast<const uint4 *>(w2_codes_at(a, s_ids[jj], b, t, st, lane));
+    sb[i] = *reinterpret_cast<const uint4 *>(w2_sb_at(a, s_ids[jj], b, t, st, lane));
   }
   // routing weights: softmax over the selected logits, s_z[0] the largest (or, on the
   // small-T path, the weights themselves); the shared expert (slot k) has weight 1
@@ -668,6 +688,73 @@ __global__ __launch_bounds__(DT) void k_st_b(DecodeArgs a) {
     if (u + 2 * G < nunits) unit_compute(u + 2 * G, d2);
     d2 = unit_load(min(u + 5 * G, last));
   }
+}
+
+// ---- weight-read ceilings (measurement aids) ----------------------------------------------
+// Each kernel issues exactly the weight loads of one decode kernel, from the same grid and
+// addresses (the helpers above), with the arithmetic taken out: a thread only XORs the words
+// it read and stores the result when it equals a fixed word (practically never), so the loads
+// cannot be dropped. The selected experts come from a.sel_ids (k ids) and the shared expert.
+// Timed beside the product kernels they give the fastest rate of the same access pattern.
+MOE_DEV uint32_t xor4(uint4 v) { return v.x ^ v.y ^ v.z ^ v.w; }
+constexpr uint32_t kSinkWord = 0x9E3779B9u;
+
+__global__ __launch_bounds__(DT) void k_read_router(DecodeArgs a, uint32_t *sink) {
+  const int w = blockIdx.x, tid = threadIdx.x;
+  if (w >= a.E) return;
+  const uint4 wr = reinterpret_cast<const uint4 *>(a.router_w + (size_t)w * DH)[tid];
+  const uint2 xb = reinterpret_cast<const uint2 *>(a.x)[tid];
+  const uint32_t v = xor4(wr) ^ xb.x ^ xb.y;
+  if (v == kSinkWord) sink[0] = v;
+}
+
+__global__ __launch_bounds__(DT) void k_read_gateup(DecodeArgs a, uint32_t *sink) {
+  const int w = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int e, b, f;
+  if (w >= DWG) {
+    e = a.E;
+    b = (w - DWG) >> 1;
+    f = (w - DWG) & 1;
+  } else {
+    const int j = w >> 5;
+    if (j >= a.k) return;
+    e = a.sel_ids[j];
+    b = (w >> 1) & 15;
+    f = w & 1;
+  }
+  const uint8_t *tq = w13_codes_at(a, e, b, f, wave, lane);
+  uint32_t v = xor4(*reinterpret_cast<const uint4 *>(w13_sb_at(a, e, b, f, wave, lane)));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v ^= xor4(*reinterpret_cast<const uint4 *>(tq + i * 2048));
+  if (v == kSinkWord) sink[0] = v;
+}
+
+__global__ __launch_bounds__(DT) void k_read_down(DecodeArgs a, uint32_t *sink) {
+  const int w = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nslot = a.k + a.S, b = w >> 4, t = w & 15, ug = lane >> 3;
+  uint32_t v = 0;
+  constexpr int kMaxOcts = (kSlots * kNS2 / 8 + DT / 64 - 1) / (DT / 64);
+#pragma unroll
+  for (int i = 0; i < kMaxOcts; ++i) {
+    const int u = 8 * (wave + (DT / 64) * i) + ug, jj = u >> 3, st = u & 7;
+    if (jj < nslot) {  // only the units the product kernel uses
+      const int e = jj < a.k ? a.sel_ids[jj] : a.E;
+      v ^= xor4(*reinterpret_cast<const uint4 *>(w2_codes_at(a, e, b, t, st, lane)));
+      v ^= xor4(*reinterpret_cast<const uint4 *>(w2_sb_at(a, e, b, t, st, lane)));
+    }
+  }
+  if (v == kSinkWord) sink[0] = v;
+}
+
+hipError_t launch_read_ceiling(const DecodeArgs &a, int part, uint32_t *sink, hipStream_t s) {
+  if (part == 0)
+    MOE_LAUNCH("k_read_router", k_read_router, dim3(DWG), dim3(DT), 0, s, a, sink);
+  else if (part == 1)
+    MOE_LAUNCH("k_read_gateup", k_read_gateup, dim3(DWG + (a.S ? kSharedWG : 0)), dim3(DT), 0, s,
+               a, sink);
+  else
+    MOE_LAUNCH("k_read_down", k_read_down, dim3(kDownWG), dim3(DT), 0, s, a, sink);
+  return hipSuccess;
 }
 
 bool decode_gemv_supported(int H, int I, int E, int k, int S, bool int4) {

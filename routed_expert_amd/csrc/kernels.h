@@ -178,6 +178,13 @@ bool decode_gemv_supported(int H, int I, int E, int k, int S, bool int4);
 hipError_t launch_decode_gemv(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_small_t(const DecodeArgs &a, hipStream_t s);
 
+// Measurement aids: the decode kernels' weight loads without their arithmetic (part 0:
+// router, 1: gate/up, 2: down; experts from a.sel_ids), and a dense MFMA loop of
+// kMfmaCeilingWG workgroups x 4 waves x iters x 8 v_mfma_f32_32x32x16_f16.
+hipError_t launch_read_ceiling(const DecodeArgs &a, int part, uint32_t *sink, hipStream_t s);
+constexpr int kMfmaCeilingWG = 512;
+hipError_t launch_mfma_ceiling(int iters, uint32_t *sink, hipStream_t s);
+
 hipError_t launch_rmsnorm(const void *h, int64_t T, int H, float eps, bool bf16, void *out,
                           hipStream_t s);
 

@@ -1099,6 +1099,40 @@ moe_status moe_rmsnorm(const void *h, int64_t T, int32_t hidden, float eps, int3
   return MOE_OK;
 }
 
+moe_status moe_decode_read_ceiling(const moe_layer *layer, const int32_t *ids, int32_t part,
+                                   uint32_t *sink, void *stream) {
+  g_err.clear();
+  moe_status st = check_layer(layer);
+  if (st) return st;
+  if (!decode_fast(layer))
+    return fail(MOE_E_UNSUPPORTED, "read ceilings exist for the packed decode-shaped layer only");
+  if (part < 0 || part > 2) return fail(MOE_E_INVALID, "part must be 0, 1 or 2");
+  if (!sink || (part > 0 && !ids)) return fail(MOE_E_INVALID, "ids and sink must be non-NULL");
+  moe::DecodeArgs da{};
+  da.x = static_cast<const uint16_t *>(static_cast<const void *>(layer->router_w));
+  da.router_w = layer->router_w;
+  da.wt = weights_of(layer);
+  da.sel_ids = const_cast<int32_t *>(ids);
+  da.H = layer->hidden;
+  da.I = layer->inter;
+  da.E = layer->n_experts;
+  da.k = layer->top_k;
+  da.S = layer->n_shared;
+  da.T = 1;
+  const hipError_t e = moe::launch_read_ceiling(da, part, sink, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "moe_decode_read_ceiling");
+  return MOE_OK;
+}
+
+moe_status moe_mfma_ceiling(int32_t iters, uint32_t *sink, double *flops, void *stream) {
+  g_err.clear();
+  if (iters < 1 || !sink || !flops) return fail(MOE_E_INVALID, "iters >= 1, sink and flops needed");
+  *flops = (double)moe::kMfmaCeilingWG * 4 * iters * 8 * 32768.0;
+  const hipError_t e = moe::launch_mfma_ceiling(iters, sink, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "moe_mfma_ceiling");
+  return MOE_OK;
+}
+
 moe_status moe_profile_enable(int32_t on) {
   g_err.clear();
   g_prof_on.store(on != 0);

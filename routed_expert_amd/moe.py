@@ -29,7 +29,8 @@ EXPORTS = ("moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_pack
            "moe_profile_enable", "moe_profile_query", "moe_profile_reset",
            "moe_ablation_workspace_bytes", "moe_prefill_ablation",
            "moe_attn_workspace_bytes", "moe_attn_decode", "moe_attn_decode_unpacked",
-           "moe_gdn_scan", "moe_gdn_chunked_workspace_bytes", "moe_gdn_scan_chunked")
+           "moe_gdn_scan", "moe_gdn_chunked_workspace_bytes", "moe_gdn_scan_chunked",
+           "moe_decode_read_ceiling", "moe_mfma_ceiling")
 (ABL_NONE, ABL_SEPARATE_DEQUANT, ABL_HOST_ROUTING, ABL_TILE_64, ABL_FIXED_TILE,
  ABL_TILE_128) = range(6)
 ABLATIONS = {"none": ABL_NONE, "separate_dequant": ABL_SEPARATE_DEQUANT,
@@ -117,6 +118,8 @@ def lib():
                                             ctypes.c_int),
         "moe_gdn_scan_chunked": ([P, P, P, P, P, I64, I32, I32, I32, I32, P, P, P, SZ, P],
                                  ctypes.c_int),
+        "moe_decode_read_ceiling": ([P, P, I32, P, P], ctypes.c_int),
+        "moe_mfma_ceiling": ([I32, P, ctypes.POINTER(ctypes.c_double), P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -391,6 +394,23 @@ def moe_rmsnorm(h: torch.Tensor, eps: float = 1e-6, out=None, stream=None) -> to
     _check("moe_rmsnorm", lib().moe_rmsnorm(_ptr(h), h.shape[0], h.shape[1], float(eps), act,
                                             _ptr(out), _stream(stream)))
     return out
+
+
+def decode_read_ceiling(layer: DeviceLayer, ids: torch.Tensor, part: int, sink: torch.Tensor,
+                        stream=None):
+    """The weight loads of decode kernel `part` (0 router, 1 gate/up, 2 down) with the
+    arithmetic taken out (a measurement aid); ids: device int32 [k] selected experts."""
+    _check("moe_decode_read_ceiling",
+           lib().moe_decode_read_ceiling(layer.ref, _ptr(ids), int(part), _ptr(sink),
+                                         _stream(stream)))
+
+
+def mfma_ceiling(iters: int, sink: torch.Tensor, stream=None) -> float:
+    """Launches the dense MFMA loop; returns the FLOP it executes."""
+    f = ctypes.c_double(0)
+    _check("moe_mfma_ceiling", lib().moe_mfma_ceiling(int(iters), _ptr(sink), ctypes.byref(f),
+                                                      _stream(stream)))
+    return f.value
 
 
 def profile_enable(on: bool = True):

@@ -312,3 +312,19 @@ def test_decode_noalloc_rejects_layers_beyond_its_scratch(M):
     st, need = ws_bytes(M, fake_layer(M), 1)
     assert st == 0 and need <= (4 << 20)
     assert lib.moe_decode_noalloc(ctypes.byref(fake_layer(M)), x, None, None, None) == M.E_INVALID
+
+
+def test_measurement_aids_argument_errors(M):
+    """The read ceilings and the MFMA loop reject bad arguments on the host."""
+    lib = M.lib()
+    L = fake_layer(M)
+    sink = ctypes.c_void_p(0x4000000)
+    ids = ctypes.c_void_p(0x5000000)
+    assert lib.moe_decode_read_ceiling(ctypes.byref(L), ids, 3, sink, None) == M.E_INVALID
+    assert lib.moe_decode_read_ceiling(ctypes.byref(L), None, 1, sink, None) == M.E_INVALID
+    assert lib.moe_decode_read_ceiling(ctypes.byref(L), ids, 1, None, None) == M.E_INVALID
+    odd = fake_layer(M, inter=256)            # not the batch-1 fast path
+    assert lib.moe_decode_read_ceiling(ctypes.byref(odd), ids, 1, sink, None) == M.E_UNSUPPORTED
+    f = ctypes.c_double(0)
+    assert lib.moe_mfma_ceiling(0, sink, ctypes.byref(f), None) == M.E_INVALID
+    assert lib.moe_mfma_ceiling(10, sink, None, None) == M.E_INVALID
