@@ -50,6 +50,13 @@ constexpr int kStageBytes = kABytes + kBBytes;
 // 4 groups x {scale, bias}) into a 2-slot ring.
 constexpr int kSSlot = 4 * 1024;
 constexpr int kSmemBytes = kStages * kStageBytes + 2 * kSSlot;  // 80 KB: two workgroups per CU
+// A tile of five 32-row blocks (an expert's last full tile with its short remainder, see
+// group_tables) has 20 KB of activation rows per step; three such stages would not fit two
+// workgroups per CU, so it runs a two-stage ring (loads one K step ahead instead of two):
+// 2 x (20 + 8) KB + 8 KB of scales = 64 KB.
+constexpr int kMaxMB = 5;
+template <int MB> constexpr int ring_stages() { return MB > 4 ? 2 : kStages; }
+template <int MB> constexpr int a_stage_bytes() { return (MB > 4 ? MB : 4) * 32 * BK * 2; }
 // Expanded-weight variant (separate dequantisation pass, an ablation): each wave's B operand
 // of a step is 8 KB of fp16 instead of 2 KB of codes, so a stage is 48 KB and the 144 KB
 // ring leaves room for one workgroup per CU.
@@ -69,8 +76,9 @@ MOE_DEV void wait_vmcnt() {
 }
 
 // One tile: rows [row0, row0 + nvalid) of group e, weight rows of N tile n_tile. MB is the
-// number of 32-row blocks holding valid rows (1..4); blocks past them are neither loaded nor
-// multiplied, so a group's last, partial tile costs MFMA work in proportion to its rows.
+// number of 32-row blocks holding valid rows (1..4, or 5 for a full tile that took in its
+// group's short remainder); blocks past them are neither loaded nor multiplied, so a
+// group's last, partial tile costs MFMA work in proportion to its rows.
 // kX: B operands come ready-made from the expanded fp16 weights (launch_expand) instead of
 // being dequantised from the codes; every other step is the same, and so are the results.
 // kComb (down projection of the shared expert over token tiles only): instead of storing the
@@ -79,8 +87,12 @@ MOE_DEV void wait_vmcnt() {
 template <bool kGateUp, int MB, bool kX, bool kComb = false>
 MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, int nvalid,
                           int n_tile) {
-  constexpr int kSB = kX ? kXStageBytes : kStageBytes;  // bytes of one ring stage
+  constexpr int kSt = ring_stages<MB>();                 // ring depth
+  constexpr int kAB = a_stage_bytes<MB>();               // activation rows of one stage
+  constexpr int kSB = kAB + (kX ? kXBBytes : kBBytes);   // bytes of one ring stage
   constexpr int kLB = kX ? 8 : 2;  // B loads per wave and step (besides the scale blocks)
+  static_assert(kX ? kSt * kSB <= kXSmemBytes : kSt * kSB + 2 * kSSlot <= kSmemBytes,
+                "ring does not fit the kernel's LDS");
   const int gbase = a.offsets[e];
   const int slot0 = gbase + row0;
   const int K = kGateUp ? a.H : a.I;
@@ -145,20 +157,20 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
   // expanded weights: MB + 8)
 #define MOE_ISSUE(step)                                                                 \
   do {                                                                                  \
-    const uint32_t base_ = smem_lds + ((step) % kStages) * kSB;                         \
+    const uint32_t base_ = smem_lds + ((step) % kSt) * kSB;                             \
     const int k0_ = (step) * BK;                                                        \
     _Pragma("unroll") for (int j = 0; j < MB; ++j)                                      \
       MOE_DMA16(asrc[j] + k0_, base_ + (wave_u + 4 * j) * 1024);                        \
     if constexpr (kX) {                                                                 \
-      const uint32_t bb_ = base_ + kABytes + wave_u * 8192;                             \
+      const uint32_t bb_ = base_ + kAB + wave_u * 8192;                                 \
       _Pragma("unroll") for (int q = 0; q < 8; ++q)                                     \
         MOE_DMA16(txq + (size_t)(step) * 8192 + q * 1024, bb_ + q * 1024);              \
     } else {                                                                            \
-      const uint32_t bb_ = base_ + kABytes + wave_u * 2048;                             \
+      const uint32_t bb_ = base_ + kAB + wave_u * 2048;                                 \
       MOE_DMA16(tq + (size_t)(step) * 2048, bb_);                                       \
       MOE_DMA16(tq + (size_t)(step) * 2048 + 1024, bb_ + 1024);                         \
       if (((step) & 3) == 0) {                                                          \
-        const uint32_t sb_ = smem_lds + kStages * kStageBytes + (((step) >> 2) & 1) * kSSlot + \
+        const uint32_t sb_ = smem_lds + kSt * kSB + (((step) >> 2) & 1) * kSSlot +      \
                              wave_u * 1024;                                             \
         MOE_DMA16(tsb + (size_t)((step) >> 2) * 512, sb_);                              \
       }                                                                                 \
@@ -183,18 +195,18 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
   const int bn = lane & 31, bh = lane >> 5;
 #define MOE_READ_BX(step)                                                               \
   do {                                                                                  \
-    const uint8_t *bsrc_ = smem + ((step) % kStages) * kSB + kABytes + wave * 8192 + 16 * lane; \
+    const uint8_t *bsrc_ = smem + ((step) % kSt) * kSB + kAB + wave * 8192 + 16 * lane; \
     _Pragma("unroll") for (int q = 0; q < 8; ++q)                                       \
       bx[q] = *reinterpret_cast<const uint4 *>(bsrc_ + q * 1024);                       \
   } while (0)
 #define MOE_READ_B(step)                                                                \
   do {                                                                                  \
-    const uint8_t *bsrc_ = smem + ((step) % kStages) * kStageBytes + kABytes + wave * 2048 + \
+    const uint8_t *bsrc_ = smem + ((step) % kSt) * kSB + kAB + wave * 2048 +            \
                            32 * bn + 16 * bh;                                           \
     const uint4 q0_ = *reinterpret_cast<const uint4 *>(bsrc_);                          \
     const uint4 q1_ = *reinterpret_cast<const uint4 *>(bsrc_ + 1024);                   \
     const uint32_t *sv_ = reinterpret_cast<const uint32_t *>(                           \
-        smem + kStages * kStageBytes + (((step) >> 2) & 1) * kSSlot + wave * 1024 + 16 * bn + \
+        smem + kSt * kSB + (((step) >> 2) & 1) * kSSlot + wave * 1024 + 16 * bn +        \
         4 * ((step) & 3));                                                              \
     const uint32_t sb0_ = sv_[0], sb1_ = sv_[128];                                      \
     s0 = f16_pair_from_bf16((uint16_t)sb0_);                                            \
@@ -210,9 +222,10 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
   // every lane's source pointers are computed (their loads done) before the first DMA
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   MOE_ISSUE(0);
-  if (nsteps > 1) MOE_ISSUE(1);
-  // step 0's own loads: everything after them is step 1's (MB + kLB loads, step 1 is odd)
-  if (nsteps > 1)
+  if (kSt > 2 && nsteps > 1) MOE_ISSUE(1);
+  // step 0's own loads: everything after them is step 1's (MB + kLB loads, step 1 is odd;
+  // none with the two-stage ring)
+  if (kSt > 2 && nsteps > 1)
     wait_vmcnt<MB + kLB>();
   else
     wait_vmcnt<0>();
@@ -235,10 +248,10 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
   MOE_B_OPS(0);
   for (int st = 0; st < nsteps; ++st) {
     // every wave's loads of step st have landed (each wave waited for its own before its
-    // mid-step read of step st's codes), and every wave is done with the stage step st+2
-    // will reuse
+    // mid-step read of step st's codes), and every wave is done with the stage that step
+    // st + kSt - 1 will reuse
     asm volatile("s_barrier" ::: "memory");
-    const uint8_t *arow = smem + (st % kStages) * kSB + arow_l * 128;
+    const uint8_t *arow = smem + (st % kSt) * kSB + arow_l * 128;
     // A fragments are double-buffered: substep kk+1's are read while kk's MFMAs run
     f16x8_t av[2][MB];
 #pragma unroll
@@ -257,7 +270,7 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
         acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[kk & 1][m], bc0, acc[m][0], 0, 0, 0);
         acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[kk & 1][m], bc1, acc[m][1], 0, 0, 0);
       }
-      if (kk == 0 && st + 2 < nsteps) MOE_ISSUE(st + 2);
+      if (kk == 0 && st + kSt - 1 < nsteps) MOE_ISSUE(st + kSt - 1);
       if (kk < 3) {
         // next substep's weights while the MFMAs above run (the compiler's own order: an
         // explicit MFMA / VALU / LDS interleave measured about 1 % slower)
@@ -265,7 +278,7 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
       } else if (st + 1 < nsteps) {
         // the next step's codes and its first substep's weights, before its barrier, once
         // this wave's loads of step st+1 have landed (only step st+2's are younger)
-        if (st + 2 < nsteps) {
+        if (kSt > 2 && st + 2 < nsteps) {
           if (!kX && ((st + 2) & 3) == 0)
             wait_vmcnt<MB + 3>();
           else
@@ -369,26 +382,31 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
     }
   } else {
     // rows x 256 columns fp16 in slot order: a routed slot pre-weighted by its routing
-    // weight, a shared-expert slot (weight 1) as it is
+    // weight, a shared-expert slot (weight 1) as it is; staged through LDS 128 rows at a time
     constexpr int OP = BNW + 8;
     _Float16 *ot = reinterpret_cast<_Float16 *>(smem);
     float *sw = reinterpret_cast<float *>(smem + BM * OP * 2);
-    if (tid < BM) sw[tid] = tid < nvalid ? (e < a.E ? a.slot_w[slot0 + tid] : 1.0f) : 0.f;
-    __syncthreads();
+    static_assert(BM * OP * 2 + kMaxMB * 32 * 4 <= kSmemBytes, "epilogue staging");
+    if (tid < 32 * MB) sw[tid] = tid < nvalid ? (e < a.E ? a.slot_w[slot0 + tid] : 1.0f) : 0.f;
 #pragma unroll
-    for (int m = 0; m < MB; ++m)
+    for (int m0 = 0; m0 < MB; m0 += 4) {
+      __syncthreads();  // sw is written; the previous round's rows have left
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 32 * m + (r >> 2) * 8 + rq4 + (r & 3);
-        const float wv = sw[row];
-        ot[row * OP + 64 * wave + col] = (_Float16)(wv * acc[m][0][r]);
-        ot[row * OP + 64 * wave + 32 + col] = (_Float16)(wv * acc[m][1][r]);
-      }
-    __syncthreads();
-    for (int rr = tid >> 5; rr < nvalid; rr += 8)
-      *reinterpret_cast<uint4 *>(a.out + (size_t)(slot0 + rr) * a.H + n_tile * BNW +
-                                 8 * (tid & 31)) =
-          *reinterpret_cast<const uint4 *>(ot + rr * OP + 8 * (tid & 31));
+      for (int m = m0; m < (MB < m0 + 4 ? MB : m0 + 4); ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * m + (r >> 2) * 8 + rq4 + (r & 3);
+          const float wv = sw[row];
+          ot[(row - 32 * m0) * OP + 64 * wave + col] = (_Float16)(wv * acc[m][0][r]);
+          ot[(row - 32 * m0) * OP + 64 * wave + 32 + col] = (_Float16)(wv * acc[m][1][r]);
+        }
+      __syncthreads();
+      const int r1 = min(nvalid, 32 * (m0 + 4));
+      for (int rr = 32 * m0 + (tid >> 5); rr < r1; rr += 8)
+        *reinterpret_cast<uint4 *>(a.out + (size_t)(slot0 + rr) * a.H + n_tile * BNW +
+                                   8 * (tid & 31)) =
+            *reinterpret_cast<const uint4 *>(ot + (rr - 32 * m0) * OP + 8 * (tid & 31));
+    }
   }
 }
 
@@ -410,7 +428,8 @@ MOE_DEV void grouped_body(const GroupedArgs &a, uint8_t *smem) {
     case 1: grouped_tile<kGateUp, 1, kX>(a, smem, e, row0, nvalid, n_tile); break;
     case 2: grouped_tile<kGateUp, 2, kX>(a, smem, e, row0, nvalid, n_tile); break;
     case 3: grouped_tile<kGateUp, 3, kX>(a, smem, e, row0, nvalid, n_tile); break;
-    default: grouped_tile<kGateUp, 4, kX>(a, smem, e, row0, nvalid, n_tile); break;
+    case 4: grouped_tile<kGateUp, 4, kX>(a, smem, e, row0, nvalid, n_tile); break;
+    default: grouped_tile<kGateUp, 5, kX>(a, smem, e, row0, nvalid, n_tile); break;
   }
 }
 

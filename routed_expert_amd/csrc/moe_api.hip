@@ -636,26 +636,37 @@ int host_tables(const std::vector<int32_t> &ids, int64_t T, int E, int k, int S,
   }
   off[E] = (int32_t)acc;
   off[E + 1] = (int32_t)(acc + (S ? T : 0));
-  if (tile_shift <= 0) {
+  const bool chosen = tile_shift <= 0;
+  if (chosen) {
     int64_t nblk = S ? (T + 31) / 32 : 0;
     for (int e = 0; e < E; ++e) nblk += (run[e] + 31) / 32;
     const int fill = moe::gemm_fill(I);
     tile_shift = nblk >= 4 * fill ? 7 : nblk >= 2 * fill ? 6 : 5;
   }
   const int64_t tr = int64_t(1) << tile_shift;
+  // a group's remainder rows: those left to a partial tile (0 when they joined the last
+  // full tile, which 128-row tiles chosen from the load do for 1..32 rows)
+  const bool merge = chosen && tile_shift == 7;
+  auto rem_of = [&](int64_t rows) {
+    const int64_t r = rows % tr;
+    return merge && rows >= tr && r <= 32 ? 0 : r;
+  };
   int2 *tiles = reinterpret_cast<int2 *>(tab.data() + ap.tab_tiles);
   auto tile = [](int g, int64_t rows, int64_t r0) { return make_int2(g | (int)rows << 16, (int)r0); };
-  int n = 0;
-  for (int e = 0; e < E; ++e)
-    for (int64_t r = 0; r + tr <= run[e]; r += tr) tiles[n++] = tile(e, tr, r);
-  if (S)
-    for (int64_t r = 0; r + tr <= T; r += tr) tiles[n++] = tile(E, tr, r);
+  int n_out = 0;
+  auto full_tiles = [&](int g, int64_t rows) {
+    const int64_t nf = rows / tr, extra = rows % tr - rem_of(rows);
+    for (int64_t i = 0; i < nf; ++i) tiles[n_out++] = tile(g, i + 1 < nf ? tr : tr + extra, i * tr);
+  };
+  for (int e = 0; e < E; ++e) full_tiles(e, run[e]);
+  if (S) full_tiles(E, T);
   for (int mb = 4; mb >= 1; --mb)
     for (int e = 0; e < E; ++e) {
-      const int64_t rem = run[e] % tr;
-      if (rem && (rem + 31) / 32 == mb) tiles[n++] = tile(e, rem, run[e] - rem);
+      const int64_t rem = rem_of(run[e]);
+      if (rem && (rem + 31) / 32 == mb) tiles[n_out++] = tile(e, rem, run[e] - rem);
     }
-  if (S && T % tr) tiles[n++] = tile(E, T % tr, T - T % tr);
+  if (S && rem_of(T)) tiles[n_out++] = tile(E, rem_of(T), T - rem_of(T));
+  const int n = n_out;
   tab[ap.tab_ntiles] = n;
   return n;
 }

@@ -360,12 +360,21 @@ MOE_DEV int group_tables(int run, bool write, int E, int T, int S, int32_t *__re
   // long tiles go first and the short ones fill the end): every full tile of 2^tsh rows
   // (routed experts in order, then the shared expert), then the partial tiles by their
   // number of 32-row blocks, 4 down to 1: each expert's last tile is only as high as its
-  // remaining rows need. One 64-bit scan places them all: bits [0, 22) count full tiles,
+  // remaining rows need. With 128-row tiles chosen from the load, a remainder of at most
+  // 32 rows joins the group's last full tile instead (one tile of 129..160 rows, five
+  // blocks, rather than a one-block tile that would pay the whole weight tile's loads for a
+  // quarter of the work). One 64-bit scan places them all: bits [0, 22) count full tiles,
   // 9-bit fields at 22 + 9q count partial tiles of 4 - q blocks. A tile entry is
   // (group | rows << 16, first row).
   const int trows = 1 << tsh;
-  const int rem = run & (trows - 1);
-  const int nfull = run >> tsh, mb = (rem + 31) >> 5;
+  const bool merge = tsh_fixed <= 0 && tsh == 7;
+  const int nfull = run >> tsh;
+  int rem = run & (trows - 1), last = trows;
+  if (merge && nfull > 0 && rem > 0 && rem <= 32) {
+    last = trows + rem;
+    rem = 0;
+  }
+  const int mb = (rem + 31) >> 5;
   const uint64_t packed = (uint64_t)nfull | (mb ? (1ull << (22 + 9 * (4 - mb))) : 0ull);
   const uint64_t pincl = block_scan_incl(packed, sc64);
   if (!write) return off;
@@ -375,7 +384,12 @@ MOE_DEV int group_tables(int run, bool write, int E, int T, int S, int32_t *__re
   __syncthreads();
   const uint64_t tot = ptot[0];
   const int nfull_tot = (int)(tot & 0x3FFFFF);
-  const int sh_full = S ? T >> tsh : 0, sh_rem = S ? (T & (trows - 1)) : 0;
+  const int sh_full = S ? T >> tsh : 0;
+  int sh_rem = S ? (T & (trows - 1)) : 0, sh_last = trows;
+  if (merge && sh_full > 0 && sh_rem > 0 && sh_rem <= 32) {
+    sh_last = trows + sh_rem;
+    sh_rem = 0;
+  }
   int bstart[4];
   bstart[0] = nfull_tot + sh_full;
 #pragma unroll
@@ -386,14 +400,16 @@ MOE_DEV int group_tables(int run, bool write, int E, int T, int S, int32_t *__re
     if (counts_user) counts_user[e] = run;
     if (offsets_user) offsets_user[e] = off;
     const int f0 = (int)(pexcl & 0x3FFFFF);
-    for (int i = 0; i < nfull; ++i) tiles[f0 + i] = make_int2(e | trows << 16, i * trows);
+    for (int i = 0; i < nfull; ++i)
+      tiles[f0 + i] = make_int2(e | (i + 1 < nfull ? trows : last) << 16, i * trows);
     if (mb) {
       const int q = 4 - mb;
       tiles[bstart[q] + (int)((pexcl >> (22 + 9 * q)) & 0x1FF)] =
           make_int2(e | rem << 16, nfull * trows);
     }
   }
-  for (int i = e; i < sh_full; i += 256) tiles[nfull_tot + i] = make_int2(E | trows << 16, i * trows);
+  for (int i = e; i < sh_full; i += 256)
+    tiles[nfull_tot + i] = make_int2(E | (i + 1 < sh_full ? trows : sh_last) << 16, i * trows);
   if (e == 0) {
     if (sh_rem) tiles[npart] = make_int2(E | sh_rem << 16, sh_full * trows);
     offsets[E] = nassign;
