@@ -33,7 +33,9 @@
 // every 8-element chunk, so the A operand is a plain 16-byte LDS read.
 // Pipeline: activation rows, codes, scales and biases travel global -> LDS directly
 // (global_load_lds, no registers) into a 3-stage ring, issued two K steps ahead of use;
-// each wave reads back its own codes and dequantises them one MFMA substep ahead.
+// each wave reads back its own codes and dequantises them one MFMA substep ahead, between
+// the MFMAs of the substep before (the matrix unit runs an MFMA while the wave issues
+// independent vector instructions, so about six of them per MFMA cost no time).
 // Scale and bias arrays must be 4-byte aligned and K must be a multiple of 128.
 #include "common.h"
 #include "kernels.h"
@@ -45,15 +47,12 @@ constexpr int BM = kTileM, BNW = 256, BK = 64;
 constexpr int kStages = 3;                         // LDS ring depth (loads run 2 steps ahead)
 constexpr int kABytes = BM * BK * 2;               // activation rows of one step: 16 KB
 constexpr int kBBytes = 4 * 2 * 1024;              // codes: 4 waves x 2 columns x 64 lanes x 16 B
-constexpr int kStageBytes = kABytes + kBBytes;
-// Scales and biases arrive four K steps at a time (one tiled 1 KB block per wave: 64 rows x
-// 4 groups x {scale, bias}) into a 2-slot ring.
-constexpr int kSSlot = 4 * 1024;
-constexpr int kSmemBytes = kStages * kStageBytes + 2 * kSSlot;  // 80 KB: two workgroups per CU
+// Scales and biases of one step (one K group): 4 waves x 64 weight rows x {scale, bias}.
+constexpr int kSBBytes = 4 * 256;
+constexpr int kSmemBytes = 80 * 1024;              // two workgroups per CU
 // A tile of five 32-row blocks (an expert's last full tile with its short remainder, see
 // group_tables) has 20 KB of activation rows per step; three such stages would not fit two
-// workgroups per CU, so it runs a two-stage ring (loads one K step ahead instead of two):
-// 2 x (20 + 8) KB + 8 KB of scales = 64 KB.
+// workgroups per CU, so it runs a two-stage ring (loads one K step ahead instead of two).
 constexpr int kMaxMB = 5;
 template <int MB> constexpr int ring_stages() { return MB > 4 ? 2 : kStages; }
 template <int MB> constexpr int a_stage_bytes() { return (MB > 4 ? MB : 4) * 32 * BK * 2; }
@@ -61,8 +60,7 @@ template <int MB> constexpr int a_stage_bytes() { return (MB > 4 ? MB : 4) * 32 
 // of a step is 8 KB of fp16 instead of 2 KB of codes, so a stage is 48 KB and the 144 KB
 // ring leaves room for one workgroup per CU.
 constexpr int kXBBytes = 4 * 8 * 1024;
-constexpr int kXStageBytes = kABytes + kXBBytes;
-constexpr int kXSmemBytes = kStages * kXStageBytes;
+constexpr int kXSmemBytes = kStages * (kABytes + kXBBytes);
 }  // namespace
 
 MOE_DEV f16x2_t f16_pair_from_bf16(uint16_t v) {
@@ -89,10 +87,10 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
                           int n_tile) {
   constexpr int kSt = ring_stages<MB>();                 // ring depth
   constexpr int kAB = a_stage_bytes<MB>();               // activation rows of one stage
-  constexpr int kSB = kAB + (kX ? kXBBytes : kBBytes);   // bytes of one ring stage
-  constexpr int kLB = kX ? 8 : 2;  // B loads per wave and step (besides the scale blocks)
-  static_assert(kX ? kSt * kSB <= kXSmemBytes : kSt * kSB + 2 * kSSlot <= kSmemBytes,
-                "ring does not fit the kernel's LDS");
+  constexpr int kBB = kX ? kXBBytes : kBBytes;          // weight operands of one stage
+  constexpr int kSB = kAB + kBB + (kX ? 0 : kSBBytes);   // bytes of one ring stage
+  constexpr int kLB = kX ? 8 : 3;  // B loads per wave and step (codes 2 + scales 1)
+  static_assert(kSt * kSB <= (kX ? kXSmemBytes : kSmemBytes), "ring does not fit the LDS");
   const int gbase = a.offsets[e];
   const int slot0 = gbase + row0;
   const int K = kGateUp ? a.H : a.I;
@@ -123,14 +121,15 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
   // This wave's weight rows are one 64-row block of the tiled layout: gate rows 32w..+32
   // of the N tile and the matching up rows (gate/up), or output rows 64w..+64 (down). Per
   // K step the block's codes are 2 KB contiguous (column block c = rows 32c..32c+31 at
-  // c * 1 KB); its scales and biases come as 1 KB per four steps.
+  // c * 1 KB); its scales and biases are tiled 1 KB per four steps, lane l = 32c + row
+  // holding 4 steps x {scale, bias} in 16 bytes, of which each step loads its 4 bytes.
   const int nb = kGateUp ? 2 * a.I / 64 : a.H / 64;
   const int blk = n_tile * 4 + wave;
   const int ns = K / BK, ns4 = (ns + 3) / 4;
   const uint8_t *tq = (kGateUp ? a.wt.w13_t : a.wt.w2_t) +
                       ((size_t)e * nb + blk) * ns * 2048 + 16 * lane;
-  const uint16_t *tsb = (kGateUp ? a.wt.w13_tsb : a.wt.w2_tsb) +
-                        ((size_t)e * nb + blk) * ns4 * 512 + 8 * lane;
+  const uint8_t *tsb = reinterpret_cast<const uint8_t *>(
+      (kGateUp ? a.wt.w13_tsb : a.wt.w2_tsb) + ((size_t)e * nb + blk) * ns4 * 512 + 8 * lane);
   // expanded weights: the same block's 8 KB of fp16 per K step, 1 KB per (column block,
   // substep), lane l's 8 values at 16 l
   const uint8_t *txq = kX ? reinterpret_cast<const uint8_t *>(kGateUp ? a.w13_x : a.w2_x) +
@@ -140,11 +139,13 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
   // The direct-to-LDS loads and the step barrier are issued as inline assembly: the
   // compiler cannot tell the ring stages apart and would wait for every load in flight
   // (vmcnt(0)) before each LDS read and at each barrier, which serialises the pipeline.
-  // Completion is tracked explicitly instead: during step st each wave waits until only
-  // the loads of step st+2 are outstanding (MB + 2, plus the scale/bias block when st+2 is
-  // a multiple of 4), so its own loads of step st+1 have landed; the barrier at the top of
-  // step st+1 then covers every wave's. Compiler-generated vmcnt waits stay correct (outstanding
-  // loads only add).
+  // Completion is tracked explicitly instead: every step issues the same MB + kLB loads per
+  // wave (past the last step, a harmless reload of the last step's sources into the free
+  // stage), so during step st each wave waits until only the loads of step st+2 are
+  // outstanding and its own loads of step st+1 have landed; the barrier at the top of step
+  // st+1 then covers every wave's. Compiler-generated vmcnt waits stay correct (outstanding
+  // loads only add). The step body has no branches: one scheduling region from the DMA
+  // issue to the mid-step wait, in which the dequantisation interleaves with the MFMAs.
   // M0 holds the wave-uniform LDS byte address; lane l's data lands at M0 + l * size.
   // The s_nop covers the wait states a load that reads M0 needs after M0 is written.
   const uint32_t smem_lds = (uint32_t)(uintptr_t)smem;
@@ -152,12 +153,15 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
 #define MOE_DMA16(gptr, lds)                                                            \
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %0, off"         \
                :: "v"(gptr), "s"(lds) : "memory", "m0")
-  // issue the direct-to-LDS loads of K step `step` (MB + 2 memory instructions per wave,
-  // one more on every fourth step, which fetches the scales and biases of four steps;
+#define MOE_DMA4(gptr, lds)                                                             \
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 1\n\tglobal_load_lds_dword %0, off"           \
+               :: "v"(gptr), "s"(lds) : "memory", "m0")
+  // issue the direct-to-LDS loads of K step `step` into ring stage `slot` (MB + 3 memory
+  // instructions per wave: activation rows, two code blocks, the step's scales and biases;
   // expanded weights: MB + 8)
-#define MOE_ISSUE(step)                                                                 \
+#define MOE_ISSUE(step, slot)                                                           \
   do {                                                                                  \
-    const uint32_t base_ = smem_lds + ((step) % kSt) * kSB;                             \
+    const uint32_t base_ = smem_lds + (slot) * kSB;                                     \
     const int k0_ = (step) * BK;                                                        \
     _Pragma("unroll") for (int j = 0; j < MB; ++j)                                      \
       MOE_DMA16(asrc[j] + k0_, base_ + (wave_u + 4 * j) * 1024);                        \
@@ -169,11 +173,8 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
       const uint32_t bb_ = base_ + kAB + wave_u * 2048;                                 \
       MOE_DMA16(tq + (size_t)(step) * 2048, bb_);                                       \
       MOE_DMA16(tq + (size_t)(step) * 2048 + 1024, bb_ + 1024);                         \
-      if (((step) & 3) == 0) {                                                          \
-        const uint32_t sb_ = smem_lds + kSt * kSB + (((step) >> 2) & 1) * kSSlot +      \
-                             wave_u * 1024;                                             \
-        MOE_DMA16(tsb + (size_t)((step) >> 2) * 512, sb_);                              \
-      }                                                                                 \
+      MOE_DMA4(tsb + (size_t)((step) >> 2) * 1024 + 4 * ((step) & 3),                   \
+               base_ + kAB + kBB + wave_u * 256);                                       \
     }                                                                                   \
   } while (0)
 
@@ -193,22 +194,20 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
   f16x2_t s0, b0, s1, b1, s0q, s1q;
   uint4 bx[8];  // expanded weights: the step's B operands, [column block][substep]
   const int bn = lane & 31, bh = lane >> 5;
-#define MOE_READ_BX(step)                                                               \
+#define MOE_READ_BX(slot)                                                               \
   do {                                                                                  \
-    const uint8_t *bsrc_ = smem + ((step) % kSt) * kSB + kAB + wave * 8192 + 16 * lane; \
+    const uint8_t *bsrc_ = smem + (slot) * kSB + kAB + wave * 8192 + 16 * lane;         \
     _Pragma("unroll") for (int q = 0; q < 8; ++q)                                       \
       bx[q] = *reinterpret_cast<const uint4 *>(bsrc_ + q * 1024);                       \
   } while (0)
-#define MOE_READ_B(step)                                                                \
+#define MOE_READ_B(slot)                                                                \
   do {                                                                                  \
-    const uint8_t *bsrc_ = smem + ((step) % kSt) * kSB + kAB + wave * 2048 +            \
-                           32 * bn + 16 * bh;                                           \
+    const uint8_t *bsrc_ = smem + (slot) * kSB + kAB + wave * 2048 + 32 * bn + 16 * bh; \
     const uint4 q0_ = *reinterpret_cast<const uint4 *>(bsrc_);                          \
     const uint4 q1_ = *reinterpret_cast<const uint4 *>(bsrc_ + 1024);                   \
     const uint32_t *sv_ = reinterpret_cast<const uint32_t *>(                           \
-        smem + kSt * kSB + (((step) >> 2) & 1) * kSSlot + wave * 1024 + 16 * bn +        \
-        4 * ((step) & 3));                                                              \
-    const uint32_t sb0_ = sv_[0], sb1_ = sv_[128];                                      \
+        smem + (slot) * kSB + kAB + kBB + wave * 256 + 4 * bn);                         \
+    const uint32_t sb0_ = sv_[0], sb1_ = sv_[32];                                       \
     s0 = f16_pair_from_bf16((uint16_t)sb0_);                                            \
     b0 = f16_pair_from_bf16((uint16_t)(sb0_ >> 16));                                    \
     s1 = f16_pair_from_bf16((uint16_t)sb1_);                                            \
@@ -221,14 +220,13 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
 
   // every lane's source pointers are computed (their loads done) before the first DMA
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  MOE_ISSUE(0);
-  if (kSt > 2 && nsteps > 1) MOE_ISSUE(1);
-  // step 0's own loads: everything after them is step 1's (MB + kLB loads, step 1 is odd;
-  // none with the two-stage ring)
-  if (kSt > 2 && nsteps > 1)
-    wait_vmcnt<MB + kLB>();
-  else
+  MOE_ISSUE(0, 0);
+  if constexpr (kSt > 2) {
+    MOE_ISSUE(min(1, nsteps - 1), 1);
+    wait_vmcnt<MB + kLB>();  // step 0's own loads: only stage 1's are younger
+  } else {
     wait_vmcnt<0>();
+  }
   // B operands of substep kk of the step whose codes (or expanded weights) are loaded
 #define MOE_B_OPS(kk)                                                                   \
   do {                                                                                  \
@@ -246,17 +244,21 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
   else
     MOE_READ_B(0);
   MOE_B_OPS(0);
+  int slot = 0;  // ring stage of step st
   for (int st = 0; st < nsteps; ++st) {
     // every wave's loads of step st have landed (each wave waited for its own before its
     // mid-step read of step st's codes), and every wave is done with the stage that step
     // st + kSt - 1 will reuse
     asm volatile("s_barrier" ::: "memory");
-    const uint8_t *arow = smem + (st % kSt) * kSB + arow_l * 128;
+    const int nslot = slot + 1 == kSt ? 0 : slot + 1;          // stage of step st + 1
+    const int fslot = slot == 0 ? kSt - 1 : slot - 1;          // stage of step st + kSt - 1
+    const uint8_t *arow = smem + slot * kSB + arow_l * 128;
     // A fragments are double-buffered: substep kk+1's are read while kk's MFMAs run
     f16x8_t av[2][MB];
 #pragma unroll
     for (int m = 0; m < MB; ++m)
       av[0][m] = *reinterpret_cast<const f16x8_t *>(arow + m * 4096 + ((4 * ahalf) ^ asw) * 16);
+    MOE_ISSUE(min(st + kSt - 1, nsteps - 1), fslot);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       if (kk < 3) {
@@ -270,34 +272,37 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
         acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[kk & 1][m], bc0, acc[m][0], 0, 0, 0);
         acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[kk & 1][m], bc1, acc[m][1], 0, 0, 0);
       }
-      if (kk == 0 && st + kSt - 1 < nsteps) MOE_ISSUE(st + kSt - 1);
-      if (kk < 3) {
-        // next substep's weights while the MFMAs above run (the compiler's own order: an
-        // explicit MFMA / VALU / LDS interleave measured about 1 % slower)
-        MOE_B_OPS(kk + 1);
-      } else if (st + 1 < nsteps) {
-        // the next step's codes and its first substep's weights, before its barrier, once
-        // this wave's loads of step st+1 have landed (only step st+2's are younger)
-        if (kSt > 2 && st + 2 < nsteps) {
-          if (!kX && ((st + 2) & 3) == 0)
-            wait_vmcnt<MB + 3>();
-          else
-            wait_vmcnt<MB + kLB>();
-        } else {
-          wait_vmcnt<0>();
-        }
+      // the next substep's weights while these MFMAs run
+      if (kk < 3) MOE_B_OPS(kk + 1);
+      if (kk == 2) {
+        // the next step's codes, scales and biases (past the last step: the reloaded
+        // stage, unused), once this wave's loads of step st+1 have landed, so that their
+        // dequantisation overlaps the last substep's MFMAs
+        wait_vmcnt<(kSt > 2 ? MB + kLB : 0)>();
         if constexpr (kX)
-          MOE_READ_BX(st + 1);
+          MOE_READ_BX(nslot);
         else
-          MOE_READ_B(st + 1);
-        MOE_B_OPS(0);
+          MOE_READ_B(nslot);
+      }
+      if (kk == 3) MOE_B_OPS(0);
+      // A wave issues in order, and the matrix unit runs one MFMA while the same wave issues
+      // independent vector instructions: spread the dequantisation and the LDS reads between
+      // the MFMAs (a few VALU per MFMA) instead of leaving them in a block after the last one.
+#pragma unroll
+      for (int i = 0; i < 2 * MB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // up to 4 VALU
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // up to 1 LDS read
       }
     }
+    slot = nslot;
   }
+  wait_vmcnt<0>();  // the reloads past the last step land before the stages are reused
 #undef MOE_B_OPS
 #undef MOE_READ_BX
 #undef MOE_READ_B
 #undef MOE_ISSUE
+#undef MOE_DMA4
 #undef MOE_DMA16
 
   // 32x32 accumulator layout: lane l holds column l%32, register r holds row
