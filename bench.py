@@ -17,10 +17,11 @@ Also reported in the same line:
     the same loads from the same grid with the arithmetic taken out (the page's "fastest
     sustained rate for the access pattern");
   - the cost of one kernel inside a HIP graph, and a dense MFMA loop (the matrix-core rate
-    the GPU sustains);
+    the GPU sustains, on full-mantissa operands like the GEMMs' and on low-entropy ones: the
+    part clocks down at its power limit in proportion to the bits the matrix cores switch);
   - prefill of T=4096 tokens with near-uniform routing and with Zipf(1.1)-skewed routing
     (median per call; tokens/s, fraction of the dense bf16 MFMA peak and of the measured
-    MFMA ceiling);
+    full-mantissa MFMA ceiling);
   - a stack of 40 such layers (pre-norm residual blocks): batch-1 decode of 256 tokens and a
     32,768-token prompt in chunks of 4096 tokens;
   - moe_prefill with 2, 4 and 8 tokens (the small-T kernels) over the 20 layer copies, and
@@ -272,25 +273,33 @@ def bench_read_ceilings(moe, torch, layers, xs, n):
 
 
 def bench_mfma_ceiling(moe, torch, dev, iters=1500, reps=20):
-    """Dense v_mfma_f32_32x32x16_f16 loop (no memory traffic), 512 workgroups of 4 waves:
-    the matrix-core rate this GPU sustains, median of `reps` timed launches after a warm-up."""
+    """Dense v_mfma_f32_32x32x16_f16 loop (no memory traffic), 512 workgroups of 4 waves: the
+    matrix-core rate this GPU sustains, median of `reps` back-to-back timed launches after a
+    warm-up, once on full-mantissa operands (like the GEMMs' data) and once on low-entropy
+    ones. The part clocks down at its power limit in proportion to the bits the matrix cores
+    switch, so only the second comes near the nominal peak."""
     import numpy as np
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
-    flops = moe.mfma_ceiling(iters, sink)
-    warm_up(lambda: moe.mfma_ceiling(iters, sink))
-    ms = []
-    for _ in range(reps):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        moe.mfma_ceiling(iters, sink)
-        b.record()
-        torch.cuda.synchronize()
-        ms.append(a.elapsed_time(b))
-    med = float(np.median(ms))
-    return {"tflops": round(flops / (med * 1e-3) / 1e12, 1), "flop_per_launch": flops,
-            "ms_median": round(med, 4), "frac_of_spec": round(flops / (med * 1e-3) / 1e12 /
-                                                             BF16_PEAK_TFLOPS, 3)}
+    res = {}
+    for name, kind in (("full_mantissa", moe.CEIL_FULL_MANTISSA),
+                       ("low_entropy", moe.CEIL_LOW_ENTROPY)):
+        flops = moe.mfma_ceiling(iters, sink, kind)
+        warm_up(lambda: moe.mfma_ceiling(iters, sink, kind))
+        ms = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            moe.mfma_ceiling(iters, sink, kind)
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        med = float(np.median(ms))
+        tf = flops / (med * 1e-3) / 1e12
+        res[name] = {"tflops": round(tf, 1), "flop_per_launch": flops, "ms_median": round(med, 4),
+                     "frac_of_spec": round(tf / BF16_PEAK_TFLOPS, 3)}
+    res["tflops"] = res["full_mantissa"]["tflops"]
+    return res
 
 
 def bench_launch_floor(torch, dev, n=30, reps=20):

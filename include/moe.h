@@ -309,10 +309,16 @@ moe_status moe_rmsnorm(const void *h, int64_t T, int32_t hidden, float eps, int3
  *
  * moe_mfma_ceiling: a dense loop of v_mfma_f32_32x32x16_f16 on register operands over 512
  * workgroups of four waves (two per CU, like the grouped GEMMs), iters x 8 per wave; *flops
- * (host) receives the FLOP it executes. sink as above. */
+ * (host) receives the FLOP it executes. sink as above. The sustained rate depends on the
+ * operands (the matrix cores draw power in proportion to the bits they switch, and the part
+ * clocks down at its power limit): operands MOE_CEIL_FULL_MANTISSA runs on values with full
+ * fp16 mantissas in (-1, 1), like a GEMM's activations and dequantised weights;
+ * MOE_CEIL_LOW_ENTROPY on multiples of 1/2 below 4. Other values: MOE_E_INVALID. */
+enum { MOE_CEIL_FULL_MANTISSA = 0, MOE_CEIL_LOW_ENTROPY = 1 };
 moe_status moe_decode_read_ceiling(const moe_layer *layer, const int32_t *ids, int32_t part,
                                    uint32_t *sink, void *stream);
-moe_status moe_mfma_ceiling(int32_t iters, uint32_t *sink, double *flops, void *stream);
+moe_status moe_mfma_ceiling(int32_t iters, int32_t operands, uint32_t *sink, double *flops,
+                            void *stream);
 
 /* Kernel timing for measurement tools. When enabled, every kernel the library launches
  * is dispatched with a start/stop HIP event pair bound to the dispatch itself

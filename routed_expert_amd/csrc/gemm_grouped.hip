@@ -94,7 +94,6 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
   const int gbase = a.offsets[e];
   const int slot0 = gbase + row0;
   const int K = kGateUp ? a.H : a.I;
-  const int Nw = kGateUp ? 2 * a.I : a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   // Activation rows of one step land in LDS swizzled: 16-byte chunk c of row r sits at

@@ -183,7 +183,7 @@ hipError_t launch_small_t(const DecodeArgs &a, hipStream_t s);
 // kMfmaCeilingWG workgroups x 4 waves x iters x 8 v_mfma_f32_32x32x16_f16.
 hipError_t launch_read_ceiling(const DecodeArgs &a, int part, uint32_t *sink, hipStream_t s);
 constexpr int kMfmaCeilingWG = 512;
-hipError_t launch_mfma_ceiling(int iters, uint32_t *sink, hipStream_t s);
+hipError_t launch_mfma_ceiling(int iters, int low_entropy, uint32_t *sink, hipStream_t s);
 
 hipError_t launch_rmsnorm(const void *h, int64_t T, int H, float eps, bool bf16, void *out,
                           hipStream_t s);

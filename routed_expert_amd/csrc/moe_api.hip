@@ -1135,11 +1135,15 @@ moe_status moe_decode_read_ceiling(const moe_layer *layer, const int32_t *ids, i
   return MOE_OK;
 }
 
-moe_status moe_mfma_ceiling(int32_t iters, uint32_t *sink, double *flops, void *stream) {
+moe_status moe_mfma_ceiling(int32_t iters, int32_t operands, uint32_t *sink, double *flops,
+                            void *stream) {
   g_err.clear();
   if (iters < 1 || !sink || !flops) return fail(MOE_E_INVALID, "iters >= 1, sink and flops needed");
+  if (operands != MOE_CEIL_FULL_MANTISSA && operands != MOE_CEIL_LOW_ENTROPY)
+    return fail(MOE_E_INVALID, "unknown operand kind %d", operands);
   *flops = (double)moe::kMfmaCeilingWG * 4 * iters * 8 * 32768.0;
-  const hipError_t e = moe::launch_mfma_ceiling(iters, sink, static_cast<hipStream_t>(stream));
+  const hipError_t e = moe::launch_mfma_ceiling(iters, operands == MOE_CEIL_LOW_ENTROPY, sink,
+                                                static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "moe_mfma_ceiling");
   return MOE_OK;
 }

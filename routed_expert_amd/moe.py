@@ -119,7 +119,7 @@ def lib():
         "moe_gdn_scan_chunked": ([P, P, P, P, P, I64, I32, I32, I32, I32, P, P, P, SZ, P],
                                  ctypes.c_int),
         "moe_decode_read_ceiling": ([P, P, I32, P, P], ctypes.c_int),
-        "moe_mfma_ceiling": ([I32, P, ctypes.POINTER(ctypes.c_double), P], ctypes.c_int),
+        "moe_mfma_ceiling": ([I32, I32, P, ctypes.POINTER(ctypes.c_double), P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -405,11 +405,16 @@ def decode_read_ceiling(layer: DeviceLayer, ids: torch.Tensor, part: int, sink: 
                                          _stream(stream)))
 
 
-def mfma_ceiling(iters: int, sink: torch.Tensor, stream=None) -> float:
-    """Launches the dense MFMA loop; returns the FLOP it executes."""
+CEIL_FULL_MANTISSA, CEIL_LOW_ENTROPY = 0, 1
+
+
+def mfma_ceiling(iters: int, sink: torch.Tensor, operands: int = CEIL_FULL_MANTISSA,
+                 stream=None) -> float:
+    """Launches the dense MFMA loop on full-mantissa (0) or low-entropy (1) operands; returns
+    the FLOP it executes."""
     f = ctypes.c_double(0)
-    _check("moe_mfma_ceiling", lib().moe_mfma_ceiling(int(iters), _ptr(sink), ctypes.byref(f),
-                                                      _stream(stream)))
+    _check("moe_mfma_ceiling", lib().moe_mfma_ceiling(int(iters), int(operands), _ptr(sink),
+                                                      ctypes.byref(f), _stream(stream)))
     return f.value
 
 

@@ -326,5 +326,7 @@ def test_measurement_aids_argument_errors(M):
     odd = fake_layer(M, inter=256)            # not the batch-1 fast path
     assert lib.moe_decode_read_ceiling(ctypes.byref(odd), ids, 1, sink, None) == M.E_UNSUPPORTED
     f = ctypes.c_double(0)
-    assert lib.moe_mfma_ceiling(0, sink, ctypes.byref(f), None) == M.E_INVALID
-    assert lib.moe_mfma_ceiling(10, sink, None, None) == M.E_INVALID
+    assert lib.moe_mfma_ceiling(0, 0, sink, ctypes.byref(f), None) == M.E_INVALID
+    assert lib.moe_mfma_ceiling(10, 0, sink, None, None) == M.E_INVALID
+    assert lib.moe_mfma_ceiling(10, 2, sink, ctypes.byref(f), None) == M.E_INVALID
+    assert lib.moe_mfma_ceiling(10, -1, sink, ctypes.byref(f), None) == M.E_INVALID
