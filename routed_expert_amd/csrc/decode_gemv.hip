@@ -47,6 +47,18 @@ constexpr int kNB2 = DH / 64;       // 64-row blocks of W2
 constexpr int kNS2 = DI / 64;       // K steps of W2
 constexpr int kSharedWG = 2 * kNB13; // extra workgroups of B: shared-expert half blocks
 constexpr int kDownWG = kNB2 * 16;  // C: 4 output rows per workgroup
+static_assert(kNB2 % 8 == 0, "the down kernel spreads its 64-row blocks evenly over 8 XCDs");
+
+// Down-projection workgroup w owns output rows 64b + 4t .. +4. The 16 workgroups of one
+// 64-row block read 128-byte pieces of the same 2 KB code blocks and 64-byte pieces of the
+// same scale blocks; workgroup ids are dealt round-robin over the 8 XCDs, so the ids are
+// mapped to put all 16 on one XCD: every line is then fetched into one L2 once, instead of
+// into several L2s by halves.
+MOE_DEV void down_rows_of(int w, int &b, int &t) {
+  const int j = w >> 3;
+  b = (kNB2 / 8) * (w & 7) + (j >> 4);
+  t = j & 15;
+}
 }  // namespace
 
 // n fp32 / bf16 activations -> fp16 pairs (v[8c + p], v[8c + p + 4]) for chunk c, p < 4, in
@@ -366,7 +378,8 @@ __global__ __launch_bounds__(DT) void k_dec_c(DecodeArgs a) {
   const float my_z = sel_z[tq];
   // output rows 64b + 4t .. +4; the residual of row 64b + 4t + tid % 4 (used by threads
   // 0..3; y stands in when there is no residual, read before it is written)
-  const int b = w >> 4, t = w & 15;
+  int b, t;
+  down_rows_of(w, b, t);
   const int orow = 64 * b + 4 * t + (tid & 3);
   const uint16_t resid = (residual ? residual : yrow)[orow];
   const int nch = nslot * DI / 8;
@@ -731,7 +744,9 @@ __global__ __launch_bounds__(DT) void k_read_gateup(DecodeArgs a, uint32_t *sink
 
 __global__ __launch_bounds__(DT) void k_read_down(DecodeArgs a, uint32_t *sink) {
   const int w = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int nslot = a.k + a.S, b = w >> 4, t = w & 15, ug = lane >> 3;
+  const int nslot = a.k + a.S, ug = lane >> 3;
+  int b, t;
+  down_rows_of(w, b, t);
   uint32_t v = 0;
   constexpr int kMaxOcts = (kSlots * kNS2 / 8 + DT / 64 - 1) / (DT / 64);
 #pragma unroll
