@@ -4,10 +4,10 @@
 // "Optimizing On-Device Inference for Apple Silicon", section "Reduce intermediate
 // and state traffic": each expert's output projection is combined with its routing
 // score and with the shared-expert result. In the prefill path the down GEMM writes each
-// routed slot's output already scaled by its routing weight and the shared expert's
-// output after them (slots kT + t), all fp16; this kernel gathers a token's rows in a
-// fixed order (shared first, then ascending expert id) and sums them in fp32, so the
-// result is deterministic.
+// routed slot's output already scaled by its routing weight, in fp16. With a shared expert
+// the combine runs in the shared expert's down projection (k_shared_down_combine); this
+// kernel serves layers without one: it gathers a token's k rows in a fixed order
+// (ascending expert id) and sums them in fp32, so the result is deterministic.
 #include "common.h"
 #include "kernels.h"
 
@@ -25,15 +25,8 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
     const size_t o = (size_t)t * H + c;
     float acc[8];
-    if (a.S) {
-      const uint4 v =
-          *reinterpret_cast<const uint4 *>(a.out + ((size_t)k * a.T + t) * H + c);
-      acc[0] = f16lo(v.x); acc[1] = f16hi(v.x); acc[2] = f16lo(v.y); acc[3] = f16hi(v.y);
-      acc[4] = f16lo(v.z); acc[5] = f16hi(v.z); acc[6] = f16lo(v.w); acc[7] = f16hi(v.w);
-    } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    }
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
       if (j >= k) break;

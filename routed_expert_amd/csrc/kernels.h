@@ -122,14 +122,14 @@ size_t expanded_bytes(int n_mat, int rows, int K);
 hipError_t launch_expand(const GroupedArgs &a, hipStream_t s);
 
 // Weighted combine of the slot-ordered expert outputs back to token order.
+// (layers without a shared expert)
 struct CombineArgs {
-  const uint16_t *out;       // [(k+S) T, H] fp16: weighted routed outputs, then the shared
-                             // expert's rows in token order
+  const uint16_t *out;       // [k T, H] fp16: weighted routed outputs in slot order
   const int32_t *slot_of;    // [T, k]
   const uint16_t *residual;  // [T, H] or null
   uint16_t *y;               // [T, H]
   int64_t T;
-  int H, k, S;
+  int H, k;
 };
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 

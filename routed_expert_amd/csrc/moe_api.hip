@@ -149,7 +149,8 @@ Plan make_plan(const moe_layer *L, int64_t T, int tile_shift = 0) {
     p.slot_w = take(k * Tn * 4);
     p.x16 = take(Tn * H * 2);
     p.h = take((k + S) * Tn * I * 2);
-    p.out = take((k + S) * Tn * H * 2);
+    // the routed rows only: the shared expert's down projection adds them into y itself
+    p.out = take(k * Tn * H * 2);
   } else {
     p.h = take((k + S) * Tn * I * 4);
     p.slot_w = p.x16 = p.out = off;
@@ -472,7 +473,6 @@ static moe_status run_grouped(const moe_layer *layer, const moe::GroupedArgs &ga
   ca.T = ra.T;
   ca.H = layer->hidden;
   ca.k = layer->top_k;
-  ca.S = layer->n_shared;
   if ((e = moe::launch_combine(ca, s)) != hipSuccess) return hip_fail(e, "moe_prefill combine");
   return MOE_OK;
 }
