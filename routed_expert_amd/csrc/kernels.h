@@ -96,9 +96,8 @@ struct GroupedArgs {
   int H, I, E, k;
   ExpertWeights wt;
   uint16_t *h16;   // [(k+S) T, I] fp16, slot order
-  uint16_t *out;   // [(k+S) T, H] fp16, slot order: routed slots already scaled by the
-                   // routing weight, then the shared expert's slots (token order; not
-                   // written when the combine is fused)
+  uint16_t *out;   // [k T, H] fp16, slot order: routed slots already scaled by the
+                   // routing weight
   // Weighted combine fused into the shared expert's down projection (S == 1): the routed
   // down launch skips the shared expert's tiles and launch_shared_down_combine writes y.
   int fused_combine = 0;

@@ -175,12 +175,27 @@ def _prefill_big(M, layer, dl, seed, T=4096, n_sample=None):
     return g, unsure, rel_err(got, ref), y
 
 
+def tile_cases(c):
+    """Group sizes by the tile shapes they take at 128-row tiles: a remainder of 1..32 rows
+    joined to the last full tile (a 160-row tile), the same behind further full tiles, a
+    partial last tile above 32 rows, groups of one partial tile, exact multiples of 128."""
+    r = c % 128
+    merged = (c > 128) & (r > 0) & (r <= 32)
+    return {"merged": int(merged.sum()), "merged_multi": int((merged & (c > 256)).sum()),
+            "partial": int(((c > 128) & (r > 32)).sum()), "single": int(((c > 0) & (c < 128)).sum()),
+            "multiple": int(((c > 0) & (r == 0)).sum())}
+
+
 def test_prefill_uniform_4096(M, big):
     layer, dl = big
     announce("moe_prefill int4 T=4096 near-uniform routing, x seed 2")
     g, unsure, err, _ = _prefill_big(M, layer, dl, 2)
     c = g["counts"]
     assert c.sum() == 8 * 4096 and c.min() > 0
+    # the call exercises merged 160-row tiles, partial and single tiles, and full tiles alone
+    cases = tile_cases(c)
+    assert cases["merged"] >= 50 and cases["partial"] >= 1 and cases["single"] >= 50, cases
+    assert cases["multiple"] >= 1, cases
     assert unsure <= 20
     assert err <= BF16_TOL, err
 
@@ -191,6 +206,9 @@ def test_prefill_skewed_4096(M, skewed):
     g, unsure, err, _ = _prefill_big(M, layer, dl, 2)
     c = g["counts"]
     assert c.max() > 500 and (c <= 5).sum() >= 32   # very uneven groups, some empty-ish
+    # merged tiles behind several full tiles, partial last tiles of large groups
+    cases = tile_cases(c)
+    assert cases["merged_multi"] >= 3 and cases["partial"] >= 10, cases
     assert unsure <= 20
     assert err <= BF16_TOL, err
 
