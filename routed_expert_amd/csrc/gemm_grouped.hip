@@ -186,9 +186,9 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
   const int arow_l = lane & 31, ahalf = lane >> 5, asw = (arow_l >> 1) & 7;
 
   // This wave's codes, scales and biases of a step come from its own direct loads, so
-  // they are read into registers as soon as this wave's loads of that step have landed,
-  // half a step early and without a barrier; only the activation rows, which all four
-  // waves load together, wait for the step barrier.
+  // they are read into registers during the third substep of the step before, once this
+  // wave's loads of that step have landed, without a barrier; only the activation rows,
+  // which all four waves load together, wait for the step barrier.
   uint32_t w0[4], w1[4];
   f16x2_t s0, b0, s1, b1, s0q, s1q;
   uint4 bx[8];  // expanded weights: the step's B operands, [column block][substep]
