@@ -213,6 +213,17 @@ def test_prefill_skewed_4096(M, skewed):
     assert err <= BF16_TOL, err
 
 
+def test_prefill_shared_expert_merged_tail(M, big):
+    # T = 4100 = 32 x 128 + 4: the shared expert's last 4 rows join its last full tile (a
+    # 132-row tile); every row against the oracle
+    layer, dl = big
+    announce("moe_prefill int4 T=4100 (shared expert's 4-row remainder merged), x seed 12")
+    g, unsure, err, _ = _prefill_big(M, layer, dl, 12, T=4100)
+    assert g["counts"].sum() == 8 * 4100
+    assert unsure <= 20
+    assert err <= BF16_TOL, err
+
+
 def test_prefill_skewed_ragged_1000(M, skewed):
     # the router bias with a token count that is not a multiple of 64 (the last routing
     # block holds 40 tokens): every token's routing and output against the oracle
