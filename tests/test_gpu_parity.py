@@ -213,6 +213,21 @@ def test_prefill_skewed_4096(M, skewed):
     assert err <= BF16_TOL, err
 
 
+@pytest.mark.timeout(600)
+def test_prefill_uniform_8192(M, big):
+    # twice the workload's prompt: most experts fill two or more 128-row tiles, so merged
+    # remainders sit behind several full tiles; every row against the oracle
+    layer, dl = big
+    announce("moe_prefill int4 T=8192 near-uniform routing, x seed 13")
+    g, unsure, err, _ = _prefill_big(M, layer, dl, 13, T=8192)
+    c = g["counts"]
+    assert c.sum() == 8 * 8192
+    cases = tile_cases(c)
+    assert cases["merged_multi"] >= 20 and cases["partial"] >= 20, cases
+    assert unsure <= 40
+    assert err <= BF16_TOL, err
+
+
 def test_prefill_shared_expert_merged_tail(M, big):
     # T = 4100 = 32 x 128 + 4: the shared expert's last 4 rows join its last full tile (a
     # 132-row tile); every row against the oracle
