@@ -219,6 +219,15 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
 
   // every lane's source pointers are computed (their loads done) before the first DMA
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // fused combine: the routed slots of this tile's tokens (row r, rank j at r * k + j),
+  // requested now so that their latency hides behind the K loop
+  int32_t slot_pre[2] = {0, 0};
+  if constexpr (kComb) {
+    static_assert(MB <= 2, "the fused combine takes token tiles of at most 64 rows");
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      slot_pre[q] = a.slot_of[(size_t)row0 * a.k + min(tid + 256 * q, nvalid * a.k - 1)];
+  }
   MOE_ISSUE(0, 0);
   if constexpr (kSt > 2) {
     MOE_ISSUE(min(1, nsteps - 1), 1);
@@ -333,51 +342,64 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
           *reinterpret_cast<const uint4 *>(ht + rr * HP + 8 * (tid & 15));
   } else if (kComb) {
     // y[t] = shared(x_t) + sum_j out[slot_of[t, j]] (+ residual[t]) over this tile's 256
-    // columns, fp32 in that order, bf16 out. The shared result goes through LDS in fp32, one
-    // 32-row block at a time; then thread (row rr, 8 columns) gathers the routed rows with
-    // 16-byte loads (all k requested together) and writes 16 bytes of y.
+    // columns, fp32 in that order, bf16 out. The shared result of every row goes through LDS
+    // in fp32, the routed slots (requested before the K loop) beside it; then thread (row,
+    // 8 columns) gathers the routed rows with 16-byte loads, two rows at a time with all
+    // their loads in flight together (rows past the tile repeat its last row's loads and are
+    // not stored, so no load sits under a branch), and writes 16 bytes of y per row.
     constexpr int SP = BNW + 4;
     float *st = reinterpret_cast<float *>(smem);
+    int32_t *s_slot = reinterpret_cast<int32_t *>(smem + 32 * MB * SP * 4);
+    static_assert(64 * SP * 4 + 64 * kMaxTopK * 4 <= kSmemBytes, "combine staging");
     const int k = a.k;
     const int cc = 8 * (tid & 31), col0 = n_tile * BNW + cc;
 #pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      __syncthreads();  // the previous block's reads of st are done
+    for (int q = 0; q < 2; ++q)
+      if (tid + 256 * q < 64 * kMaxTopK) s_slot[tid + 256 * q] = slot_pre[q];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = (r >> 2) * 8 + rq4 + (r & 3);
+        const int row = 32 * m + (r >> 2) * 8 + rq4 + (r & 3);
         st[row * SP + 64 * wave + col] = acc[m][0][r];
         st[row * SP + 64 * wave + 32 + col] = acc[m][1][r];
       }
-      __syncthreads();
+    __syncthreads();
 #pragma unroll
-      for (int pass = 0; pass < 4; ++pass) {
-        const int rr = 8 * pass + (tid >> 5), r_tile = 32 * m + rr;
-        if (r_tile >= nvalid) continue;
-        const int64_t t = row0 + r_tile;
-        const float4 s0 = *reinterpret_cast<const float4 *>(st + rr * SP + cc);
-        const float4 s1 = *reinterpret_cast<const float4 *>(st + rr * SP + cc + 4);
-        float v[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-        uint4 o[kMaxTopK];
+    for (int p0 = 0; p0 < 4 * MB; p0 += 2) {
+      uint4 o[2][kMaxTopK], rv[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int rc = min(8 * (p0 + q) + (tid >> 5), nvalid - 1);
 #pragma unroll
         for (int j = 0; j < kMaxTopK; ++j) {
-          // unused ranks (j >= k) repeat the last one's load and are not added, so that every
-          // load is issued before the first is waited for
-          const int32_t slot = a.slot_of[t * k + min(j, k - 1)];
-          o[j] = *reinterpret_cast<const uint4 *>(a.out + (size_t)slot * a.H + col0);
+          // unused ranks (j >= k) repeat the last one's load and are not added
+          const int32_t slot = s_slot[rc * k + min(j, k - 1)];
+          o[q][j] = *reinterpret_cast<const uint4 *>(a.out + (size_t)slot * a.H + col0);
         }
-        uint4 rv = make_uint4(0, 0, 0, 0);
-        if (a.residual) rv = *reinterpret_cast<const uint4 *>(a.residual + (size_t)t * a.H + col0);
+        rv[q] = a.residual ? *reinterpret_cast<const uint4 *>(
+                                 a.residual + (size_t)(row0 + rc) * a.H + col0)
+                           : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int r_tile = 8 * (p0 + q) + (tid >> 5);
+        if (r_tile >= nvalid) continue;
+        const int64_t t = row0 + r_tile;
+        const float4 s0 = *reinterpret_cast<const float4 *>(st + r_tile * SP + cc);
+        const float4 s1 = *reinterpret_cast<const float4 *>(st + r_tile * SP + cc + 4);
+        float v[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
         for (int j = 0; j < kMaxTopK; ++j) {
           if (j >= k) break;
-          v[0] += f16lo(o[j].x); v[1] += f16hi(o[j].x); v[2] += f16lo(o[j].y);
-          v[3] += f16hi(o[j].y); v[4] += f16lo(o[j].z); v[5] += f16hi(o[j].z);
-          v[6] += f16lo(o[j].w); v[7] += f16hi(o[j].w);
+          v[0] += f16lo(o[q][j].x); v[1] += f16hi(o[q][j].x); v[2] += f16lo(o[q][j].y);
+          v[3] += f16hi(o[q][j].y); v[4] += f16lo(o[q][j].z); v[5] += f16hi(o[q][j].z);
+          v[6] += f16lo(o[q][j].w); v[7] += f16hi(o[q][j].w);
         }
         if (a.residual) {
-          v[0] += bf16lo(rv.x); v[1] += bf16hi(rv.x); v[2] += bf16lo(rv.y); v[3] += bf16hi(rv.y);
-          v[4] += bf16lo(rv.z); v[5] += bf16hi(rv.z); v[6] += bf16lo(rv.w); v[7] += bf16hi(rv.w);
+          const uint4 w4 = rv[q];
+          v[0] += bf16lo(w4.x); v[1] += bf16hi(w4.x); v[2] += bf16lo(w4.y); v[3] += bf16hi(w4.y);
+          v[4] += bf16lo(w4.z); v[5] += bf16hi(w4.z); v[6] += bf16lo(w4.w); v[7] += bf16hi(w4.w);
         }
         *reinterpret_cast<uint4 *>(a.y + (size_t)t * a.H + col0) =
             make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
