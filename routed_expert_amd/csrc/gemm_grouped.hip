@@ -344,7 +344,7 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
     // y[t] = shared(x_t) + sum_j out[slot_of[t, j]] (+ residual[t]) over this tile's 256
     // columns, fp32 in that order, bf16 out. The shared result of every row goes through LDS
     // in fp32, the routed slots (requested before the K loop) beside it; then thread (row,
-    // 8 columns) gathers the routed rows with 16-byte loads, two rows at a time with all
+    // 8 columns) gathers the routed rows with 16-byte loads, four rows at a time with all
     // their loads in flight together (rows past the tile repeat its last row's loads and are
     // not stored, so no load sits under a branch), and writes 16 bytes of y per row.
     constexpr int SP = BNW + 4;
@@ -353,6 +353,7 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
     static_assert(64 * SP * 4 + 64 * kMaxTopK * 4 <= kSmemBytes, "combine staging");
     const int k = a.k;
     const int cc = 8 * (tid & 31), col0 = n_tile * BNW + cc;
+    constexpr int kCombRows = 4;  // rows per thread gathered together
 #pragma unroll
     for (int q = 0; q < 2; ++q)
       if (tid + 256 * q < 64 * kMaxTopK) s_slot[tid + 256 * q] = slot_pre[q];
@@ -366,10 +367,10 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
       }
     __syncthreads();
 #pragma unroll
-    for (int p0 = 0; p0 < 4 * MB; p0 += 2) {
-      uint4 o[2][kMaxTopK], rv[2];
+    for (int p0 = 0; p0 < 4 * MB; p0 += kCombRows) {
+      uint4 o[kCombRows][kMaxTopK], rv[kCombRows];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+      for (int q = 0; q < kCombRows; ++q) {
         const int rc = min(8 * (p0 + q) + (tid >> 5), nvalid - 1);
 #pragma unroll
         for (int j = 0; j < kMaxTopK; ++j) {
@@ -382,7 +383,7 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
                            : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+      for (int q = 0; q < kCombRows; ++q) {
         const int r_tile = 8 * (p0 + q) + (tid >> 5);
         if (r_tile >= nvalid) continue;
         const int64_t t = row0 + r_tile;
