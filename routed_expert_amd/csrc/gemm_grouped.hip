@@ -16,16 +16,18 @@
 //     per lane per K step). Only the gathered activation rows (shared by the four waves)
 //     and the raw codes are staged in LDS.
 //
-// Tile: up to 128 slot rows x 256 weight rows, K in steps of 64 (one quantisation group).
-// Wave w computes all rows x weight rows {w's 64}: MB x 2 tiles of v_mfma_f32_32x32x16_f16
-// (up to 128 fp32 accumulators), MB = the tile's 32-row blocks that hold valid rows.
+// Tile: up to 128 slot rows (160 when a group's short remainder joins its last full tile)
+// x 256 weight rows, K in steps of 64 (one quantisation group). Wave w computes all rows x
+// weight rows {w's 64}: MB x 2 tiles of v_mfma_f32_32x32x16_f16 (up to 160 fp32
+// accumulators), MB = the tile's 32-row blocks that hold valid rows.
 //   gate/up: weight rows = gate rows i0 + 32w .. +32 and the matching up rows, so the gate
 //            and up accumulators of a (row, i) sit in the same lane and SwiGLU is applied
 //            in registers; h is written in slot order [slots, I] fp16.
-//   down:    weight rows = output columns n0 + 64w .. +64. Every row is written fp16 in
-//            slot order: a routed slot's row scaled by its routing weight, a shared-expert
-//            slot's row as it is (section "Reduce intermediate and state traffic": the
-//            output projection is combined with the routing score).
+//   down:    weight rows = output columns n0 + 64w .. +64. Every routed row is written
+//            fp16 in slot order, scaled by its routing weight (section "Reduce intermediate
+//            and state traffic": the output projection is combined with the routing
+//            score). The shared expert's down projection runs over token tiles with the
+//            weighted combine in its epilogue (k_shared_down_combine).
 // MFMA K order: lane (n, half) of a B operand holds the 8 K of substep kk at
 // 32*half + 8*kk (inside that chunk in the order 0,4,1,5,2,6,3,7 in which the packed
 // dequantisation produces them), so over the 4 substeps a lane covers 32 consecutive K =
