@@ -66,6 +66,15 @@ MOE_DEV uint32_t pack_f16x2(float lo, float hi) {
   v[1] = (_Float16)hi;
   return __builtin_bit_cast(uint32_t, v);
 }
+// fp16 pair (w * lo, w * hi), each product rounded once (to nearest even) from its exact
+// value: v_fma_mix with f32 sources and a zero addend, the low half then the high half
+MOE_DEV uint32_t mul_pack_f16x2(float w, float lo, float hi) {
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, %1, %2, 0\n\tv_fma_mixhi_f16 %0, %1, %3, 0"
+      : "=&v"(r)
+      : "v"(w), "v"(lo), "v"(hi));
+  return r;
+}
 MOE_DEV uint16_t f32_to_f16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 
 MOE_DEV float f16lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w)[0]; }

@@ -93,6 +93,11 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
   constexpr int kSB = kAB + kBB + (kX ? 0 : kSBBytes);   // bytes of one ring stage
   constexpr int kLB = kX ? 8 : 3;  // B loads per wave and step (codes 2 + scales 1)
   static_assert(kSt * kSB <= (kX ? kXSmemBytes : kSmemBytes), "ring does not fit the LDS");
+  // Down tiles multiply with the operands exchanged (weights first): the product is the
+  // transposed tile, so a lane's accumulators hold four adjacent output columns of one row,
+  // which go to LDS in one write instead of four. The operand fragments of the two forms
+  // have the same register layout, and every sum is the same.
+  constexpr bool kWT = !kGateUp;
   const int gbase = a.offsets[e];
   const int slot0 = gbase + row0;
   const int K = kGateUp ? a.H : a.I;
@@ -279,8 +284,13 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
       }
 #pragma unroll
       for (int m = 0; m < MB; ++m) {
-        acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[kk & 1][m], bc0, acc[m][0], 0, 0, 0);
-        acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[kk & 1][m], bc1, acc[m][1], 0, 0, 0);
+        if constexpr (kWT) {
+          acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bc0, av[kk & 1][m], acc[m][0], 0, 0, 0);
+          acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bc1, av[kk & 1][m], acc[m][1], 0, 0, 0);
+        } else {
+          acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[kk & 1][m], bc0, acc[m][0], 0, 0, 0);
+          acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[kk & 1][m], bc1, acc[m][1], 0, 0, 0);
+        }
       }
       // the next substep's weights while these MFMAs run
       if (kk < 3) MOE_B_OPS(kk + 1);
@@ -323,7 +333,7 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
   // writes (l < 32 and l >= 32) fall into different bank halves.
   const int col = lane & 31, rq4 = (lane >> 5) * 4;
   __syncthreads();  // every wave is done reading the stages
-  if (kGateUp) {
+  if constexpr (kGateUp) {
     // h: rows x 128 columns, stored in the chunk order of the fp16 operand rows (h is the
     // down GEMM's A operand)
     constexpr int HP = 128 + 8;
@@ -342,7 +352,7 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
       *reinterpret_cast<uint4 *>(a.h16 + (size_t)(slot0 + rr) * a.I + n_tile * (BNW / 2) +
                                  8 * (tid & 15)) =
           *reinterpret_cast<const uint4 *>(ht + rr * HP + 8 * (tid & 15));
-  } else if (kComb) {
+  } else if constexpr (kComb) {
     // y[t] = shared(x_t) + sum_j out[slot_of[t, j]] (+ residual[t]) over this tile's 256
     // columns, fp32 in that order, bf16 out. The shared result of every row goes through LDS
     // in fp32, the routed slots (requested before the K loop) beside it; then thread (row,
@@ -359,14 +369,18 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
 #pragma unroll
     for (int q = 0; q < 2; ++q)
       if (tid + 256 * q < 64 * kMaxTopK) s_slot[tid + 256 * q] = slot_pre[q];
+    // transposed accumulators: lane l holds token row 32m + l%32, register r the column
+    // 8*(r/4) + 4*(l/32) + r%4 of its 32-column block
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 32 * m + (r >> 2) * 8 + rq4 + (r & 3);
-        st[row * SP + 64 * wave + col] = acc[m][0][r];
-        st[row * SP + 64 * wave + 32 + col] = acc[m][1][r];
-      }
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<float4 *>(st + (32 * m + col) * SP + 64 * wave + 32 * nb + 8 * g +
+                                      rq4) =
+              make_float4(acc[m][nb][4 * g], acc[m][nb][4 * g + 1], acc[m][nb][4 * g + 2],
+                          acc[m][nb][4 * g + 3]);
     __syncthreads();
 #pragma unroll
     for (int p0 = 0; p0 < 4 * MB; p0 += kCombRows) {
@@ -411,7 +425,10 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
     }
   } else {
     // rows x 256 columns fp16 in slot order: a routed slot pre-weighted by its routing
-    // weight, a shared-expert slot (weight 1) as it is; staged through LDS 128 rows at a time
+    // weight, a shared-expert slot (weight 1) as it is; staged through LDS 128 rows at a time.
+    // Transposed accumulators (kWT): lane l holds slot row 32m + l%32, and register r the
+    // output column 8*(r/4) + 4*(l/32) + r%4 of its 32-column block. Rows are padded by
+    // 16 bytes, which spreads the 8-byte writes of 16 rows over all banks.
     constexpr int OP = BNW + 8;
     _Float16 *ot = reinterpret_cast<_Float16 *>(smem);
     float *sw = reinterpret_cast<float *>(smem + BM * OP * 2);
@@ -421,14 +438,18 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
     for (int m0 = 0; m0 < MB; m0 += 4) {
       __syncthreads();  // sw is written; the previous round's rows have left
 #pragma unroll
-      for (int m = m0; m < (MB < m0 + 4 ? MB : m0 + 4); ++m)
+      for (int m = m0; m < (MB < m0 + 4 ? MB : m0 + 4); ++m) {
+        const int row = 32 * m + col;
+        const float wv = sw[row];
+        _Float16 *orow = ot + (row - 32 * m0) * OP + 64 * wave + rq4;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = 32 * m + (r >> 2) * 8 + rq4 + (r & 3);
-          const float wv = sw[row];
-          ot[(row - 32 * m0) * OP + 64 * wave + col] = (_Float16)(wv * acc[m][0][r]);
-          ot[(row - 32 * m0) * OP + 64 * wave + 32 + col] = (_Float16)(wv * acc[m][1][r]);
-        }
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<uint2 *>(orow + 32 * nb + 8 * g) =
+                make_uint2(mul_pack_f16x2(wv, acc[m][nb][4 * g], acc[m][nb][4 * g + 1]),
+                           mul_pack_f16x2(wv, acc[m][nb][4 * g + 2], acc[m][nb][4 * g + 3]));
+      }
       __syncthreads();
       const int r1 = min(nvalid, 32 * (m0 + 4));
       for (int rr = 32 * m0 + (tid >> 5); rr < r1; rr += 8)
