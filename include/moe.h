@@ -145,9 +145,12 @@ moe_status moe_route(const moe_layer *layer, const void *x, int64_t T,
  * weights during matrix multiplication" and "Match tile size to expert load"): routing as
  * moe_route, then for int4 (tiled weights required, see moe_pack_weights) a grouped
  * gate/up GEMM with SwiGLU, a grouped down GEMM (int4 codes dequantised to fp16 in
- * registers, fp16 MFMA, fp32 accumulation) and a weighted combine back to token order. y[t] = shared(x_t) + sum_j w[t,j] expert_{ids[t,j]}(x_t)
+ * registers, fp16 MFMA, fp32 accumulation; the two in one persistent launch) and a weighted
+ * combine back to token order. y[t] = shared(x_t) + sum_j w[t,j] expert_{ids[t,j]}(x_t)
  * (+ residual[t]). x, y, residual: [T, H] of act_dtype; residual may be NULL and may
  * alias y. route_out may be NULL; when given it receives the routing results.
+ * Int4 calls with T * H * 2 >= 2^32 bytes run as consecutive calls of fewer tokens (the
+ * same y); with route_out such a call returns MOE_E_UNSUPPORTED.
  * Results are deterministic: identical inputs give identical bytes. */
 moe_status moe_prefill(const moe_layer *layer, const void *x, int64_t T, void *y,
                        const void *residual, const moe_route_out *route_out, void *ws,
@@ -183,7 +186,8 @@ moe_status moe_decode_noalloc(const moe_layer *layer, const void *x, void *y,
  *   MOE_ABL_SEPARATE_DEQUANT  "Dequantize weights during matrix multiplication", its
  *       ablation: a separate pass expands the int4 weights of every expert that received
  *       rows (and the shared expert) into fp16 arrays in the workspace, and the GEMMs read
- *       those back instead of dequantising tiles on chip
+ *       those back instead of dequantising tiles on chip (as two launches, gate/up then
+ *       down, instead of the persistent one)
  *   MOE_ABL_HOST_ROUTING      "Keep expert routing on the GPU", its ablation: the GPU stops
  *       after the router and top-k; the host reads the ids back, builds the histogram,
  *       offsets, per-block bases and tile map, uploads them and only then enqueues the
@@ -195,8 +199,8 @@ moe_status moe_decode_noalloc(const moe_layer *layer, const void *x, void *y,
  *       worth of blocks, however few rows it holds (no load adaptivity at all)
  *   MOE_ABL_TILE_128          tiles of at most 128 rows whatever the load (the per-call
  *       height choice off; each expert's last tile still only as high as its rows need)
- * Int4 layers only (MOE_E_UNSUPPORTED otherwise), tiled weights required. Arguments as
- * moe_prefill; the workspace must hold moe_ablation_workspace_bytes for the same variant
+ * Int4 layers only (MOE_E_UNSUPPORTED otherwise, and for T * H * 2 >= 2^32 bytes), tiled
+ * weights required. Arguments as moe_prefill; the workspace must hold moe_ablation_workspace_bytes for the same variant
  * (for MOE_ABL_SEPARATE_DEQUANT that includes 2 bytes per expert weight). */
 typedef enum {
   MOE_ABL_NONE = 0,

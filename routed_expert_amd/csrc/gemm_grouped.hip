@@ -52,6 +52,8 @@ constexpr int kBBytes = 4 * 2 * 1024;              // codes: 4 waves x 2 columns
 // Scales and biases of one step (one K group): 4 waves x 64 weight rows x {scale, bias}.
 constexpr int kSBBytes = 4 * 256;
 constexpr int kSmemBytes = 80 * 1024;              // two workgroups per CU
+// LDS word of the persistent launch's next ticket, above everything a tile uses
+constexpr int kTicketOff = kSmemBytes - 16;
 // A tile of five 32-row blocks (an expert's last full tile with its short remainder, see
 // group_tables) has 20 KB of activation rows per step; three such stages would not fit two
 // workgroups per CU, so it runs a two-stage ring (loads one K step ahead instead of two).
@@ -86,60 +88,74 @@ MOE_DEV void wait_vmcnt() {
 // the residual, and writes y in bf16 (the weighted combine, fused).
 template <bool kGateUp, int MB, bool kX, bool kComb = false>
 MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, int nvalid,
-                          int n_tile) {
+                          int n_tile, int wave, int32_t *tk = nullptr) {
   constexpr int kSt = ring_stages<MB>();                 // ring depth
   constexpr int kAB = a_stage_bytes<MB>();               // activation rows of one stage
   constexpr int kBB = kX ? kXBBytes : kBBytes;          // weight operands of one stage
   constexpr int kSB = kAB + kBB + (kX ? 0 : kSBBytes);   // bytes of one ring stage
   constexpr int kLB = kX ? 8 : 3;  // B loads per wave and step (codes 2 + scales 1)
-  static_assert(kSt * kSB <= (kX ? kXSmemBytes : kSmemBytes), "ring does not fit the LDS");
+  static_assert(kSt * kSB <= (kX ? kXSmemBytes : kTicketOff), "ring does not fit the LDS");
   // Down tiles multiply with the operands exchanged (weights first): the product is the
   // transposed tile, so a lane's accumulators hold four adjacent output columns of one row,
   // which go to LDS in one write instead of four. The operand fragments of the two forms
   // have the same register layout, and every sum is the same.
   constexpr bool kWT = !kGateUp;
-  const int gbase = a.offsets[e];
+  // tables are uniform per tile; in the persistent launch the compiler cannot prove it (the
+  // loads follow stores of earlier items), so the values are made scalar explicitly
+  const int gbase = __builtin_amdgcn_readfirstlane(a.offsets[e]);
   const int slot0 = gbase + row0;
   const int K = kGateUp ? a.H : a.I;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // wave (uniform) comes from the caller; the lane index is formed here by an opaque
+  // instruction pair. In the persistent launch the tile runs in a loop, and the lane-dependent
+  // offsets would otherwise be computed once before it and held in registers across it
+  // (spilled, at 256 in use), as would the thread index register itself.
+  int lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  const int tid = 64 * wave + lane;
 
   // Activation rows of one step land in LDS swizzled: 16-byte chunk c of row r sits at
   // chunk c ^ ((r >> 1) & 7) of the row, which keeps the MFMA operand reads (16 rows, one
   // chunk) free of bank conflicts. The 4*MB groups of 8 rows are spread over the waves:
   // direct load j of wave w fills row group w + 4j; lane l fills physical chunk l % 8 of
   // row l / 8 of its group.
-  const uint16_t *asrc[MB];
+  // Every direct load takes a wave-uniform 64-bit base in SGPRs and a 32-bit byte offset per
+  // lane (the instruction's saddr form): the activation rows' base is x16 (gathered tokens;
+  // T * H * 2 < 2^32 bytes, which the host guarantees by splitting larger calls) or the
+  // tile's first h row, the weights' base is the wave's block, and one lane offset (16 l)
+  // serves codes, scales and expanded weights.
+  const uint8_t *abase = kGateUp ? reinterpret_cast<const uint8_t *>(a.x16)
+                                 : reinterpret_cast<const uint8_t *>(a.h16 + (size_t)slot0 * a.I);
+  uint32_t aoff[MB];
 #pragma unroll
   for (int j = 0; j < MB; ++j) {
     const int r = 8 * (wave + 4 * j) + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     const int rr = min(r, nvalid - 1);
-    const uint16_t *row;
     if (kGateUp) {
       const int tok = (e == a.E) ? (row0 + rr) : a.sorted_tok[slot0 + rr];
-      row = a.x16 + (size_t)tok * a.H;
+      aoff[j] = (uint32_t)tok * (uint32_t)(2 * a.H) + 16u * c;
     } else {
-      row = a.h16 + (size_t)(slot0 + rr) * a.I;
+      aoff[j] = (uint32_t)rr * (uint32_t)(2 * a.I) + 16u * c;
     }
-    asrc[j] = row + 8 * c;
   }
+  const uint32_t loff = 16u * lane;
 
   // This wave's weight rows are one 64-row block of the tiled layout: gate rows 32w..+32
   // of the N tile and the matching up rows (gate/up), or output rows 64w..+64 (down). Per
   // K step the block's codes are 2 KB contiguous (column block c = rows 32c..32c+31 at
   // c * 1 KB); its scales and biases are tiled 1 KB per four steps, lane l = 32c + row
   // holding 4 steps x {scale, bias} in 16 bytes, of which each step loads its 4 bytes.
+  const int wave_u = wave;
   const int nb = kGateUp ? 2 * a.I / 64 : a.H / 64;
-  const int blk = n_tile * 4 + wave;
+  const int blk = n_tile * 4 + wave_u;
   const int ns = K / BK, ns4 = (ns + 3) / 4;
-  const uint8_t *tq = (kGateUp ? a.wt.w13_t : a.wt.w2_t) +
-                      ((size_t)e * nb + blk) * ns * 2048 + 16 * lane;
+  const uint8_t *tq = (kGateUp ? a.wt.w13_t : a.wt.w2_t) + ((size_t)e * nb + blk) * ns * 2048;
   const uint8_t *tsb = reinterpret_cast<const uint8_t *>(
-      (kGateUp ? a.wt.w13_tsb : a.wt.w2_tsb) + ((size_t)e * nb + blk) * ns4 * 512 + 8 * lane);
+      (kGateUp ? a.wt.w13_tsb : a.wt.w2_tsb) + ((size_t)e * nb + blk) * ns4 * 512);
   // expanded weights: the same block's 8 KB of fp16 per K step, 1 KB per (column block,
   // substep), lane l's 8 values at 16 l
   const uint8_t *txq = kX ? reinterpret_cast<const uint8_t *>(kGateUp ? a.w13_x : a.w2_x) +
-                                ((size_t)e * nb + blk) * ns * 8192 + 16 * lane
+                                ((size_t)e * nb + blk) * ns * 8192
                           : nullptr;
 
   // The direct-to-LDS loads and the step barrier are issued as inline assembly: the
@@ -155,31 +171,30 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
   // M0 holds the wave-uniform LDS byte address; lane l's data lands at M0 + l * size.
   // The s_nop covers the wait states a load that reads M0 needs after M0 is written.
   const uint32_t smem_lds = (uint32_t)(uintptr_t)smem;
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-#define MOE_DMA16(gptr, lds)                                                            \
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %0, off"         \
-               :: "v"(gptr), "s"(lds) : "memory", "m0")
-#define MOE_DMA4(gptr, lds)                                                             \
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 1\n\tglobal_load_lds_dword %0, off"           \
-               :: "v"(gptr), "s"(lds) : "memory", "m0")
+#define MOE_DMA16(voff, sbase, lds)                                                     \
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %0, %1"          \
+               :: "v"(voff), "s"(sbase), "s"(lds) : "memory", "m0")
+#define MOE_DMA4(voff, sbase, lds)                                                      \
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 1\n\tglobal_load_lds_dword %0, %1"            \
+               :: "v"(voff), "s"(sbase), "s"(lds) : "memory", "m0")
   // issue the direct-to-LDS loads of K step `step` into ring stage `slot` (MB + 3 memory
   // instructions per wave: activation rows, two code blocks, the step's scales and biases;
   // expanded weights: MB + 8)
 #define MOE_ISSUE(step, slot)                                                           \
   do {                                                                                  \
     const uint32_t base_ = smem_lds + (slot) * kSB;                                     \
-    const int k0_ = (step) * BK;                                                        \
+    const uint8_t *as_ = abase + (size_t)(step) * (BK * 2);                             \
     _Pragma("unroll") for (int j = 0; j < MB; ++j)                                      \
-      MOE_DMA16(asrc[j] + k0_, base_ + (wave_u + 4 * j) * 1024);                        \
+      MOE_DMA16(aoff[j], as_, base_ + (wave_u + 4 * j) * 1024);                         \
     if constexpr (kX) {                                                                 \
       const uint32_t bb_ = base_ + kAB + wave_u * 8192;                                 \
       _Pragma("unroll") for (int q = 0; q < 8; ++q)                                     \
-        MOE_DMA16(txq + (size_t)(step) * 8192 + q * 1024, bb_ + q * 1024);              \
+        MOE_DMA16(loff, txq + (size_t)(step) * 8192 + q * 1024, bb_ + q * 1024);        \
     } else {                                                                            \
       const uint32_t bb_ = base_ + kAB + wave_u * 2048;                                 \
-      MOE_DMA16(tq + (size_t)(step) * 2048, bb_);                                       \
-      MOE_DMA16(tq + (size_t)(step) * 2048 + 1024, bb_ + 1024);                         \
-      MOE_DMA4(tsb + (size_t)((step) >> 2) * 1024 + 4 * ((step) & 3),                   \
+      MOE_DMA16(loff, tq + (size_t)(step) * 2048, bb_);                                 \
+      MOE_DMA16(loff, tq + (size_t)(step) * 2048 + 1024, bb_ + 1024);                   \
+      MOE_DMA4(loff, tsb + (size_t)((step) >> 2) * 1024 + 4 * ((step) & 3),             \
                base_ + kAB + kBB + wave_u * 256);                                       \
     }                                                                                   \
   } while (0)
@@ -333,6 +348,10 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
   // writes (l < 32 and l >= 32) fall into different bank halves.
   const int col = lane & 31, rq4 = (lane >> 5) * 4;
   __syncthreads();  // every wave is done reading the stages
+  // persistent launch: the workgroup's next ticket, requested here (few registers live) and
+  // stored to its LDS word once the tile is written, so its latency hides behind the epilogue
+  int32_t tn = 0;
+  if (tk && tid == 0) tn = __hip_atomic_fetch_add(tk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if constexpr (kGateUp) {
     // h: rows x 128 columns, stored in the chunk order of the fp16 operand rows (h is the
     // down GEMM's A operand)
@@ -362,7 +381,7 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
     constexpr int SP = BNW + 4;
     float *st = reinterpret_cast<float *>(smem);
     int32_t *s_slot = reinterpret_cast<int32_t *>(smem + 32 * MB * SP * 4);
-    static_assert(64 * SP * 4 + 64 * kMaxTopK * 4 <= kSmemBytes, "combine staging");
+    static_assert(64 * SP * 4 + 64 * kMaxTopK * 4 <= kTicketOff, "combine staging");
     const int k = a.k;
     const int cc = 8 * (tid & 31), col0 = n_tile * BNW + cc;
     constexpr int kCombRows = 4;  // rows per thread gathered together
@@ -432,7 +451,7 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
     constexpr int OP = BNW + 8;
     _Float16 *ot = reinterpret_cast<_Float16 *>(smem);
     float *sw = reinterpret_cast<float *>(smem + BM * OP * 2);
-    static_assert(BM * OP * 2 + kMaxMB * 32 * 4 <= kSmemBytes, "epilogue staging");
+    static_assert(BM * OP * 2 + kMaxMB * 32 * 4 <= kTicketOff, "epilogue staging");
     if (tid < 32 * MB) sw[tid] = tid < nvalid ? (e < a.E ? a.slot_w[slot0 + tid] : 1.0f) : 0.f;
 #pragma unroll
     for (int m0 = 0; m0 < MB; m0 += 4) {
@@ -458,6 +477,27 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
             *reinterpret_cast<const uint4 *>(ot + (rr - 32 * m0) * OP + 8 * (tid & 31));
     }
   }
+  if (tk && tid == 0) *reinterpret_cast<int32_t *>(smem + kTicketOff) = tn;
+}
+
+// N tile n_tile of entry m_tile of the tile map
+template <bool kGateUp, bool kX>
+MOE_DEV bool grouped_item(const GroupedArgs &a, uint8_t *smem, int m_tile, int n_tile, int wave,
+                          int32_t *tk = nullptr) {
+  const int2 tile = a.tiles[m_tile];
+  const int tx = __builtin_amdgcn_readfirstlane(tile.x), row0 = __builtin_amdgcn_readfirstlane(tile.y);
+  const int e = tx & 0xFFFF, nvalid = tx >> 16;
+  // the shared expert's down projection runs in its own launch with the combine fused
+  if (!kGateUp && a.fused_combine && e == a.E) return false;
+  // load-adaptive height: only the 32-row blocks that hold rows (all four when fixed)
+  switch (a.fixed_mb ? 4 : (nvalid + 31) >> 5) {
+    case 1: grouped_tile<kGateUp, 1, kX>(a, smem, e, row0, nvalid, n_tile, wave, tk); break;
+    case 2: grouped_tile<kGateUp, 2, kX>(a, smem, e, row0, nvalid, n_tile, wave, tk); break;
+    case 3: grouped_tile<kGateUp, 3, kX>(a, smem, e, row0, nvalid, n_tile, wave, tk); break;
+    case 4: grouped_tile<kGateUp, 4, kX>(a, smem, e, row0, nvalid, n_tile, wave, tk); break;
+    default: grouped_tile<kGateUp, 5, kX>(a, smem, e, row0, nvalid, n_tile, wave, tk); break;
+  }
+  return true;
 }
 
 template <bool kGateUp, bool kX>
@@ -469,18 +509,8 @@ MOE_DEV void grouped_body(const GroupedArgs &a, uint8_t *smem) {
   const int id = blockIdx.x, xcd = id & 7, j = id >> 3;
   const int n_tile = j % nN, m_tile = (j / nN) * 8 + xcd;
   if (m_tile >= *a.n_tiles) return;
-  const int2 tile = a.tiles[m_tile];
-  const int e = tile.x & 0xFFFF, row0 = tile.y, nvalid = tile.x >> 16;
-  // the shared expert's down projection runs in its own launch with the combine fused
-  if (!kGateUp && a.fused_combine && e == a.E) return;
-  // load-adaptive height: only the 32-row blocks that hold rows (all four when fixed)
-  switch (a.fixed_mb ? 4 : (nvalid + 31) >> 5) {
-    case 1: grouped_tile<kGateUp, 1, kX>(a, smem, e, row0, nvalid, n_tile); break;
-    case 2: grouped_tile<kGateUp, 2, kX>(a, smem, e, row0, nvalid, n_tile); break;
-    case 3: grouped_tile<kGateUp, 3, kX>(a, smem, e, row0, nvalid, n_tile); break;
-    case 4: grouped_tile<kGateUp, 4, kX>(a, smem, e, row0, nvalid, n_tile); break;
-    default: grouped_tile<kGateUp, 5, kX>(a, smem, e, row0, nvalid, n_tile); break;
-  }
+  grouped_item<kGateUp, kX>(a, smem, m_tile, n_tile,
+                            __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6));
 }
 
 template <bool kGateUp>
@@ -500,10 +530,89 @@ __global__ __launch_bounds__(256, 2) void k_shared_down_combine(GroupedArgs a) {
   const int row0 = 64 * m_tile;
   if (row0 >= a.T) return;
   const int nvalid = min(64, (int)(a.T - row0));
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   if (nvalid > 32)
-    grouped_tile<false, 2, false, true>(a, smem, a.E, row0, nvalid, n_tile);
+    grouped_tile<false, 2, false, true>(a, smem, a.E, row0, nvalid, n_tile, wave);
   else
-    grouped_tile<false, 1, false, true>(a, smem, a.E, row0, nvalid, n_tile);
+    grouped_tile<false, 1, false, true>(a, smem, a.E, row0, nvalid, n_tile, wave);
+}
+
+// gate/up and down of every tile in one persistent launch. The down GEMM of a tile needs all
+// of its rows' h, so as two launches the down work waits for the whole gate/up grid, and the
+// gate/up grid's last, partly filled round of workgroups leaves CUs idle. Here each XCD
+// works through its own queue: the tiles m = q, q + Q, q + 2Q, ... of the tile map (Q queues,
+// one per XCD; q is read from the XCC_ID register), first every gate/up item (tile, N
+// tile), then every down item. A workgroup takes the next item with an atomic ticket, so
+// only running workgroups hold work. A gate/up item writes its h rows, waits until the
+// stores are acknowledged and then counts itself done on the tile; a down item first waits
+// for its tile's count to reach the gate/up N tiles. Every workgroup that touches a tile's
+// h, ticket or count runs on the same XCD and so goes through one L2, where the atomics are
+// performed and the counts polled (device-scope loads miss L1); the h loads themselves may
+// go through L1, which cannot hold an older copy of those rows: nothing in the launch reads
+// them before they are complete, and L1 starts empty at each launch. Deadlock-free: gate/up
+// items wait for nothing, and a down item waits only for gate/up items with earlier tickets,
+// all taken by running workgroups. The waits are bounded anyway (kSpinTicks of the 100 MHz
+// clock, then the flag at kSyncErr is raised and the item computed as it stands).
+constexpr uint64_t kSpinTicks = 50000000ull;  // 0.5 s
+
+__global__ __launch_bounds__(256, 2) void k_grouped_fused(GroupedArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const bool lead = threadIdx.x == 0;
+  const int nq = a.n_queues;
+  const int q = (int)(__builtin_amdgcn_s_getreg(20 | (31 << 11)) & (uint32_t)(nq - 1));
+  const int nt = *a.n_tiles;
+  const int ntq = nt > q ? (nt - 1 - q) / nq + 1 : 0;  // tiles of this queue
+  const int nNg = a.I / (BNW / 2), nNd = a.H / BNW;
+  const int n_gu = ntq * nNg, n_all = n_gu + ntq * nNd;
+  int32_t *ticket = a.sync + kSyncQStride * q;
+  int32_t *s_t = reinterpret_cast<int32_t *>(smem + kTicketOff);  // the next ticket
+  if (lead) *s_t = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  int t = __builtin_amdgcn_readfirstlane(*s_t);  // uniform: addresses stay scalar
+  __syncthreads();
+  while (t < n_all) {
+    // The arguments are read through an opaque copy of the kernel-argument pointer, so that
+    // the compiler loads them per item (scalar loads) instead of holding every field and
+    // what it derives from them in SGPRs across the loop.
+    typedef const GroupedArgs __attribute__((address_space(4))) KArgs;
+    KArgs *ap = (KArgs *)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(ap));
+    const GroupedArgs &ai = *(const GroupedArgs *)ap;
+    int32_t *tk = ai.sync + kSyncQStride * q;
+    bool ran;
+    if (t < n_gu) {
+      const int i = t / nNg, m = q + nq * i;
+      ran = grouped_item<true, false>(ai, smem, m, t - i * nNg, wave, tk);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's h stores are in L2
+      __syncthreads();
+      if (lead)
+        __hip_atomic_fetch_add(ai.sync + kSyncDone + m, 1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      const int u = t - n_gu, i = u / nNd, m = q + nq * i;
+      if (lead) {
+        int32_t *done = ai.sync + kSyncDone + m, *err = ai.sync + kSyncErr;
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        while (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nNg) {
+          if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
+          if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
+            __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+      __syncthreads();
+      ran = grouped_item<false, false>(ai, smem, m, u - i * nNd, wave, tk);
+    }
+    // a skipped item (the shared expert's down tiles, whose launch is the fused combine)
+    // took no ticket
+    if (!ran && lead) *s_t = __hip_atomic_fetch_add(tk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();  // the next ticket is in LDS
+    t = __builtin_amdgcn_readfirstlane(*s_t);
+    __syncthreads();  // every wave has read it before it is replaced
+  }
 }
 
 template <bool kGateUp>
@@ -570,6 +679,15 @@ hipError_t launch_shared_down_combine(const GroupedArgs &a, hipStream_t s) {
   const int mt = (int)((a.T + 63) / 64);
   const dim3 g((unsigned)((mt + 7) / 8 * 8 * (a.H / BNW)));
   MOE_LAUNCH("k_shared_down_combine", k_shared_down_combine, g, dim3(256), 0, s, a);
+  return hipSuccess;
+}
+
+hipError_t launch_grouped_fused(const GroupedArgs &a, hipStream_t s) {
+  if (!a.sync || a.n_queues < 1 || a.n_queues > kMaxQueues || (a.n_queues & (a.n_queues - 1)))
+    return hipErrorInvalidValue;
+  // two resident workgroups per CU, 32 CUs per XCD
+  MOE_LAUNCH("k_grouped_fused", k_grouped_fused, dim3((unsigned)(64 * a.n_queues)), dim3(256),
+             0, s, a);
   return hipSuccess;
 }
 

@@ -47,6 +47,8 @@ struct RouteArgs {
   int32_t *n_tiles;       // [1]
   int tile_shift = 0;     // grouped-GEMM tile height: 0 = chosen from the load on the GPU,
                           // else fixed at 2^tile_shift rows (5..7)
+  int32_t *sync = nullptr;  // [n_sync] work-queue words of k_grouped_fused, zeroed by k_group
+  int n_sync = 0;
 };
 
 // Router, top-k and per-block histogram (launch_route_topk), then one kernel that forms the
@@ -110,9 +112,22 @@ struct GroupedArgs {
   // fp16 weights expanded by launch_expand (tiled order, see expanded_bytes); when set, the
   // GEMMs read them instead of the int4 codes
   const uint16_t *w13_x = nullptr, *w2_x = nullptr;
+  // Work queues of the fused gate/up + down launch (launch_grouped_fused): sync_words words,
+  // zero at launch; n_queues = the device's XCDs (a power of two, at most kMaxQueues).
+  int32_t *sync = nullptr;
+  int n_queues = 0;
 };
+// Work-queue words of k_grouped_fused: queue q's ticket at kSyncQStride * q (one 256-byte
+// line each), the give-up flag of the bounded waits at kSyncErr, then one completion counter
+// per tile of the tile map.
+constexpr int kMaxQueues = 8, kSyncQStride = 64, kSyncErr = kMaxQueues * kSyncQStride;
+constexpr int kSyncDone = kSyncErr + 64;
+inline size_t sync_words(int max_tiles) { return (size_t)kSyncDone + (size_t)max_tiles; }
 hipError_t launch_grouped_gateup(const GroupedArgs &a, hipStream_t s);
 hipError_t launch_grouped_down(const GroupedArgs &a, hipStream_t s);
+// gate/up and down in one persistent launch (a.sync set): every XCD runs its own queue of
+// tiles, all gate/up work first, and a down tile starts once its rows' h is complete.
+hipError_t launch_grouped_fused(const GroupedArgs &a, hipStream_t s);
 hipError_t launch_shared_down_combine(const GroupedArgs &a, hipStream_t s);
 // Separate dequantisation pass: every expert that received rows (and the shared expert)
 // expanded to fp16, [E+S][R/64][K/64][2 column blocks][4 substeps][64 lanes][8], the B

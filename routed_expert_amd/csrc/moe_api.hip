@@ -87,7 +87,7 @@ moe_status check_layer(const moe_layer *L) {
 struct Plan {
   size_t dec_logits, dec_ids, dec_z, dec_h, dec_xn, st_z, st_ids, st_w, st_h;
   size_t logits, planes, ids, w, blk, offsets, sorted, slot, slot_w, x16, tiles, ntiles,
-      h, out;
+      h, out, sync;
   size_t total;
   int max_tiles;
 };
@@ -151,9 +151,10 @@ Plan make_plan(const moe_layer *L, int64_t T, int tile_shift = 0) {
     p.h = take((k + S) * Tn * I * 2);
     // the routed rows only: the shared expert's down projection adds them into y itself
     p.out = take(k * Tn * H * 2);
+    p.sync = take(moe::sync_words(p.max_tiles) * 4);
   } else {
     p.h = take((k + S) * Tn * I * 4);
-    p.slot_w = p.x16 = p.out = off;
+    p.slot_w = p.x16 = p.out = p.sync = off;
   }
   p.total = off;
   return p;
@@ -422,6 +423,25 @@ moe_status moe_route(const moe_layer *layer, const void *x, int64_t T, const moe
   return MOE_OK;
 }
 
+// Work queues of the fused gate/up + down launch: one per XCD of the current device (32 CUs
+// each), or 0 where the count is not a power of two up to kMaxQueues (then the two GEMMs run
+// as separate launches).
+static int device_queues() {
+  static std::atomic<int> cache[64];  // queues + 1 per device id, 0 = not yet known
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int c = cache[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    const int x = cus % 32 == 0 ? cus / 32 : 0;
+    c = 1 + ((x >= 1 && x <= moe::kMaxQueues && (x & (x - 1)) == 0) ? x : 0);
+    cache[dev].store(c, std::memory_order_relaxed);
+  }
+  return c - 1;
+}
+
 // Grouped GEMMs of an int4 layer over the routing in ra (tables already on the device).
 static moe::GroupedArgs grouped_args(const moe_layer *layer, const moe::RouteArgs &ra, void *ws,
                                      const Plan &p) {
@@ -442,6 +462,9 @@ static moe::GroupedArgs grouped_args(const moe_layer *layer, const moe::RouteArg
   ga.wt = weights_of(layer);
   ga.h16 = at<uint16_t>(ws, p.h);
   ga.out = at<uint16_t>(ws, p.out);
+  // the fused launch needs the queue words zeroed by this call's k_group (ra.sync)
+  ga.n_queues = ra.sync ? device_queues() : 0;
+  ga.sync = ga.n_queues ? ra.sync : nullptr;
   return ga;
 }
 
@@ -450,21 +473,30 @@ static moe_status run_grouped(const moe_layer *layer, const moe::GroupedArgs &ga
                               const moe::RouteArgs &ra, const void *residual, void *y,
                               hipStream_t s) {
   hipError_t e;
-  if ((e = moe::launch_grouped_gateup(ga, s)) != hipSuccess)
-    return hip_fail(e, "moe_prefill gate/up");
+  moe::GroupedArgs gd = ga;
   if (layer->n_shared) {
-    // the routed experts' down projection, then the shared expert's with the combine fused
-    moe::GroupedArgs gd = ga;
+    // the routed experts' down projection skips the shared expert, whose down projection
+    // runs afterwards with the combine fused
     gd.fused_combine = 1;
     gd.slot_of = ra.slot_of;
     gd.residual = static_cast<const uint16_t *>(residual);
     gd.y = static_cast<uint16_t *>(y);
-    if ((e = moe::launch_grouped_down(gd, s)) != hipSuccess) return hip_fail(e, "moe_prefill down");
+  }
+  if (gd.sync && !gd.w13_x) {
+    // gate/up and down in one persistent launch
+    if ((e = moe::launch_grouped_fused(gd, s)) != hipSuccess)
+      return hip_fail(e, "moe_prefill gate/up + down");
+  } else {
+    if ((e = moe::launch_grouped_gateup(ga, s)) != hipSuccess)
+      return hip_fail(e, "moe_prefill gate/up");
+    if ((e = moe::launch_grouped_down(gd, s)) != hipSuccess)
+      return hip_fail(e, "moe_prefill down");
+  }
+  if (layer->n_shared) {
     if ((e = moe::launch_shared_down_combine(gd, s)) != hipSuccess)
       return hip_fail(e, "moe_prefill shared down + combine");
     return MOE_OK;
   }
-  if ((e = moe::launch_grouped_down(ga, s)) != hipSuccess) return hip_fail(e, "moe_prefill down");
   moe::CombineArgs ca{};
   ca.out = ga.out;
   ca.slot_of = ra.slot_of;
@@ -508,12 +540,34 @@ static moe_status prefill_impl(const moe_layer *layer, const void *x, int64_t T,
     if (e != hipSuccess) return hip_fail(e, "moe_prefill (small T)");
     return MOE_OK;
   }
+  const bool int4 = layer->w_format == MOE_W_INT4_G64;
+  // The grouped GEMMs address gathered x rows by 32-bit byte offsets: T * H * 2 < 2^32.
+  // Larger calls run as consecutive calls of fewer tokens (every token's result is the same).
+  const int64_t t_max = (int64_t)(0xFFFFFFFFull / (2ull * (uint64_t)layer->hidden)) & ~int64_t(63);
+  if (int4 && T > t_max) {
+    if (route_out)
+      return fail(MOE_E_UNSUPPORTED, "route_out needs T * hidden * 2 < 2^32 (T = %lld)",
+                  (long long)T);
+    const bool bf16 = layer->act_dtype == MOE_ACT_BF16;
+    const size_t row = (size_t)layer->hidden * (bf16 ? 2 : 4), yrow = row;  // x, y, residual
+    for (int64_t r0 = 0; r0 < T; r0 += t_max) {
+      const int64_t n = std::min(t_max, T - r0);
+      const moe_status st = prefill_impl(
+          layer, static_cast<const char *>(x) + r0 * row, n,
+          static_cast<char *>(y) + r0 * yrow,
+          residual ? static_cast<const char *>(residual) + r0 * yrow : nullptr, nullptr, ws, p,
+          s);
+      if (st) return st;
+    }
+    return MOE_OK;
+  }
   moe::RouteArgs ra = route_args(layer, x, T);
   route_targets(ra, p, ws, route_out);
-  const bool int4 = layer->w_format == MOE_W_INT4_G64;
   if (int4) {
     ra.slot_w = at<float>(ws, p.slot_w);
     ra.x16 = at<uint16_t>(ws, p.x16);
+    ra.sync = at<int32_t>(ws, p.sync);
+    ra.n_sync = (int)moe::sync_words(p.max_tiles);
   }
   hipError_t e = moe::launch_route_prefill(ra, s);
   if (e != hipSuccess) return hip_fail(e, "moe_prefill route");
@@ -699,6 +753,8 @@ moe_status moe_prefill_ablation(const moe_layer *layer, int32_t variant, const v
     return fail(MOE_E_UNSUPPORTED, "ablations cover the int4 grouped-GEMM path only");
   if (T < 0 || T > kMaxTokens) return fail(MOE_E_INVALID, "T %lld out of range", (long long)T);
   if (T == 0) return MOE_OK;
+  if ((uint64_t)T * 2 * (uint64_t)layer->hidden > 0xFFFFFFFFull)
+    return fail(MOE_E_UNSUPPORTED, "ablations need T * hidden * 2 < 2^32 (T = %lld)", (long long)T);
   if (!x || !y || !aligned16(x) || !aligned16(y))
     return fail(MOE_E_INVALID, "x and y must be non-NULL and 16-byte aligned");
   if (residual && !aligned16(residual)) return fail(MOE_E_INVALID, "residual misaligned");
@@ -715,6 +771,12 @@ moe_status moe_prefill_ablation(const moe_layer *layer, int32_t variant, const v
   ra.slot_w = at<float>(ws, p.slot_w);
   ra.x16 = at<uint16_t>(ws, p.x16);
   ra.tile_shift = abl_shift(variant);
+  // the persistent gate/up + down launch as in moe_prefill, except with the separate
+  // dequantisation pass (its expanded-weight GEMMs run as two launches)
+  if (variant != MOE_ABL_SEPARATE_DEQUANT) {
+    ra.sync = at<int32_t>(ws, p.sync);
+    ra.n_sync = (int)moe::sync_words(p.max_tiles);
+  }
   hipError_t e;
   int host_tiles = -1;
   if (variant == MOE_ABL_HOST_ROUTING) {
@@ -731,6 +793,11 @@ moe_status moe_prefill_ablation(const moe_layer *layer, int32_t variant, const v
     if ((e = hipMemcpyAsync(dtab, tab.data(), ap.tab_bytes, hipMemcpyHostToDevice, s)) ||
         (e = hipStreamSynchronize(s)))  // tab is host memory local to this call
       return hip_fail(e, "ablation: uploading the routing tables");
+    // the queue words k_group would have zeroed
+    const std::vector<int32_t> zeros((size_t)ra.n_sync, 0);
+    if ((e = hipMemcpyAsync(ra.sync, zeros.data(), zeros.size() * 4, hipMemcpyHostToDevice, s)) ||
+        (e = hipStreamSynchronize(s)))
+      return hip_fail(e, "ablation: clearing the work-queue words");
     ra.offsets = dtab + ap.tab_offsets;
     ra.n_tiles = dtab + ap.tab_ntiles;
     ra.tiles = reinterpret_cast<int2 *>(dtab + ap.tab_tiles);

@@ -435,10 +435,13 @@ __global__ __launch_bounds__(256) void k_group(const int32_t *__restrict__ blk_c
                                                int32_t *__restrict__ n_tiles, int tsh_fixed,
                                                int fill, int32_t *__restrict__ sorted_tok,
                                                int32_t *__restrict__ slot_of,
-                                               float *__restrict__ slot_w) {
+                                               float *__restrict__ slot_w,
+                                               int32_t *__restrict__ sync, int n_sync) {
   __shared__ unsigned long long mask[kMaxExperts];
   __shared__ int start[kMaxExperts];
   const int b = blockIdx.x, t0 = b * kRouteBlock, tid = threadIdx.x;
+  // the fused GEMM launch's queue words start at zero
+  for (int i = b * 256 + tid; i < n_sync; i += NB * 256) sync[i] = 0;
   int run = 0, base = 0;
   if (tid < E) {
     for (int b0 = 0; b0 < NB; b0 += 32) {
@@ -548,7 +551,7 @@ hipError_t launch_route_prefill(const RouteArgs &a, hipStream_t s) {
   const int NB = (int)((a.T + kRouteBlock - 1) / kRouteBlock);
   MOE_LAUNCH("k_group", k_group, dim3(NB), dim3(256), 0, s, a.blk, a.ids, a.w, NB, a.E, (int)a.T,
              a.k, a.S, a.offsets, a.counts_user, a.offsets_user, a.tiles, a.n_tiles, a.tile_shift,
-             gemm_fill(a.I), a.sorted_tok, a.slot_of, a.slot_w);
+             gemm_fill(a.I), a.sorted_tok, a.slot_of, a.slot_w, a.sync, a.n_sync);
   return hipSuccess;
 }
 
