@@ -54,6 +54,9 @@ constexpr int kSBBytes = 4 * 256;
 constexpr int kSmemBytes = 80 * 1024;              // two workgroups per CU
 // LDS word of the persistent launch's next ticket, above everything a tile uses
 constexpr int kTicketOff = kSmemBytes - 16;
+// Routing weights of a down tile's rows (up to 160 floats), requested at the tile's start into
+// LDS above the ring and below the ticket word, read by the epilogue
+constexpr int kSwOff = kTicketOff - 5 * 32 * 4;
 // A tile of five 32-row blocks (an expert's last full tile with its short remainder, see
 // group_tables) has 20 KB of activation rows per step; three such stages would not fit two
 // workgroups per CU, so it runs a two-stage ring (loads one K step ahead instead of two).
@@ -241,6 +244,20 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
 
   // every lane's source pointers are computed (their loads done) before the first DMA
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // Down tiles of routed experts: the rows' routing weights travel to LDS with the first
+  // step's operands (wave w fetches rows 64w .. 64w+63, past the tile's rows the last row's
+  // weight again, which no stored row uses), so the epilogue does not wait for them. They are
+  // older than every load of the ring, so the ring's first wait covers them.
+  constexpr bool kPreSw = !kGateUp && !kComb && !kX;
+  if constexpr (kPreSw) {
+    static_assert(kSt * kSB <= kSwOff, "routing weights overlap the ring");
+    if (e < a.E && 64 * wave < 32 * MB) {
+      const uint32_t voff = 4u * (uint32_t)min(64 * wave + lane, nvalid - 1);
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 1\n\tglobal_load_lds_dword %0, %1"
+                   :: "v"(voff), "s"(a.slot_w + slot0), "s"(smem_lds + kSwOff + 256 * wave)
+                   : "memory", "m0");
+    }
+  }
   // fused combine: the routed slots of this tile's tokens (row r, rank j at r * k + j),
   // requested now so that their latency hides behind the K loop
   int32_t slot_pre[2] = {0, 0};
@@ -450,12 +467,15 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
     // 16 bytes, which spreads the 8-byte writes of 16 rows over all banks.
     constexpr int OP = BNW + 8;
     _Float16 *ot = reinterpret_cast<_Float16 *>(smem);
-    float *sw = reinterpret_cast<float *>(smem + BM * OP * 2);
-    static_assert(BM * OP * 2 + kMaxMB * 32 * 4 <= kTicketOff, "epilogue staging");
-    if (tid < 32 * MB) sw[tid] = tid < nvalid ? (e < a.E ? a.slot_w[slot0 + tid] : 1.0f) : 0.f;
+    float *sw = reinterpret_cast<float *>(smem + (kPreSw ? kSwOff : BM * OP * 2));
+    static_assert(BM * OP * 2 + kMaxMB * 32 * 4 <= kSwOff, "epilogue staging");
+    // the routed weights are in LDS already (kPreSw); the shared expert's rows have weight 1
+    if (!kPreSw || e == a.E)
+      if (tid < 32 * MB) sw[tid] = tid < nvalid ? (e < a.E ? a.slot_w[slot0 + tid] : 1.0f) : 0.f;
 #pragma unroll
     for (int m0 = 0; m0 < MB; m0 += 4) {
-      __syncthreads();  // sw is written; the previous round's rows have left
+      // sw is written; the previous round's rows have left
+      if (!kPreSw || e == a.E || m0 > 0) __syncthreads();
 #pragma unroll
       for (int m = m0; m < (MB < m0 + 4 ? MB : m0 + 4); ++m) {
         const int row = 32 * m + col;
