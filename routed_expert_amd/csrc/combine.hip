@@ -85,6 +85,63 @@ __global__ __launch_bounds__(512) void k_rmsnorm(const void *h, int H, float eps
       }
 }
 
+// The same normalisation for bf16 rows whose H is a multiple of 2048 (at most kNormMaxH): one
+// wave per row, four rows per workgroup, with the bits of k_rmsnorm. Lane l stands in for the
+// threads l + 64 w (w = 0..7) of k_rmsnorm's 512: each virtual thread's partial is the fma
+// chain over its four elements of every 2048-element stretch in index order, each of the eight
+// partials goes through the xor butterfly of a wave, and the eight wave totals are added in
+// wave order. Every element is read once (four bf16 per 8-byte load, 512 contiguous bytes per
+// load instruction) and scaled from registers; h and out may alias.
+constexpr int kNormMaxH = 8192;
+template <int NS>  // 2048-element stretches per row
+__global__ __launch_bounds__(256) void k_rmsnorm_rows(const uint16_t *h, int64_t T, float eps,
+                                                      uint16_t *out) {
+  constexpr int H = 2048 * NS;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= T) return;
+  const size_t base = (size_t)row * H + 4 * lane;
+  uint2 v[NS][8];
+#pragma unroll
+  for (int j = 0; j < NS; ++j)
+#pragma unroll
+    for (int w = 0; w < 8; ++w)
+      v[j][w] = *reinterpret_cast<const uint2 *>(h + base + 2048 * j + 256 * w);
+  double p[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    p[w] = 0.0;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const double e0 = bf16lo(v[j][w].x), e1 = bf16hi(v[j][w].x);
+      const double e2 = bf16lo(v[j][w].y), e3 = bf16hi(v[j][w].y);
+      p[w] = __builtin_fma(e0, e0, p[w]);
+      p[w] = __builtin_fma(e1, e1, p[w]);
+      p[w] = __builtin_fma(e2, e2, p[w]);
+      p[w] = __builtin_fma(e3, e3, p[w]);
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1)
+#pragma unroll
+    for (int w = 0; w < 8; ++w) p[w] += __shfl_xor(p[w], m, kWave);
+  double total = p[0];
+#pragma unroll
+  for (int w = 1; w < 8; ++w) total += p[w];
+  const double inv = 1.0 / sqrt(total / (double)H + (double)eps);
+#pragma unroll
+  for (int j = 0; j < NS; ++j)
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const uint2 u = v[j][w];
+      const uint32_t lo = (uint32_t)f64_to_bf16_rne((double)bf16lo(u.x) * inv) |
+                          ((uint32_t)f64_to_bf16_rne((double)bf16hi(u.x) * inv) << 16);
+      const uint32_t hi = (uint32_t)f64_to_bf16_rne((double)bf16lo(u.y) * inv) |
+                          ((uint32_t)f64_to_bf16_rne((double)bf16hi(u.y) * inv) << 16);
+      *reinterpret_cast<uint2 *>(out + base + 2048 * j + 256 * w) = make_uint2(lo, hi);
+    }
+}
+
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s) {
   MOE_LAUNCH("k_combine", k_combine, dim3((unsigned)a.T), dim3(256), 0, s, a);
   return hipSuccess;
@@ -92,7 +149,20 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t s) {
 
 hipError_t launch_rmsnorm(const void *h, int64_t T, int H, float eps, bool bf16, void *out,
                           hipStream_t s) {
-  if (bf16)
+  const dim3 g4((unsigned)((T + 3) / 4));
+  const uint16_t *hb = static_cast<const uint16_t *>(h);
+  uint16_t *ob = static_cast<uint16_t *>(out);
+  // the one-wave-per-row kernel loads and stores 8-byte pieces
+  const bool rows = bf16 && !(((uintptr_t)h | (uintptr_t)out) & 7);
+  if (rows && H == 2048)
+    MOE_LAUNCH("k_rmsnorm_rows", k_rmsnorm_rows<1>, g4, dim3(256), 0, s, hb, T, eps, ob);
+  else if (rows && H == 4096)
+    MOE_LAUNCH("k_rmsnorm_rows", k_rmsnorm_rows<2>, g4, dim3(256), 0, s, hb, T, eps, ob);
+  else if (rows && H == 6144)
+    MOE_LAUNCH("k_rmsnorm_rows", k_rmsnorm_rows<3>, g4, dim3(256), 0, s, hb, T, eps, ob);
+  else if (rows && H == kNormMaxH)
+    MOE_LAUNCH("k_rmsnorm_rows", k_rmsnorm_rows<4>, g4, dim3(256), 0, s, hb, T, eps, ob);
+  else if (bf16)
     MOE_LAUNCH("k_rmsnorm", k_rmsnorm<true>, dim3((unsigned)T), dim3(512), 0, s, h, H, eps, out);
   else
     MOE_LAUNCH("k_rmsnorm", k_rmsnorm<false>, dim3((unsigned)T), dim3(512), 0, s, h, H, eps,
