@@ -423,7 +423,8 @@ def test_empty_prefill_is_noop(M, big):
 
 
 def test_rmsnorm(M):
-    announce("moe_rmsnorm bf16 and fp32, T=33 H=2048, and H=320 (a partial 2048 stretch)")
+    announce("moe_rmsnorm bf16 and fp32, T=33 H=2048, H=320 (a partial 2048 stretch), "
+             "H=4096/6144/8192 T=9 in place and misaligned")
     eps = float(np.float32(1e-6))
     for H in (2048, 320):
         hb = synth.bf16_activations(41 + H, (33, H))
@@ -432,6 +433,23 @@ def test_rmsnorm(M):
         # fp64 arithmetic rounded once: the bits of the oracle's bf16 rounding
         got = out.view(torch.int16).cpu().numpy().view(np.uint16)
         assert np.array_equal(got, oracle.round_bf16(oracle.rmsnorm(hb, eps)))
+    # the one-wave-per-row kernel at every width it takes (2048 * n up to 8192, a row count
+    # that leaves a partial workgroup), in place, and the same rows at an address that is not
+    # 8-byte aligned (the 512-thread kernel): all give the oracle's bits
+    for H in (4096, 6144, 8192):
+        hb = synth.bf16_activations(47 + H, (9, H))
+        want = oracle.round_bf16(oracle.rmsnorm(hb, eps))
+        hd = bf16_dev(M, hb)
+        out = M.moe_rmsnorm(hd, eps)
+        M.moe_rmsnorm(hd, eps, out=hd)
+        flat = torch.zeros(9 * H + 1, dtype=torch.bfloat16, device=DEV)
+        shifted = flat[1:].view(9, H)
+        shifted.copy_(bf16_dev(M, hb))
+        M.moe_rmsnorm(shifted, eps, out=shifted)
+        torch.cuda.synchronize()
+        for got in (out, hd, shifted):
+            assert np.array_equal(got.contiguous().view(torch.int16).cpu().numpy().view(np.uint16),
+                                  want), H
     hf = np.random.default_rng(42).standard_normal((33, 2048)).astype(np.float32)
     outf = M.moe_rmsnorm(torch.from_numpy(hf).to(DEV), eps)
     ref = oracle.rmsnorm(hf, eps)
