@@ -368,7 +368,7 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
   // persistent launch: the workgroup's next ticket, requested here (few registers live) and
   // stored to its LDS word once the tile is written, so its latency hides behind the epilogue
   int32_t tn = 0;
-  if (tk && tid == 0) tn = __hip_atomic_fetch_add(tk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tk && tid == 0) tn = __hip_atomic_fetch_add(tk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   if constexpr (kGateUp) {
     // h: rows x 128 columns, stored in the chunk order of the fp16 operand rows (h is the
     // down GEMM's A operand)
@@ -384,10 +384,18 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
         ht[row * HP + pos] = (_Float16)(silu_fast(acc[m][0][r]) * acc[m][1][r]);
       }
     __syncthreads();
-    for (int rr = tid >> 4; rr < nvalid; rr += 16)
-      *reinterpret_cast<uint4 *>(a.h16 + (size_t)(slot0 + rr) * a.I + n_tile * (BNW / 2) +
-                                 8 * (tid & 15)) =
-          *reinterpret_cast<const uint4 *>(ht + rr * HP + 8 * (tid & 15));
+    // In the persistent launch a down tile may run on another XCD, whose L2 does not see
+    // this one's: h is written through to memory (sc1), where that L2 fetches it.
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    for (int rr = tid >> 4; rr < nvalid; rr += 16) {
+      uint16_t *dst = a.h16 + (size_t)(slot0 + rr) * a.I + n_tile * (BNW / 2) + 8 * (tid & 15);
+      const u32x4_t v = *reinterpret_cast<const u32x4_t *>(ht + rr * HP + 8 * (tid & 15));
+      if (tk)
+        asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"((uint64_t)(uintptr_t)dst),
+                     "v"(v) : "memory");
+      else
+        *reinterpret_cast<u32x4_t *>(dst) = v;
+    }
   } else if constexpr (kComb) {
     // y[t] = shared(x_t) + sum_j out[slot_of[t, j]] (+ residual[t]) over this tile's 256
     // columns, fp32 in that order, bf16 out. The shared result of every row goes through LDS
@@ -559,20 +567,23 @@ __global__ __launch_bounds__(256, 2) void k_shared_down_combine(GroupedArgs a) {
 
 // gate/up and down of every tile in one persistent launch. The down GEMM of a tile needs all
 // of its rows' h, so as two launches the down work waits for the whole gate/up grid, and the
-// gate/up grid's last, partly filled round of workgroups leaves CUs idle. Here each XCD
-// works through its own queue: the tiles m = q, q + Q, q + 2Q, ... of the tile map (Q queues,
-// one per XCD; q is read from the XCC_ID register), first every gate/up item (tile, N
-// tile), then every down item. A workgroup takes the next item with an atomic ticket, so
-// only running workgroups hold work. A gate/up item writes its h rows, waits until the
-// stores are acknowledged and then counts itself done on the tile; a down item first waits
-// for its tile's count to reach the gate/up N tiles. Every workgroup that touches a tile's
-// h, ticket or count runs on the same XCD and so goes through one L2, where the atomics are
-// performed and the counts polled (device-scope loads miss L1); the h loads themselves may
-// go through L1, which cannot hold an older copy of those rows: nothing in the launch reads
-// them before they are complete, and L1 starts empty at each launch. Deadlock-free: gate/up
-// items wait for nothing, and a down item waits only for gate/up items with earlier tickets,
-// all taken by running workgroups. The waits are bounded anyway (kSpinTicks of the 100 MHz
-// clock, then the flag at kSyncErr is raised and the item computed as it stands).
+// gate/up grid's last, partly filled round of workgroups leaves CUs idle. Here the tiles are
+// dealt to one queue per XCD: queue q holds the tiles m = q, q + Q, q + 2Q, ... of the tile
+// map (Q queues), first every gate/up item (tile, N tile), then every down item. A workgroup
+// serves its own XCD's queue first (q is read from the XCC_ID register), so a tile's x rows,
+// weights and h mostly stay in one L2; once that queue is empty it serves the next queues in
+// turn, because equal shares of work do not finish together on every XCD. A workgroup takes
+// the next item of a queue with an atomic ticket, so only running workgroups hold work. A
+// gate/up item writes its h rows through to memory, waits until the stores are acknowledged
+// and then counts itself done on the tile; a down item first waits for its tile's count to
+// reach the gate/up N tiles. Tickets and counts are system-scope atomics and loads, performed
+// in memory, so workgroups on any XCD see the same values; a down item's h loads go through
+// its own L2 and L1, which hold no copy of those rows: nothing in the launch reads them
+// before they are complete, and the caches hold nothing older from before the launch.
+// Deadlock-free: gate/up items wait for nothing, and a down item waits only for gate/up items
+// of its queue with earlier tickets, all taken by running workgroups. The waits are bounded
+// anyway (kSpinTicks of the 100 MHz clock, then the flag at kSyncErr is raised and the item
+// computed as it stands).
 constexpr uint64_t kSpinTicks = 50000000ull;  // 0.5 s
 
 __global__ __launch_bounds__(256, 2) void k_grouped_fused(GroupedArgs a) {
@@ -580,18 +591,32 @@ __global__ __launch_bounds__(256, 2) void k_grouped_fused(GroupedArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const bool lead = threadIdx.x == 0;
   const int nq = a.n_queues;
-  const int q = (int)(__builtin_amdgcn_s_getreg(20 | (31 << 11)) & (uint32_t)(nq - 1));
   const int nt = *a.n_tiles;
-  const int ntq = nt > q ? (nt - 1 - q) / nq + 1 : 0;  // tiles of this queue
   const int nNg = a.I / (BNW / 2), nNd = a.H / BNW;
-  const int n_gu = ntq * nNg, n_all = n_gu + ntq * nNd;
-  int32_t *ticket = a.sync + kSyncQStride * q;
   int32_t *s_t = reinterpret_cast<int32_t *>(smem + kTicketOff);  // the next ticket
-  if (lead) *s_t = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // the queue served now (this XCD's first), and the queues not yet found empty
+  int cq = (int)(__builtin_amdgcn_s_getreg(20 | (31 << 11)) & (uint32_t)(nq - 1)), left = nq;
+  if (lead)
+    *s_t = __hip_atomic_fetch_add(a.sync + kSyncQStride * cq, 1, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_SYSTEM);
   __syncthreads();
   int t = __builtin_amdgcn_readfirstlane(*s_t);  // uniform: addresses stay scalar
   __syncthreads();
-  while (t < n_all) {
+  while (true) {
+    const int ntq = nt > cq ? (nt - 1 - cq) / nq + 1 : 0;  // tiles of queue cq
+    const int n_gu = ntq * nNg, n_all = n_gu + ntq * nNd;
+    if (t >= n_all) {
+      // queue cq is empty: the next one
+      if (--left == 0) break;
+      cq = (cq + 1) & (nq - 1);
+      if (lead)
+        *s_t = __hip_atomic_fetch_add(a.sync + kSyncQStride * cq, 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_SYSTEM);
+      __syncthreads();
+      t = __builtin_amdgcn_readfirstlane(*s_t);
+      __syncthreads();
+      continue;
+    }
     // The arguments are read through an opaque copy of the kernel-argument pointer, so that
     // the compiler loads them per item (scalar loads) instead of holding every field and
     // what it derives from them in SGPRs across the loop.
@@ -599,25 +624,25 @@ __global__ __launch_bounds__(256, 2) void k_grouped_fused(GroupedArgs a) {
     KArgs *ap = (KArgs *)__builtin_amdgcn_kernarg_segment_ptr();
     asm volatile("" : "+s"(ap));
     const GroupedArgs &ai = *(const GroupedArgs *)ap;
-    int32_t *tk = ai.sync + kSyncQStride * q;
+    int32_t *tk = ai.sync + kSyncQStride * cq;
     bool ran;
     if (t < n_gu) {
-      const int i = t / nNg, m = q + nq * i;
+      const int i = t / nNg, m = cq + nq * i;
       ran = grouped_item<true, false>(ai, smem, m, t - i * nNg, wave, tk);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's h stores are in L2
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's h stores are in memory
       __syncthreads();
       if (lead)
         __hip_atomic_fetch_add(ai.sync + kSyncDone + m, 1, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+                               __HIP_MEMORY_SCOPE_SYSTEM);
     } else {
-      const int u = t - n_gu, i = u / nNd, m = q + nq * i;
+      const int u = t - n_gu, i = u / nNd, m = cq + nq * i;
       if (lead) {
         int32_t *done = ai.sync + kSyncDone + m, *err = ai.sync + kSyncErr;
         const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-        while (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nNg) {
-          if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
+        while (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) < nNg) {
+          if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)) break;
           if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
-            __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
             break;
           }
           __builtin_amdgcn_s_sleep(2);
@@ -628,7 +653,8 @@ __global__ __launch_bounds__(256, 2) void k_grouped_fused(GroupedArgs a) {
     }
     // a skipped item (the shared expert's down tiles, whose launch is the fused combine)
     // took no ticket
-    if (!ran && lead) *s_t = __hip_atomic_fetch_add(tk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!ran && lead)
+      *s_t = __hip_atomic_fetch_add(tk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     __syncthreads();  // the next ticket is in LDS
     t = __builtin_amdgcn_readfirstlane(*s_t);
     __syncthreads();  // every wave has read it before it is replaced
