@@ -50,8 +50,10 @@ MOE_DEV uint16_t f64_to_bf16_rne(double v) {
   if (mag > 0x7FF0000000000000ull) return 0x7FC0;                        // NaN
   if (mag >= 0x47F0000000000000ull) return (uint16_t)((u >> 48) & 0x8000u) | 0x7F80u;  // >= 2^128
   if (mag < 0x3810000000000000ull) {                                     // |v| < 2^-126
-    const double r = __builtin_rint(v * 0x1p133) * 0x1p-133;
-    return (uint16_t)(__float_as_uint((float)r) >> 16);
+    // the nearest multiple m of 2^-133 (0..128; 128 is the smallest normal), built as bits
+    // so that no fp32 subnormal is formed; a value that rounds to zero keeps its sign
+    const uint32_t m = (uint32_t)__builtin_rint(__longlong_as_double((long long)mag) * 0x1p133);
+    return (uint16_t)(((u >> 48) & 0x8000u) | m);
   }
   u += 0x00000FFFFFFFFFFFull + ((u >> 45) & 1ull);
   u &= ~0x00001FFFFFFFFFFFull;

@@ -450,6 +450,24 @@ def test_rmsnorm(M):
         for got in (out, hd, shifted):
             assert np.array_equal(got.contiguous().view(torch.int16).cpu().numpy().view(np.uint16),
                                   want), H
+    # degenerate rows on both kernels (H = 2048: one wave per row; H = 320: the 512-thread
+    # kernel): all zeros (the output is zero), one non-zero element, magnitudes near the bf16
+    # maximum (their squares overflow fp32, not fp64), bf16 subnormal inputs, alternating
+    # signs, and a row whose outputs land on the bf16 subnormal grid or round to a signed zero
+    for H in (2048, 320):
+        rows = np.zeros((6, H), np.float32)
+        rows[1, H // 3] = -3.0
+        rows[2] = np.where(np.arange(H) % 2, 3.0e38, -2.5e38)
+        rows[3] = 1.0e-39 * (1 + np.arange(H) % 7)
+        rows[4] = np.where(np.arange(H) % 3, 1.0, -1.0)
+        rows[5, :9] = [1.0e30, 1.0e-30, -7.0, 0.0, 2.0, -1.0e-30, 1.0e-10, -2.0e-12, 3.0e-9]
+        hb = synth.f32_to_bf16_bits(rows)
+        want = oracle.round_bf16(oracle.rmsnorm(hb, eps))
+        assert not np.any(want[0]) and np.any(want[3])
+        assert want[5, 5] == 0x8000 and 0 < want[5, 6] < 0x80 and want[5, 7] >> 15
+        got = M.moe_rmsnorm(bf16_dev(M, hb), eps)
+        torch.cuda.synchronize()
+        assert np.array_equal(got.view(torch.int16).cpu().numpy().view(np.uint16), want), H
     hf = np.random.default_rng(42).standard_normal((33, 2048)).astype(np.float32)
     outf = M.moe_rmsnorm(torch.from_numpy(hf).to(DEV), eps)
     ref = oracle.rmsnorm(hf, eps)
