@@ -11,6 +11,8 @@ distinct workload shapes" and "Dequantize weights during matrix multiplication")
 Bar: routing ids/weights exact off the tie window, grouping bit-exact, outputs within
 1e-4 (fp32) or 2e-2 (bf16) of the output RMS.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -412,6 +414,47 @@ def test_model_width_layers_other_routing(M, E, k, S):
     check_routing(layer, xb, g["topk_ids"], g["topk_w"], delta_for(2048))
     check_grouping(layer, g)
     assert rel_err(y_np(y)[sure], ref[sure]) <= BF16_TOL
+
+
+def test_bias_only_routing_fills_eight_experts(M, big):
+    # Zero router weights and a strictly decreasing router bias: every logit is its bias
+    # exactly, so every token selects experts 0..7 with the weights softmax(b_0..b_7) (the
+    # top-k and its renormalisation pinned by the definition, no rounding in the logits).
+    # At T = 4096 those eight experts hold all 32,768 routed rows (32 full tiles each) and
+    # the other 248 none: the far end of uneven expert groups ("Qwen creates three distinct
+    # workload shapes"). Rows of x = 0 are mixed in; with no biases inside the experts their
+    # output is exactly zero. Every row of the prefill, the small-T path and decode tokens
+    # are compared with the oracle.
+    layer0, _ = big
+    E = layer0.n_experts
+    layer = dataclasses.replace(layer0, router_w=np.zeros_like(layer0.router_w),
+                                router_b=(-0.25 * np.arange(E)).astype(np.float32))
+    dl = M.DeviceLayer.from_host(layer, DEV)
+    T = 4096
+    announce(f"moe_prefill/moe_decode int4 bias-only routing, T={T}, all rows to experts 0..7")
+    xb = synth.prefill_x(T, seed=23)
+    zero_rows = np.array([0, 17, 2048, T - 1])
+    xb[zero_rows] = 0
+    buf = M.route_buffers(dl, T, DEV)
+    y = M.moe_prefill(dl, bf16_dev(M, xb), route_out=buf)
+    y5 = M.moe_prefill(dl, bf16_dev(M, xb[:5]))          # small-T kernels
+    ws = M.workspace(dl, 1)
+    dec = [M.moe_decode(dl, bf16_dev(M, xb[t:t + 1]), ws=ws) for t in (0, 1, 2)]
+    torch.cuda.synchronize()
+    g = to_np(buf)
+    assert np.array_equal(g["topk_ids"], np.tile(np.arange(8, dtype=g["topk_ids"].dtype), (T, 1)))
+    assert check_routing(layer, xb, g["topk_ids"], g["topk_w"], delta_for(2048)) == 0
+    check_grouping(layer, g)
+    assert np.array_equal(g["counts"], np.r_[np.full(8, T), np.zeros(E - 8)].astype(g["counts"].dtype))
+    ref = oracle.moe(layer, xb)
+    got = y_np(y)
+    assert np.all(got[zero_rows] == 0) and np.all(ref[zero_rows] == 0)
+    assert rel_err(got, ref) <= BF16_TOL
+    assert rel_err(y_np(y5), ref[:5]) <= BF16_TOL
+    assert np.all(y_np(y5)[0] == 0)
+    assert np.all(y_np(dec[0]) == 0)
+    for t in (1, 2):
+        assert rel_err(y_np(dec[t])[0], ref[t]) <= BF16_TOL, t
 
 
 def test_empty_prefill_is_noop(M, big):
