@@ -121,6 +121,9 @@ __global__ __launch_bounds__(256) void k_rmsnorm_rows(const uint16_t *h, int64_t
       p[w] = __builtin_fma(e3, e3, p[w]);
     }
   }
+  // the xor butterfly over the wave (32, 16, 8, 4, 2, 1; the pairs of block512_sum_f64),
+  // the eight chains side by side: here the crossbar's latency overlaps across the chains,
+  // and __shfl_xor measured faster than the DPP form that a single chain prefers
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1)
 #pragma unroll

@@ -43,21 +43,24 @@ MOE_DEV uint32_t pack_bf16x2(float lo, float hi) {
 // the mantissa is cut at 7 explicit bits with the usual carry trick on the integer bits,
 // which is exact; below 2^-126 the bf16 subnormal grid (spacing 2^-133) applies, past the
 // bf16 range the result is +-inf. The rounded value has at most 8 significant bits, so the
-// conversion to fp32 that extracts its top half is exact.
+// conversion to fp32 that extracts its top half is exact (and gives inf at or past 2^128).
+// Both results are formed and one is selected, with no branch: callers round many values
+// per thread, and a branch per value costs more than the few extra instructions.
 MOE_DEV uint16_t f64_to_bf16_rne(double v) {
-  uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
   const uint64_t mag = u & 0x7FFFFFFFFFFFFFFFull;
-  if (mag > 0x7FF0000000000000ull) return 0x7FC0;                        // NaN
-  if (mag >= 0x47F0000000000000ull) return (uint16_t)((u >> 48) & 0x8000u) | 0x7F80u;  // >= 2^128
-  if (mag < 0x3810000000000000ull) {                                     // |v| < 2^-126
-    // the nearest multiple m of 2^-133 (0..128; 128 is the smallest normal), built as bits
-    // so that no fp32 subnormal is formed; a value that rounds to zero keeps its sign
-    const uint32_t m = (uint32_t)__builtin_rint(__longlong_as_double((long long)mag) * 0x1p133);
-    return (uint16_t)(((u >> 48) & 0x8000u) | m);
-  }
-  u += 0x00000FFFFFFFFFFFull + ((u >> 45) & 1ull);
-  u &= ~0x00001FFFFFFFFFFFull;
-  return (uint16_t)(__float_as_uint((float)__longlong_as_double((long long)u)) >> 16);
+  const uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
+  // |v| >= 2^-126
+  const uint64_t r =
+      (mag + 0x00000FFFFFFFFFFFull + ((mag >> 45) & 1ull)) & ~0x00001FFFFFFFFFFFull;
+  const uint32_t nb = __float_as_uint((float)__longlong_as_double((long long)r)) >> 16;
+  // |v| < 2^-126: the nearest multiple m of 2^-133 (0..128; 128 is the smallest normal),
+  // built as bits so that no fp32 subnormal is formed; a value that rounds to zero keeps its
+  // sign (the clamp only keeps the conversion defined for the values this branch discards)
+  const uint32_t sb = (uint32_t)__builtin_fmin(
+      __builtin_rint(__longlong_as_double((long long)mag) * 0x1p133), 256.0);
+  const uint32_t m = mag < 0x3810000000000000ull ? sb : nb;
+  return mag > 0x7FF0000000000000ull ? (uint16_t)0x7FC0 : (uint16_t)(sign | m);  // NaN
 }
 
 // Round to nearest even fp16 (v_cvt_pk_f16_f32). Values outside the fp16 range
@@ -210,6 +213,27 @@ MOE_DEV T xor_sum(T v) {
   }
 }
 
+// The same step for a double: both of its 32-bit halves take the same lane permutation.
+template <int M>
+MOE_DEV double xor_sum_f64(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+  auto join = [](uint32_t l, uint32_t h) {
+    return __longlong_as_double((long long)(((uint64_t)h << 32) | l));
+  };
+  if constexpr (M == 16) {
+    const auto pl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto ph = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    return join((uint32_t)pl[0], (uint32_t)ph[0]) + join((uint32_t)pl[1], (uint32_t)ph[1]);
+  } else if constexpr (M == 32) {
+    const auto pl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto ph = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    return join((uint32_t)pl[0], (uint32_t)ph[0]) + join((uint32_t)pl[1], (uint32_t)ph[1]);
+  } else {
+    return v + join(xor_peer_dpp<M>(lo), xor_peer_dpp<M>(hi));
+  }
+}
+
 // Sum over the wave, reduction order 32, 16, 8, 4, 2, 1 (xor 4 as a rotation is exact here:
 // after the xor-8 step v is equal on lanes l and l ^ 8).
 MOE_DEV float wave_sum(float v) {
@@ -267,11 +291,17 @@ MOE_DEV uint32_t wave_min_u32(uint32_t v) {
 }
 
 // Sum over a workgroup of 512 threads of each thread's fp64 partial, in one fixed order:
-// xor butterfly inside each wave (every lane ends with the same bits), then the eight wave
-// totals in wave order. red8 holds 8 doubles of LDS. Every thread returns the total.
+// xor butterfly inside each wave (32, 16, 8, 4, 2, 1; every lane ends with the same bits),
+// then the eight wave totals in wave order. red8 holds 8 doubles of LDS. Every thread
+// returns the total. The butterfly moves the doubles by DPP and lane swaps instead of the
+// LDS crossbar: it is one dependent chain on the stacked decode step's critical path.
 MOE_DEV double block512_sum_f64(double v, double *red8) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  v = xor_sum_f64<32>(v);
+  v = xor_sum_f64<16>(v);
+  v = xor_sum_f64<8>(v);
+  v = xor_sum_f64<4>(v);
+  v = xor_sum_f64<2>(v);
+  v = xor_sum_f64<1>(v);
   if ((threadIdx.x & 63) == 0) red8[threadIdx.x >> 6] = v;
   __syncthreads();
   double t = red8[0];
