@@ -416,6 +416,27 @@ def test_model_width_layers_other_routing(M, E, k, S):
     assert rel_err(y_np(y)[sure], ref[sure]) <= BF16_TOL
 
 
+@pytest.mark.parametrize("which,T", [("uniform", 4096), ("skewed", 4096), ("uniform", 777)])
+def test_route_api_int4_full_width(M, big, skewed, which, T):
+    # moe_route alone on the model-width layer (bf16 activations, the MFMA router): ids and
+    # weights against the oracle off the tie window, the grouping bit for bit, and the same
+    # routing as moe_prefill's route_out on the same input
+    layer, dl = big if which == "uniform" else skewed
+    announce(f"moe_route int4 H=2048 E=256 k=8 {which} T={T}")
+    xb = synth.prefill_x(T, seed=31)
+    xd = bf16_dev(M, xb)
+    g = to_np(M.moe_route(dl, xd))
+    buf = M.route_buffers(dl, T, DEV)
+    M.moe_prefill(dl, xd, route_out=buf)
+    torch.cuda.synchronize()
+    gp = to_np(buf)
+    unsure = check_routing(layer, xb, g["topk_ids"], g["topk_w"], delta_for(2048))
+    assert unsure <= max(2, T // 200)
+    check_grouping(layer, g)
+    for key in g:
+        assert np.array_equal(g[key], gp[key]), key
+
+
 def test_bias_only_routing_fills_eight_experts(M, big):
     # Zero router weights and a strictly decreasing router bias: every logit is its bias
     # exactly, so every token selects experts 0..7 with the weights softmax(b_0..b_7) (the
