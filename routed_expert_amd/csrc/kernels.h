@@ -23,6 +23,11 @@ bool prof_events(const char *name, hipEvent_t *start, hipEvent_t *stop);
     if (moe_err_ != hipSuccess) return moe_err_;                                            \
   } while (0)
 
+// Routing blocks per chunk of the two-level count scan, and the call size (in routing blocks)
+// above which it is used: the grouping kernel's reads then grow with T instead of T^2, at the
+// price of one more launch (k_chunk_sum).
+constexpr int kChunkBlocks = 64;
+constexpr int kChunkFromBlocks = 4 * kChunkBlocks;
 struct RouteArgs {
   bool bf16;
   const void *x;
@@ -36,6 +41,8 @@ struct RouteArgs {
   int32_t *ids;           // [T, k]
   float *w;               // [T, k]
   int32_t *blk;           // [NB, E] per-block counts, then per-block bases
+  int32_t *chunk = nullptr;  // [ceil(NB / kChunkBlocks), E] per-chunk counts; set (by the
+                             // host) only when NB > kChunkFromBlocks
   int32_t *offsets;       // [E + 2]
   int32_t *counts_user;   // [E] or null
   int32_t *offsets_user;  // [E + 1] or null

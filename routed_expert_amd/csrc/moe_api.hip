@@ -86,7 +86,7 @@ moe_status check_layer(const moe_layer *L) {
 // Workspace layout: the batch-1 decode buffers first, then the T-dependent region.
 struct Plan {
   size_t dec_logits, dec_ids, dec_z, dec_h, dec_xn, st_z, st_ids, st_w, st_h;
-  size_t logits, planes, ids, w, blk, offsets, sorted, slot, slot_w, x16, tiles, ntiles,
+  size_t logits, planes, ids, w, blk, chunk, offsets, sorted, slot, slot_w, x16, tiles, ntiles,
       h, out, sync;
   size_t total;
   int max_tiles;
@@ -140,6 +140,7 @@ Plan make_plan(const moe_layer *L, int64_t T, int tile_shift = 0) {
   p.ids = take(Tn * k * 4);
   p.w = take(Tn * k * 4);
   p.blk = take(NB * E * 4);
+  p.chunk = take((NB + moe::kChunkBlocks - 1) / moe::kChunkBlocks * E * 4);
   p.offsets = take((E + 2) * 4);
   p.sorted = take(k * Tn * 4);
   p.slot = take(k * Tn * 4);
@@ -275,6 +276,9 @@ void route_targets(moe::RouteArgs &a, const Plan &p, void *ws, const moe_route_o
   a.logits = at<float>(ws, p.logits);
   if (!a.planes_ready) a.router_planes = at<uint16_t>(ws, p.planes);
   a.blk = at<int32_t>(ws, p.blk);
+  a.chunk = (a.T + moe::kRouteBlock - 1) / moe::kRouteBlock > moe::kChunkFromBlocks
+                ? at<int32_t>(ws, p.chunk)
+                : nullptr;
   a.offsets = at<int32_t>(ws, p.offsets);
   a.tiles = at<int2>(ws, p.tiles);
   a.n_tiles = at<int32_t>(ws, p.ntiles);

@@ -420,12 +420,29 @@ MOE_DEV int group_tables(int run, bool write, int E, int T, int S, int32_t *__re
   return off;
 }
 
+// Per-chunk expert counts for long calls: workgroup c adds the block rows of chunk c
+// (kChunkBlocks routing blocks), thread e its expert's column, in block order.
+__global__ __launch_bounds__(256) void k_chunk_sum(const int32_t *__restrict__ blk_cnt, int NB,
+                                                   int E, int32_t *__restrict__ chunk_cnt) {
+  const int c = blockIdx.x, e = threadIdx.x;
+  if (e >= E) return;
+  const int b0 = c * kChunkBlocks, b1 = min(NB, b0 + kChunkBlocks);
+  int v[kChunkBlocks];
+#pragma unroll
+  for (int i = 0; i < kChunkBlocks; ++i) v[i] = b0 + i < b1 ? blk_cnt[(size_t)(b0 + i) * E + e] : 0;
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < kChunkBlocks; ++i) sum += v[i];
+  chunk_cnt[(size_t)c * E + e] = sum;
+}
+
 // Scan and scatter in one kernel, one workgroup per routing block of 64 tokens: thread e sums
 // the block counts of expert e over all blocks (its total) and over the blocks before this one
 // (its base), every workgroup forms the same offsets from the totals (same inputs, same
 // order), workgroup 0 also writes the tables, and the block's assignments are placed as in
 // k_scatter. The histogram is only read, so the workgroups need no ordering between them.
 __global__ __launch_bounds__(256) void k_group(const int32_t *__restrict__ blk_cnt,
+                                               const int32_t *__restrict__ chunk_cnt,
                                                const int32_t *__restrict__ ids,
                                                const float *__restrict__ w, int NB, int E, int T,
                                                int k, int S, int32_t *__restrict__ offsets,
@@ -442,16 +459,35 @@ __global__ __launch_bounds__(256) void k_group(const int32_t *__restrict__ blk_c
   const int b = blockIdx.x, t0 = b * kRouteBlock, tid = threadIdx.x;
   // the fused GEMM launch's queue words start at zero
   for (int i = b * 256 + tid; i < n_sync; i += NB * 256) sync[i] = 0;
+  // thread e: its expert's total over all blocks (run) and over the blocks before this one
+  // (base). For long calls k_chunk_sum has added the block rows per chunk of kChunkBlocks
+  // blocks: the totals then come from the chunk rows, and the base from the chunks before
+  // this block's chunk plus at most kChunkBlocks - 1 block rows, so every workgroup reads
+  // about T / 4096 + 64 rows instead of all T / 64. Integer sums: the same values either
+  // way.
   int run = 0, base = 0;
   if (tid < E) {
-    for (int b0 = 0; b0 < NB; b0 += 32) {
+    const int32_t *rows = chunk_cnt ? chunk_cnt : blk_cnt;
+    const int nrows = chunk_cnt ? (NB + kChunkBlocks - 1) / kChunkBlocks : NB;
+    const int below = chunk_cnt ? b / kChunkBlocks : b;  // rows that precede this block
+    for (int b0 = 0; b0 < nrows; b0 += 32) {
       int c[32];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) c[i] = b0 + i < NB ? blk_cnt[(size_t)(b0 + i) * E + tid] : 0;
+      for (int i = 0; i < 32; ++i) c[i] = b0 + i < nrows ? rows[(size_t)(b0 + i) * E + tid] : 0;
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
-        base += b0 + i < b ? c[i] : 0;
+        base += b0 + i < below ? c[i] : 0;
         run += c[i];
+      }
+    }
+    if (chunk_cnt) {
+      const int b1 = below * kChunkBlocks;  // first block of this block's chunk
+      for (int b0 = b1; b0 < b; b0 += 32) {
+        int c[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) c[i] = b0 + i < b ? blk_cnt[(size_t)(b0 + i) * E + tid] : 0;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) base += c[i];
       }
     }
   }
@@ -549,7 +585,11 @@ hipError_t launch_route_prefill(const RouteArgs &a, hipStream_t s) {
   const hipError_t e = launch_route_topk(a, s);
   if (e != hipSuccess) return e;
   const int NB = (int)((a.T + kRouteBlock - 1) / kRouteBlock);
-  MOE_LAUNCH("k_group", k_group, dim3(NB), dim3(256), 0, s, a.blk, a.ids, a.w, NB, a.E, (int)a.T,
+  if (a.chunk)
+    MOE_LAUNCH("k_chunk_sum", k_chunk_sum, dim3((unsigned)((NB + kChunkBlocks - 1) / kChunkBlocks)),
+               dim3(256), 0, s, a.blk, NB, a.E, a.chunk);
+  MOE_LAUNCH("k_group", k_group, dim3(NB), dim3(256), 0, s, a.blk, a.chunk, a.ids, a.w, NB, a.E,
+             (int)a.T,
              a.k, a.S, a.offsets, a.counts_user, a.offsets_user, a.tiles, a.n_tiles, a.tile_shift,
              gemm_fill(a.I), a.sorted_tok, a.slot_of, a.slot_w, a.sync, a.n_sync);
   return hipSuccess;

@@ -436,11 +436,13 @@ def test_model_width_layers_other_routing(M, E, k, S):
     assert rel_err(y_np(y)[sure], ref[sure]) <= BF16_TOL
 
 
-@pytest.mark.parametrize("which,T", [("uniform", 4096), ("skewed", 4096), ("uniform", 777)])
+@pytest.mark.parametrize("which,T", [("uniform", 4096), ("skewed", 4096), ("uniform", 777),
+                                     ("skewed", 20000)])
 def test_route_api_int4_full_width(M, big, skewed, which, T):
     # moe_route alone on the model-width layer (bf16 activations, the MFMA router): ids and
     # weights against the oracle off the tie window, the grouping bit for bit, and the same
-    # routing as moe_prefill's route_out on the same input
+    # routing as moe_prefill's route_out on the same input. T = 20,000 is 313 routing blocks:
+    # the grouping counts per chunk of 64 blocks (five chunks, the last one partial)
     layer, dl = big if which == "uniform" else skewed
     announce(f"moe_route int4 H=2048 E=256 k=8 {which} T={T}")
     xb = synth.prefill_x(T, seed=31)
