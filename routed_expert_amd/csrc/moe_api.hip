@@ -140,7 +140,6 @@ Plan make_plan(const moe_layer *L, int64_t T, int tile_shift = 0) {
   p.ids = take(Tn * k * 4);
   p.w = take(Tn * k * 4);
   p.blk = take(NB * E * 4);
-  p.chunk = take((NB + moe::kChunkBlocks - 1) / moe::kChunkBlocks * E * 4);
   p.offsets = take((E + 2) * 4);
   p.sorted = take(k * Tn * 4);
   p.slot = take(k * Tn * 4);
@@ -157,6 +156,7 @@ Plan make_plan(const moe_layer *L, int64_t T, int tile_shift = 0) {
     p.h = take((k + S) * Tn * I * 4);
     p.slot_w = p.x16 = p.out = p.sync = off;
   }
+  p.chunk = take((NB + moe::kChunkBlocks - 1) / moe::kChunkBlocks * E * 4);  // long calls
   p.total = off;
   return p;
 }

@@ -441,6 +441,7 @@ __global__ __launch_bounds__(256) void k_chunk_sum(const int32_t *__restrict__ b
 // (its base), every workgroup forms the same offsets from the totals (same inputs, same
 // order), workgroup 0 also writes the tables, and the block's assignments are placed as in
 // k_scatter. The histogram is only read, so the workgroups need no ordering between them.
+template <bool kChunked>
 __global__ __launch_bounds__(256) void k_group(const int32_t *__restrict__ blk_cnt,
                                                const int32_t *__restrict__ chunk_cnt,
                                                const int32_t *__restrict__ ids,
@@ -466,29 +467,35 @@ __global__ __launch_bounds__(256) void k_group(const int32_t *__restrict__ blk_c
   // about T / 4096 + 64 rows instead of all T / 64. Integer sums: the same values either
   // way.
   int run = 0, base = 0;
-  if (tid < E) {
-    const int32_t *rows = chunk_cnt ? chunk_cnt : blk_cnt;
-    const int nrows = chunk_cnt ? (NB + kChunkBlocks - 1) / kChunkBlocks : NB;
-    const int below = chunk_cnt ? b / kChunkBlocks : b;  // rows that precede this block
-    for (int b0 = 0; b0 < nrows; b0 += 32) {
+  if (tid < E && !kChunked) {
+    for (int b0 = 0; b0 < NB; b0 += 32) {
       int c[32];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) c[i] = b0 + i < nrows ? rows[(size_t)(b0 + i) * E + tid] : 0;
+      for (int i = 0; i < 32; ++i) c[i] = b0 + i < NB ? blk_cnt[(size_t)(b0 + i) * E + tid] : 0;
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
-        base += b0 + i < below ? c[i] : 0;
+        base += b0 + i < b ? c[i] : 0;
         run += c[i];
       }
     }
-    if (chunk_cnt) {
-      const int b1 = below * kChunkBlocks;  // first block of this block's chunk
-      for (int b0 = b1; b0 < b; b0 += 32) {
-        int c[32];
+  } else if (kChunked && tid < E) {
+    const int NC = (NB + kChunkBlocks - 1) / kChunkBlocks, cb = b / kChunkBlocks;
+    for (int c0 = 0; c0 < NC; c0 += 32) {
+      int c[32];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) c[i] = b0 + i < b ? blk_cnt[(size_t)(b0 + i) * E + tid] : 0;
+      for (int i = 0; i < 32; ++i) c[i] = c0 + i < NC ? chunk_cnt[(size_t)(c0 + i) * E + tid] : 0;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) base += c[i];
+      for (int i = 0; i < 32; ++i) {
+        base += c0 + i < cb ? c[i] : 0;
+        run += c[i];
       }
+    }
+    for (int b0 = cb * kChunkBlocks; b0 < b; b0 += 32) {  // this chunk's blocks before b
+      int c[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) c[i] = b0 + i < b ? blk_cnt[(size_t)(b0 + i) * E + tid] : 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) base += c[i];
     }
   }
   const int off = group_tables(run, b == 0, E, T, S, offsets, counts_user, offsets_user, tiles,
@@ -585,13 +592,19 @@ hipError_t launch_route_prefill(const RouteArgs &a, hipStream_t s) {
   const hipError_t e = launch_route_topk(a, s);
   if (e != hipSuccess) return e;
   const int NB = (int)((a.T + kRouteBlock - 1) / kRouteBlock);
-  if (a.chunk)
+  if (a.chunk) {
     MOE_LAUNCH("k_chunk_sum", k_chunk_sum, dim3((unsigned)((NB + kChunkBlocks - 1) / kChunkBlocks)),
                dim3(256), 0, s, a.blk, NB, a.E, a.chunk);
-  MOE_LAUNCH("k_group", k_group, dim3(NB), dim3(256), 0, s, a.blk, a.chunk, a.ids, a.w, NB, a.E,
-             (int)a.T,
-             a.k, a.S, a.offsets, a.counts_user, a.offsets_user, a.tiles, a.n_tiles, a.tile_shift,
-             gemm_fill(a.I), a.sorted_tok, a.slot_of, a.slot_w, a.sync, a.n_sync);
+    MOE_LAUNCH("k_group", k_group<true>, dim3(NB), dim3(256), 0, s, a.blk, a.chunk, a.ids, a.w,
+               NB, a.E, (int)a.T, a.k, a.S, a.offsets, a.counts_user, a.offsets_user, a.tiles,
+               a.n_tiles, a.tile_shift, gemm_fill(a.I), a.sorted_tok, a.slot_of, a.slot_w, a.sync,
+               a.n_sync);
+  } else {
+    MOE_LAUNCH("k_group", k_group<false>, dim3(NB), dim3(256), 0, s, a.blk, a.chunk, a.ids, a.w,
+               NB, a.E, (int)a.T, a.k, a.S, a.offsets, a.counts_user, a.offsets_user, a.tiles,
+               a.n_tiles, a.tile_shift, gemm_fill(a.I), a.sorted_tok, a.slot_of, a.slot_w, a.sync,
+               a.n_sync);
+  }
   return hipSuccess;
 }
 
