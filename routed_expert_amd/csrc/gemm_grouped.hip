@@ -568,8 +568,10 @@ __global__ __launch_bounds__(256, 2) void k_shared_down_combine(GroupedArgs a) {
 // gate/up and down of every tile in one persistent launch. The down GEMM of a tile needs all
 // of its rows' h, so as two launches the down work waits for the whole gate/up grid, and the
 // gate/up grid's last, partly filled round of workgroups leaves CUs idle. Here the tiles are
-// dealt to one queue per XCD: queue q holds the tiles m = q, q + Q, q + 2Q, ... of the tile
-// map (Q queues), first every gate/up item (tile, N tile), then every down item. A workgroup
+// dealt to one queue per XCD in runs of kRun consecutive tiles of the map (run j to queue
+// j mod Q, Q queues), so that the tiles of an expert with several tiles mostly share one L2
+// for its weights; a queue holds first every gate/up item (tile, N tile), then every down
+// item. A workgroup
 // serves its own XCD's queue first (q is read from the XCC_ID register), so a tile's x rows,
 // weights and h mostly stay in one L2; once that queue is empty it serves the next queues in
 // turn, because equal shares of work do not finish together on every XCD. A workgroup takes
@@ -585,6 +587,7 @@ __global__ __launch_bounds__(256, 2) void k_shared_down_combine(GroupedArgs a) {
 // anyway (kSpinTicks of the 100 MHz clock, then the flag at kSyncErr is raised and the item
 // computed as it stands).
 constexpr uint64_t kSpinTicks = 50000000ull;  // 0.5 s
+constexpr int kRun = 4;  // consecutive tiles of the map dealt to one queue
 
 __global__ __launch_bounds__(256, 2) void k_grouped_fused(GroupedArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
@@ -603,7 +606,9 @@ __global__ __launch_bounds__(256, 2) void k_grouped_fused(GroupedArgs a) {
   int t = __builtin_amdgcn_readfirstlane(*s_t);  // uniform: addresses stay scalar
   __syncthreads();
   while (true) {
-    const int ntq = nt > cq ? (nt - 1 - cq) / nq + 1 : 0;  // tiles of queue cq
+    // tiles of queue cq: runs of kRun consecutive tiles of the map, run j to queue j % nq
+    const int per_round = nq * kRun, rounds = nt / per_round;
+    const int ntq = rounds * kRun + min(kRun, max(0, nt - rounds * per_round - cq * kRun));
     const int n_gu = ntq * nNg, n_all = n_gu + ntq * nNd;
     if (t >= n_all) {
       // queue cq is empty: the next one
@@ -627,7 +632,7 @@ __global__ __launch_bounds__(256, 2) void k_grouped_fused(GroupedArgs a) {
     int32_t *tk = ai.sync + kSyncQStride * cq;
     bool ran;
     if (t < n_gu) {
-      const int i = t / nNg, m = cq + nq * i;
+      const int i = t / nNg, m = (i / kRun) * (nq * kRun) + cq * kRun + i % kRun;
       ran = grouped_item<true, false>(ai, smem, m, t - i * nNg, wave, tk);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's h stores are in memory
       __syncthreads();
@@ -635,7 +640,7 @@ __global__ __launch_bounds__(256, 2) void k_grouped_fused(GroupedArgs a) {
         __hip_atomic_fetch_add(ai.sync + kSyncDone + m, 1, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_SYSTEM);
     } else {
-      const int u = t - n_gu, i = u / nNd, m = cq + nq * i;
+      const int u = t - n_gu, i = u / nNd, m = (i / kRun) * (nq * kRun) + cq * kRun + i % kRun;
       if (lead) {
         int32_t *done = ai.sync + kSyncDone + m, *err = ai.sync + kSyncErr;
         const uint64_t t0 = __builtin_amdgcn_s_memrealtime();

@@ -132,9 +132,9 @@ constexpr int kSyncDone = kSyncErr + 64;
 inline size_t sync_words(int max_tiles) { return (size_t)kSyncDone + (size_t)max_tiles; }
 hipError_t launch_grouped_gateup(const GroupedArgs &a, hipStream_t s);
 hipError_t launch_grouped_down(const GroupedArgs &a, hipStream_t s);
-// gate/up and down in one persistent launch (a.sync set): one queue of tiles per XCD, all
-// gate/up work first, a down tile starting once its rows' h is complete; workgroups serve
-// their own XCD's queue, then the others.
+// gate/up and down in one persistent launch (a.sync set): one queue of tiles per XCD (runs of
+// consecutive tiles), all gate/up work first, a down tile starting once its rows' h is
+// complete; workgroups serve their own XCD's queue, then the others.
 hipError_t launch_grouped_fused(const GroupedArgs &a, hipStream_t s);
 hipError_t launch_shared_down_combine(const GroupedArgs &a, hipStream_t s);
 // Separate dequantisation pass: every expert that received rows (and the shared expert)
