@@ -500,6 +500,41 @@ def test_bias_only_routing_fills_eight_experts(M, big):
         assert rel_err(y_np(dec[t])[0], ref[t]) <= BF16_TOL, t
 
 
+@pytest.mark.timeout(600)
+def test_prefill_beyond_32bit_offsets_runs_as_consecutive_calls(M, big):
+    # x of more than 2^32 bytes: the library runs the call as consecutive calls of at most
+    # t_max tokens (the GEMMs gather rows by 32-bit byte offsets). T = t_max + 200 with
+    # t_max = 1,048,512 at hidden 2048 (about 62 GB on the device). x is drawn on the GPU from
+    # a seeded generator; 40 rows (both sides of the split, the first and last rows, seeded
+    # rows between) against the oracle, and the rows around the split bit for bit against a
+    # separate 128-token call (a token's result does not depend on the rest of its call)
+    layer, dl = big
+    t_max = (0xFFFFFFFF // (2 * 2048)) & ~63
+    T = t_max + 200
+    announce(f"moe_prefill int4 T={T} (x beyond 2^32 bytes, split at {t_max})")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(77)
+    x = torch.randn((T, 2048), generator=g, device=DEV).to(torch.bfloat16)
+    y = M.moe_prefill(dl, x)
+    near = x[t_max - 64:t_max + 64].clone()
+    y_near = M.moe_prefill(dl, near)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(78)
+    rows = np.unique(np.concatenate([[0, t_max - 2, t_max - 1, t_max, t_max + 1, T - 1],
+                                     rng.choice(T, 34, replace=False)]))
+    rows_d = torch.from_numpy(rows).to(DEV)
+    xb = x[rows_d].view(torch.int16).cpu().numpy().view(np.uint16)
+    got = y_np(y[rows_d])
+    _, _, margin = oracle.route(layer, xb)
+    sure = margin >= delta_for(2048)
+    assert sure.sum() >= len(rows) - 2
+    ref = oracle.moe(layer, xb)
+    assert rel_err(got[sure], ref[sure]) <= BF16_TOL
+    assert torch.equal(y[t_max - 64:t_max + 64].view(torch.int16), y_near.view(torch.int16))
+    del x, y
+    torch.cuda.empty_cache()
+
+
 def test_empty_prefill_is_noop(M, big):
     _, dl = big
     announce("moe_prefill T=0")
