@@ -80,7 +80,6 @@ MOE_DEV uint32_t mul_pack_f16x2(float w, float lo, float hi) {
       : "v"(w), "v"(lo), "v"(hi));
   return r;
 }
-MOE_DEV uint16_t f32_to_f16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 
 MOE_DEV float f16lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w)[0]; }
 MOE_DEV float f16hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w)[1]; }
@@ -102,29 +101,12 @@ MOE_DEV void unpack8(uint32_t w, float q[8]) {
   q[7] = (float)(hi >> 24);
 }
 
-// Dequantise 8 codes to 4 packed fp16 pairs: w = fp16_rne(fma(s, q, b)).
-MOE_DEV uint4 dequant8_f16(uint32_t w, float s, float b) {
-  float q[8];
-  unpack8(w, q);
-  uint4 r;
-  r.x = pack_f16x2(__builtin_fmaf(s, q[0], b), __builtin_fmaf(s, q[1], b));
-  r.y = pack_f16x2(__builtin_fmaf(s, q[2], b), __builtin_fmaf(s, q[3], b));
-  r.z = pack_f16x2(__builtin_fmaf(s, q[4], b), __builtin_fmaf(s, q[5], b));
-  r.w = pack_f16x2(__builtin_fmaf(s, q[6], b), __builtin_fmaf(s, q[7], b));
-  return r;
-}
-
 // K order inside every 8-element chunk of the fp16 operand rows of the grouped GEMMs
 // (the copy of x and h): position p holds element kChunkOrder[p] = 0,4,1,5,2,6,3,7. It
-// is the order in which dequant8_pk produces the eight weights of one 32-bit code word,
+// is the order in which dequant8_pk_q produces the eight weights of one 32-bit code word,
 // so A and B operands agree without shuffles. kChunkPos is the inverse map.
 __device__ constexpr int kChunkPos[8] = {0, 2, 4, 6, 1, 3, 5, 7};
 
-// Eight codes of one 32-bit word to fp16 weights w = fp16_rne(s * q + b), packed math:
-// a nibble pair OR-ed into 0x6400 is the fp16 pair (1024 + q_lo, 1024 + q_hi); subtracting
-// 1024 is exact, and one fused multiply-add rounds s*q + b once. Output pairs are
-// (q0,q4), (q1,q5), (q2,q6), (q3,q7). s2 / b2 hold the scale / bias twice; both must be
-// representable in fp16 (true for bf16 values in [2^-14, 65504]).
 MOE_DEV uint32_t and_or(uint32_t v, uint32_t mask, uint32_t bits) {
   // (v & mask) | bits in one v_and_or_b32 (the compiler emits two instructions here)
   uint32_t r;
@@ -132,11 +114,16 @@ MOE_DEV uint32_t and_or(uint32_t v, uint32_t mask, uint32_t bits) {
   return r;
 }
 
-// The same eight weights with one shift instead of three: the nibbles at bits 4..7 (and
-// 20..23) are masked in place, giving the fp16 pair (1024 + 16 q_lo, 1024 + 16 q_hi), and
-// are scaled by s / 16 (s2q) instead of s. 16 q (s / 16) equals q s exactly when s / 16 is
-// exact in fp16, which holds for bf16 scales with |s| >= 2^-13; the single rounding of the
-// fused multiply-add then gives the same bits as dequant8_pk.
+// Eight codes of one 32-bit word to fp16 weights w = fp16_rne(s * q + b), packed math: a
+// nibble pair OR-ed into 0x6400 is the fp16 pair (1024 + q_lo, 1024 + q_hi); subtracting
+// 1024 is exact, and one fused multiply-add rounds s*q + b once. Output pairs are
+// (q0,q4), (q1,q5), (q2,q6), (q3,q7). One shift serves the word: the nibbles at bits 0..3
+// and 16..19 (of w and of w >> 8) are taken as they are, those at bits 4..7 and 20..23 are
+// masked in place, giving (1024 + 16 q_lo, 1024 + 16 q_hi), and scaled by s / 16 (s2q)
+// instead of s. 16 q (s / 16) equals q s exactly when s / 16 is exact in fp16, which holds
+// for bf16 scales with |s| >= 2^-13, so every weight gets the same single rounding as with a
+// shift per nibble. s2 / s2q / b2 hold their value twice; scale and bias must be
+// representable in fp16 (true for bf16 values in [2^-14, 65504]).
 MOE_DEV uint4 dequant8_pk_q(uint32_t w, f16x2_t s2, f16x2_t s2q, f16x2_t b2) {
   constexpr uint32_t kLo = 0x000F000Fu, kHi = 0x00F000F0u, kMagic = 0x64006400u;
   const f16x2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
@@ -152,23 +139,6 @@ MOE_DEV uint4 dequant8_pk_q(uint32_t w, f16x2_t s2, f16x2_t s2q, f16x2_t b2) {
                                          __builtin_bit_cast(f16x2_t, t2) - k1024, s2, b2));
   r.w = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(
                                          __builtin_bit_cast(f16x2_t, t3) - k1024, s2q, b2));
-  return r;
-}
-
-MOE_DEV uint4 dequant8_pk(uint32_t w, f16x2_t s2, f16x2_t b2) {
-  constexpr uint32_t kMask = 0x000F000Fu, kMagic = 0x64006400u;
-  const f16x2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
-  const uint32_t t0 = and_or(w, kMask, kMagic), t1 = and_or(w >> 4, kMask, kMagic);
-  const uint32_t t2 = and_or(w >> 8, kMask, kMagic), t3 = and_or(w >> 12, kMask, kMagic);
-  uint4 r;
-  r.x = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(
-                                         __builtin_bit_cast(f16x2_t, t0) - k1024, s2, b2));
-  r.y = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(
-                                         __builtin_bit_cast(f16x2_t, t1) - k1024, s2, b2));
-  r.z = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(
-                                         __builtin_bit_cast(f16x2_t, t2) - k1024, s2, b2));
-  r.w = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(
-                                         __builtin_bit_cast(f16x2_t, t3) - k1024, s2, b2));
   return r;
 }
 
@@ -280,14 +250,6 @@ MOE_DEV float wave_sum_dpp(float v) {
     return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
   });
   return __uint_as_float(r);
-}
-
-MOE_DEV uint32_t wave_max_u32(uint32_t v) {
-  return wave_reduce_u32(v, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
-}
-
-MOE_DEV uint32_t wave_min_u32(uint32_t v) {
-  return wave_reduce_u32(v, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
 }
 
 // Sum over a workgroup of 512 threads of each thread's fp64 partial, in one fixed order:
