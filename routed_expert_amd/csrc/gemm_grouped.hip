@@ -172,7 +172,10 @@ MOE_DEV void grouped_tile(const GroupedArgs &a, uint8_t *smem, int e, int row0, 
   // loads only add). The step body has no branches: one scheduling region from the DMA
   // issue to the mid-step wait, in which the dequantisation interleaves with the MFMAs.
   // M0 holds the wave-uniform LDS byte address; lane l's data lands at M0 + l * size.
-  // The s_nop covers the wait states a load that reads M0 needs after M0 is written.
+  // The s_nop covers the wait states a load that reads M0 needs after M0 is written. M0 is
+  // listed as clobbered, and hipcc warns that it does not preserve a reserved register across
+  // such a statement: nothing else in these kernels uses M0 (in the generated code every M0
+  // write is one of these statements and only these loads read it).
   const uint32_t smem_lds = (uint32_t)(uintptr_t)smem;
 #define MOE_DMA16(voff, sbase, lds)                                                     \
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %0, %1"          \
